@@ -1,0 +1,28 @@
+"""Writes the stored expected values under tests/golden/ from the CPU oracle only.
+
+    python tests/golden/make_golden.py
+
+nf4_codebook.txt: the 16 float32 NF4 levels (index, hex, decimal) of the oracle's derivation
+(QLoRA construction from standard-normal quantiles; the Unsloth pages name NF4 in the
+v0.1.463-beta release article, "About the Unsloth Project", but print no values).
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+from oracle import nf4  # noqa: E402
+
+
+def main():
+    c = nf4.codebook()
+    with open(os.path.join(HERE, "nf4_codebook.txt"), "w") as f:
+        f.write("# NF4 levels, float32, written by tests/golden/make_golden.py from oracle/nf4.py\n")
+        f.write("# index  hex  decimal\n")
+        for i, v in enumerate(c):
+            f.write(f"{i:2d} {float(v).hex()} {float(v):.9g}\n")
+
+
+if __name__ == "__main__":
+    main()

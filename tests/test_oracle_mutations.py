@@ -1,0 +1,206 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case below patches one plausible mistake into the oracle (a dropped term, a wrong sign, a
+wrong operand or index, a wrong rounding or nibble order, a wrong codebook constant) and runs the
+pin tests of test_oracle_codebook/quant/gemm against it; at least one pin must fail. The patches
+live only inside this test (pytest's monkeypatch undoes them).
+"""
+import numpy as np
+import pytest
+
+from oracle import nf4, qlora
+from tests import test_oracle_codebook as tc
+from tests import test_oracle_gemm as tg
+from tests import test_oracle_quant as tq
+
+PINS = [
+    tc.test_codebook_structure,
+    tc.test_levels_sit_at_evenly_spaced_probabilities,
+    tc.test_codebook_golden_file,
+    tc.test_bf16_rounding_matches_torch,
+    tq.test_encode_brute_force_near_midpoints,
+    tq.test_encode_brute_force_random,
+    tq.test_encode_ties_go_to_lower_code,
+    tq.test_special_blocks,
+    tq.test_pack_known_pattern,
+    tq.test_round_trip_exact_on_codebook_points,
+    tq.test_double_quant_definition_and_bound,
+    tq.test_dequantize_definition,
+    lambda: tg.test_forward_backward_brute_force(3, 64, 5, 2, 0, 2.0),
+    lambda: tg.test_forward_backward_brute_force(4, 128, 3, 3, 256, 0.5),
+    lambda: tg.test_adjoint_identities(1),
+    tg.test_finite_differences_are_exact_by_linearity,
+    tg.test_rank_zero_equals_b_zero_equals_plain_gemm,
+    tg.test_zero_base_leaves_lora_term,
+    tg.test_identity_input_returns_dequantised_weight,
+]
+
+_fwd, _bwd = qlora.forward, qlora.backward
+_f64 = qlora._f64
+
+
+def fwd_no_lora(X, Wd, A, B, s):
+    Y, T = _fwd(X, Wd, A, B, s)
+    return Y - s * (T @ _f64(B).T), T
+
+
+def fwd_wrong_sign(X, Wd, A, B, s):
+    Y, T = _fwd(X, Wd, A, B, s)
+    return Y - 2 * s * (T @ _f64(B).T), T
+
+
+def fwd_s_twice(X, Wd, A, B, s):
+    return _fwd(X, Wd, A, B, s * s) if s != 1 else _fwd(X, Wd, A, B, 2 * s)
+
+
+def fwd_reversed_adapter_rows(X, Wd, A, B, s):
+    return _fwd(X, Wd, _f64(A)[::-1], B, s)
+
+
+def bwd_dx_no_lora(dY, X, Wd, A, B, s):
+    dX, dA, dB = _bwd(dY, X, Wd, A, B, s)
+    return dX - s * (_f64(dY) @ _f64(B)) @ _f64(A), dA, dB
+
+
+def bwd_da_no_s(dY, X, Wd, A, B, s):
+    dX, dA, dB = _bwd(dY, X, Wd, A, B, s)
+    return dX, dA / s, dB
+
+
+def bwd_db_uses_u(dY, X, Wd, A, B, s):
+    dX, dA, _ = _bwd(dY, X, Wd, A, B, s)
+    return dX, dA, s * (_f64(dY).T @ (_f64(dY) @ _f64(B)))
+
+
+def bwd_da_uses_t(dY, X, Wd, A, B, s):
+    dX, _, dB = _bwd(dY, X, Wd, A, B, s)
+    return dX, s * ((_f64(X) @ _f64(A).T).T @ _f64(X)), dB
+
+
+def bwd_dx_transposed_weight_rows(dY, X, Wd, A, B, s):
+    dX, dA, dB = _bwd(dY, X, _f64(Wd)[::-1], A, B, s)
+    return dX, dA, dB
+
+
+_encode = nf4.encode
+_double_quant = nf4.double_quant
+_levels = nf4.nf4_levels_f64
+
+
+def encode_ties_up(w, absmax, chunk=1 << 20):
+    out = _encode(w, absmax, chunk)
+    w = np.asarray(w, np.float32).reshape(-1)
+    a = np.repeat(np.asarray(absmax, np.float32), 64)
+    c = nf4._CODEBOOK.astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        v = (w / np.where(a == 0, 1, a)).astype(np.float32).astype(np.float64)
+    for i in range(15):
+        tie = (v - c[i]) == (c[i + 1] - v)
+        out[tie & (a != 0)] = i + 1
+    return out
+
+
+def encode_rne_midpoints(w, absmax, chunk=1 << 20):
+    w = np.asarray(w, np.float32).reshape(-1)
+    a = np.repeat(np.asarray(absmax, np.float32), 64)
+    c = nf4._CODEBOOK.astype(np.float64)
+    mids = np.array([(c[i] + c[i + 1]) / 2 for i in range(15)]).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        v = (w / np.where(a == 0, 1, a)).astype(np.float32)
+    out = (v[:, None] > mids[None, :]).sum(axis=1).astype(np.uint8)
+    out[a == 0] = 7
+    return out
+
+
+def pack_swapped(codes):
+    c = np.asarray(codes, np.uint8).reshape(-1)
+    return ((c[1::2] << 4) | c[0::2]).astype(np.uint8)
+
+
+def unpack_swapped(packed):
+    p = np.asarray(packed, np.uint8).reshape(-1)
+    out = np.empty(p.size * 2, np.uint8)
+    out[1::2] = p >> 4
+    out[0::2] = p & 0x0F
+    return out
+
+
+def dq_by_128(absmax, dq_block):
+    a = np.asarray(absmax, np.float32).reshape(-1)
+    runs = (a.size + dq_block - 1) // dq_block
+    q = np.zeros(a.size, np.int8)
+    S = np.zeros(runs, np.float32)
+    for j in range(runs):
+        seg = a[j * dq_block:(j + 1) * dq_block]
+        S[j] = np.float32(seg.max() / np.float32(128))
+        if S[j]:
+            q[j * dq_block:(j + 1) * dq_block] = np.clip(np.rint(seg / S[j]), 0, 127)
+    return q, S
+
+
+def dq_truncating(absmax, dq_block):
+    q, S = _double_quant(absmax, dq_block)
+    a = np.asarray(absmax, np.float32).reshape(-1)
+    Sx = np.repeat(S, dq_block)[: a.size]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = np.where(Sx > 0, np.floor((a / np.where(Sx > 0, Sx, 1)).astype(np.float32)), 0)
+    return np.clip(t, 0, 127).astype(np.int8), S
+
+
+def bf16_truncate(x):
+    return (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def deq_code_off_by_one(wq):
+    c = nf4._CODEBOOK[np.minimum(nf4.unpack(wq.codes) + 1, 15)]
+    a = np.repeat(nf4.decode_absmax(wq), 64)
+    return (c * a).astype(np.float32).reshape(wq.n, wq.k)
+
+
+def decode_absmax_next_run(wq):
+    if wq.dq_block == 0:
+        return np.asarray(wq.absmax, np.float32)
+    q = np.asarray(wq.absmax, np.int8).astype(np.float32)
+    S = np.repeat(np.roll(wq.scale, 1), wq.dq_block)[: q.size]
+    return (q * S).astype(np.float32)
+
+
+MUTATIONS = {
+    "fwd drops the LoRA term": [(qlora, "forward", fwd_no_lora)],
+    "fwd flips the LoRA sign": [(qlora, "forward", fwd_wrong_sign)],
+    "fwd applies s twice": [(qlora, "forward", fwd_s_twice)],
+    "fwd reverses adapter rows": [(qlora, "forward", fwd_reversed_adapter_rows)],
+    "bwd dX drops the LoRA term": [(qlora, "backward", bwd_dx_no_lora)],
+    "bwd dA misses s": [(qlora, "backward", bwd_da_no_s)],
+    "bwd dB uses U instead of T": [(qlora, "backward", bwd_db_uses_u)],
+    "bwd dA uses T instead of U": [(qlora, "backward", bwd_da_uses_t)],
+    "bwd dX reads weight rows reversed": [(qlora, "backward", bwd_dx_transposed_weight_rows)],
+    "encode ties go up": [(nf4, "encode", encode_ties_up)],
+    "encode by rounded-to-nearest midpoints": [(nf4, "encode", encode_rne_midpoints)],
+    "nibble order swapped": [(nf4, "pack", pack_swapped), (nf4, "unpack", unpack_swapped)],
+    "double quant divides by 128": [(nf4, "double_quant", dq_by_128)],
+    "double quant truncates": [(nf4, "double_quant", dq_truncating)],
+    "bf16 truncates": [(nf4, "bf16_bits", bf16_truncate)],
+    "dequant code off by one": [(nf4, "dequantize_f32", deq_code_off_by_one)],
+    "dequant uses the wrong run's scale": [(nf4, "decode_absmax", decode_absmax_next_run)],
+    "codebook delta wrong": [(nf4, "DELTA", 1.0 - 1.0 / 32.0)],
+    "codebook sides swapped": [(nf4, "nf4_levels_f64", lambda quantile=nf4.normal_quantile:
+                                -_levels(quantile)[::-1])],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    for mod, attr, val in MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, val)
+    if any(attr in ("DELTA", "nf4_levels_f64") for _, attr, _ in MUTATIONS[name]):
+        monkeypatch.setattr(nf4, "_CODEBOOK", nf4.codebook())
+        monkeypatch.setattr(tq, "C", nf4.codebook())
+        monkeypatch.setattr(tg, "C", nf4.codebook())
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError as e:
+            caught.append((getattr(pin, "__name__", "pin"), type(e).__name__))
+    assert caught, f"no pin catches: {name}"

@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the QLoRA linear layer, shared by the tests and the benchmark.
+
+This module only draws random numbers and rounds them to bf16 storage. It holds none of the
+layer's arithmetic (no quantisation, no products), so the CPU oracle and the HIP path can both
+take their inputs from here without sharing any of the computation they are compared on.
+
+The five workloads are Llama-class projection shapes of a QLoRA fine-tune (a frozen NF4 base
+weight, bf16 LoRA adapters A [r,K] and B [N,r], Hu et al.'s Delta W = B A at rank r as restated on
+the Unsloth pages' "About the Unsloth Project" section):
+
+  small   M=64    K=256    N=256    r=8   s=2   absmax fp32         fwd+bwd
+  q_proj  M=4096  K=4096   N=4096   r=16  s=2   absmax int8/256     fwd
+  mlp_up  M=8192  K=4096   N=11008  r=64  s=0.5 absmax int8/256     fwd+bwd
+  decode  M=16    K=8192   N=28672  r=16  s=2   absmax int8/256     fwd (weight-stream bound)
+  down    M=16384 K=14336  N=4096   r=32  s=1   absmax int8/256     fwd+bwd
+
+Distributions (std is the standard deviation of a normal): X ~ N(0,1); W ~ N(0,0.02) (0.015 for
+decode); A ~ N(0, 1/K) read as variance 1/K, i.e. std K**-0.5; B ~ N(0,0.01); dY ~ N(0,1)
+(N(0,1e-2) for down). Workloads that name no A/B distribution use the mlp_up one.
+
+Every tensor is drawn as float32 standard normals from numpy's PCG64 generator with
+seed = 1000*cfg + t (cfg 1..5 in the order above; t: X=1, W=2, A=3, B=4, dY=5), scaled by its
+std in float32 and rounded to bf16 (round-to-nearest-even, by torch's conversion).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Tuple
+
+import numpy as np
+import torch
+
+TENSOR_IDS = {"X": 1, "W": 2, "A": 3, "B": 4, "dY": 5}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # 1..5, used in the seeds
+    M: int
+    K: int
+    N: int
+    r: int
+    s: float
+    dq_block: int       # 0: fp32 absmax; 256: int8 absmax + fp32 scale per 256 absmax values
+    std_x: float
+    std_w: float
+    std_b: float
+    std_dy: float
+    backward: bool
+
+    @property
+    def std_a(self) -> float:
+        return self.K ** -0.5
+
+    def std(self, tensor: str) -> float:
+        return {"X": self.std_x, "W": self.std_w, "A": self.std_a, "B": self.std_b,
+                "dY": self.std_dy}[tensor]
+
+    def shape(self, tensor: str) -> Tuple[int, int]:
+        return {"X": (self.M, self.K), "W": (self.N, self.K), "A": (self.r, self.K),
+                "B": (self.N, self.r), "dY": (self.M, self.N)}[tensor]
+
+    def seed(self, tensor: str) -> int:
+        return 1000 * self.index + TENSOR_IDS[tensor]
+
+    def fwd_flops(self) -> int:
+        M, K, N, r = self.M, self.K, self.N, self.r
+        return 2 * M * N * K + 2 * M * K * r + 2 * M * N * r
+
+    def bwd_flops(self) -> int:
+        M, K, N, r = self.M, self.K, self.N, self.r
+        # U = dY B, dX = dY deq(W) + s U A, dB = s dY^T T, dA = s U^T X
+        return 2 * M * N * r + (2 * M * N * K + 2 * M * r * K) + 2 * N * M * r + 2 * r * M * K
+
+    def weight_stream_bytes(self) -> int:
+        nblk = self.N * self.K // 64
+        codes = self.N * self.K // 2
+        if self.dq_block:
+            return codes + nblk + 4 * ((nblk + self.dq_block - 1) // self.dq_block)
+        return codes + 4 * nblk
+
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    Workload("small", 1, 64, 256, 256, 8, 2.0, 0, 1.0, 0.02, 0.01, 1.0, True),
+    Workload("q_proj", 2, 4096, 4096, 4096, 16, 2.0, 256, 1.0, 0.02, 0.01, 1.0, False),
+    Workload("mlp_up", 3, 8192, 4096, 11008, 64, 0.5, 256, 1.0, 0.02, 0.01, 1.0, True),
+    Workload("decode", 4, 16, 8192, 28672, 16, 2.0, 256, 1.0, 0.015, 0.01, 1.0, False),
+    Workload("down", 5, 16384, 14336, 4096, 32, 1.0, 256, 1.0, 0.02, 0.01, 1e-2, True),
+]}
+
+
+def normal_bf16(seed: int, shape, std: float) -> torch.Tensor:
+    """float32 standard normals from PCG64(seed), times std (float32), rounded to bf16 (CPU)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+    a *= np.float32(std)
+    return torch.from_numpy(a).to(torch.bfloat16)
+
+
+def uniform_f32(seed: int, shape, lo: float, hi: float) -> torch.Tensor:
+    """float32 uniforms on [lo, hi) from PCG64(seed) (CPU)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return torch.from_numpy(rng.uniform(lo, hi, size=tuple(shape)).astype(np.float32))
+
+
+def tensor(w: Workload, name: str, rows: int | None = None) -> torch.Tensor:
+    """The named input of workload w as a bf16 CPU tensor.
+
+    rows (X and dY only) keeps just the first `rows` rows of the same draw, which is how the
+    bounded CPU samples of the large workloads are taken.
+    """
+    t = normal_bf16(w.seed(name), w.shape(name), w.std(name))
+    if rows is not None:
+        t = t[:rows].contiguous()
+    return t
