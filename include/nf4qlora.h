@@ -1,0 +1,152 @@
+/*
+ * nf4qlora.h -- C ABI of the fused NF4 QLoRA linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the QLoRA linear layer of Unsloth-style fine-tuning: a frozen base weight W [n,k]
+ * stored as 4-bit NormalFloat (NF4) codes with per-block absmax constants that may themselves be
+ * quantised ("double quantisation"), and trainable bf16 LoRA adapters A [r,k], B [n,r] with
+ * Delta W = B A at rank r [Unsloth v0.1.463-beta release article, "About the Unsloth Project";
+ * v0.1.47-beta article, section on lowering the fine-tuning barrier]. NF4 dequantisation, the
+ * matmul and the LoRA correction are computed together, without materialising a dequantised
+ * copy of W ["Inside Unsloth" book listing, "What You'll Learn", "LoRA and QLoRA"; pyshine
+ * Unsloth code tour, "Why You Need This" and "Detailed view"]:
+ *
+ *     T  = X A^T                 Y  = X deq(W)^T + s T B^T
+ *     U  = dY B                  dX = dY deq(W) + s U A
+ *     dA = s U^T X               dB = s dY^T T              (W is frozen: no dW)
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers, owned and allocated by the caller; the library never
+ *     allocates or frees device memory. Matrices are dense row-major. bf16 is IEEE bfloat16
+ *     stored as 16-bit words. Base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls are asynchronous on it; the
+ *     outputs are ready once the stream has reached the call.
+ *   - Every argument is validated on the host before anything is launched, so a call that
+ *     returns an error has launched nothing. A launch failure returns NF4_EHIP. Faults inside a
+ *     kernel surface at the caller's next synchronisation. The library never aborts.
+ *   - nf4_last_error() returns a thread-local message describing the last non-OK status.
+ *   - Inputs must be finite; results for NaN or Inf inputs are not specified.
+ *   - Results are deterministic: the same inputs give bitwise-identical outputs on every call.
+ *
+ * NF4 format (the pages name NF4 and double quantisation but fix no constants; these are the
+ * QLoRA constructions):
+ *   - levels: the 16 NF4 levels from standard-normal quantiles (7 negative, an exact 0,
+ *     8 positive, ends -1 and +1), float32; nf4_codebook() returns them.
+ *   - blocks of 64 consecutive elements of the row-major W (k % 64 == 0, so a block never
+ *     straddles a row); block constant a = max |w| over the block (float32).
+ *   - code = index of the level nearest to fl32(w / a), ties to the lower index; an all-zero
+ *     block has a = 0 and every code 7 (the exact zero level).
+ *   - packing: byte i of `codes` holds element 2i in bits 7..4 and element 2i+1 in bits 3..0.
+ *   - dq_block == 0: absmax is float[n*k/64] holding a.
+ *     dq_block == 256: absmax is int8_t[n*k/64] and absmax_scale is float[ceil(n*k/64/256)];
+ *     run j of 256 consecutive block constants (flattened order; the last run may be short)
+ *     has S_j = fl32(max a / 127) and q = rint(fl32(a / S_j)) in [0,127] (S_j == 0 gives q = 0);
+ *     blocks decode with a' = fl32(q * S_j). Codes are always taken against the exact a.
+ *   - dequantised element: w' = fl32(level[code] * a'); the GEMMs consume w' rounded to bf16
+ *     (round-to-nearest-even) and accumulate in float32.
+ */
+#ifndef NF4QLORA_H
+#define NF4QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NF4_OK = 0,
+  NF4_EINVAL = -1,       /* a pointer, size, alignment or workspace argument is invalid */
+  NF4_EUNSUPPORTED = -2, /* a well-formed request outside what the library implements */
+  NF4_EHIP = -3          /* the HIP runtime reported an error at launch */
+} nf4_status;
+
+typedef enum { NF4_BF16 = 0, NF4_F32 = 1 } nf4_dtype;
+
+/* An NF4-quantised weight W [n,k]. The struct itself is a host object; its pointers are device
+ * pointers owned by the caller. */
+typedef struct {
+  int64_t n, k;         /* logical shape of W; n >= 1, k >= 64, k % 64 == 0                  */
+  int32_t block;        /* absmax block length: must be 64                                   */
+  int32_t dq_block;     /* 0 (float32 absmax) or 256 (int8 absmax + float32 scale per run)   */
+  uint8_t *codes;       /* [n*k/2] packed codes                                              */
+  void *absmax;         /* float[n*k/64] if dq_block == 0, else int8_t[n*k/64]               */
+  float *absmax_scale;  /* float[ceil(n*k/64/dq_block)] if dq_block > 0, else ignored         */
+} nf4_tensor;
+
+/* Quantise W (bf16 or float32, [q->n, q->k]) into the buffers of *q, as described above.
+ * One kernel launch; no workspace. Bit-exact: the codes, absmax and scales equal those of the
+ * definition for every finite input.
+ * Errors: NF4_EINVAL for a NULL pointer, a misaligned pointer or n < 1;
+ *         NF4_EUNSUPPORTED for k % 64 != 0, block != 64, dq_block not in {0, 256}, or
+ *         n*k >= 2^40. */
+int nf4_quantize(const void *w, int w_dtype, const nf4_tensor *q, void *stream);
+
+/* Write deq(W) to out [n,k] as float32 (w', exact) or bf16 (w' rounded to nearest-even).
+ * Diagnostic and ablation path; the fused calls never materialise it.
+ * Errors: as nf4_quantize, plus NF4_EINVAL for an unknown out_dtype. */
+int nf4_dequantize(const nf4_tensor *q, void *out, int out_dtype, void *stream);
+
+/* Host-only: copy the 16 float32 NF4 levels (ascending) into levels[16] and, when thresholds is
+ * not NULL, the 15 float32 decision thresholds into thresholds[15] (thresholds[i] is the largest
+ * float32 not above the midpoint of levels i and i+1; code = number of thresholds below v).
+ * No device access. Returns NF4_EINVAL when levels is NULL. */
+int nf4_codebook(float *levels, float *thresholds);
+
+/* Bytes of device workspace qlora_fwd needs for these sizes (0 when r == 0). */
+size_t qlora_fwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
+
+/* Forward of the QLoRA layer:  T = bf16(X A^T),  Y = bf16(X deq(W)^T + s T B^T).
+ *   X  bf16 [m, k]   input activations                     (k == W->k)
+ *   W  NF4 [n, k]    frozen base weight
+ *   A  bf16 [r, k]   LoRA down-projection; B bf16 [n, r] LoRA up-projection (NULL when r == 0)
+ *   s  LoRA scaling (lora_alpha / r by the usual convention)
+ *   Y  bf16 [m, n]   output
+ *   T  bf16 [m, r]   output: X A^T, kept for qlora_bwd (NULL when r == 0)
+ *   ws workspace of at least qlora_fwd_workspace_bytes(m, n, k, r) bytes (NULL when that is 0)
+ * The LoRA term uses T as rounded to bf16 and s*B rounded to bf16 (exact when s is a power of
+ * two). Requires m >= 1, n % 8 == 0, 0 <= r <= 128.
+ * Errors: NF4_EINVAL for NULL/misaligned pointers, m < 1, r out of range, a short workspace;
+ *         NF4_EUNSUPPORTED for n % 8 != 0 and the NF4 format limits of nf4_quantize. */
+int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
+              int32_t r, float s, void *Y, void *T, void *ws, size_t ws_bytes, void *stream);
+
+/* The two launches qlora_fwd is made of, for callers that already hold T or that time them:
+ *
+ * qlora_lora_down: T = bf16(X A^T), X bf16 [m, k], A bf16 [r, k], T bf16 [m, r], 1 <= r <= 128.
+ * ws: at least qlora_fwd_workspace_bytes(m, n, k, r) bytes (float partial sums over k).
+ * Errors: NF4_EINVAL for NULL/misaligned pointers, m < 1, r out of range, a short workspace;
+ *         NF4_EUNSUPPORTED for k not a positive multiple of 64. */
+int qlora_lora_down(const void *X, int64_t m, int64_t k, const void *A, int32_t r, void *T,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* qlora_fwd_fused: Y = bf16(X deq(W)^T + s T B^T) in ONE kernel launch: the NF4 weight is decoded
+ * on the fly inside the GEMM and the rank-r term runs as extra reduction steps of the same output
+ * tile. T bf16 [m, r] as produced by qlora_lora_down (NULL when r == 0). No workspace.
+ * Errors: as qlora_fwd. */
+int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T, const void *B,
+                    int32_t r, float s, void *Y, void *stream);
+
+/* Bytes of device workspace qlora_bwd needs for these sizes. */
+size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
+
+/* Backward of the QLoRA layer, given the upstream gradient dY bf16 [m, n] and T from qlora_fwd:
+ *   U  = bf16(dY B)                               (kept in the workspace)
+ *   dX = bf16(dY deq(W) + s U A)      bf16 [m, k]  (skipped when dX is NULL)
+ *   dA = bf16(s U^T X)                bf16 [r, k]
+ *   dB = bf16(s dY^T T)               bf16 [n, r]
+ * Sums over m are taken in float32 in a fixed order (deterministic). With r == 0, A, B, T, dA
+ * and dB are ignored and only dX is produced.
+ * Errors: as qlora_fwd, plus NF4_EINVAL when ws is smaller than qlora_bwd_workspace_bytes. */
+int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, const void *A,
+              const void *B, int32_t r, float s, const void *T, void *dX, void *dA, void *dB,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+const char *nf4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4QLORA_H */

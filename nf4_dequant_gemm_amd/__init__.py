@@ -1,0 +1,258 @@
+"""Python binding of libnf4qlora, the fused NF4 QLoRA linear layer for MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of the C-ABI library
+(include/nf4qlora.h). torch provides device memory and the current stream. There is no CPU or
+torch fallback: if the library is not built, every call raises.
+
+    q = nf4_quantize(W_bf16, dq_block=256)          # NF4Tensor (frozen base weight)
+    Y, T = qlora_fwd(X, q, A, B, s)                  # Y = X deq(W)^T + s (X A^T) B^T
+    dX, dA, dB = qlora_bwd(dY, X, q, A, B, s, T)
+    Y = QLoRALinearFunction.apply(X, q, A, B, s)     # autograd: gradients for X, A, B
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnf4qlora.so")
+_lib = None
+
+NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, -1, -2, -3
+NF4_BF16, NF4_F32 = 0, 1
+
+EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
+            "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
+            "qlora_bwd", "nf4_last_error")
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+class _NF4TensorC(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("block", ctypes.c_int32),
+                ("dq_block", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("absmax", ctypes.c_void_p), ("absmax_scale", ctypes.c_void_p)]
+
+
+def library() -> ctypes.CDLL:
+    """Load libnf4qlora.so (built by nf4_dequant_gemm_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run python -m nf4_dequant_gemm_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    P = ctypes.POINTER(_NF4TensorC)
+    sig = {
+        "nf4_quantize": (ctypes.c_int, [vp, ctypes.c_int, P, vp]),
+        "nf4_dequantize": (ctypes.c_int, [P, vp, ctypes.c_int, vp]),
+        "nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
+        "qlora_fwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "qlora_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_lora_down": (ctypes.c_int, [vp, i64, i64, vp, i32, vp, vp, sz, vp]),
+        "qlora_fwd_fused": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
+        "qlora_bwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "qlora_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
+        "nf4_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != NF4_OK:
+        raise NF4Error(status, library().nf4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+@dataclasses.dataclass
+class NF4Tensor:
+    """An NF4-quantised weight [n, k]: packed codes, block constants and (double quant) scales."""
+    n: int
+    k: int
+    dq_block: int
+    codes: torch.Tensor                   # uint8 [n*k/2]
+    absmax: torch.Tensor                  # float32 or int8 [n*k/64]
+    scale: Optional[torch.Tensor] = None  # float32 [ceil(n*k/64/256)] when dq_block
+
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
+    def c_struct(self) -> _NF4TensorC:
+        return _NF4TensorC(self.n, self.k, 64, self.dq_block, self.codes.data_ptr(),
+                           self.absmax.data_ptr(),
+                           self.scale.data_ptr() if self.scale is not None else None)
+
+    @staticmethod
+    def empty(n: int, k: int, dq_block: int, device) -> "NF4Tensor":
+        nblk = n * k // 64
+        codes = torch.empty(n * k // 2, dtype=torch.uint8, device=device)
+        if dq_block:
+            absmax = torch.empty(nblk, dtype=torch.int8, device=device)
+            scale = torch.empty((nblk + dq_block - 1) // dq_block, dtype=torch.float32, device=device)
+        else:
+            absmax = torch.empty(nblk, dtype=torch.float32, device=device)
+            scale = None
+        return NF4Tensor(n, k, dq_block, codes, absmax, scale)
+
+
+def nf4_codebook():
+    """(levels[16], thresholds[15]) as float lists, read from the library (host only)."""
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(library().nf4_codebook(lv, th))
+    return list(lv), list(th)
+
+
+def nf4_quantize(w: torch.Tensor, dq_block: int = 256) -> NF4Tensor:
+    """Quantise a bf16 or float32 device weight [n, k] to NF4 (blocks of 64)."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [n, k]")
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be bfloat16 or float32")
+    _need(w, "w", w.dtype)
+    n, k = w.shape
+    if k % 64:
+        raise NF4Error(NF4_EUNSUPPORTED, "k must be a multiple of 64")
+    q = NF4Tensor.empty(n, k, dq_block, w.device)
+    st = q.c_struct()
+    _check(library().nf4_quantize(_ptr(w), NF4_F32 if w.dtype == torch.float32 else NF4_BF16,
+                                  ctypes.byref(st), _stream(w.device)))
+    return q
+
+
+def nf4_dequantize(q: NF4Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+    """deq(W) [n, k] as bfloat16 (rounded) or float32 (exact)."""
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be bfloat16 or float32")
+    out = torch.empty(q.n, q.k, dtype=dtype, device=q.device)
+    st = q.c_struct()
+    _check(library().nf4_dequantize(ctypes.byref(st), _ptr(out),
+                                    NF4_F32 if dtype == torch.float32 else NF4_BF16,
+                                    _stream(q.device)))
+    return out
+
+
+def qlora_fwd(X: torch.Tensor, q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+              s: float) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """(Y, T): Y = X deq(W)^T + s T B^T with T = X A^T (T is None when r == 0)."""
+    m = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, q.k))
+        _need(B, "B", torch.bfloat16, (q.n, r))
+    Y = torch.empty(m, q.n, dtype=torch.bfloat16, device=X.device)
+    T = torch.empty(m, r, dtype=torch.bfloat16, device=X.device) if r else None
+    lib = library()
+    wsb = lib.qlora_fwd_workspace_bytes(m, q.n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=X.device)
+    st = q.c_struct()
+    _check(lib.qlora_fwd(_ptr(X), m, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
+                         _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    return Y, T
+
+
+def qlora_lora_down(X: torch.Tensor, A: torch.Tensor) -> torch.Tensor:
+    """T = X A^T (bf16 [m, r])."""
+    m, k = X.shape
+    r = A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, k))
+    _need(A, "A", torch.bfloat16, (r, k))
+    T = torch.empty(m, r, dtype=torch.bfloat16, device=X.device)
+    lib = library()
+    wsb = lib.qlora_fwd_workspace_bytes(m, 0, k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=X.device)
+    _check(lib.qlora_lora_down(_ptr(X), m, k, _ptr(A), r, _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    return T
+
+
+def qlora_fwd_fused(X: torch.Tensor, q: NF4Tensor, T: Optional[torch.Tensor],
+                    B: Optional[torch.Tensor], s: float) -> torch.Tensor:
+    """Y = X deq(W)^T + s T B^T in one kernel launch, given T = X A^T."""
+    m = X.shape[0]
+    r = 0 if T is None else T.shape[1]
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    if r:
+        _need(T, "T", torch.bfloat16, (m, r))
+        _need(B, "B", torch.bfloat16, (q.n, r))
+    Y = torch.empty(m, q.n, dtype=torch.bfloat16, device=X.device)
+    st = q.c_struct()
+    _check(library().qlora_fwd_fused(_ptr(X), m, ctypes.byref(st), _ptr(T), _ptr(B), r, float(s),
+                                     _ptr(Y), _stream(X.device)))
+    return Y
+
+
+def qlora_bwd(dY: torch.Tensor, X: torch.Tensor, q: NF4Tensor, A: Optional[torch.Tensor],
+              B: Optional[torch.Tensor], s: float, T: Optional[torch.Tensor], need_dx: bool = True):
+    """(dX, dA, dB) of the layer; dX is None when need_dx is False, dA/dB None when r == 0."""
+    m = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(dY, "dY", torch.bfloat16, (m, q.n))
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, q.k))
+        _need(B, "B", torch.bfloat16, (q.n, r))
+        _need(T, "T", torch.bfloat16, (m, r))
+    dev = X.device
+    dX = torch.empty(m, q.k, dtype=torch.bfloat16, device=dev) if need_dx else None
+    dA = torch.empty(r, q.k, dtype=torch.bfloat16, device=dev) if r else None
+    dB = torch.empty(q.n, r, dtype=torch.bfloat16, device=dev) if r else None
+    lib = library()
+    wsb = lib.qlora_bwd_workspace_bytes(m, q.n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.c_struct()
+    _check(lib.qlora_bwd(_ptr(dY), _ptr(X), m, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s),
+                         _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(dev)))
+    return dX, dA, dB
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """Y = X deq(W)^T + s (X A^T) B^T with W frozen; gradients flow to X, A and B."""
+
+    @staticmethod
+    def forward(ctx, X, q: NF4Tensor, A, B, s: float):
+        Y, T = qlora_fwd(X, q, A, B, s)
+        ctx.q, ctx.s = q, s
+        ctx.save_for_backward(X, A, B, T)
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, T = ctx.saved_tensors
+        dX, dA, dB = qlora_bwd(dY.contiguous(), X, ctx.q, A, B, ctx.s, T,
+                               need_dx=ctx.needs_input_grad[0])
+        return dX, None, dA, dB, None

@@ -1,0 +1,345 @@
+// Host side of the C ABI declared in include/nf4qlora.h: argument validation (before any HIP
+// call), the NF4 tables, workspace layout and kernel launches.
+#include "nf4qlora.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return NF4_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(NF4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------- NF4 codebook
+// The 16 NF4 levels follow the QLoRA construction of 4-bit NormalFloat (the pages name NF4 but
+// print no levels [Unsloth v0.1.463-beta release article, "About the Unsloth Project"]):
+// normal quantiles of 8 (positive side) and 7 (negative side) evenly spaced probabilities between
+// delta = 1 - (1/30 + 1/32)/2 and 1/2, plus an exact zero, normalised by the largest. The
+// quantile is solved here by Newton's method on erfc in double precision, then rounded to float.
+double normal_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double normal_ppf(double p) {
+  // Phi is concave on x > 0, so Newton's iteration from 0 rises monotonically to the root.
+  double x = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    const double f = normal_cdf(x) - p;
+    const double d = std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+    const double step = f / d;
+    const double nx = x - step;
+    if (nx == x || std::fabs(step) <= 1e-17 * std::fabs(nx)) {
+      x = nx;
+      break;
+    }
+    x = nx;
+  }
+  return x;
+}
+
+struct TablesHolder {
+  nf4q::Tables t;
+  TablesHolder() {
+    const double delta = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+    double v[16];
+    int n = 0;
+    for (int j = 0; j < 8; ++j) v[n++] = normal_ppf(delta + (0.5 - delta) * j / 8.0);
+    for (int j = 0; j < 7; ++j) v[n++] = -normal_ppf(delta + (0.5 - delta) * j / 7.0);
+    v[n++] = 0.0;
+    std::sort(v, v + 16);
+    double top = 0.0;
+    for (double x : v) top = std::max(top, std::fabs(x));
+    for (int i = 0; i < 16; ++i) t.level[i] = (float)(v[i] / top);
+    for (int i = 0; i < 15; ++i) {
+      const double mid = ((double)t.level[i] + (double)t.level[i + 1]) / 2.0;  // exact
+      float th = (float)mid;
+      if ((double)th > mid) th = std::nextafter(th, -INFINITY);
+      t.thresh[i] = th;
+    }
+  }
+};
+
+const nf4q::Tables &tables() {
+  static const TablesHolder h;
+  return h.t;
+}
+
+// ------------------------------------------------------------------------------ validation
+int check_weight(const nf4_tensor *q) {
+  if (!q) return fail(NF4_EINVAL, "weight descriptor is NULL");
+  if (q->n < 1) return fail(NF4_EINVAL, "weight n must be >= 1 (got %lld)", (long long)q->n);
+  if (q->k < 64 || q->k % 64)
+    return fail(NF4_EUNSUPPORTED, "weight k must be a positive multiple of 64 (got %lld)",
+                (long long)q->k);
+  if (q->block != 64) return fail(NF4_EUNSUPPORTED, "block must be 64 (got %d)", q->block);
+  if (q->dq_block != 0 && q->dq_block != 256)
+    return fail(NF4_EUNSUPPORTED, "dq_block must be 0 or 256 (got %d)", q->dq_block);
+  if (q->n > (int64_t(1) << 40) / q->k)
+    return fail(NF4_EUNSUPPORTED, "n*k must be below 2^40");
+  if (!q->codes || !q->absmax) return fail(NF4_EINVAL, "codes/absmax pointer is NULL");
+  if (q->dq_block && !q->absmax_scale) return fail(NF4_EINVAL, "absmax_scale is NULL");
+  if (!aligned16(q->codes) || !aligned16(q->absmax) || (q->dq_block && !aligned16(q->absmax_scale)))
+    return fail(NF4_EINVAL, "weight buffers must be 16-byte aligned");
+  return NF4_OK;
+}
+
+nf4q::WDesc desc(const nf4_tensor *q) {
+  nf4q::WDesc w;
+  w.codes = q->codes;
+  w.absmax = q->absmax;
+  w.scale = q->absmax_scale;
+  w.n = q->n;
+  w.k = q->k;
+  w.dq = q->dq_block ? 1 : 0;
+  return w;
+}
+
+int check_layer(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
+                int32_t r) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (m < 1) return fail(NF4_EINVAL, "m must be >= 1 (got %lld)", (long long)m);
+  if (m > (int64_t(1) << 24)) return fail(NF4_EUNSUPPORTED, "m must be <= 2^24");
+  if (W->n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)W->n);
+  if (r < 0 || r > 128) return fail(NF4_EINVAL, "r must lie in [0, 128] (got %d)", r);
+  if (!X) return fail(NF4_EINVAL, "X is NULL");
+  if (!aligned16(X)) return fail(NF4_EINVAL, "X must be 16-byte aligned");
+  if (r > 0) {
+    if (!A || !B) return fail(NF4_EINVAL, "A and B must be non-NULL when r > 0");
+    if (!aligned16(A) || !aligned16(B)) return fail(NF4_EINVAL, "A and B must be 16-byte aligned");
+  }
+  return NF4_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct FwdWs {
+  int splits = 1;
+  size_t part = 0, total = 0;
+};
+
+FwdWs fwd_ws(int64_t m, int64_t k, int32_t r) {
+  FwdWs w;
+  if (r <= 0) return w;
+  w.splits = nf4q::rowproj_splits(m, k);
+  if (w.splits > 1) w.part = align256((size_t)w.splits * m * r * 4);
+  w.total = w.part;
+  return w;
+}
+
+struct BwdWs {
+  int splits_u = 1, splits_a = 1, splits_b = 1;
+  size_t u = 0, bt = 0, part = 0, total = 0;   // byte offsets: U at 0, Bt at u, partials at u+bt
+};
+
+BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
+  BwdWs w;
+  if (r <= 0) return w;
+  w.u = align256((size_t)m * r * 2);
+  w.bt = align256((size_t)r * n * 2);
+  w.splits_u = nf4q::rowproj_splits(m, n);
+  w.splits_a = nf4q::mreduce_splits(m, k);
+  w.splits_b = nf4q::mreduce_splits(m, n);
+  size_t p = 0;
+  if (w.splits_u > 1) p = std::max(p, (size_t)w.splits_u * m * r * 4);
+  p = std::max(p, (size_t)w.splits_a * r * k * 4);
+  p = std::max(p, (size_t)w.splits_b * r * n * 4);
+  w.part = align256(p);
+  w.total = w.u + w.bt + w.part;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nf4_last_error(void) { return g_err.c_str(); }
+
+int nf4_codebook(float *levels, float *thresholds) {
+  if (!levels) return fail(NF4_EINVAL, "levels is NULL");
+  const nf4q::Tables &t = tables();
+  for (int i = 0; i < 16; ++i) levels[i] = t.level[i];
+  if (thresholds)
+    for (int i = 0; i < 15; ++i) thresholds[i] = t.thresh[i];
+  return ok();
+}
+
+int nf4_quantize(const void *w, int w_dtype, const nf4_tensor *q, void *stream) {
+  int st = check_weight(q);
+  if (st) return st;
+  if (!w) return fail(NF4_EINVAL, "w is NULL");
+  if (!aligned16(w)) return fail(NF4_EINVAL, "w must be 16-byte aligned");
+  if (w_dtype != NF4_BF16 && w_dtype != NF4_F32) return fail(NF4_EINVAL, "unknown w_dtype %d", w_dtype);
+  const int64_t nblk = q->n * q->k / 64;
+  return hip_status(nf4q::launch_quantize(w, w_dtype == NF4_F32, q->codes, q->absmax,
+                                          q->absmax_scale, nblk, q->dq_block ? 1 : 0, tables(),
+                                          (hipStream_t)stream),
+                    "nf4_quantize launch");
+}
+
+int nf4_dequantize(const nf4_tensor *q, void *out, int out_dtype, void *stream) {
+  int st = check_weight(q);
+  if (st) return st;
+  if (!out) return fail(NF4_EINVAL, "out is NULL");
+  if (!aligned16(out)) return fail(NF4_EINVAL, "out must be 16-byte aligned");
+  if (out_dtype != NF4_BF16 && out_dtype != NF4_F32)
+    return fail(NF4_EINVAL, "unknown out_dtype %d", out_dtype);
+  return hip_status(nf4q::launch_dequantize(desc(q), out, out_dtype == NF4_F32, tables(),
+                                            (hipStream_t)stream),
+                    "nf4_dequantize launch");
+}
+
+size_t qlora_fwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  (void)n;
+  if (m < 1 || k < 1 || r < 0) return 0;
+  return fwd_ws(m, k, r).total;
+}
+
+int qlora_lora_down(const void *X, int64_t m, int64_t k, const void *A, int32_t r, void *T,
+                    void *ws, size_t ws_bytes, void *stream) {
+  if (m < 1) return fail(NF4_EINVAL, "m must be >= 1 (got %lld)", (long long)m);
+  if (m > (int64_t(1) << 24)) return fail(NF4_EUNSUPPORTED, "m must be <= 2^24");
+  if (k < 64 || k % 64)
+    return fail(NF4_EUNSUPPORTED, "k must be a positive multiple of 64 (got %lld)", (long long)k);
+  if (r < 1 || r > 128) return fail(NF4_EINVAL, "r must lie in [1, 128] (got %d)", r);
+  if (!X || !A || !T) return fail(NF4_EINVAL, "X, A and T must be non-NULL");
+  if (!aligned16(X) || !aligned16(A) || !aligned16(T))
+    return fail(NF4_EINVAL, "X, A and T must be 16-byte aligned");
+  const FwdWs lay = fwd_ws(m, k, r);
+  if (ws_bytes < lay.total || (lay.total && !ws))
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                lay.total);
+  if (lay.total && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  return hip_status(nf4q::launch_rowproj((const uint16_t *)X, k, (const uint16_t *)A, k, m, k, r,
+                                         lay.splits, (float *)ws, (uint16_t *)T,
+                                         (hipStream_t)stream),
+                    "qlora_lora_down launch");
+}
+
+int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T, const void *B,
+                    int32_t r, float s, void *Y, void *stream) {
+  int st = check_layer(X, m, W, T, B, r);
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  nf4q::GemmArgs g;
+  g.a_side = (const uint16_t *)X;
+  g.lda = W->k;
+  g.lora_a = (const uint16_t *)T;
+  g.lora_b = (const uint16_t *)B;
+  g.w = desc(W);
+  g.M = m;
+  g.C = W->n;
+  g.R = W->k;
+  g.r = r;
+  g.s = s;
+  g.out = (uint16_t *)Y;
+  g.ldo = W->n;
+  g.t = tables();
+  return hip_status(nf4q::launch_gemm_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
+}
+
+int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
+              int32_t r, float s, void *Y, void *T, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_layer(X, m, W, A, B, r);
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  if (r > 0) {
+    st = qlora_lora_down(X, m, W->k, A, r, T, ws, ws_bytes, stream);
+    if (st) return st;
+  }
+  return qlora_fwd_fused(X, m, W, T, B, r, s, Y, stream);
+}
+
+size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  if (m < 1 || n < 1 || k < 1 || r < 0) return 0;
+  return bwd_ws(m, n, k, r).total;
+}
+
+int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, const void *A,
+              const void *B, int32_t r, float s, const void *T, void *dX, void *dA, void *dB,
+              void *ws, size_t ws_bytes, void *stream) {
+  int st = check_layer(X, m, W, A, B, r);
+  if (st) return st;
+  if (!dY || !aligned16(dY)) return fail(NF4_EINVAL, "dY must be non-NULL and 16-byte aligned");
+  if (dX && !aligned16(dX)) return fail(NF4_EINVAL, "dX must be 16-byte aligned");
+  if (r > 0) {
+    if (!T || !dA || !dB) return fail(NF4_EINVAL, "T, dA and dB must be non-NULL when r > 0");
+    if (!aligned16(T) || !aligned16(dA) || !aligned16(dB))
+      return fail(NF4_EINVAL, "T, dA and dB must be 16-byte aligned");
+  }
+  if (!dX && r == 0) return ok();
+  const int64_t n = W->n, k = W->k;
+  const BwdWs lay = bwd_ws(m, n, k, r);
+  if (ws_bytes < lay.total || (lay.total && !ws))
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                lay.total);
+  if (lay.total && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  hipStream_t sm = (hipStream_t)stream;
+  char *base = (char *)ws;
+  uint16_t *U = (uint16_t *)base;
+  uint16_t *Bt = (uint16_t *)(base + lay.u);
+  float *part = (float *)(base + lay.u + lay.bt);
+  const uint16_t *dy = (const uint16_t *)dY;
+  hipError_t e;
+  if (r > 0) {
+    e = nf4q::launch_transpose((const uint16_t *)B, n, r, Bt, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd transpose launch");
+    e = nf4q::launch_rowproj(dy, n, Bt, n, m, n, r, lay.splits_u, part, U, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd U launch");
+  }
+  if (dX) {
+    nf4q::GemmArgs g;
+    g.a_side = dy;
+    g.lda = n;
+    g.lora_a = U;
+    g.lora_b = (const uint16_t *)A;
+    g.w = desc(W);
+    g.M = m;
+    g.C = k;
+    g.R = n;
+    g.r = r;
+    g.s = s;
+    g.out = (uint16_t *)dX;
+    g.ldo = k;
+    g.t = tables();
+    e = nf4q::launch_gemm_dx(g, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd dX launch");
+  }
+  if (r > 0) {
+    e = nf4q::launch_mreduce(U, (const uint16_t *)X, k, m, k, r, s, lay.splits_a, part,
+                             (uint16_t *)dA, false, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd dA launch");
+    e = nf4q::launch_mreduce((const uint16_t *)T, dy, n, m, n, r, s, lay.splits_b, part,
+                             (uint16_t *)dB, true, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd dB launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch wrappers of the NF4 QLoRA kernels (host-callable, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace nf4q {
+
+hipError_t launch_quantize(const void *w, bool f32_in, uint8_t *codes, void *absmax, float *scale,
+                           int64_t nblk, int dq, const Tables &t, hipStream_t st);
+hipError_t launch_dequantize(const WDesc &w, void *out, bool f32_out, const Tables &t,
+                             hipStream_t st);
+
+// out[m][c] = bf16( sum_red a_side[m][red] * deq-side[c][red] + sum_j lora_a[m][j] * s*lora_b(c, j) )
+//   fwd: a_side = X [M,K], weight rows c = n (reduction over k), lora_a = T [M,r], lora_b = B [N,r]
+//   dx:  a_side = dY [M,N], weight columns c = k (reduction over n), lora_a = U [M,r], lora_b = A [r,K]
+struct GemmArgs {
+  const uint16_t *a_side;
+  int64_t lda;
+  const uint16_t *lora_a;   // [M, r] or NULL when r == 0
+  const uint16_t *lora_b;   // fwd: B [N, r]; dx: A [r, K]
+  WDesc w;
+  int64_t M;                // rows of out
+  int64_t C;                // columns of out (N for fwd, K for dx)
+  int64_t R;                // reduction length (K for fwd, N for dx)
+  int r;
+  float s;
+  uint16_t *out;
+  int64_t ldo;
+  Tables t;
+};
+
+hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
+hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
+
+// out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).
+// With splits > 1 the partial sums go to part (float [splits][M][r]) and are reduced by
+// launch_rowproj_reduce into out.
+hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t ldp,
+                          int64_t M, int64_t L, int r, int splits, float *part, uint16_t *out,
+                          hipStream_t st);
+int rowproj_splits(int64_t M, int64_t L);
+
+// out = bf16(s * sum over m of P[m][j] * Q[m][c]); P [M][r] (ld r), Q [M][C] (ld ldq).
+// transposed_out: out[c][j] (ld r) else out[j][c] (ld C). part: float [splits][r][C].
+hipError_t launch_mreduce(const uint16_t *P, const uint16_t *Q, int64_t ldq, int64_t M, int64_t C,
+                          int r, float s, int splits, float *part, uint16_t *out,
+                          bool transposed_out, hipStream_t st);
+int mreduce_splits(int64_t M, int64_t C);
+
+// dst[j][l] = src[l][j] for a bf16 [L][r] matrix.
+hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst, hipStream_t st);
+
+}  // namespace nf4q

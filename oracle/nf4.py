@@ -1,4 +1,6 @@
-"""NF4 quantisation in plain numpy -- test infrastructure (see the package docstring).
+"""NF4 quantisation in plain numpy (plus one plain C loop) -- test infrastructure.
+
+See the package docstring for who may use it.
 
 What the pages fix: the frozen base weight is stored as 4-bit NormalFloat (NF4), a code whose
 levels suit normally distributed weights, and the quantisation constants are themselves
@@ -22,11 +24,18 @@ below is a reading, stated where it is taken:
   [0, 127] and stored as int8; S == 0 gives q = 0. Decode a' = fl32(q * S). Codes are always
   taken against the exact float32 absmax, before double quantisation.
 * Dequantise: w' = fl32(level[code] * a'); the bf16 form is w' rounded to nearest-even.
+
+The encoder exists twice: encode_numpy (vectorised numpy) and encode_c (the same definition as a
+C loop in nf4_encode.c, for full-size weights); tests pin both to exact-rational brute force and
+to each other.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 import math
+import os
+import subprocess
 from typing import Optional
 
 import numpy as np
@@ -104,7 +113,7 @@ def block_absmax(w: np.ndarray) -> np.ndarray:
     return np.abs(w).max(axis=1)
 
 
-def encode(w: np.ndarray, absmax: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
+def encode_numpy(w: np.ndarray, absmax: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
     """4-bit codes (uint8, one per element) of the flattened float32 weight against absmax."""
     w = np.asarray(w, dtype=np.float32).reshape(-1)
     a = np.repeat(np.asarray(absmax, dtype=np.float32), BLOCK)
@@ -120,6 +129,55 @@ def encode(w: np.ndarray, absmax: np.ndarray, chunk: int = 1 << 20) -> np.ndarra
         code[zero] = 7
         out[lo:lo + chunk] = code
     return out
+
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_C_SRC = os.path.join(_HERE, "nf4_encode.c")
+_C_LIB = os.path.join(_HERE, "libnf4oracle.so")
+_c = None
+
+
+def build_c() -> str:
+    """Compile the C twin of the encoder (plain loop, gcc -O2 -fopenmp, no fast-math)."""
+    tmp = _C_LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", _C_SRC, "-o", tmp, "-lm"],
+                   check=True)
+    os.replace(tmp, _C_LIB)
+    return _C_LIB
+
+
+def _c_lib():
+    global _c
+    if _c is None:
+        if not os.path.exists(_C_LIB) or os.path.getmtime(_C_LIB) < os.path.getmtime(_C_SRC):
+            build_c()
+        lib = ctypes.CDLL(_C_LIB)
+        lib.oracle_nf4_encode.restype = None
+        lib.oracle_nf4_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        _c = lib
+    return _c
+
+
+def encode_c(w: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """The same definition as encode_numpy, as a C loop (oracle/nf4_encode.c)."""
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    if a.size * BLOCK != w.size:
+        raise ValueError("absmax must hold one value per 64 elements")
+    lv = np.ascontiguousarray(_CODEBOOK, dtype=np.float32)
+    out = np.empty(w.size, dtype=np.uint8)
+    _c_lib().oracle_nf4_encode(w.ctypes.data, a.ctypes.data, w.size, lv.ctypes.data,
+                               out.ctypes.data)
+    return out
+
+
+def encode(w: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """4-bit codes of the flattened float32 weight: the C loop for large inputs, numpy else."""
+    w = np.asarray(w, dtype=np.float32)
+    if w.size >= (1 << 16):
+        return encode_c(w, absmax)
+    return encode_numpy(w, absmax)
 
 
 def pack(codes: np.ndarray) -> np.ndarray:

@@ -1,0 +1,146 @@
+"""Host-only checks of the C-ABI library (no GPU needed, no kernel launched).
+
+The library must load without a device, export every function include/nf4qlora.h declares, carry
+the same NF4 tables as the oracle (derived independently: Newton's method in C++ against the
+oracle's bisection in Python), and reject invalid arguments on the host before any HIP call.
+Every call below is invalid by construction, so validation fails before a pointer is used.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import nf4_dequant_gemm_amd as m
+from oracle import nf4
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nf4qlora.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(names) == set(m.EXPORTED), names
+    assert {"nf4_quantize", "qlora_fwd", "qlora_bwd"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_codebook_matches_oracle_bitwise():
+    lv, th = m.nf4_codebook()
+    assert np.array(lv, np.float32).view(np.uint32).tolist() == nf4.codebook().view(np.uint32).tolist()
+    c = nf4.codebook().astype(np.float64)
+    for i, t in enumerate(th):
+        mid = (c[i] + c[i + 1]) / 2
+        assert float(np.float32(t)) <= mid
+        assert float(np.nextafter(np.float32(t), np.float32(np.inf))) > mid
+
+
+def test_thresholds_reproduce_oracle_encoding():
+    """code = #{thresholds below v} equals the oracle's nearest-level rule on dense float32 grids."""
+    _, th = m.nf4_codebook()
+    th = np.array(th, np.float32)
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.uniform(-1, 1, 200_000).astype(np.float32),
+                        np.linspace(-1, 1, 100_001, dtype=np.float32)])
+    c = nf4.codebook().astype(np.float64)
+    for t in th:                       # every float32 within 50 ulps of each threshold
+        b = np.array([t], np.float32).view(np.int32)[0]
+        near = (np.arange(-50, 51, dtype=np.int64) * (1 if t >= 0 else -1) + b).astype(np.int32)
+        v = np.concatenate([v, near.view(np.float32)])
+    v = np.concatenate([v, np.zeros((-v.size) % 64, np.float32)])
+    want = nf4.encode(v, np.ones(v.size // 64, np.float32))
+    got = (v[:, None] > th[None, :]).sum(axis=1)
+    assert np.array_equal(got, want)
+    assert c[0] == -1 and c[15] == 1
+
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: every call below fails validation first
+
+
+def wdesc(n=64, k=128, block=64, dq=0, codes=FAKE, absmax=FAKE, scale=None):
+    return m._NF4TensorC(n, k, block, dq, codes, absmax, scale)
+
+
+@pytest.mark.parametrize("desc,status", [
+    (dict(k=96), m.NF4_EUNSUPPORTED),
+    (dict(block=32), m.NF4_EUNSUPPORTED),
+    (dict(dq=128), m.NF4_EUNSUPPORTED),
+    (dict(n=0), m.NF4_EINVAL),
+    (dict(codes=None), m.NF4_EINVAL),
+    (dict(dq=256, scale=None), m.NF4_EINVAL),
+    (dict(codes=ctypes.c_void_p(4100)), m.NF4_EINVAL),
+])
+def test_quantize_rejects_bad_weight(desc, status):
+    lib = m.library()
+    q = wdesc(**desc)
+    assert lib.nf4_quantize(FAKE, m.NF4_BF16, ctypes.byref(q), None) == status
+    assert lib.nf4_last_error()
+    assert lib.nf4_dequantize(ctypes.byref(q), FAKE, m.NF4_F32, None) == status
+
+
+def test_quantize_rejects_null_and_dtype():
+    lib = m.library()
+    q = wdesc()
+    assert lib.nf4_quantize(None, m.NF4_BF16, ctypes.byref(q), None) == m.NF4_EINVAL
+    assert lib.nf4_quantize(FAKE, 7, ctypes.byref(q), None) == m.NF4_EINVAL
+    assert lib.nf4_quantize(FAKE, m.NF4_BF16, None, None) == m.NF4_EINVAL
+    assert lib.nf4_dequantize(ctypes.byref(q), FAKE, 9, None) == m.NF4_EINVAL
+    assert lib.nf4_codebook(None, None) == m.NF4_EINVAL
+
+
+def test_layer_calls_reject_bad_arguments():
+    lib = m.library()
+    q = wdesc(n=64, k=128)
+    ws = lib.qlora_fwd_workspace_bytes(100, 64, 128, 8)
+    fwd = lambda **kw: lib.qlora_fwd(kw.get("X", FAKE), kw.get("m", 100), ctypes.byref(kw.get("q", q)),
+                                      kw.get("A", FAKE), kw.get("B", FAKE), kw.get("r", 8), 1.0,
+                                      kw.get("Y", FAKE), kw.get("T", FAKE), kw.get("ws", FAKE),
+                                      kw.get("wsb", 0), None)
+    if ws:
+        assert fwd(wsb=ws - 1) == m.NF4_EINVAL
+    assert fwd(m=0, wsb=ws) == m.NF4_EINVAL
+    assert fwd(r=129, wsb=ws) == m.NF4_EINVAL
+    assert fwd(r=-1, wsb=ws) == m.NF4_EINVAL
+    assert fwd(A=None, wsb=ws) == m.NF4_EINVAL
+    assert fwd(T=None, wsb=ws) == m.NF4_EINVAL
+    assert fwd(Y=None, wsb=ws) == m.NF4_EINVAL
+    assert fwd(X=ctypes.c_void_p(4098), wsb=ws) == m.NF4_EINVAL
+    assert fwd(q=wdesc(n=60, k=128), wsb=ws) == m.NF4_EUNSUPPORTED
+    assert fwd(q=wdesc(n=64, k=100), wsb=ws) == m.NF4_EUNSUPPORTED
+    wsb = lib.qlora_bwd_workspace_bytes(100, 64, 128, 8)
+    assert wsb > 0
+    bwd = lambda **kw: lib.qlora_bwd(FAKE, FAKE, 100, ctypes.byref(q), FAKE, FAKE, kw.get("r", 8), 1.0,
+                                      kw.get("T", FAKE), FAKE, kw.get("dA", FAKE), FAKE,
+                                      kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert bwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert bwd(ws=None) == m.NF4_EINVAL
+    assert bwd(T=None) == m.NF4_EINVAL
+    assert bwd(dA=None) == m.NF4_EINVAL
+    assert bwd(r=200) == m.NF4_EINVAL
+    assert "workspace" in lib.nf4_last_error().decode() or lib.nf4_last_error()
+
+
+def test_workspace_sizes_are_consistent():
+    lib = m.library()
+    assert lib.qlora_fwd_workspace_bytes(100, 64, 128, 0) == 0
+    assert lib.qlora_bwd_workspace_bytes(100, 64, 128, 0) == 0
+    # bwd workspace holds at least U (bf16 [m, r]) and B^T (bf16 [r, n])
+    assert lib.qlora_bwd_workspace_bytes(16384, 4096, 14336, 32) >= 16384 * 32 * 2 + 32 * 4096 * 2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "_LIB_PATH", "/nonexistent/libnf4qlora.so")
+    with pytest.raises(ImportError):
+        m.library()

@@ -87,8 +87,8 @@ _double_quant = nf4.double_quant
 _levels = nf4.nf4_levels_f64
 
 
-def encode_ties_up(w, absmax, chunk=1 << 20):
-    out = _encode(w, absmax, chunk)
+def encode_ties_up(w, absmax):
+    out = _encode(w, absmax)
     w = np.asarray(w, np.float32).reshape(-1)
     a = np.repeat(np.asarray(absmax, np.float32), 64)
     c = nf4._CODEBOOK.astype(np.float64)
@@ -100,7 +100,7 @@ def encode_ties_up(w, absmax, chunk=1 << 20):
     return out
 
 
-def encode_rne_midpoints(w, absmax, chunk=1 << 20):
+def encode_rne_midpoints(w, absmax):
     w = np.asarray(w, np.float32).reshape(-1)
     a = np.repeat(np.asarray(absmax, np.float32), 64)
     c = nf4._CODEBOOK.astype(np.float64)

@@ -186,3 +186,18 @@ def test_dequantised_error_within_half_step():
 def test_k_not_multiple_of_block_rejected():
     with pytest.raises(ValueError):
         nf4.quantize(np.zeros((2, 96), np.float32))
+
+
+def test_c_encoder_equals_numpy_encoder():
+    """The C twin (oracle/nf4_encode.c) and the numpy encoder agree on every case above."""
+    rng = np.random.default_rng(13)
+    w = np.concatenate([
+        rng.standard_normal(64 * 3000).astype(np.float32) * np.float32(0.02),
+        near_midpoints(), np.zeros(64, np.float32), np.full(64, -0.0, np.float32)])
+    w = np.concatenate([w, np.zeros((-w.size) % 64, np.float32)])
+    for a in (nf4.block_absmax(w), np.ones(w.size // 64, np.float32)):
+        assert np.array_equal(nf4.encode_c(w, a), nf4.encode_numpy(w, a))
+    v = near_midpoints()
+    v = np.concatenate([v, np.zeros((-v.size) % 64, np.float32)])
+    got = nf4.encode_c(v, np.ones(v.size // 64, np.float32))
+    assert np.array_equal(got[: near_midpoints().size], [nearest_exact(x) for x in near_midpoints()])
