@@ -47,6 +47,97 @@ __device__ __forceinline__ float block_absmax(const WDesc &w, int64_t b) {
   return reinterpret_cast<const float *>(w.absmax)[b];
 }
 
+// Buffer resource over [p, p + bytes): loads past the end return 0 (raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) {
+  return (m & a) | (~m & b);
+}
+
+// NF4 decode table of one 64-element block: the 16 values bf16(level_i * a) split into byte
+// planes L (low bytes) and H (high bytes), four entries per 32-bit word.
+struct RowTable {
+  uint32_t L[4], H[4];
+};
+
+__device__ __forceinline__ RowTable make_row_table(float a, const Tables &t) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(t.level[2 * j] * a, t.level[2 * j + 1] * a);
+  RowTable r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r.L[q] = perm(pk[2 * q + 1], pk[2 * q], 0x06040200u);
+    r.H[q] = perm(pk[2 * q + 1], pk[2 * q], 0x07050301u);
+  }
+  return r;
+}
+
+// Look up 4 codes at once: s7 = the codes' low 3 bits (one per byte), m = 0xFF bytes where the
+// code is >= 8. Returns the table's low (L) or high (H) bytes of the 4 entries.
+__device__ __forceinline__ uint32_t lookup4(const uint32_t P[4], uint32_t s7, uint32_t m) {
+  return bitsel(m, perm(P[3], P[2], s7), perm(P[1], P[0], s7));
+}
+
+// Decode one 32-bit word of packed codes (8 elements; byte b = element 2b in bits 7..4 and
+// element 2b+1 in bits 3..0) into 4 words of bf16 pairs in element order.
+__device__ __forceinline__ void decode8(const RowTable &t, uint32_t d, uint32_t out[4]) {
+  const uint32_t se7 = (d >> 4) & 0x07070707u;                             // even elements
+  const uint32_t so7 = d & 0x07070707u;                                    // odd elements
+  const uint32_t me = perm(0u, 0u, ((d >> 7) & 0x01010101u) | 0x0C0C0C0Cu); // bit 3 of even codes
+  const uint32_t mo = perm(0u, 0u, ((d >> 3) & 0x01010101u) | 0x0C0C0C0Cu); // bit 3 of odd codes
+  const uint32_t Le = lookup4(t.L, se7, me), He = lookup4(t.H, se7, me);
+  const uint32_t Lo = lookup4(t.L, so7, mo), Ho = lookup4(t.H, so7, mo);
+  const uint32_t E01 = perm(He, Le, 0x05010400u), E23 = perm(He, Le, 0x07030602u);
+  const uint32_t O01 = perm(Ho, Lo, 0x05010400u), O23 = perm(Ho, Lo, 0x07030602u);
+  out[0] = perm(O01, E01, 0x05040100u);
+  out[1] = perm(O01, E01, 0x07060302u);
+  out[2] = perm(O23, E23, 0x05040100u);
+  out[3] = perm(O23, E23, 0x07060302u);
+}
+
+// decode8 split into five pieces of about six VALU instructions each, so the decode of a chunk
+// can be spread between MFMA issues.
+struct Dec8 {
+  uint32_t d, se7, so7, me, mo, Le, He, Lo, Ho, E01, E23;
+};
+
+__device__ __forceinline__ void dec_piece(const RowTable &t, Dec8 &x, int piece, uint32_t out[4]) {
+  switch (piece) {
+    case 0:
+      x.se7 = (x.d >> 4) & 0x07070707u;
+      x.so7 = x.d & 0x07070707u;
+      x.me = perm(0u, 0u, ((x.d >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
+      break;
+    case 1:
+      x.mo = perm(0u, 0u, ((x.d >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+      x.Le = lookup4(t.L, x.se7, x.me);
+      break;
+    case 2:
+      x.He = lookup4(t.H, x.se7, x.me);
+      x.Lo = lookup4(t.L, x.so7, x.mo);
+      break;
+    case 3:
+      x.Ho = lookup4(t.H, x.so7, x.mo);
+      x.E01 = perm(x.He, x.Le, 0x05010400u);
+      x.E23 = perm(x.He, x.Le, 0x07030602u);
+      break;
+    default: {
+      const uint32_t O01 = perm(x.Ho, x.Lo, 0x05010400u), O23 = perm(x.Ho, x.Lo, 0x07030602u);
+      out[0] = perm(O01, x.E01, 0x05040100u);
+      out[1] = perm(O01, x.E01, 0x07060302u);
+      out[2] = perm(O23, x.E23, 0x05040100u);
+      out[3] = perm(O23, x.E23, 0x07060302u);
+    }
+  }
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -1,0 +1,294 @@
+// Fused forward kernel of the QLoRA layer: Y = X deq(W)^T + s T B^T in one launch (gfx950).
+//
+// NF4 dequantisation, the base GEMM and the rank-r LoRA correction run in the same kernel and the
+// same output tile; the weight is decoded on the fly and never written to HBM [Unsloth pages:
+// "Inside Unsloth" listing, "What You'll Learn", "LoRA and QLoRA" (dequant, matmul and LoRA
+// correction fused into a single launch); pyshine code tour, "Detailed view" (LoRA delta computed
+// inside the matmul instead of two extra matmuls); v0.1.463-beta release article, "About the
+// Unsloth Project" (no redundant buffers during dequantisation)].
+//
+// Work split. One workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of Y and walks K in steps of
+// 64 = one NF4 block per weight row. Each wave accumulates 128 x 128 with 16 MFMA 32x32x16 tiles.
+// Thread t owns weight row n0 + t of the tile: per step it turns the row's 32 bytes of codes and
+// its block constant into 64 bf16 values through a 16-entry table of bf16(level_i * a) held in
+// registers (byte-select lookups, no LDS lookups, no per-element multiply).
+//
+// Pipeline per step s (one workgroup barrier per step):
+//   * loads for step s+2 are issued into registers (X tile chunks, codes, block constant),
+//   * the 64 MFMAs of step s run on LDS buffer s & 1, with the fragments of the next k-slice read
+//     while the current one is multiplied,
+//   * between MFMA issues, the X chunks and the decoded W rows of step s+1 (loaded one step
+//     earlier) are written to LDS buffer (s+1) & 1, so the decode's VALU work overlaps the MFMAs.
+// LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
+// c ^ ((r >> 1) & 7), which keeps 16 consecutive rows on distinct slots of the 256-byte bank
+// window that a 16-byte LDS access covers per pass on gfx950.
+#include "common.h"
+#include "launch.h"
+
+namespace nf4q {
+namespace {
+
+constexpr int kT = 256;      // output tile rows and columns
+constexpr int kS = 64;       // reduction step = NF4 block
+constexpr int kThreads = 256;
+constexpr int kChunks = kT * kS / 8;
+
+__device__ __forceinline__ int swzf(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+
+// Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of tiles so
+// the n-tiles of one m-block (which share X) run on one XCD and share its L2.
+__device__ __forceinline__ int tile_remap(int hw, int tiles) {
+  const int per = tiles >> 3, rem = tiles & 7, x = hw & 7;
+  return x * per + (x < rem ? x : rem) + (hw >> 3);
+}
+
+struct XStage {
+  u32x4 v[8];
+};
+struct CStage {
+  u32x4 c0, c1;      // the row's 32 bytes of codes
+  uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
+};
+
+// LoRA step staging: A-side T columns jb..jb+63, B-side s * B (rows n), both zero-padded.
+__device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int jb, uint4 *sA, uint4 *sB) {
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int i = 0; i < 8; ++i) {
+    const int q = tid + kThreads * i;
+    const int row = q >> 3, c = q & 7;
+    uint32_t wa[4], wb[4];
+    const int64_t m = m0 + row, n = n0 + row;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int j0 = jb + c * 8 + e, j1 = j0 + 1;
+      uint32_t lo = 0, hi = 0;
+      if (m < g.M) {
+        if (j0 < g.r) lo = g.lora_a[m * g.r + j0];
+        if (j1 < g.r) hi = g.lora_a[m * g.r + j1];
+      }
+      wa[e >> 1] = lo | (hi << 16);
+      float b0 = 0.f, b1 = 0.f;
+      if (n < g.C) {
+        if (j0 < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + j0]);
+        if (j1 < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + j1]);
+      }
+      wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
+    }
+    sA[swzf(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  }
+}
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
+  __shared__ uint4 sX[2][kChunks];
+  __shared__ uint4 sW[2][kChunks];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (int)((g.C + kT - 1) / kT);
+  const int logical = tile_remap(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(logical / tiles_n) * kT;
+  const int64_t n0 = (int64_t)(logical % tiles_n) * kT;
+  const int64_t K = g.w.k;
+  const int64_t rows_m = (g.M - m0 < kT) ? g.M - m0 : kT;
+  const int64_t rows_n = (g.C - n0 < kT) ? g.C - n0 : kT;
+  const int kblk = (int)(K / kS);
+  const int last = kblk - 1;
+
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.a_side + m0 * K, rows_m * K * 2);
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + n0 * (K / 2), rows_n * (K / 2));
+  const __amdgpu_buffer_rsrc_t rQ =
+      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows_n * kblk)
+          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + n0 * kblk, rows_n * kblk * 4);
+  const int64_t nruns = (g.w.n * kblk + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
+
+  // X chunk i of this thread: tile row 32 i + tid / 8, chunk tid % 8.
+  const uint32_t xoff = (uint32_t)((tid >> 3) * K * 2 + (tid & 7) * 16);
+  const uint32_t xrow_stride = (uint32_t)(32 * K * 2);
+  const uint32_t coff = (uint32_t)(tid * (K / 2));
+  const uint32_t qoff = (uint32_t)(tid * kblk);
+  const int64_t sbase = (n0 + tid) * kblk;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  auto load_x = [&](int s, XStage &x) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, xoff + i * xrow_stride + s * 128, 0, 0);
+  };
+  auto load_c = [&](int s, CStage &c) {
+    c.c0 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
+    c.c1 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32 + 16, 0, 0);
+    if (kDQ) {
+      c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, qoff + s, 0, 0);
+      c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)(((sbase + s) >> 8) * 4), 0, 0);
+    } else {
+      c.q = __builtin_amdgcn_raw_buffer_load_b32(rQ, (qoff + s) * 4, 0, 0);
+    }
+  };
+  auto absmax_of = [&](const CStage &c) {
+    return kDQ ? float((int8_t)(uint8_t)c.q) * __uint_as_float(c.sc) : __uint_as_float(c.q);
+  };
+  auto word = [](const CStage &c, int j) {
+    return j == 0 ? c.c0.x : j == 1 ? c.c0.y : j == 2 ? c.c0.z : j == 3 ? c.c0.w
+         : j == 4 ? c.c1.x : j == 5 ? c.c1.y : j == 6 ? c.c1.z : c.c1.w;
+  };
+  auto write_x = [&](const XStage &x, int i, uint4 *sA) {
+    sA[swzf(i * 32 + (tid >> 3), tid & 7)] = __builtin_bit_cast(uint4, x.v[i]);
+  };
+  auto decode_all = [&](const CStage &c, uint4 *sB) {
+    const RowTable t = make_row_table(absmax_of(c), g.t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t o[4];
+      decode8(t, word(c, j), o);
+      sB[swzf(tid, j)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  auto read_frags = [&](const uint4 *sA, const uint4 *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      af[t] = __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + t * 32 + (lane & 31), c)]);
+      bw[t] = __builtin_bit_cast(bf16x8, sB[swzf(wn * 128 + t * 32 + (lane & 31), c)]);
+    }
+  };
+  // Plain MFMA pass over one step (used for the LoRA steps).
+  auto mma = [&](const uint4 *sA, const uint4 *sB) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[4], bw[4];
+      read_frags(sA, sB, kk, af, bw);
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32x32x16(bw[tn], af[tm], acc[tn][tm]);
+    }
+  };
+
+  // One step: MFMAs on buffer P; the X chunks (xn) and the W rows (decoded from cn) of step s+1
+  // go to buffer P^1 in between; loads of step s+2 go to xm / cm.
+  auto body = [&](int s, int P, XStage &xm, XStage &xn, CStage &cm, CStage &cn) {
+    const int s2 = s + 2 < last ? s + 2 : last;
+    load_x(s2, xm);
+    load_c(s2, cm);
+    const uint4 *A = sX[P];
+    const uint4 *B = sW[P];
+    uint4 *An = sX[P ^ 1];
+    uint4 *Bn = sW[P ^ 1];
+    bf16x8 af[2][4], bw[2][4];
+    read_frags(A, B, 0, af[0], bw[0]);
+
+    const float a = absmax_of(cn);
+    uint32_t pk[8];
+    RowTable t;
+    Dec8 dx;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tn = i >> 2, tm = i & 3;
+        const int slot = kk * 16 + i;
+        acc[tn][tm] = mfma32x32x16(bw[kk & 1][tn], af[kk & 1][tm], acc[tn][tm]);
+        // fragments of the next k-slice
+        if (kk < 3 && i < 4) {
+          const int c = (kk + 1) * 2 + (lane >> 5);
+          af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzf(wm * 128 + i * 32 + (lane & 31), c)]);
+          bw[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, B[swzf(wn * 128 + i * 32 + (lane & 31), c)]);
+        }
+        // X tile of step s+1: one chunk every 8 MFMAs
+        if ((slot & 7) == 2) write_x(xn, slot >> 3, An);
+        // decode table of step s+1 in slots 0..3, then chunk j = (slot - 4) / 7, piece (slot - 4) % 7
+        if (slot < 4) {
+          pk[2 * slot] = pack_bf16x2(g.t.level[4 * slot] * a, g.t.level[4 * slot + 1] * a);
+          pk[2 * slot + 1] = pack_bf16x2(g.t.level[4 * slot + 2] * a, g.t.level[4 * slot + 3] * a);
+          t.L[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x06040200u);
+          t.H[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x07050301u);
+        } else if (slot < 4 + 8 * 7) {
+          const int j = (slot - 4) / 7, p = (slot - 4) % 7;
+          if (p < 5) {
+            if (p == 0) dx.d = word(cn, j);
+            uint32_t o[4];
+            dec_piece(t, dx, p, o);
+            if (p == 4) Bn[swzf(tid, j)] = make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+    }
+    // This wave's LDS writes are done; the barrier publishes buffer P^1 (the newer global loads
+    // stay in flight).
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  XStage x0, x1;
+  CStage c0, c1;
+  load_x(0, x0);
+  load_c(0, c0);
+  load_x(kblk > 1 ? 1 : 0, x1);
+  load_c(kblk > 1 ? 1 : 0, c1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) write_x(x0, i, sX[0]);
+  decode_all(c0, sW[0]);
+  __syncthreads();
+  int s = 0;
+#pragma unroll 1
+  for (; s + 2 <= kblk; s += 2) {
+    body(s, 0, x0, x1, c0, c1);
+    body(s + 1, 1, x1, x0, c1, c0);
+  }
+  if (s < kblk) body(s, 0, x0, x1, c0, c1);
+  __syncthreads();
+
+  // LoRA steps: [T | s B] as extra reduction steps of the same tile.
+  const int nlora = (g.r + kS - 1) / kS;
+#pragma unroll 1
+  for (int j = 0; j < nlora; ++j) {
+    const int buf = j & 1;
+    stage_lora(g, m0, n0, j * kS, sX[buf], sW[buf]);
+    __syncthreads();
+    mma(sX[buf], sW[buf]);
+    __syncthreads();
+  }
+
+  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m
+  // for each (tn, tm, group of 4 accumulator registers).
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int64_t m = m0 + wm * 128 + tm * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * 128 + tn * 32 + 8 * q + 4 * (lane >> 5);
+        if (m < g.M && n < g.C) {
+          const uint2 v = make_uint2(pack_bf16x2(acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1]),
+                                     pack_bf16x2(acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3]));
+          *reinterpret_cast<uint2 *>(g.out + m * g.ldo + n) = v;
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st) {
+  const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
+  if (g.w.dq)
+    fwd_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else
+    fwd_fused_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace nf4q

@@ -256,7 +256,6 @@ static hipError_t launch_gemm(const GemmArgs &g, bool dx, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st) { return launch_gemm(g, false, st); }
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st) { return launch_gemm(g, true, st); }
 
 }  // namespace nf4q
