@@ -127,6 +127,9 @@ int check_layer(const void *X, int64_t m, const nf4_tensor *W, const void *A, co
   if (m < 1) return fail(NF4_EINVAL, "m must be >= 1 (got %lld)", (long long)m);
   if (m > (int64_t(1) << 24)) return fail(NF4_EUNSUPPORTED, "m must be <= 2^24");
   if (W->n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)W->n);
+  // the GEMM kernels address the codes, X and dY tiles with 32-bit buffer offsets
+  if (W->n * W->k >= (int64_t(1) << 32) || W->k > (int64_t(1) << 22) || W->n > (int64_t(1) << 22))
+    return fail(NF4_EUNSUPPORTED, "n*k must be below 2^32 and n, k at most 2^22 for the GEMM calls");
   if (r < 0 || r > 128) return fail(NF4_EINVAL, "r must lie in [0, 128] (got %d)", r);
   if (!X) return fail(NF4_EINVAL, "X is NULL");
   if (!aligned16(X)) return fail(NF4_EINVAL, "X must be 16-byte aligned");

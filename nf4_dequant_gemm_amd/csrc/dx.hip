@@ -1,0 +1,321 @@
+// Fused input-gradient kernel of the QLoRA layer: dX = dY deq(W) + s U A (gfx950).
+//
+// The backward pass of the frozen-base QLoRA layer needs the gradient through the dequantised
+// base weight and through the adapters; W itself gets no gradient [Unsloth v0.1.463-beta release
+// article, "About the Unsloth Project": the 4-bit base is frozen, only the adapters train; the
+// Unsloth kernels rewrite the backward pass]. As in the forward kernel, the NF4 weight is decoded
+// on the fly into LDS and the rank-r term runs as extra reduction steps into the same tile.
+//
+// Work split. One workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of dX (rows m, columns k) and
+// walks the reduction index n in steps of 64. The reduction runs over the weight's ROW index,
+// so the decoded weight tile is stored transposed in LDS (256 k-rows of 64 n). Thread t decodes
+// two weight rows (n, n+1) x 32 columns per step through two 16-entry bf16 tables (one per row
+// and block), pairs the rows per column with byte permutes and writes 4-byte (n, n+1) words.
+//
+// Pipeline per step s as in the forward kernel: dY chunks and codes of step s+2 are loaded into
+// registers, the 64 MFMAs of step s run on LDS buffer s & 1 while the dY chunks and the decoded,
+// transposed weight of step s+1 are written to buffer (s+1) & 1 between MFMA issues.
+//
+// LDS: rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot c ^ ((r >> 1) & 7). The
+// transposed weight tile keeps column k in row p(k) = 32 (k / 32) + (k + k / 32) % 32, so the two
+// half-waves of a write (columns k and k + 32) land in different halves of the 256-byte bank
+// window.
+#include "common.h"
+#include "launch.h"
+
+namespace nf4q {
+namespace {
+
+constexpr int kT = 256;
+constexpr int kS = 64;
+constexpr int kThreads = 256;
+constexpr int kChunks = kT * kS / 8;
+
+__device__ __forceinline__ int swzd(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+// Row of column k (0..255) in the transposed weight tile: rotated by k / 32 inside its group of
+// 32 rows (a bijection), so columns k and k + 32 sit in rows of opposite parity.
+__device__ __forceinline__ int prow(int k) { return (k & ~31) | ((k + (k >> 5)) & 31); }
+
+__device__ __forceinline__ int tile_remap(int hw, int tiles) {
+  const int per = tiles >> 3, rem = tiles & 7, x = hw & 7;
+  return x * per + (x < rem ? x : rem) + (hw >> 3);
+}
+
+struct YStage {
+  u32x4 v[8];
+};
+struct CStage2 {
+  u32x4 c[2];        // 16 bytes of codes (32 columns) of rows n and n+1
+  uint32_t q[2];     // block constants (int8 or float bits)
+  uint32_t sc[2];    // run scale bits (double quantisation)
+};
+
+// LoRA step staging: A-side U columns jb..jb+63 (rows m), B-side s * A^T (rows k, columns j).
+__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sA, uint4 *sB) {
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int i = 0; i < 8; ++i) {
+    const int q = tid + kThreads * i;
+    const int row = q >> 3, c = q & 7;
+    uint32_t wa[4], wb[4];
+    const int64_t m = m0 + row, k = k0 + row;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int j0 = jb + c * 8 + e, j1 = j0 + 1;
+      uint32_t lo = 0, hi = 0;
+      if (m < g.M) {
+        if (j0 < g.r) lo = g.lora_a[m * g.r + j0];
+        if (j1 < g.r) hi = g.lora_a[m * g.r + j1];
+      }
+      wa[e >> 1] = lo | (hi << 16);
+      float b0 = 0.f, b1 = 0.f;
+      if (k < g.C) {
+        if (j0 < g.r) b0 = bf16_to_f32(g.lora_b[(int64_t)j0 * g.C + k]);
+        if (j1 < g.r) b1 = bf16_to_f32(g.lora_b[(int64_t)j1 * g.C + k]);
+      }
+      wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
+    }
+    sA[swzd(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    sB[swzd(prow(row), c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  }
+}
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
+  __shared__ uint4 sY[2][kChunks];   // dY tiles [m][n]
+  __shared__ uint4 sW[2][kChunks];   // decoded weight tiles, transposed [p(k)][n]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wk = wave & 1;
+  const int tiles_k = (int)((g.C + kT - 1) / kT);
+  const int logical = tile_remap(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(logical / tiles_k) * kT;
+  const int64_t k0 = (int64_t)(logical % tiles_k) * kT;
+  const int64_t K = g.w.k, N = g.w.n;
+  const int64_t rows_m = (g.M - m0 < kT) ? g.M - m0 : kT;
+  const int kblk = (int)(K / kS);
+  const int nsteps = (int)((N + kS - 1) / kS);
+  const int last = nsteps - 1;
+
+  // dY rows m0.. (reduction index n contiguous). Chunks past n = N read the next row's values
+  // (finite) and meet weight rows past N, which decode to exact zeros (codes and constants read
+  // past the end of their buffers are 0), so they add nothing.
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(g.a_side + m0 * N, rows_m * N * 2);
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes, N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rQ =
+      kDQ ? make_rsrc(g.w.absmax, N * kblk) : make_rsrc(g.w.absmax, N * kblk * 4);
+  const int64_t nruns = (N * kblk + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
+
+  // dY chunk i of this thread: tile row 32 i + tid / 8, chunk tid % 8.
+  const uint32_t yoff = (uint32_t)((tid >> 3) * N * 2 + (tid & 7) * 16);
+  const uint32_t yrow_stride = (uint32_t)(32 * N * 2);
+  // Weight rows n = 64 s + 2 np + {0, 1}, columns k0 + 32 kq .. + 31.
+  const int np = tid & 31, kq = tid >> 5;
+  const int64_t kcol = k0 + kq * 32;
+  const bool kvalid = kcol < K;
+  const uint32_t coff = (uint32_t)((2 * np) * (K / 2) + (kvalid ? kcol / 2 : 0));
+  const uint32_t crow = (uint32_t)(K / 2);
+  const uint32_t qoff = (uint32_t)((2 * np) * kblk + (kvalid ? kcol / 64 : 0));
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  auto load_y = [&](int s, YStage &y) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      y.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rY, yoff + i * yrow_stride + s * 128, 0, 0);
+  };
+  auto load_c = [&](int s, CStage2 &c) {
+    const uint32_t rowbase = (uint32_t)(s * kS);   // first weight row of the step
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      c.c[r] = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + (rowbase + r) * crow, 0, 0);
+      const uint32_t b = qoff + (rowbase + r) * (uint32_t)kblk;
+      if (kDQ) {
+        c.q[r] = __builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0);
+        c.sc[r] = __builtin_amdgcn_raw_buffer_load_b32(rS, (b >> 8) * 4, 0, 0);
+      } else {
+        c.q[r] = __builtin_amdgcn_raw_buffer_load_b32(rQ, b * 4, 0, 0);
+      }
+    }
+  };
+  auto absmax_of = [&](const CStage2 &c, int r) {
+    const float a = kDQ ? float((int8_t)(uint8_t)c.q[r]) * __uint_as_float(c.sc[r]) : __uint_as_float(c.q[r]);
+    return kvalid ? a : 0.f;
+  };
+  auto cword = [](const CStage2 &c, int r, int w) {
+    const u32x4 &v = c.c[r];
+    return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+  };
+  auto write_y = [&](const YStage &y, int i, uint4 *sA) {
+    sA[swzd(i * 32 + (tid >> 3), tid & 7)] = __builtin_bit_cast(uint4, y.v[i]);
+  };
+  // Transposed weight write: the 4-byte word (n, n+1) of column k = kq * 32 + kl.
+  auto write_w = [&](uint4 *sB, int kl, uint32_t v) {
+    const int p = prow(kq * 32 + kl);
+    uint32_t *base = reinterpret_cast<uint32_t *>(&sB[swzd(p, np >> 2)]);
+    base[np & 3] = v;
+  };
+  auto decode_all = [&](const CStage2 &c, uint4 *sB) {
+    RowTable t[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) t[r] = make_row_table(absmax_of(c, r), g.t);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o[2][4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) decode8(t[r], cword(c, r, w), o[r]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        write_w(sB, w * 8 + 2 * q, perm(o[1][q], o[0][q], 0x05040100u));
+        write_w(sB, w * 8 + 2 * q + 1, perm(o[1][q], o[0][q], 0x07060302u));
+      }
+    }
+  };
+  auto read_frags = [&](const uint4 *sA, const uint4 *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      af[t] = __builtin_bit_cast(bf16x8, sA[swzd(wm * 128 + t * 32 + (lane & 31), c)]);
+      bw[t] = __builtin_bit_cast(bf16x8, sB[swzd(prow(wk * 128 + t * 32 + (lane & 31)), c)]);
+    }
+  };
+  auto mma = [&](const uint4 *sA, const uint4 *sB) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[4], bw[4];
+      read_frags(sA, sB, kk, af, bw);
+#pragma unroll
+      for (int tk = 0; tk < 4; ++tk)
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) acc[tk][tm] = mfma32x32x16(bw[tk], af[tm], acc[tk][tm]);
+    }
+  };
+
+  // One step: MFMAs on buffer P; dY chunks (yn) and the transposed weight (decoded from cn) of
+  // step s+1 go to buffer P^1 in between; loads of step s+2 go to ym / cm.
+  auto body = [&](int s, int P, YStage &ym, YStage &yn, CStage2 &cm, CStage2 &cn) {
+    const int s2 = s + 2 < last ? s + 2 : last;
+    load_y(s2, ym);
+    load_c(s2, cm);
+    const uint4 *A = sY[P];
+    const uint4 *B = sW[P];
+    uint4 *An = sY[P ^ 1];
+    uint4 *Bn = sW[P ^ 1];
+    bf16x8 af[2][4], bw[2][4];
+    read_frags(A, B, 0, af[0], bw[0]);
+
+    float a[2];
+    a[0] = absmax_of(cn, 0);
+    a[1] = absmax_of(cn, 1);
+    uint32_t pk[2][8];
+    RowTable t[2];
+    Dec8 dx[2];
+    uint32_t o[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tk = i >> 2, tm = i & 3;
+        const int slot = kk * 16 + i;
+        acc[tk][tm] = mfma32x32x16(bw[kk & 1][tk], af[kk & 1][tm], acc[tk][tm]);
+        if (kk < 3 && i < 4) {
+          const int c = (kk + 1) * 2 + (lane >> 5);
+          af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzd(wm * 128 + i * 32 + (lane & 31), c)]);
+          bw[(kk + 1) & 1][i] =
+              __builtin_bit_cast(bf16x8, B[swzd(prow(wk * 128 + i * 32 + (lane & 31)), c)]);
+        }
+        if ((slot & 7) == 2) write_y(yn, slot >> 3, An);
+        if (slot < 8) {
+          // tables: slot = 4 r + quarter
+          const int r = slot >> 2, qq = slot & 3;
+          pk[r][2 * qq] = pack_bf16x2(g.t.level[4 * qq] * a[r], g.t.level[4 * qq + 1] * a[r]);
+          pk[r][2 * qq + 1] = pack_bf16x2(g.t.level[4 * qq + 2] * a[r], g.t.level[4 * qq + 3] * a[r]);
+          t[r].L[qq] = perm(pk[r][2 * qq + 1], pk[r][2 * qq], 0x06040200u);
+          t[r].H[qq] = perm(pk[r][2 * qq + 1], pk[r][2 * qq], 0x07050301u);
+        } else {
+          // word w: slots 8 + 14 w .. : pieces of rows 0 and 1 interleaved (10 slots), then the
+          // 4 transposed pairs (4 slots)
+          const int w = (slot - 8) / 14, u = (slot - 8) % 14;
+          if (u < 10) {
+            const int r = u & 1, p = u >> 1;
+            if (p == 0) dx[r].d = cword(cn, r, w);
+            dec_piece(t[r], dx[r], p, o[r]);
+          } else {
+            const int q = u - 10;
+            write_w(Bn, w * 8 + 2 * q, perm(o[1][q], o[0][q], 0x05040100u));
+            write_w(Bn, w * 8 + 2 * q + 1, perm(o[1][q], o[0][q], 0x07060302u));
+          }
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  YStage y0, y1;
+  CStage2 c0, c1;
+  load_y(0, y0);
+  load_c(0, c0);
+  load_y(nsteps > 1 ? 1 : 0, y1);
+  load_c(nsteps > 1 ? 1 : 0, c1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) write_y(y0, i, sY[0]);
+  decode_all(c0, sW[0]);
+  __syncthreads();
+  int s = 0;
+#pragma unroll 1
+  for (; s + 2 <= nsteps; s += 2) {
+    body(s, 0, y0, y1, c0, c1);
+    body(s + 1, 1, y1, y0, c1, c0);
+  }
+  if (s < nsteps) body(s, 0, y0, y1, c0, c1);
+  __syncthreads();
+
+  const int nlora = (g.r + kS - 1) / kS;
+#pragma unroll 1
+  for (int j = 0; j < nlora; ++j) {
+    const int buf = j & 1;
+    stage_lora_dx(g, m0, k0, j * kS, sY[buf], sW[buf]);
+    __syncthreads();
+    mma(sY[buf], sW[buf]);
+    __syncthreads();
+  }
+
+  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns k..k+3 of row m.
+#pragma unroll
+  for (int tk = 0; tk < 4; ++tk)
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int64_t m = m0 + wm * 128 + tm * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + wk * 128 + tk * 32 + 8 * q + 4 * (lane >> 5);
+        if (m < g.M && k < g.C) {
+          const uint2 v = make_uint2(pack_bf16x2(acc[tk][tm][4 * q], acc[tk][tm][4 * q + 1]),
+                                     pack_bf16x2(acc[tk][tm][4 * q + 2], acc[tk][tm][4 * q + 3]));
+          *reinterpret_cast<uint2 *>(g.out + m * g.ldo + k) = v;
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st) {
+  const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
+  if (g.w.dq)
+    dx_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else
+    dx_fused_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace nf4q
