@@ -12,14 +12,15 @@
 // two weight rows (n, n+1) x 32 columns per step through two 16-entry bf16 tables (one per row
 // and block), pairs the rows per column with byte permutes and writes 4-byte (n, n+1) words.
 //
-// Pipeline per step s as in the forward kernel: dY chunks and codes of step s+2 are loaded into
-// registers, the 64 MFMAs of step s run on LDS buffer s & 1 while the dY chunks and the decoded,
-// transposed weight of step s+1 are written to buffer (s+1) & 1 between MFMA issues.
+// Pipeline per step s as in the forward kernel: the dY chunks of step s+1 and the codes of step
+// s+2 are loaded into registers, the 64 MFMAs of step s run on LDS buffer s & 1 while the decoded,
+// transposed weight and (in the second half) the dY chunks of step s+1 are written to buffer
+// (s+1) & 1 between MFMA issues.
 //
-// LDS: rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot c ^ ((r >> 1) & 7). The
-// transposed weight tile keeps column k in row p(k) = 32 (k / 32) + (k + k / 32) % 32, so the two
-// half-waves of a write (columns k and k + 32) land in different halves of the 256-byte bank
-// window.
+// LDS: the dY tile has rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot
+// c ^ ((r >> 1) & 7). The transposed weight tile pads its rows to 144 bytes (conflict-free for
+// both the 4-byte writes and the 16-byte fragment reads) and keeps column k in row
+// k ^ ((k / 32) & 1).
 #include "common.h"
 #include "launch.h"
 
@@ -32,9 +33,11 @@ constexpr int kThreads = 256;
 constexpr int kChunks = kT * kS / 8;
 
 __device__ __forceinline__ int swzd(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
-// Row of column k (0..255) in the transposed weight tile: rotated by k / 32 inside its group of
-// 32 rows (a bijection), so columns k and k + 32 sit in rows of opposite parity.
-__device__ __forceinline__ int prow(int k) { return (k & ~31) | ((k + (k >> 5)) & 31); }
+// Transposed weight tile: row p(k) of column k (0..255) holds 64 n-values in 144 bytes (128 bytes
+// of data, 16 of padding). p(k) flips the lowest bit of k in odd groups of 32 columns, so the two
+// half-waves of a write (columns k and k + 32) land in different halves of the bank window.
+constexpr int kWRow = 36;    // 32-bit words per transposed row (144 bytes)
+__device__ __forceinline__ int prow(int k) { return k ^ ((k >> 5) & 1); }
 
 __device__ __forceinline__ int tile_remap(int hw, int tiles) {
   const int per = tiles >> 3, rem = tiles & 7, x = hw & 7;
@@ -51,7 +54,7 @@ struct CStage2 {
 };
 
 // LoRA step staging: A-side U columns jb..jb+63 (rows m), B-side s * A^T (rows k, columns j).
-__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sA, uint4 *sB) {
+__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sA, uint32_t *sB) {
   const int tid = threadIdx.x;
 #pragma unroll 1
   for (int i = 0; i < 8; ++i) {
@@ -76,14 +79,14 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb,
       wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
     }
     sA[swzd(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-    sB[swzd(prow(row), c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    reinterpret_cast<uint4 *>(sB)[prow(row) * (kWRow / 4) + c] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
   }
 }
 
 template <bool kDQ>
 __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
   __shared__ uint4 sY[2][kChunks];   // dY tiles [m][n]
-  __shared__ uint4 sW[2][kChunks];   // decoded weight tiles, transposed [p(k)][n]
+  __shared__ uint32_t sW[2][kT * kWRow];   // decoded weight tiles, transposed [p(k)][n], padded
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,12 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
     sA[swzd(i * 32 + (tid >> 3), tid & 7)] = __builtin_bit_cast(uint4, y.v[i]);
   };
   // Transposed weight write: the 4-byte word (n, n+1) of column k = kq * 32 + kl.
-  auto write_w = [&](uint4 *sB, int kl, uint32_t v) {
-    const int p = prow(kq * 32 + kl);
-    uint32_t *base = reinterpret_cast<uint32_t *>(&sB[swzd(p, np >> 2)]);
-    base[np & 3] = v;
-  };
-  auto decode_all = [&](const CStage2 &c, uint4 *sB) {
+  auto write_w = [&](uint32_t *sB, int kl, uint32_t v) { sB[prow(kq * 32 + kl) * kWRow + np] = v; };
+  auto decode_all = [&](const CStage2 &c, uint32_t *sB) {
     RowTable t[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) t[r] = make_row_table(absmax_of(c, r), g.t);
@@ -180,15 +179,19 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
       }
     }
   };
-  auto read_frags = [&](const uint4 *sA, const uint4 *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
+  auto wfrag = [&](const uint32_t *sB, int t, int c) {
+    return __builtin_bit_cast(
+        bf16x8, reinterpret_cast<const uint4 *>(sB)[prow(wk * 128 + t * 32 + (lane & 31)) * (kWRow / 4) + c]);
+  };
+  auto read_frags = [&](const uint4 *sA, const uint32_t *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       af[t] = __builtin_bit_cast(bf16x8, sA[swzd(wm * 128 + t * 32 + (lane & 31), c)]);
-      bw[t] = __builtin_bit_cast(bf16x8, sB[swzd(prow(wk * 128 + t * 32 + (lane & 31)), c)]);
+      bw[t] = wfrag(sB, t, c);
     }
   };
-  auto mma = [&](const uint4 *sA, const uint4 *sB) {
+  auto mma = [&](const uint4 *sA, const uint32_t *sB) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 af[4], bw[4];
@@ -202,14 +205,16 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
 
   // One step: MFMAs on buffer P; dY chunks (yn) and the transposed weight (decoded from cn) of
   // step s+1 go to buffer P^1 in between; loads of step s+2 go to ym / cm.
-  auto body = [&](int s, int P, YStage &ym, YStage &yn, CStage2 &cm, CStage2 &cn) {
+  auto body = [&](int s, int P, CStage2 &cm, CStage2 &cn) {
+    const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    load_y(s2, ym);
+    YStage yn;
+    load_y(s1, yn);
     load_c(s2, cm);
     const uint4 *A = sY[P];
-    const uint4 *B = sW[P];
+    const uint32_t *B = sW[P];
     uint4 *An = sY[P ^ 1];
-    uint4 *Bn = sW[P ^ 1];
+    uint32_t *Bn = sW[P ^ 1];
     bf16x8 af[2][4], bw[2][4];
     read_frags(A, B, 0, af[0], bw[0]);
 
@@ -230,10 +235,9 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
         if (kk < 3 && i < 4) {
           const int c = (kk + 1) * 2 + (lane >> 5);
           af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzd(wm * 128 + i * 32 + (lane & 31), c)]);
-          bw[(kk + 1) & 1][i] =
-              __builtin_bit_cast(bf16x8, B[swzd(prow(wk * 128 + i * 32 + (lane & 31)), c)]);
+          bw[(kk + 1) & 1][i] = wfrag(B, i, c);
         }
-        if ((slot & 7) == 2) write_y(yn, slot >> 3, An);
+        if (kk >= 2 && (slot & 3) == 1) write_y(yn, (slot - 32) >> 2, An);
         if (slot < 8) {
           // tables: slot = 4 r + quarter
           const int r = slot >> 2, qq = slot & 3;
@@ -260,23 +264,24 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  YStage y0, y1;
   CStage2 c0, c1;
-  load_y(0, y0);
-  load_c(0, c0);
-  load_y(nsteps > 1 ? 1 : 0, y1);
-  load_c(nsteps > 1 ? 1 : 0, c1);
+  {
+    YStage y0;
+    load_y(0, y0);
+    load_c(0, c0);
+    load_c(nsteps > 1 ? 1 : 0, c1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) write_y(y0, i, sY[0]);
+    for (int i = 0; i < 8; ++i) write_y(y0, i, sY[0]);
+  }
   decode_all(c0, sW[0]);
   __syncthreads();
   int s = 0;
 #pragma unroll 1
   for (; s + 2 <= nsteps; s += 2) {
-    body(s, 0, y0, y1, c0, c1);
-    body(s + 1, 1, y1, y0, c1, c0);
+    body(s, 0, c0, c1);
+    body(s + 1, 1, c1, c0);
   }
-  if (s < nsteps) body(s, 0, y0, y1, c0, c1);
+  if (s < nsteps) body(s, 0, c0, c1);
   __syncthreads();
 
   const int nlora = (g.r + kS - 1) / kS;
