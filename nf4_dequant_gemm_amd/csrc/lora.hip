@@ -12,21 +12,28 @@
 
 namespace nf4q {
 
-__device__ __forceinline__ int swz8(int row, int c) { return row * 8 + (c ^ (row & 7)); }
-__device__ __forceinline__ int swz16(int row, int c) { return row * 16 + (c ^ (row & 7)); }
 
 // ------------------------------------------------------------------------------------ rowproj
-// Workgroup: 64 rows of `in` (one 16-row MFMA tile per wave) x all r (<= 128) columns; the
-// reduction [l_begin, l_end) of this split runs in steps of 64. p is staged in LDS per step.
+// out[m][j] = sum over l of in[m][l] * p[j][l]  (T: in = X, p = A;  U: in = dY, p = B^T).
+// Workgroup: 64 rows of `in` (one 16-row MFMA 16x16x32 tile per wave) x all r (<= 128) columns,
+// over one split of the reduction in steps of 64. Each step's in-tile (64 rows x 128 bytes) and
+// p-tile (r rows x 128 bytes) are loaded with fully coalesced 16-byte loads (8 lanes per
+// 128-byte row), two steps ahead, and staged in LDS (rows of 8 chunks, chunk c of row i at slot
+// c ^ ((i >> 1) & 7)), from where the fragments are read.
+__device__ __forceinline__ int swzr(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+
 template <int TN>
 __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict__ in, int64_t ldin,
                                                       const uint16_t *__restrict__ p, int64_t ldp,
                                                       int64_t M, int64_t L, int r, int64_t lsplit,
                                                       float *__restrict__ part,
                                                       uint16_t *__restrict__ out) {
-  __shared__ uint4 sP[TN * 16 * 8];
+  constexpr int PCH = TN * 16 * 8;                 // p-tile chunks per step
+  constexpr int PPT = (PCH + 255) / 256;           // p-tile chunks per thread
+  __shared__ uint4 sI[2][64 * 8];
+  __shared__ uint4 sP[2][TN * 16 * 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m = (int64_t)blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const int64_t mbase = (int64_t)blockIdx.x * 64;
   const int split = blockIdx.y;
   const int64_t lb = split * lsplit;
   const int64_t le = (lb + lsplit < L) ? lb + lsplit : L;
@@ -35,46 +42,78 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
 #pragma unroll
   for (int t = 0; t < TN; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 1
-  for (int64_t l0 = lb; l0 < le; l0 += 64) {
-    // stage p[j][l0 .. l0+63] for j < TN*16
+  struct Stage {
+    uint4 x[2];
+    uint4 q[PPT];
+  };
+  auto load = [&](int64_t l0, Stage &st) {
 #pragma unroll
-    for (int i = 0; i < (TN * 16 * 8 + 255) / 256; ++i) {
-      const int q = tid + 256 * i;
-      if (q < TN * 16 * 8) {
-        const int j = q >> 3, c = q & 7;
-        const int64_t l = l0 + c * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (j < r && l < le) v = *reinterpret_cast<const uint4 *>(p + (int64_t)j * ldp + l);
-        sP[swz8(j, c)] = v;
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int qd = tid + 256 * i;
+      const int row = qd >> 3, c = qd & 7;
+      const int64_t m = mbase + row, l = l0 + c * 8;
+      st.x[i] = (m < M && l < le) ? *reinterpret_cast<const uint4 *>(in + m * ldin + l) : make_uint4(0, 0, 0, 0);
     }
-    bf16x8 af[2];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int qd = tid + 256 * i;
+      const int j = qd >> 3, c = qd & 7;
+      const int64_t l = l0 + c * 8;
+      st.q[i] = (qd < PCH && j < r && l < le) ? *reinterpret_cast<const uint4 *>(p + (int64_t)j * ldp + l)
+                                              : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](const Stage &st, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int qd = tid + 256 * i;
+      sI[buf][swzr(qd >> 3, qd & 7)] = st.x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int qd = tid + 256 * i;
+      if (qd < PCH) sP[buf][swzr(qd >> 3, qd & 7)] = st.q[i];
+    }
+  };
+  auto mma = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int64_t l = l0 + kk * 32 + (lane >> 4) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < M && l < le) v = *reinterpret_cast<const uint4 *>(in + m * ldin + l);
-      af[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, sI[buf][swzr(wave * 16 + (lane & 15), c)]);
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        const bf16x8 bf =
-            __builtin_bit_cast(bf16x8, sP[swz8(t * 16 + (lane & 15), kk * 4 + (lane >> 4))]);
-        acc[t] = mfma16x16x32(af[kk], bf, acc[t]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, sP[buf][swzr(t * 16 + (lane & 15), c)]);
+        acc[t] = mfma16x16x32(a, b, acc[t]);
       }
     }
+  };
+
+  Stage s0, s1;
+  const int64_t nst = (le - lb + 63) / 64;
+  if (nst > 0) load(lb, s0);
+  if (nst > 1) load(lb + 64, s1);
+  if (nst > 0) store(s0, 0);
+  __syncthreads();
+  // step i: MFMAs on buffer i & 1; loads of step i+2; stores of step i+1 into the other buffer
+#pragma unroll 1
+  for (int64_t i = 0; i < nst; i += 2) {
+    if (i + 2 < nst) load(lb + (i + 2) * 64, s0);
+    mma(0);
+    if (i + 1 < nst) store(s1, 1);
+    __syncthreads();
+    if (i + 1 >= nst) break;
+    if (i + 3 < nst) load(lb + (i + 3) * 64, s1);
+    mma(1);
+    if (i + 2 < nst) store(s0, 0);
     __syncthreads();
   }
 
+  // D[m][j]: lane l holds column j = l % 16 and rows 4 (l / 16) + v.
 #pragma unroll
   for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      const int64_t row = mbase + wave * 16 + 4 * (lane >> 4) + v;
       const int j = t * 16 + (lane & 15);
       if (row < M && j < r) {
         if (part)
@@ -129,90 +168,155 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
 }
 
 // ------------------------------------------------------------------------------------ mreduce
-// Workgroup: 128 output columns c x all r (<= 128) rows, over one split of the M rows in steps of
-// 128. Both operands are transposed through LDS so that MFMA fragments read 8 consecutive m.
+// out[j][c] = sum over m of P[m][j] * Q[m][c]  (dA: P = U, Q = X;  dB: P = T, Q = dY).
+// Workgroup: 128 columns c x all r (<= 128) rows j, over one split of the M rows in stages of 64,
+// loaded two stages ahead with coalesced 16-byte loads (16 lanes per 256-byte row).
+// Both tiles are staged row-major in LDS (rows padded by 32 bytes so that the 4 rows a 16-lane
+// group touches fall in different bank ranges) and read with the gfx950 transposing LDS load
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive rows (m) of one column: exactly the
+// MFMA 16x16x32 operand layout with m as the reduction index.
+constexpr int kMR_BM = 64;                 // m per stage
+constexpr int kMR_BC = 128;                // columns per workgroup
+constexpr int kMR_QROW = kMR_BC + 16;      // Q row stride in bf16 (288 bytes)
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+}
+
 template <int TJ>
 __global__ __launch_bounds__(256) void mreduce_kernel(const uint16_t *__restrict__ P,
                                                       const uint16_t *__restrict__ Q, int64_t ldq,
                                                       int64_t M, int64_t C, int r, int64_t msplit,
                                                       float *__restrict__ part) {
-  __shared__ uint4 sPt[TJ * 32 * 16];   // [j][128 m]
-  __shared__ uint4 sQt[128 * 16];       // [c][128 m]
+  constexpr int PROW = TJ * 16 + 16;          // P row stride in bf16 (padded by 32 bytes)
+  __shared__ uint16_t sQ[2][kMR_BM * kMR_QROW];
+  __shared__ uint16_t sP[2][kMR_BM * PROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * 128;
+  const int64_t c0 = (int64_t)blockIdx.x * kMR_BC;
   const int split = blockIdx.y;
   const int64_t mb = split * msplit;
   const int64_t me = (mb + msplit < M) ? mb + msplit : M;
+  const bool pvec = (r & 7) == 0;
 
-  f32x16 acc[TJ];
+  f32x4 acc[TJ][2];
 #pragma unroll
   for (int t = 0; t < TJ; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+    for (int u = 0; u < 2; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int mg = tid & 15;     // m-group of 8
-  const int cg = tid >> 4;     // c-group (Q) / j-group (P) of 8
-#pragma unroll 1
-  for (int64_t ms = mb; ms < me; ms += 128) {
-    // Q tile: 8 rows x 8 columns per thread, transposed into sQt[c][m]
-    {
-      uint4 rows[8];
-      const int64_t c = c0 + cg * 8;
+  // staging registers: Q 4 chunks of 16 bytes, P up to TJ / 2 chunks (vector path)
+  struct Stage {
+    uint4 q[4];
+    uint4 p[(TJ + 1) / 2];
+  };
+  auto load = [&](int64_t ms, Stage &st) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = ms + mg * 8 + i;
-        rows[i] = (m < me && c < C) ? *reinterpret_cast<const uint4 *>(Q + m * ldq + c)
-                                    : make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t *w = reinterpret_cast<const uint32_t *>(rows);
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      const int row = q >> 4, ch = q & 15;
+      const int64_t m = ms + row, c = c0 + ch * 8;
+      st.q[i] = (m < me && c < C) ? *reinterpret_cast<const uint4 *>(Q + m * ldq + c)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+    if (pvec) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = (w[i * 4 + (e >> 1)] >> ((e & 1) * 16)) & 0xFFFFu;
-        sQt[swz16(cg * 8 + e, mg)] =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      for (int i = 0; i < (TJ + 1) / 2; ++i) {
+        const int q = tid + 256 * i;               // chunk q of the P tile: row q / (2 TJ)
+        const int row = q / (2 * TJ), ch = q % (2 * TJ);
+        const int64_t m = ms + row;
+        const int j = ch * 8;
+        st.p[i] = (row < kMR_BM && m < me && j < r) ? *reinterpret_cast<const uint4 *>(P + m * r + j)
+                                                    : make_uint4(0, 0, 0, 0);
       }
     }
-    // P tile: 8 rows x 8 j per thread, transposed into sPt[j][m]
-    if (cg < TJ * 4) {
-      uint32_t h[8][8];
+  };
+  auto store = [&](int64_t ms, const Stage &st, int buf) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = ms + mg * 8 + i;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = cg * 8 + e;
-          h[e][i] = (m < me && j < r) ? P[m * r + j] : 0u;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sPt[swz16(cg * 8 + e, mg)] = make_uint4(h[e][0] | (h[e][1] << 16), h[e][2] | (h[e][3] << 16),
-                                                h[e][4] | (h[e][5] << 16), h[e][6] | (h[e][7] << 16));
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      const int row = q >> 4, ch = q & 15;
+      *reinterpret_cast<uint4 *>(&sQ[buf][row * kMR_QROW + ch * 8]) = st.q[i];
     }
-    __syncthreads();
+    if (pvec) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      const bf16x8 bq = __builtin_bit_cast(bf16x8, sQt[swz16(wave * 32 + (lane & 31), c)]);
+      for (int i = 0; i < (TJ + 1) / 2; ++i) {
+        const int q = tid + 256 * i;
+        const int row = q / (2 * TJ), ch = q % (2 * TJ);
+        if (row < kMR_BM) *reinterpret_cast<uint4 *>(&sP[buf][row * PROW + ch * 8]) = st.p[i];
+      }
+    } else {
+      for (int q = tid; q < kMR_BM * TJ * 16; q += 256) {
+        const int row = q / (TJ * 16), j = q % (TJ * 16);
+        const int64_t m = ms + row;
+        sP[buf][row * PROW + j] = (m < me && j < r) ? P[m * r + j] : (uint16_t)0;
+      }
+    }
+  };
+
+  // transposing fragment reads: lane i of a 16-lane group gets rows 4 i' .. of its column
+  const int g16 = lane >> 4, l16 = lane & 15;
+  auto frag = [&](const uint16_t *S, int rowstride, int colbase, int kslice) {
+    // 8 consecutive m (= 8 g16 .. + 7 of the k-slice) of column colbase + l16, as two 4-row reads
+    const int m0 = kslice * 32 + g16 * 8 + (l16 >> 2);
+    const int col = colbase + 4 * (l16 & 3);
+    const s16x4 lo = lds_tr16(S + m0 * rowstride + col);
+    const s16x4 hi = lds_tr16(S + (m0 + 4) * rowstride + col);
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  auto mma = [&](int buf) {
+    const uint16_t *Sq = sQ[buf];
+    const uint16_t *Sp = sP[buf];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 bq[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) bq[u] = frag(Sq, kMR_QROW, wave * 32 + u * 16, ks);
 #pragma unroll
       for (int t = 0; t < TJ; ++t) {
-        const bf16x8 ap = __builtin_bit_cast(bf16x8, sPt[swz16(t * 32 + (lane & 31), c)]);
-        acc[t] = mfma32x32x16(ap, bq, acc[t]);
+        const bf16x8 ap = frag(Sp, PROW, t * 16, ks);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[t][u] = mfma16x16x32(ap, bq[u], acc[t][u]);
       }
     }
+  };
+
+  // stage i: MFMAs on buffer i & 1; loads of stage i+2; stores of stage i+1 into the other buffer
+  const int64_t nst = (me > mb) ? (me - mb + kMR_BM - 1) / kMR_BM : 0;
+  Stage s0, s1;
+  if (nst > 0) load(mb, s0);
+  if (nst > 1) load(mb + kMR_BM, s1);
+  if (nst > 0) store(mb, s0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int64_t i = 0; i < nst; i += 2) {
+    if (i + 2 < nst) load(mb + (i + 2) * kMR_BM, s0);
+    mma(0);
+    if (i + 1 < nst) store(mb + (i + 1) * kMR_BM, s1, 1);
+    __syncthreads();
+    if (i + 1 >= nst) break;
+    if (i + 3 < nst) load(mb + (i + 3) * kMR_BM, s1);
+    mma(1);
+    if (i + 2 < nst) store(mb + (i + 2) * kMR_BM, s0, 0);
     __syncthreads();
   }
 
+  // D[j][c] (16 x 16 blocks): lane l holds column c = l % 16 and rows j = 4 (l / 16) + v.
 #pragma unroll
   for (int t = 0; t < TJ; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int64_t c = c0 + wave * 32 + (lane & 31);
-      if (j < r && c < C) part[((int64_t)split * r + j) * C + c] = acc[t][v];
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = t * 16 + 4 * g16 + v;
+        const int64_t c = c0 + wave * 32 + u * 16 + l16;
+        if (j < r && c < C) part[((int64_t)split * r + j) * C + c] = acc[t][u][v];
+      }
 }
 
 __global__ void mreduce_final_kernel(const float *__restrict__ part, int64_t C, int r, int splits,
@@ -232,9 +336,9 @@ __global__ void mreduce_final_kernel(const float *__restrict__ part, int64_t C, 
 }
 
 int mreduce_splits(int64_t M, int64_t C) {
-  const int64_t ct = (C + 127) / 128;
+  const int64_t ct = (C + kMR_BC - 1) / kMR_BC;
   int64_t s = (1024 + ct - 1) / ct;
-  const int64_t maxs = (M + 127) / 128;
+  const int64_t maxs = (M + kMR_BM - 1) / kMR_BM;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
   return (int)s;
@@ -244,13 +348,13 @@ hipError_t launch_mreduce(const uint16_t *P, const uint16_t *Q, int64_t ldq, int
                           int r, float s, int splits, float *part, uint16_t *out,
                           bool transposed_out, hipStream_t st) {
   int64_t msplit = (M + splits - 1) / splits;
-  msplit = (msplit + 127) / 128 * 128;
-  const dim3 grid((unsigned)((C + 127) / 128), (unsigned)splits);
-  const int tj = (r + 31) / 32;
+  msplit = (msplit + kMR_BM - 1) / kMR_BM * kMR_BM;
+  const dim3 grid((unsigned)((C + kMR_BC - 1) / kMR_BC), (unsigned)splits);
+  const int tj = (r + 15) / 16;
   switch (tj) {
 #define MR_CASE(T) \
   case T: mreduce_kernel<T><<<grid, dim3(256), 0, st>>>(P, Q, ldq, M, C, r, msplit, part); break;
-    MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4)
+    MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4) MR_CASE(5) MR_CASE(6) MR_CASE(7) MR_CASE(8)
 #undef MR_CASE
     default: return hipErrorInvalidValue;
   }
