@@ -1,0 +1,399 @@
+// Decode-shaped (M <= 64) forward kernel: dequantise-on-the-fly GEMV of the NF4 weight with the
+// LoRA correction, Y = X deq(W)^T + s T B^T, bound by the weight stream [pyshine Unsloth code
+// tour, "Why You Need This": dequantize-on-the-fly GEMV for NF4 weights; "Inside Unsloth"
+// listing, "What You'll Learn", "LoRA and QLoRA": dequant, matmul and LoRA correction in one
+// launch; Unsloth v0.1.463-beta release article, "Background" on INT4: a separate dequantisation
+// step eats into the bandwidth that 4-bit storage saves].
+//
+// With M <= 64 rows of X the work is the 0.52 bytes per weight element streamed from HBM, so the
+// kernel is organised around the stream and around the vector-memory pipeline of the CU, whose
+// L1 tag lookups (not HBM) limit a naive version:
+//   * codes reach LDS by DMA (buffer_load ... lds) in fully coalesced 1 KB pieces, two stages
+//     ahead in a three-slot ring; a row's 16-byte chunks are XOR-swizzled by the row index so
+//     the MFMA-layout reads below hit 64 distinct banks;
+//   * the block constants of a stage (int8 codes and run scales of the double quantisation, or
+//     fp32 values) reach LDS by DMA too, one coalesced piece per row; every LDS byte arrives by
+//     DMA, so no LDS store waits for the DMA stages still in flight;
+//   * X fragments are read straight from global memory (L2-resident: every workgroup reads the
+//     same X), each instruction covering whole 64-byte pieces of 16 rows;
+//   * a code byte (two elements) becomes a pair of bf16 NF4 levels through a 256-entry table
+//     replicated 16 times in LDS; the table reads of the next row group are issued before the
+//     MFMAs of the current one;
+//   * MFMA 16x16x32 multiplies the unscaled levels by X; the block constant a (per weight row and
+//     64-element block) is applied to the block's fp32 partial sum afterwards:
+//         Y[m][n] += a(n, b) * sum_{k in block b} X[m][k] * level(code[n][k]).
+// Workgroup: 64 weight rows; its 4 waves split the K blocks (wave w takes blocks 2w, 2w+1 of each
+// 8-block stage) for all 64 rows, and the partial sums are added through LDS at the end.
+// Numerics: this path rounds the NF4 level (not level * a) to bf16 before the product, so it is
+// not bit-identical to the large-M kernel; both stay within the layer's tolerance.
+// Requires K % 256 == 0 (a whole number of 4-block groups per row keeps the block-constant DMA
+// dword-aligned and each group inside one scale run); the host sends other shapes to the
+// large-M kernel.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace nf4q {
+namespace {
+
+constexpr int kRows = 64;          // weight rows per workgroup
+constexpr int kBlkPerStage = 8;    // 64-element blocks per stage (512 columns)
+constexpr int kStages = 3;
+constexpr int kStageBytes = kRows * kBlkPerStage * 32;   // 16 KB
+constexpr int kCopies = 16;        // level-pair table copies: lane l reads copy l % 16
+constexpr int kTabBytes = 256 * kCopies * 4;              // 16 KB
+// block constants of a stage: 64 rows x 8 blocks, as int8 codes (512 B) + one scale per row and
+// 4-block half (512 B), or as fp32 (2 KB)
+template <bool kDQ> constexpr int const_bytes() { return kDQ ? 1024 : kRows * kBlkPerStage * 4; }
+
+struct DecArgs {
+  const uint16_t *X;
+  const uint16_t *T;
+  const uint16_t *B;
+  WDesc w;
+  int64_t M;
+  int r;
+  float s;
+  uint16_t *Y;
+  Tables t;
+};
+
+template <int MT, bool kDQ>
+__global__ __launch_bounds__(256) void decode_fwd_kernel(DecArgs g) {
+  // [0, 16 KB) level-pair table, then the ring of kStages slots (16 KB of codes + the stage's
+  // block constants). After the main loop the area from 0 holds the cross-wave reduction.
+  constexpr int kConst = const_bytes<kDQ>();
+  constexpr int kSlot = kStageBytes + kConst;
+  constexpr int kRedBytes = 4 * MT * 16 * 64 * 4;
+  constexpr int kArea = kTabBytes + kStages * kSlot;
+  static_assert(kRedBytes <= kArea, "reduction area");
+  __shared__ __align__(16) uint8_t smem[kArea];
+  uint8_t *stab = smem;
+  uint8_t *sring = smem + kTabBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = g.w.k, N = g.w.n;
+  const int kblk = (int)(K / 64);
+  const int nst = (kblk + kBlkPerStage - 1) / kBlkPerStage;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t rows = (N - n0 < kRows) ? N - n0 : kRows;
+
+  // byte -> (level[hi nibble], level[lo nibble]) as a packed bf16 pair (the high nibble is the
+  // earlier element); thread e writes the 16 copies of byte e
+  {
+    const uint32_t v = pack_bf16x2(g.t.level[tid >> 4], g.t.level[tid & 15]);
+    uint4 *dst = reinterpret_cast<uint4 *>(stab + tid * kCopies * 4);
+#pragma unroll
+    for (int c = 0; c < kCopies / 4; ++c) dst[c] = make_uint4(v, v, v, v);
+  }
+
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + n0 * (K / 2), rows * (K / 2));
+  const __amdgpu_buffer_rsrc_t rQ =
+      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows * kblk)
+          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + n0 * kblk, rows * kblk * 4);
+  const int64_t nruns = (N * kblk + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.X, g.M * K * 2);
+
+  // DMA: instruction i of wave w fills stage bytes [(4w + i) KB, +1 KB) = rows 4 (4w + i) .. +3
+  // (256 bytes each); lane L writes physical chunk L % 16 of row (L / 16), which holds logical
+  // chunk (L % 16) ^ (row % 16) of that row's 256-byte stage slice. Rows at or past N read as
+  // zero (outside the buffer resource).
+  uint32_t doff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 4 + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    doff[i] = (uint32_t)(row * (K / 2) + lc * 16);
+  }
+  // block-constant DMA (one instruction per wave and stage, two without double quantisation):
+  //   double quantisation: waves 0, 1 copy the int8 codes, lane l -> dword (l % 2) of the 8 codes
+  //     of row 32 w + l / 2; waves 2, 3 copy the scales, lane l -> run scale of 4-block half
+  //     (l % 2) of row 32 (w - 2) + l / 2 (a 4-aligned group of 4 blocks never straddles a run);
+  //   fp32: wave w, instruction i, lane l -> value (128 w + 64 i + l) % 8 of row / 8.
+  const __amdgpu_buffer_rsrc_t rCst = kDQ ? (wave < 2 ? rQ : rS) : rQ;
+  uint32_t coff[2];
+  if (kDQ) {
+    const int row = (wave & 1) * 32 + (lane >> 1), h = lane & 1;
+    coff[0] = wave < 2 ? (uint32_t)(row * kblk + 4 * h)                      // + 8 st
+                       : (uint32_t)((n0 + row) * kblk + 4 * h);              // block, not yet >> 8
+    coff[1] = 0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = 128 * wave + 64 * i + lane;
+      coff[i] = (uint32_t)(((idx >> 3) * kblk + (idx & 7)) * 4);              // + 32 st
+    }
+  }
+  auto dma = [&](int st) {
+    uint8_t *dst = sring + (st % kStages) * kSlot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rC, (__attribute__((address_space(3))) void *)(dst + (wave * 4 + i) * 1024), 16,
+          doff[i] + st * (kBlkPerStage * 32), 0, 0, 0);
+    uint8_t *cdst = dst + kStageBytes;
+    if (kDQ) {
+      const uint32_t o = wave < 2 ? coff[0] + st * kBlkPerStage
+                                  : ((coff[0] + st * kBlkPerStage) >> 8) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rCst, (__attribute__((address_space(3))) void *)(cdst + wave * 256), 4, o, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rQ, (__attribute__((address_space(3))) void *)(cdst + (2 * wave + i) * 256), 4,
+            coff[i] + st * (kBlkPerStage * 4), 0, 0, 0);
+    }
+  };
+  constexpr int kDmaPerStage = 4 + (kDQ ? 1 : 2);
+
+  const int nl = lane & 15, gl = lane >> 4;   // MFMA lane: column (weight row) and k-group
+
+  // This wave's X fragments of a stage, loaded one stage ahead (lane: row mt*16 + nl, columns
+  // kbase + 32 t + 8 gl .. +7 of block bb). Every load is issued, so a stage issues exactly
+  // 4 MT of them, which the stage waits below count.
+  struct Opnd {
+    bf16x8 x[2][MT][2];
+  };
+  auto load_opnd = [&](int st, Opnd &o) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int64_t kb = (int64_t)(st * kBlkPerStage + wave * 2 + bb) * 64;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t off = (uint32_t)(((int64_t)(mt * 16 + nl) * K + kb + t * 32 + gl * 8) * 2);
+          o.x[bb][mt][t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+        }
+    }
+  };
+  constexpr int kXPerStage = 4 * MT;
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Opnd o0, o1;
+  if (nst > 0) {
+    dma(0);
+    load_opnd(0, o0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (nst > 1) dma(1);
+
+  // One stage: the X operands of st are in cur; with kNext those of st + 1 are loaded into nxt,
+  // with kDma the codes and constants of st + 2 are requested. Both roles are compile-time so
+  // every path is straight-line code with a fixed number of loads in flight. The loop runs two
+  // stages per trip so cur and nxt swap roles without register copies (a copy would wait for
+  // the loads).
+  auto stage = [&](auto next_tag, auto dma_tag, int st, const Opnd &cur, Opnd &nxt) {
+    constexpr bool kNext = decltype(next_tag)::value, kDma = decltype(dma_tag)::value;
+    // Issue order per stage: X of st + 1, then the DMA of st + 2, so the newest loads are
+    // [DMA st+2, X st+1, DMA st+1, X st]; everything older, the DMA of st included, must be done
+    // before the barrier that opens the stage (the table writes too: lgkmcnt).
+    if constexpr (kNext) load_opnd(st + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);   // keep the X loads ahead of the DMA
+    if constexpr (kDma) {
+      dma(st + 2);
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerStage + 2 * kXPerStage)
+                   : "memory");
+    } else if constexpr (kNext) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStage + 2 * kXPerStage)
+                   : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    const uint8_t *S = sring + (st % kStages) * kSlot;
+    const uint8_t *C = S + kStageBytes;
+    // the lane's code dwords of (row 16 rg + nl, block bl, half t): logical bytes
+    // bl*32 + 16 t + 4 gl .. +3 of the row's stage slice, in chunk (2 bl + t) stored at
+    // chunk ^ (row % 16)
+    uint32_t cw[2][4][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = rg * 16 + nl, chunk = (wave * 2 + bb) * 2 + t;
+          cw[bb][rg][t] = *reinterpret_cast<const uint32_t *>(
+              S + row * 256 + ((chunk ^ (row & 15)) << 4) + gl * 4);
+        }
+    // block constants a(row 16 rg + nl, blocks 2 wave, 2 wave + 1); blocks past K get zero
+    float2 ca[4];
+    const bool live0 = st * kBlkPerStage + wave * 2 < kblk;
+    const bool live1 = st * kBlkPerStage + wave * 2 + 1 < kblk;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int row = rg * 16 + nl;
+      float a0, a1;
+      if (kDQ) {
+        // int8 codes as (low 7 bits) - (sign bit), times the scale of the row's 4-block half
+        const uint32_t q = *reinterpret_cast<const uint16_t *>(C + row * 8 + wave * 2);
+        const float sc = *reinterpret_cast<const float *>(C + 512 + (row * 2 + (wave >> 1)) * 4);
+        a0 = (float(q & 0x7Fu) - float(q & 0x80u)) * sc;
+        a1 = (float((q >> 8) & 0x7Fu) - float((q >> 8) & 0x80u)) * sc;
+      } else {
+        const float2 v = *reinterpret_cast<const float2 *>(C + (row * 8 + wave * 2) * 4);
+        a0 = v.x;
+        a1 = v.y;
+      }
+      ca[rg] = make_float2(live0 ? a0 : 0.f, live1 ? a1 : 0.f);
+    }
+    // table reads of group g = 4 bb + rg: element pairs of the 8 code bytes; the reads of
+    // group g + 1 are issued before the MFMAs of group g
+    const uint32_t lane_off = (uint32_t)(lane & (kCopies - 1)) * 4;
+    auto lookups = [&](int g, uint32_t o[8]) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[4 * t + j] = *reinterpret_cast<const uint32_t *>(
+              stab + ((((cw[g >> 2][g & 3][t] >> (8 * j)) & 0xFFu) << 6) | lane_off));
+    };
+    uint32_t lk[2][8];
+    lookups(0, lk[0]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int bb = g >> 2, rg = g & 3;
+      if (g + 1 < 8) lookups(g + 1, lk[(g + 1) & 1]);
+      const float a = bb ? ca[rg].y : ca[rg].x;
+      const uint32_t *o = lk[g & 1];
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(o[4], o[5], o[6], o[7]));
+      f32x4 part[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        part[mt] = mfma16x16x32(cur.x[bb][mt][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+        part[mt] = mfma16x16x32(cur.x[bb][mt][1], b1, part[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[mt][rg][v] += a * part[mt][v];
+    }
+    // every wave is done with this ring slot
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+
+  int st = 0;
+#pragma unroll 1
+  for (; st + 3 < nst; st += 2) {
+    stage(T1{}, T1{}, st, o0, o1);
+    stage(T1{}, T1{}, st + 1, o1, o0);
+  }
+  // 0 to 3 stages remain; the operands of stage st are in o0
+  if (nst - st == 3) {
+    stage(T1{}, T1{}, st, o0, o1);
+    stage(T1{}, F0{}, st + 1, o1, o0);
+    stage(F0{}, F0{}, st + 2, o0, o1);
+  } else if (nst - st == 2) {
+    stage(T1{}, F0{}, st, o0, o1);
+    stage(F0{}, F0{}, st + 1, o1, o0);
+  } else if (nst - st == 1) {
+    stage(F0{}, F0{}, st, o0, o1);
+  }
+
+  // LoRA term on the matrix cores: wave w adds s * T[m][:] . B[n][:] for its 16 output columns
+  // n = 16 w + (lane % 16) to its partial sums, in steps of 32 ranks (A operand: T row m, B
+  // operand: B row n, both k-contiguous; ranks at or past r, rows past M or N read as zero).
+  if (g.r > 0) {
+    const int r = g.r;
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, g.M * r * 2);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + n0 * r, rows * r * 2);
+    const int nrow = wave * 16 + nl;
+#pragma unroll 1
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      uint32_t tb[MT][8], bb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + gl * 8 + e;
+        const bool in = j < r;
+        bb[e] = in ? __builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)((nrow * r + j) * 2), 0, 0) : 0u;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          tb[mt][e] = in ? __builtin_amdgcn_raw_buffer_load_b16(
+                               rT, (uint32_t)(((mt * 16 + nl) * r + j) * 2), 0, 0)
+                         : 0u;
+      }
+      u32x4 bw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bw[q] = (bb[2 * q] & 0xFFFFu) | (bb[2 * q + 1] << 16);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        u32x4 tw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tw[q] = (tb[mt][2 * q] & 0xFFFFu) | (tb[mt][2 * q + 1] << 16);
+        const f32x4 lp = mfma16x16x32(__builtin_bit_cast(bf16x8, tw), __builtin_bit_cast(bf16x8, bw),
+                                      f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)   // acc[mt][wave], without a dynamic register index
+          if (rg == wave)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mt][rg][v] += g.s * lp[v];
+      }
+    }
+  }
+
+  // Sum the 4 waves' partial sums through LDS, then store.
+  // acc[mt][rg] holds D[m][n] for m = mt*16 + 4 (lane / 16) + v, n = rg*16 + lane % 16.
+  float *red = reinterpret_cast<float *>(smem);     // [4 waves][MT*16 m][64 n]
+  static_assert(4 * MT * 16 * 64 * 4 <= (int)sizeof(smem), "reduction area");
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + 4 * gl + v, n = rg * 16 + nl;
+        red[(wave * MT * 16 + m) * 64 + n] = acc[mt][rg][v];
+      }
+  __syncthreads();
+  for (int i = tid; i < MT * 16 * 64; i += 256) {
+    const int m = i / 64, n = i % 64;
+    const float y = red[m * 64 + n] + red[(MT * 16 + m) * 64 + n] +
+                    red[(2 * MT * 16 + m) * 64 + n] + red[(3 * MT * 16 + m) * 64 + n];
+    const int64_t gm = m, gn = n0 + n;
+    if (gm < g.M && gn < N) g.Y[gm * N + gn] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_fwd(const GemmArgs &ga, hipStream_t st) {
+  DecArgs g;
+  g.X = ga.a_side;
+  g.T = ga.lora_a;
+  g.B = ga.lora_b;
+  g.w = ga.w;
+  g.M = ga.M;
+  g.r = ga.r;
+  g.s = ga.s;
+  g.Y = ga.out;
+  g.t = ga.t;
+  const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
+  const int mt = (int)((ga.M + 15) / 16);
+#define DEC_CASE(T)                                                              \
+  case T:                                                                        \
+    if (ga.w.dq)                                                                 \
+      decode_fwd_kernel<T, true><<<dim3(grid), dim3(256), 0, st>>>(g);           \
+    else                                                                         \
+      decode_fwd_kernel<T, false><<<dim3(grid), dim3(256), 0, st>>>(g);          \
+    break;
+  switch (mt) {
+    DEC_CASE(1) DEC_CASE(2) DEC_CASE(3) DEC_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef DEC_CASE
+  return hipGetLastError();
+}
+
+}  // namespace nf4q

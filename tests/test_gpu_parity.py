@@ -143,6 +143,42 @@ def test_layer_parity(lib, M, K, N, r, dq, s):
         check_close("dB", f32(dBg), dB)
 
 
+# Forward with at most 64 rows of X and K % 256 == 0 takes the weight-streaming kernel: stage
+# counts 1..9 of 512 columns (one to three stages after the two-stage main loop), half-live last
+# stages, ragged last 64-row tile, every 16-row m-tile count. K % 256 != 0 falls back to the
+# large-M kernel (last two cases).
+DECODE_CASES = [
+    # M, K, N, r, dq
+    (1, 256, 8, 1, 0),
+    (16, 768, 200, 16, 256),
+    (17, 1280, 72, 8, 0),
+    (40, 2048, 136, 4, 256),
+    (64, 2560, 64, 32, 256),
+    (5, 4352, 264, 0, 0),
+    (33, 4352, 136, 16, 256),
+    (48, 3328, 520, 64, 0),
+    (16, 576, 200, 16, 256),
+    (9, 1600, 72, 8, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,dq", DECODE_CASES)
+def test_decode_forward_parity(lib, M, K, N, r, dq):
+    s = 1.5
+    say(f"decode-shaped forward M={M} K={K} N={N} r={r} dq={dq}")
+    X, W, A, _, _ = rand_layer(M, K, N, r, seed=M * 11 + K + N)
+    B = wl.normal_bf16(M * 11 + K + N + 9, (N, r), 0.1)   # LoRA term comparable to the base term
+    qo = nf4.quantize(W.float().numpy(), dq)
+    Y, T = qlora.forward(f32(X), nf4.dequantize_f32(qo), f32(A), f32(B), s)
+    qg = lib.nf4_quantize(W.to(DEV), dq)
+    Ad, Bd = (A.to(DEV), B.to(DEV)) if r else (None, None)
+    Yg, Tg = lib.qlora_fwd(X.to(DEV), qg, Ad, Bd, s)
+    torch.cuda.synchronize()
+    check_close("Y", f32(Yg), Y)
+    if r:
+        check_close("T", f32(Tg), T)
+
+
 def test_identity_probe_forward(lib):
     """X = I_K, r = 0: Y = bf16(deq(W))^T bit for bit (one exact product per output)."""
     K, N = 256, 264
