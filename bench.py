@@ -3,21 +3,35 @@
 
 One step = one forward + backward of the layer on the "down" workload (a Llama down_proj training
 step: X bf16 [16384, 14336], W NF4 [4096, 14336] with double-quantised absmax, LoRA r = 32, s = 1,
-dY ~ N(0, 1e-2)): T = X A^T, Y = X deq(W)^T + s T B^T, then U = dY B, dX, dA, dB. Inputs are
-seeded synthetic tensors of that shape, resident in HBM before timing starts; W is quantised once
-(untimed), as a frozen base weight is.
+dY ~ N(0, 1e-2)):
 
-Output: one JSON line with the whole-step throughput (algorithmic matmul flops / step time), the
-roofline of the dominant kernel (the fused dequant-GEMM-LoRA forward, timed with HIP events on
-the stream it runs on) and the CPU oracle timed on a bounded row sample of the same workload.
+    qlora_lora_down   T = X A^T
+    qlora_fwd_fused   Y = X deq(W)^T + s T B^T             (one launch)
+    qlora_bwd (dX=0)  U = dY B, dA = s U^T X, dB = s dY^T T
+    qlora_bwd_dx      dX = dY deq(W) + s U A                (one launch)
+
+Inputs are seeded synthetic tensors of that shape, resident in HBM before timing starts. W is
+quantised once (untimed), as a frozen base weight is, and then copied so that the steps rotate
+over enough distinct copies (>= 512 MB together) that no step finds its weight in the 256 MB
+last-level cache or the L2 left there by the step before (the weight is the only input read by
+every step; X and dY of the large workloads are far larger than the caches).
+
+Output: one JSON line with the whole-step throughput (algorithmic matmul flops / step time on the
+host clock), the roofline of the dominant kernel (the larger of the two fused dequant-GEMM
+launches, timed with HIP events on the stream it runs on), the weight-stream rate of the
+decode-shaped forward (M = 16, K = 8192, N = 28672: weight-stream bytes / whole qlora_fwd time)
+and the CPU oracle timed on a bounded row sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload down] [--no-cpu-baseline]
+                    [--no-weight-stream] [--copy-calibration]
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -28,6 +42,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused QLoRA fwd+bwd TFLOP/s and weight-stream GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+COLD_BYTES = 512 << 20        # rotate weight copies until they add up to this
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"qlora_fwd_fused": "fwd.hip", "qlora_bwd_dx": "dx.hip",
+                  "qlora_fwd_fused (decode)": "decode.hip"}
 
 
 def parse():
@@ -37,8 +55,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-weight-stream", action="store_true",
+                    help="skip the decode-shaped weight-stream measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--wcopies", type=int, default=0,
+                    help="distinct weight copies to rotate over (0: enough for 512 MB)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -46,10 +70,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def pct(vals, q):
+    v = sorted(vals)
+    i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
+    return v[i]
+
+
 class Layer:
     """Preallocated device buffers and direct C-ABI calls for one workload."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, wcopies=0):
         import torch
         import nf4_dequant_gemm_amd as lib
         import workloads as wl
@@ -58,13 +88,16 @@ class Layer:
         host = {t: wl.tensor(w, t) for t in ("X", "W", "A", "B")}
         if w.backward:
             host["dY"] = wl.tensor(w, "dY")
-        log(f"inputs generated in {time.time() - t0:.1f}s")
+        log(f"{w.name}: inputs generated in {time.time() - t0:.1f}s")
         self.X = host["X"].to(dev)
         self.A = host["A"].to(dev)
         self.B = host["B"].to(dev)
         self.dY = host["dY"].to(dev) if w.backward else None
-        self.q = lib.nf4_quantize(host["W"].to(dev), w.dq_block)
+        q = lib.nf4_quantize(host["W"].to(dev), w.dq_block)
         del host
+        n = wcopies or max(1, min(64, math.ceil(COLD_BYTES / w.weight_stream_bytes())))
+        self.copies = [q] + [q.clone() for _ in range(n - 1)]
+        self.qs = [c.c_struct() for c in self.copies]
         M, N, K, r = w.M, w.N, w.K, w.r
         bf = torch.bfloat16
         self.Y = torch.empty(M, N, dtype=bf, device=dev)
@@ -77,7 +110,6 @@ class Layer:
             self.dB = torch.empty(N, r, dtype=bf, device=dev)
             self.bws = self.c.qlora_bwd_workspace_bytes(M, N, K, r)
             self.ws_b = torch.empty(max(self.bws, 1), dtype=torch.uint8, device=dev)
-        self.qs = self.q.c_struct()
         self.stream = torch.cuda.current_stream(dev)
         self.sp = ctypes.c_void_p(self.stream.cuda_stream)
         p = lambda t: ctypes.c_void_p(t.data_ptr())
@@ -87,56 +119,99 @@ class Layer:
         if st != 0:
             raise RuntimeError(self.c.nf4_last_error().decode())
 
-    def lora_down(self):
+    def lora_down(self, i):
         w, p = self.w, self.p
         self.check(self.c.qlora_lora_down(p["X"], w.M, w.K, p["A"], w.r, p["T"], p["ws_f"], self.fws, self.sp))
 
-    def fwd_fused(self):
+    def fwd_fused(self, i):
         w, p = self.w, self.p
-        self.check(self.c.qlora_fwd_fused(p["X"], w.M, ctypes.byref(self.qs), p["T"], p["B"], w.r,
-                                          w.s, p["Y"], self.sp))
+        self.check(self.c.qlora_fwd_fused(p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["T"],
+                                          p["B"], w.r, w.s, p["Y"], self.sp))
 
-    def bwd(self):
+    def bwd_lora(self, i):
+        """U (left at the start of the workspace), dA and dB: qlora_bwd without dX."""
         w, p = self.w, self.p
-        self.check(self.c.qlora_bwd(p["dY"], p["X"], w.M, ctypes.byref(self.qs), p["A"], p["B"], w.r,
-                                    w.s, p["T"], p["dX"], p["dA"], p["dB"], p["ws_b"], self.bws, self.sp))
+        self.check(self.c.qlora_bwd(p["dY"], p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["A"],
+                                    p["B"], w.r, w.s, p["T"], None, p["dA"], p["dB"], p["ws_b"], self.bws,
+                                    self.sp))
+
+    def bwd_dx(self, i):
+        w, p = self.w, self.p
+        self.check(self.c.qlora_bwd_dx(p["dY"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["ws_b"],
+                                       p["A"], w.r, w.s, p["dX"], self.sp))
 
 
-def run_gpu(args, w):
+PHASES = ("lora_down", "fwd_fused", "bwd_lora", "bwd_dx")
+
+
+def time_layer(L, steps, warmup):
+    """Run warmup + steps steps; per-phase HIP-event times (ms) and the host-clock step time."""
     import torch
-    dev = torch.device("cuda:0")
-    L = Layer(w, dev)
-    for _ in range(args.warmup):
-        L.lora_down()
-        L.fwd_fused()
-        if w.backward:
-            L.bwd()
+    w = L.w
+    calls = [L.lora_down, L.fwd_fused] + ([L.bwd_lora, L.bwd_dx] if w.backward else [])
+    for i in range(warmup):
+        for c in calls:
+            c(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         e = ev[s]
         e[0].record(L.stream)
-        L.lora_down()
-        e[1].record(L.stream)
-        L.fwd_fused()
-        e[2].record(L.stream)
-        if w.backward:
-            L.bwd()
-        e[3].record(L.stream)
+        for j, c in enumerate(calls):
+            c(warmup + s)
+            e[j + 1].record(L.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = lambda a, b: sum(ev[s][a].elapsed_time(ev[s][b]) for s in range(args.steps)) / args.steps
-    return {
-        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
-        "lora_down_ms": ms(0, 1), "fused_fwd_ms": ms(1, 2), "bwd_ms": ms(2, 3), "event_step_ms": ms(0, 3),
-    }
+    per = {}
+    for j in range(len(calls)):
+        v = [ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)]
+        per[PHASES[j]] = {"mean": sum(v) / len(v), "median": pct(v, 0.5), "p10": pct(v, 0.1),
+                          "p90": pct(v, 0.9)}
+    return (t1 - t0) * 1e3 / steps, per
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "nf4_dequant_gemm_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(name, workload):
+    """HBM bytes per launch from the committed counter summary, if it still matches the source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(f"{name}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("sha256") != source_sha(name):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def run_weight_stream(dev, steps, warmup):
+    """Decode-shaped forward (M = 16): weight-stream bytes / whole qlora_fwd time, cold weights."""
+    import workloads as wl
+    w = wl.WORKLOADS["decode"]
+    L = Layer(w, dev)
+    _, per = time_layer(L, steps, warmup)
+    fwd_ms = per["lora_down"]["median"] + per["fwd_fused"]["median"]
+    wb = w.weight_stream_bytes()
+    gbs = wb / (fwd_ms * 1e-3) / 1e9
+    kern = wb / (per["fwd_fused"]["median"] * 1e-3) / 1e9
+    out = {"workload": f"decode: X [16,8192] bf16, W NF4 [28672,8192] double-quant int8/256, LoRA r=16, fwd",
+           "weight_stream_bytes": wb, "qlora_fwd_us": round(fwd_ms * 1e3, 2),
+           "value": round(gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+           "fused_kernel_us": round(per["fwd_fused"]["median"] * 1e3, 2),
+           "fused_kernel_GBps": round(kern, 1),
+           "cold": f"{len(L.copies)} rotating weight copies"}
+    del L
+    return out
 
 
 def run_cpu_baseline(w, target_s):
     """The oracle (float64 numpy/BLAS) on a row sample of the same step."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     import workloads as wl
@@ -171,35 +246,69 @@ def run_cpu_baseline(w, target_s):
                       f"(numpy/BLAS), {dt:.1f}s wall; W dequantised once outside the timing"}
 
 
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy, five times: the reference for HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
     import workloads as wl
     w = wl.WORKLOADS[args.workload]
-    g = run_gpu(args, w)
+    dev = torch.device("cuda:0")
+    L = Layer(w, dev, args.wcopies)
+    step_ms, per = time_layer(L, args.steps, args.warmup)
+    ncopies = len(L.copies)
+    del L
+    torch.cuda.empty_cache()
     flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0)
-    value = flops / (g["ms_per_step"] * 1e-3) / 1e12
-    fused_flops = 2 * w.M * w.N * w.K + 2 * w.M * w.N * w.r
-    achieved = fused_flops / (g["fused_fwd_ms"] * 1e-3) / 1e12
-    log(json.dumps(g))
+    value = flops / (step_ms * 1e-3) / 1e12
+    M, N, K, r = w.M, w.N, w.K, w.r
+    kern = {"qlora_fwd_fused": (per["fwd_fused"], 2 * M * N * K + 2 * M * N * r)}
+    if w.backward:
+        kern["qlora_bwd_dx"] = (per["bwd_dx"], 2 * M * N * K + 2 * M * r * K)
+    name = max(kern, key=lambda k: kern[k][0]["mean"])
+    t, work = kern[name]
+    if M <= 64:     # the decode-shaped forward: bound by the weight stream
+        name = "qlora_fwd_fused (decode)"
+        achieved = w.weight_stream_bytes() / (t["mean"] * 1e-3) / 1e9
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = work / (t["mean"] * 1e-3) / 1e12
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["kernel_us"] = {k: round(v * 1e3, 2) for k, v in t.items()}
+    roof["traffic"] = traffic_for(name, w.name)
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(g["ms_per_step"], 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: X [{w.M},{w.K}] bf16, W NF4 [{w.N},{w.K}] block 64"
+        "config": {"workload": f"{w.name}: X [{M},{K}] bf16, W NF4 [{N},{K}] block 64"
                                f"{' double-quant int8/256' if w.dq_block else ' fp32 absmax'}, "
-                               f"LoRA r={w.r} s={w.s}, {'fwd+bwd' if w.backward else 'fwd'}",
-                   "M": w.M, "K": w.K, "N": w.N, "r": w.r,
-                   "phase_ms": {k: round(v, 4) for k, v in g.items() if k != "ms_per_step"}},
-        "roofline": {"kernel": "qlora_fwd_fused (fused NF4-dequant GEMM + LoRA, one launch)",
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                               f"LoRA r={r} s={w.s}, {'fwd+bwd' if w.backward else 'fwd'}",
+                   "M": M, "K": K, "N": N, "r": r, "weight_copies": ncopies,
+                   "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}},
+        "roofline": roof,
     }
+    if not args.no_weight_stream and w.name != "decode":
+        out["weight_stream"] = run_weight_stream(dev, 20, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -131,16 +131,27 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
 size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 
 /* Backward of the QLoRA layer, given the upstream gradient dY bf16 [m, n] and T from qlora_fwd:
- *   U  = bf16(dY B)                               (kept in the workspace)
+ *   U  = bf16(dY B)                               (left in the workspace: see below)
  *   dX = bf16(dY deq(W) + s U A)      bf16 [m, k]  (skipped when dX is NULL)
  *   dA = bf16(s U^T X)                bf16 [r, k]
  *   dB = bf16(s dY^T T)               bf16 [n, r]
  * Sums over m are taken in float32 in a fixed order (deterministic). With r == 0, A, B, T, dA
  * and dB are ignored and only dX is produced.
+ * When r > 0 the call leaves U (bf16 [m, r], row-major) in the first m*r*2 bytes of ws, where
+ * qlora_bwd_dx can take it: qlora_bwd with dX == NULL followed by qlora_bwd_dx is the same work
+ * as one qlora_bwd call.
  * Errors: as qlora_fwd, plus NF4_EINVAL when ws is smaller than qlora_bwd_workspace_bytes. */
 int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, const void *A,
               const void *B, int32_t r, float s, const void *T, void *dX, void *dA, void *dB,
               void *ws, size_t ws_bytes, void *stream);
+
+/* The input-gradient launch of qlora_bwd on its own, for callers that hold U or that time it:
+ * dX = bf16(dY deq(W) + s U A) in ONE kernel launch (the NF4 weight decoded on the fly, read
+ * along n; the rank-r term as extra reduction steps). dY bf16 [m, n], U bf16 [m, r] (= dY B),
+ * A bf16 [r, k], dX bf16 [m, k]; U and A may be NULL when r == 0. No workspace.
+ * Errors: as qlora_fwd (dY, U, A checked where qlora_fwd checks X, A, B). */
+int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,
+                 int32_t r, float s, void *dX, void *stream);
 
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);

@@ -26,7 +26,7 @@ NF4_BF16, NF4_F32 = 0, 1
 
 EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
-            "qlora_bwd", "nf4_last_error")
+            "qlora_bwd", "qlora_bwd_dx", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -61,6 +61,7 @@ def library() -> ctypes.CDLL:
         "qlora_fwd_fused": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
         "qlora_bwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
+        "qlora_bwd_dx": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
         "nf4_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -115,6 +116,11 @@ class NF4Tensor:
         return _NF4TensorC(self.n, self.k, 64, self.dq_block, self.codes.data_ptr(),
                            self.absmax.data_ptr(),
                            self.scale.data_ptr() if self.scale is not None else None)
+
+    def clone(self) -> "NF4Tensor":
+        """A copy in new device buffers (same values, different addresses)."""
+        return NF4Tensor(self.n, self.k, self.dq_block, self.codes.clone(), self.absmax.clone(),
+                         self.scale.clone() if self.scale is not None else None)
 
     @staticmethod
     def empty(n: int, k: int, dq_block: int, device) -> "NF4Tensor":
@@ -238,6 +244,22 @@ def qlora_bwd(dY: torch.Tensor, X: torch.Tensor, q: NF4Tensor, A: Optional[torch
     _check(lib.qlora_bwd(_ptr(dY), _ptr(X), m, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s),
                          _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(dev)))
     return dX, dA, dB
+
+
+def qlora_bwd_dx(dY: torch.Tensor, q: NF4Tensor, U: Optional[torch.Tensor], A: Optional[torch.Tensor],
+                 s: float) -> torch.Tensor:
+    """dX = bf16(dY deq(W) + s U A) in one launch; U = dY B as qlora_bwd computes it."""
+    m = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(dY, "dY", torch.bfloat16, (m, q.n))
+    if r:
+        _need(U, "U", torch.bfloat16, (m, r))
+        _need(A, "A", torch.bfloat16, (r, q.k))
+    dX = torch.empty(m, q.k, dtype=torch.bfloat16, device=dY.device)
+    st = q.c_struct()
+    _check(library().qlora_bwd_dx(_ptr(dY), m, ctypes.byref(st), _ptr(U), _ptr(A), r, float(s),
+                                  _ptr(dX), _stream(dY.device)))
+    return dX
 
 
 class QLoRALinearFunction(torch.autograd.Function):

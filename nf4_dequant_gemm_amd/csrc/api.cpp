@@ -140,6 +140,25 @@ int check_layer(const void *X, int64_t m, const nf4_tensor *W, const void *A, co
   return NF4_OK;
 }
 
+hipError_t launch_dx(const uint16_t *dy, int64_t m, const nf4_tensor *W, const uint16_t *U,
+                     const uint16_t *A, int32_t r, float s, uint16_t *dX, hipStream_t sm) {
+  nf4q::GemmArgs g;
+  g.a_side = dy;
+  g.lda = W->n;
+  g.lora_a = U;
+  g.lora_b = A;
+  g.w = desc(W);
+  g.M = m;
+  g.C = W->k;
+  g.R = W->n;
+  g.r = r;
+  g.s = s;
+  g.out = dX;
+  g.ldo = W->k;
+  g.t = tables();
+  return nf4q::launch_gemm_dx(g, sm);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct FwdWs {
@@ -319,21 +338,7 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
     if (e != hipSuccess) return hip_status(e, "qlora_bwd U launch");
   }
   if (dX) {
-    nf4q::GemmArgs g;
-    g.a_side = dy;
-    g.lda = n;
-    g.lora_a = U;
-    g.lora_b = (const uint16_t *)A;
-    g.w = desc(W);
-    g.M = m;
-    g.C = k;
-    g.R = n;
-    g.r = r;
-    g.s = s;
-    g.out = (uint16_t *)dX;
-    g.ldo = k;
-    g.t = tables();
-    e = nf4q::launch_gemm_dx(g, sm);
+    e = launch_dx(dy, m, W, U, (const uint16_t *)A, r, s, (uint16_t *)dX, sm);
     if (e != hipSuccess) return hip_status(e, "qlora_bwd dX launch");
   }
   if (r > 0) {
@@ -345,6 +350,17 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
     if (e != hipSuccess) return hip_status(e, "qlora_bwd dB launch");
   }
   return ok();
+}
+
+int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,
+                 int32_t r, float s, void *dX, void *stream) {
+  // dY [m, n] plays the part of X in the layer checks, U [m, r] and A [r, k] that of A and B
+  int st = check_layer(dY, m, W, U, A, r);
+  if (st) return st;
+  if (!dX || !aligned16(dX)) return fail(NF4_EINVAL, "dX must be non-NULL and 16-byte aligned");
+  return hip_status(launch_dx((const uint16_t *)dY, m, W, (const uint16_t *)U, (const uint16_t *)A,
+                              r, s, (uint16_t *)dX, (hipStream_t)stream),
+                    "qlora_bwd_dx launch");
 }
 
 }  // extern "C"

@@ -266,3 +266,32 @@ def test_autograd_function(lib):
     check_close("dX", f32(Xd.grad), dXo)
     check_close("dA", f32(Ad.grad), dAo)
     check_close("dB", f32(Bd.grad), dBo)
+
+
+def test_bwd_split_matches_bwd(lib):
+    """qlora_bwd without dX leaves U at the start of the workspace; qlora_bwd_dx on that U gives
+    the dX of a full qlora_bwd bit for bit, and U matches dY B from the oracle."""
+    import ctypes
+    M, K, N, r, s = 200, 512, 264, 16, 0.5
+    X, W, A, B, dY = rand_layer(M, K, N, r, seed=123)
+    qg = lib.nf4_quantize(W.to(DEV), 256)
+    Xd, Ad, Bd, dYd = X.to(DEV), A.to(DEV), B.to(DEV), dY.to(DEV)
+    _, T = lib.qlora_fwd(Xd, qg, Ad, Bd, s)
+    dX_full, dA_full, dB_full = lib.qlora_bwd(dYd, Xd, qg, Ad, Bd, s, T)
+    c = lib.library()
+    wsb = c.qlora_bwd_workspace_bytes(M, N, K, r)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    dA = torch.empty(r, K, dtype=torch.bfloat16, device=DEV)
+    dB = torch.empty(N, r, dtype=torch.bfloat16, device=DEV)
+    st = qg.c_struct()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert c.qlora_bwd(p(dYd), p(Xd), M, ctypes.byref(st), p(Ad), p(Bd), r, s, p(T), None, p(dA), p(dB),
+                       p(ws), wsb, sp) == 0
+    U = ws[: M * r * 2].view(torch.bfloat16).view(M, r)
+    dX = lib.qlora_bwd_dx(dYd, qg, U, Ad, s)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), dX_full.view(torch.int16))
+    assert torch.equal(dA.view(torch.int16), dA_full.view(torch.int16))
+    assert torch.equal(dB.view(torch.int16), dB_full.view(torch.int16))
+    check_close("U", f32(U), f32(dY).astype(np.float64) @ f32(B).astype(np.float64))

@@ -129,6 +129,16 @@ def test_layer_calls_reject_bad_arguments():
     assert bwd(dA=None) == m.NF4_EINVAL
     assert bwd(r=200) == m.NF4_EINVAL
     assert "workspace" in lib.nf4_last_error().decode() or lib.nf4_last_error()
+    dx = lambda **kw: lib.qlora_bwd_dx(kw.get("dY", FAKE), kw.get("m", 100), ctypes.byref(kw.get("q", q)),
+                                        kw.get("U", FAKE), kw.get("A", FAKE), kw.get("r", 8), 1.0,
+                                        kw.get("dX", FAKE), None)
+    assert dx(dY=None) == m.NF4_EINVAL
+    assert dx(dX=None) == m.NF4_EINVAL
+    assert dx(U=None) == m.NF4_EINVAL
+    assert dx(A=ctypes.c_void_p(4104)) == m.NF4_EINVAL
+    assert dx(m=0) == m.NF4_EINVAL
+    assert dx(r=129) == m.NF4_EINVAL
+    assert dx(q=wdesc(n=60, k=128)) == m.NF4_EUNSUPPORTED
 
 
 def test_workspace_sizes_are_consistent():
