@@ -8,7 +8,7 @@
  * v0.1.47-beta article, section on lowering the fine-tuning barrier]. NF4 dequantisation, the
  * matmul and the LoRA correction are computed together, without materialising a dequantised
  * copy of W ["Inside Unsloth" book listing, "What You'll Learn", "LoRA and QLoRA"; pyshine
- * Unsloth code tour, "Why You Need This" and "Detailed view"]:
+ * Unsloth code tour, "Why You Need This"]:
  *
  *     T  = X A^T                 Y  = X deq(W)^T + s T B^T
  *     U  = dY B                  dX = dY deq(W) + s U A

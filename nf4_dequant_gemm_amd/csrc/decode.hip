@@ -2,8 +2,8 @@
 // LoRA correction, Y = X deq(W)^T + s T B^T, bound by the weight stream [pyshine Unsloth code
 // tour, "Why You Need This": dequantize-on-the-fly GEMV for NF4 weights; "Inside Unsloth"
 // listing, "What You'll Learn", "LoRA and QLoRA": dequant, matmul and LoRA correction in one
-// launch; Unsloth v0.1.463-beta release article, "Background" on INT4: a separate dequantisation
-// step eats into the bandwidth that 4-bit storage saves].
+// launch; NVFP4 update article, "NVFP4: A Quantization Format for the Next Generation of
+// Hardware": a separate dequantisation step eats into the bandwidth that 4-bit storage saves].
 //
 // With M <= 64 rows of X the work is the 0.52 bytes per weight element streamed from HBM, so the
 // kernel is organised around the stream and around the vector-memory pipeline of the CU, whose

@@ -3,7 +3,7 @@
 // NF4 dequantisation, the base GEMM and the rank-r LoRA correction run in the same kernel and the
 // same output tile; the weight is decoded on the fly and never written to HBM [Unsloth pages:
 // "Inside Unsloth" listing, "What You'll Learn", "LoRA and QLoRA" (dequant, matmul and LoRA
-// correction fused into a single launch); pyshine code tour, "Detailed view" (LoRA delta computed
+// correction fused into a single launch); pyshine code tour, "Why You Need This" (LoRA delta computed
 // inside the matmul instead of two extra matmuls); v0.1.463-beta release article, "About the
 // Unsloth Project" (no redundant buffers during dequantisation)].
 //

@@ -128,8 +128,17 @@ __global__ void rowproj_reduce_kernel(const float *__restrict__ part, int64_t n,
                                       uint16_t *__restrict__ out) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
+    // sequential sum over the splits (fixed order), its loads issued eight at a time
     float a = 0.f;
-    for (int s = 0; s < splits; ++s) a += part[(int64_t)s * n + i];
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(s + j) * n + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a += v[j];
+    }
+    for (; s < splits; ++s) a += part[(int64_t)s * n + i];
     out[i] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFFu);
   }
 }
@@ -325,7 +334,15 @@ __global__ void mreduce_final_kernel(const float *__restrict__ part, int64_t C, 
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     float a = 0.f;
-    for (int sp = 0; sp < splits; ++sp) a += part[(int64_t)sp * n + i];
+    int sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {   // fixed-order sum, loads issued eight at a time
+      float v8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v8[j] = part[(int64_t)(sp + j) * n + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a += v8[j];
+    }
+    for (; sp < splits; ++sp) a += part[(int64_t)sp * n + i];
     const uint16_t v = (uint16_t)(pack_bf16x2(s * a, 0.f) & 0xFFFFu);
     const int64_t j = i / C, c = i % C;
     if (transposed)

@@ -3,7 +3,7 @@
 The pages state the adapter algebra (Delta W = B A with rank r, only the adapters train, the
 4-bit base is frozen) [Unsloth v0.1.463-beta release article, "About the Unsloth Project"]. The
 fused kernel folds the low-rank delta into the product with the dequantised base rather than
-running it as extra separate products [pyshine Unsloth code tour, "Detailed view", the
+running it as extra separate products [pyshine Unsloth code tour, "Why You Need This", the
 kernels/fast_lora.py paragraph; "Inside Unsloth" listing, "What You'll Learn", "LoRA and QLoRA"],
 and the rewrite is numerically equivalent to the plain layer [v0.1.47-beta article, section on
 lowering the fine-tuning barrier]. So the layer is the plain definition, written out here:
