@@ -33,10 +33,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
-// Forward for M <= 64 and K % 256 == 0 (weight-stream bound): codes streamed by LDS DMA, table
+// Forward for M <= 48 and K % 256 == 0 (weight-stream bound): codes streamed by LDS DMA, table
 // decode of unscaled levels, block constant applied to the per-block partial sums.
 hipError_t launch_decode_fwd(const GemmArgs &g, hipStream_t st);
-constexpr int64_t kDecodeMaxM = 64;
+constexpr int64_t kDecodeMaxM = 48;
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).
