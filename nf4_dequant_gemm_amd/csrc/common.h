@@ -63,6 +63,14 @@ __device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) {
 
 // NF4 decode table of one 64-element block: the 16 values bf16(level_i * a) split into byte
 // planes L (low bytes) and H (high bytes), four entries per 32-bit word.
+// The int8 block code of the double quantisation (low byte of q) as a float. Written as
+// (low 7 bits) - (sign bit) rather than a sign-extending cast: the cast lets the compiler fold
+// the extension into the byte load and then move that load next to this use, after the waits
+// of the software pipeline, so it stalls on memory.
+__device__ __forceinline__ float int8_code(uint32_t q) {
+  return float(q & 0x7Fu) - float(q & 0x80u);
+}
+
 struct RowTable {
   uint32_t L[4], H[4];
 };

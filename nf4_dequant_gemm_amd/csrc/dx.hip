@@ -12,10 +12,11 @@
 // two weight rows (n, n+1) x 32 columns per step through two 16-entry bf16 tables (one per row
 // and block), pairs the rows per column with byte permutes and writes 4-byte (n, n+1) words.
 //
-// Pipeline per step s as in the forward kernel: the dY chunks of step s+1 and the codes of step
-// s+2 are loaded into registers, the 64 MFMAs of step s run on LDS buffer s & 1 while the decoded,
-// transposed weight and (in the second half) the dY chunks of step s+1 are written to buffer
-// (s+1) & 1 between MFMA issues.
+// Pipeline per step s: the dY tile of step s+1 goes straight to LDS buffer (s+1) & 1 by DMA
+// (buffer_load ... lds, issued at the start of the step, so its latency hides behind a whole
+// step) and the codes of step s+2 are loaded into registers; the 64 MFMAs of step s run on LDS
+// buffer s & 1 while the decoded, transposed weight of step s+1 is written to buffer (s+1) & 1
+// between MFMA issues.
 //
 // LDS: the dY tile has rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot
 // c ^ ((r >> 1) & 7). The transposed weight tile pads its rows to 144 bytes (conflict-free for
@@ -44,9 +45,6 @@ __device__ __forceinline__ int tile_remap(int hw, int tiles) {
   return x * per + (x < rem ? x : rem) + (hw >> 3);
 }
 
-struct YStage {
-  u32x4 v[8];
-};
 struct CStage2 {
   u32x4 c[2];        // 16 bytes of codes (32 columns) of rows n and n+1
   uint32_t q[2];     // block constants (int8 or float bits)
@@ -85,7 +83,10 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb,
 
 template <bool kDQ>
 __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
-  __shared__ uint4 sY[2][kChunks];   // dY tiles [m][n]
+  // dY tiles [m][n], two separate arrays: the compiler then knows that reads of one do not
+  // alias the DMA in flight into the other (one array of two would make it wait for the DMA)
+  __shared__ uint4 sY0[kChunks], sY1[kChunks];
+  auto ybuf = [&](int P) { return P ? sY1 : sY0; };
   __shared__ uint32_t sW[2][kT * kWRow];   // decoded weight tiles, transposed [p(k)][n], padded
 
   const int tid = threadIdx.x;
@@ -112,9 +113,16 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
   const int64_t nruns = (N * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
 
-  // dY chunk i of this thread: tile row 32 i + tid / 8, chunk tid % 8.
-  const uint32_t yoff = (uint32_t)((tid >> 3) * N * 2 + (tid & 7) * 16);
-  const uint32_t yrow_stride = (uint32_t)(32 * N * 2);
+  // dY DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (8 w + i) .. +7;
+  // lane L writes physical chunk L % 8 of row 8 (8 w + i) + L / 8, i.e. logical chunk
+  // (L % 8) ^ ((row >> 1) & 7) (the same swizzle as swzd).
+  uint32_t yoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * (8 * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    yoff[i] = (uint32_t)(row * N * 2 + c * 16);
+  }
   // Weight rows n = 64 s + 2 np + {0, 1}, columns k0 + 32 kq .. + 31.
   const int np = tid & 31, kq = tid >> 5;
   const int64_t kcol = k0 + kq * 32;
@@ -131,11 +139,14 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  auto load_y = [&](int s, YStage &y) {
+  auto dma_y = [&](int s, uint4 *sA) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      y.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rY, yoff + i * yrow_stride + s * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rY, (__attribute__((address_space(3))) void *)(sA + (8 * wave + i) * 64), 16, yoff[i],
+          s * 128, 0, 0);
   };
+  constexpr int kCodeLoads = 2 * (kDQ ? 3 : 2);   // loads issued by load_c
   auto load_c = [&](int s, CStage2 &c) {
     const uint32_t rowbase = (uint32_t)(s * kS);   // first weight row of the step
 #pragma unroll
@@ -151,15 +162,12 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
     }
   };
   auto absmax_of = [&](const CStage2 &c, int r) {
-    const float a = kDQ ? float((int8_t)(uint8_t)c.q[r]) * __uint_as_float(c.sc[r]) : __uint_as_float(c.q[r]);
+    const float a = kDQ ? int8_code(c.q[r]) * __uint_as_float(c.sc[r]) : __uint_as_float(c.q[r]);
     return kvalid ? a : 0.f;
   };
   auto cword = [](const CStage2 &c, int r, int w) {
     const u32x4 &v = c.c[r];
     return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-  };
-  auto write_y = [&](const YStage &y, int i, uint4 *sA) {
-    sA[swzd(i * 32 + (tid >> 3), tid & 7)] = __builtin_bit_cast(uint4, y.v[i]);
   };
   // Transposed weight write: the 4-byte word (n, n+1) of column k = kq * 32 + kl.
   auto write_w = [&](uint32_t *sB, int kl, uint32_t v) { sB[prow(kq * 32 + kl) * kWRow + np] = v; };
@@ -208,12 +216,11 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
   auto body = [&](int s, int P, CStage2 &cm, CStage2 &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    YStage yn;
-    load_y(s1, yn);
+    dma_y(s1, ybuf(P ^ 1));
+    __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
     load_c(s2, cm);
-    const uint4 *A = sY[P];
+    const uint4 *A = ybuf(P);
     const uint32_t *B = sW[P];
-    uint4 *An = sY[P ^ 1];
     uint32_t *Bn = sW[P ^ 1];
     bf16x8 af[2][4], bw[2][4];
     read_frags(A, B, 0, af[0], bw[0]);
@@ -237,7 +244,6 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
           af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzd(wm * 128 + i * 32 + (lane & 31), c)]);
           bw[(kk + 1) & 1][i] = wfrag(B, i, c);
         }
-        if (kk >= 2 && (slot & 3) == 1) write_y(yn, (slot - 32) >> 2, An);
         if (slot < 8) {
           // tables: slot = 4 r + quarter
           const int r = slot >> 2, qq = slot & 3;
@@ -261,19 +267,16 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
         }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the dY DMA of step s+1 (older than the code loads of step s+2) has landed
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCodeLoads) : "memory");
   };
 
   CStage2 c0, c1;
-  {
-    YStage y0;
-    load_y(0, y0);
-    load_c(0, c0);
-    load_c(nsteps > 1 ? 1 : 0, c1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) write_y(y0, i, sY[0]);
-  }
+  dma_y(0, ybuf(0));
+  load_c(0, c0);
+  load_c(nsteps > 1 ? 1 : 0, c1);
   decode_all(c0, sW[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int s = 0;
 #pragma unroll 1
@@ -288,9 +291,9 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
-    stage_lora_dx(g, m0, k0, j * kS, sY[buf], sW[buf]);
+    stage_lora_dx(g, m0, k0, j * kS, ybuf(buf), sW[buf]);
     __syncthreads();
-    mma(sY[buf], sW[buf]);
+    mma(ybuf(buf), sW[buf]);
     __syncthreads();
   }
 

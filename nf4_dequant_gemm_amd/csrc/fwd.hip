@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
     }
   };
   auto absmax_of = [&](const CStage &c) {
-    return kDQ ? float((int8_t)(uint8_t)c.q) * __uint_as_float(c.sc) : __uint_as_float(c.q);
+    return kDQ ? int8_code(c.q) * __uint_as_float(c.sc) : __uint_as_float(c.q);
   };
   auto word = [](const CStage &c, int j) {
     return j == 0 ? c.c0.x : j == 1 ? c.c0.y : j == 2 ? c.c0.z : j == 3 ? c.c0.w
