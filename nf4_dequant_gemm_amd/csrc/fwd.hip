@@ -14,11 +14,13 @@
 // registers (byte-select lookups, no LDS lookups, no per-element multiply).
 //
 // Pipeline per step s (one workgroup barrier per step):
-//   * loads for step s+2 are issued into registers (X tile chunks, codes, block constant),
+//   * the X tile of step s+1 is requested by DMA straight into LDS buffer (s+1) & 1
+//     (buffer_load ... lds: no registers, no LDS store instructions; its latency hides behind the
+//     whole step), and the codes and block constant of step s+2 are loaded into registers,
 //   * the 64 MFMAs of step s run on LDS buffer s & 1, with the fragments of the next k-slice read
 //     while the current one is multiplied,
-//   * between MFMA issues, the X chunks and the decoded W rows of step s+1 (loaded one step
-//     earlier) are written to LDS buffer (s+1) & 1, so the decode's VALU work overlaps the MFMAs.
+//   * between MFMA issues, the W rows of step s+1 (codes loaded one step earlier) are decoded and
+//     written to LDS buffer (s+1) & 1, so the decode's VALU work overlaps the MFMAs.
 // LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
 // c ^ ((r >> 1) & 7), which keeps 16 consecutive rows on distinct slots of the 256-byte bank
 // window that a 16-byte LDS access covers per pass on gfx950.
@@ -42,9 +44,6 @@ __device__ __forceinline__ int tile_remap(int hw, int tiles) {
   return x * per + (x < rem ? x : rem) + (hw >> 3);
 }
 
-struct XStage {
-  u32x4 v[8];
-};
 struct CStage {
   u32x4 c0, c1;      // the row's 32 bytes of codes
   uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
@@ -82,8 +81,12 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int jb, ui
 
 template <bool kDQ>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
-  __shared__ uint4 sX[2][kChunks];
-  __shared__ uint4 sW[2][kChunks];
+  // X and W tiles as separate arrays: the compiler then knows that LDS accesses to one do not
+  // alias the DMA in flight into another (one array of two would make it wait for the DMA)
+  __shared__ uint4 sX0[kChunks], sX1[kChunks];
+  __shared__ uint4 sW0[kChunks], sW1[kChunks];
+  auto xbuf = [&](int P) { return P ? sX1 : sX0; };
+  auto wbuf = [&](int P) { return P ? sW1 : sW0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,9 +110,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
 
-  // X chunk i of this thread: tile row 32 i + tid / 8, chunk tid % 8.
-  const uint32_t xoff = (uint32_t)((tid >> 3) * K * 2 + (tid & 7) * 16);
-  const uint32_t xrow_stride = (uint32_t)(32 * K * 2);
+  // X DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (8 w + i) .. +7;
+  // lane L writes physical chunk L % 8 of row 8 (8 w + i) + L / 8, i.e. logical chunk
+  // (L % 8) ^ ((row >> 1) & 7) (the same swizzle as swzf).
+  uint32_t xoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * (8 * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    xoff[i] = (uint32_t)(row * K * 2 + c * 16);
+  }
   const uint32_t coff = (uint32_t)(tid * (K / 2));
   const uint32_t qoff = (uint32_t)(tid * kblk);
   const int64_t sbase = (n0 + tid) * kblk;
@@ -122,11 +132,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  auto load_x = [&](int s, XStage &x) {
+  auto dma_x = [&](int s, uint4 *sA) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      x.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, xoff + i * xrow_stride + s * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rX, (__attribute__((address_space(3))) void *)(sA + (8 * wave + i) * 64), 16, xoff[i],
+          s * 128, 0, 0);
   };
+  constexpr int kCodeLoads = kDQ ? 4 : 3;   // loads issued by load_c
   auto load_c = [&](int s, CStage &c) {
     c.c0 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
     c.c1 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32 + 16, 0, 0);
@@ -143,9 +156,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   auto word = [](const CStage &c, int j) {
     return j == 0 ? c.c0.x : j == 1 ? c.c0.y : j == 2 ? c.c0.z : j == 3 ? c.c0.w
          : j == 4 ? c.c1.x : j == 5 ? c.c1.y : j == 6 ? c.c1.z : c.c1.w;
-  };
-  auto write_x = [&](const XStage &x, int i, uint4 *sA) {
-    sA[swzf(i * 32 + (tid >> 3), tid & 7)] = __builtin_bit_cast(uint4, x.v[i]);
   };
   auto decode_all = [&](const CStage &c, uint4 *sB) {
     const RowTable t = make_row_table(absmax_of(c), g.t);
@@ -177,16 +187,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
     }
   };
 
-  // One step: MFMAs on buffer P; the X chunks (xn) and the W rows (decoded from cn) of step s+1
-  // go to buffer P^1 in between; loads of step s+2 go to xm / cm.
-  auto body = [&](int s, int P, XStage &xm, XStage &xn, CStage &cm, CStage &cn) {
+  // One step: MFMAs on buffer P; the X tile of step s+1 arrives in buffer P^1 by DMA and the W
+  // rows of step s+1 (decoded from cn) are written there in between; codes of step s+2 go to cm.
+  auto body = [&](int s, int P, CStage &cm, CStage &cn) {
+    const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    load_x(s2, xm);
+    dma_x(s1, xbuf(P ^ 1));
+    __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
     load_c(s2, cm);
-    const uint4 *A = sX[P];
-    const uint4 *B = sW[P];
-    uint4 *An = sX[P ^ 1];
-    uint4 *Bn = sW[P ^ 1];
+    const uint4 *A = xbuf(P);
+    const uint4 *B = wbuf(P);
+    uint4 *Bn = wbuf(P ^ 1);
     bf16x8 af[2][4], bw[2][4];
     read_frags(A, B, 0, af[0], bw[0]);
 
@@ -207,8 +218,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
           af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzf(wm * 128 + i * 32 + (lane & 31), c)]);
           bw[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, B[swzf(wn * 128 + i * 32 + (lane & 31), c)]);
         }
-        // X tile of step s+1: one chunk every 8 MFMAs
-        if ((slot & 7) == 2) write_x(xn, slot >> 3, An);
         // decode table of step s+1 in slots 0..3, then chunk j = (slot - 4) / 7, piece (slot - 4) % 7
         if (slot < 4) {
           pk[2 * slot] = pack_bf16x2(g.t.level[4 * slot] * a, g.t.level[4 * slot + 1] * a);
@@ -226,28 +235,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
         }
       }
     }
-    // This wave's LDS writes are done; the barrier publishes buffer P^1 (the newer global loads
-    // stay in flight).
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // This wave's LDS writes are done and the X DMA of step s+1 (older than the code loads of
+    // step s+2, which stay in flight) has landed; the barrier publishes buffer P^1.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCodeLoads) : "memory");
   };
 
-  XStage x0, x1;
   CStage c0, c1;
-  load_x(0, x0);
+  dma_x(0, xbuf(0));
   load_c(0, c0);
-  load_x(kblk > 1 ? 1 : 0, x1);
   load_c(kblk > 1 ? 1 : 0, c1);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) write_x(x0, i, sX[0]);
-  decode_all(c0, sW[0]);
+  decode_all(c0, wbuf(0));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int s = 0;
 #pragma unroll 1
   for (; s + 2 <= kblk; s += 2) {
-    body(s, 0, x0, x1, c0, c1);
-    body(s + 1, 1, x1, x0, c1, c0);
+    body(s, 0, c0, c1);
+    body(s + 1, 1, c1, c0);
   }
-  if (s < kblk) body(s, 0, x0, x1, c0, c1);
+  if (s < kblk) body(s, 0, c0, c1);
   __syncthreads();
 
   // LoRA steps: [T | s B] as extra reduction steps of the same tile.
@@ -255,9 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
-    stage_lora(g, m0, n0, j * kS, sX[buf], sW[buf]);
+    stage_lora(g, m0, n0, j * kS, xbuf(buf), wbuf(buf));
     __syncthreads();
-    mma(sX[buf], sW[buf]);
+    mma(xbuf(buf), wbuf(buf));
     __syncthreads();
   }
 
