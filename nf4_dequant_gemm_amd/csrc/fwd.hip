@@ -7,20 +7,24 @@
 // inside the matmul instead of two extra matmuls); v0.1.463-beta release article, "About the
 // Unsloth Project" (no redundant buffers during dequantisation)].
 //
-// Work split. One workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of Y and walks K in steps of
-// 64 = one NF4 block per weight row. Each wave accumulates 128 x 128 with 16 MFMA 32x32x16 tiles.
-// Thread t owns weight row n0 + t of the tile: per step it turns the row's 32 bytes of codes and
-// its block constant into 64 bf16 values through a 16-entry table of bf16(level_i * a) held in
-// registers (byte-select lookups, no LDS lookups, no per-element multiply).
+// Work split. One workgroup of 8 waves (2 x 4) owns a 256 x 256 tile of Y and walks K in steps of
+// 64 = one NF4 block per weight row. Each wave accumulates 128 (m) x 64 (n) with 8 MFMA 32x32x16
+// tiles, which keeps it within 256 registers so that two waves share each SIMD: the NF4 decode of
+// one wave (vector ALU) then runs while the other wave's MFMAs execute (a lone wave overlaps only
+// a fraction of its own vector work with its MFMAs).
+// Threads 2r and 2r+1 own weight row n0 + r of the tile, 32 elements each: per step they turn
+// 16 bytes of codes and the block constant into bf16 values through a 16-entry table of
+// bf16(level_i * a) held in registers (byte-select lookups, no LDS lookups, no per-element
+// multiply).
 //
 // Pipeline per step s (one workgroup barrier per step):
 //   * the X tile of step s+1 is requested by DMA straight into LDS buffer (s+1) & 1
 //     (buffer_load ... lds: no registers, no LDS store instructions; its latency hides behind the
 //     whole step), and the codes and block constant of step s+2 are loaded into registers,
-//   * the 64 MFMAs of step s run on LDS buffer s & 1, with the fragments of the next k-slice read
+//   * the 32 MFMAs of step s run on LDS buffer s & 1, with the fragments of the next k-slice read
 //     while the current one is multiplied,
-//   * between MFMA issues, the W rows of step s+1 (codes loaded one step earlier) are decoded and
-//     written to LDS buffer (s+1) & 1, so the decode's VALU work overlaps the MFMAs.
+//   * between MFMA issues, the W half-rows of step s+1 (codes loaded one step earlier) are decoded
+//     and written to LDS buffer (s+1) & 1.
 // LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
 // c ^ ((r >> 1) & 7), which keeps 16 consecutive rows on distinct slots of the 256-byte bank
 // window that a 16-byte LDS access covers per pass on gfx950.
@@ -32,7 +36,8 @@ namespace {
 
 constexpr int kT = 256;      // output tile rows and columns
 constexpr int kS = 64;       // reduction step = NF4 block
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kChunks = kT * kS / 8;
 
 __device__ __forceinline__ int swzf(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
@@ -45,7 +50,7 @@ __device__ __forceinline__ int tile_remap(int hw, int tiles) {
 }
 
 struct CStage {
-  u32x4 c0, c1;      // the row's 32 bytes of codes
+  u32x4 c;           // 16 bytes of codes (32 elements) of the thread's half-row
   uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
 };
 
@@ -53,7 +58,7 @@ struct CStage {
 __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int jb, uint4 *sA, uint4 *sB) {
   const int tid = threadIdx.x;
 #pragma unroll 1
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kChunks / kThreads; ++i) {
     const int q = tid + kThreads * i;
     const int row = q >> 3, c = q & 7;
     uint32_t wa[4], wb[4];
@@ -80,7 +85,7 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int jb, ui
 }
 
 template <bool kDQ>
-__global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   // X and W tiles as separate arrays: the compiler then knows that LDS accesses to one do not
   // alias the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sX0[kChunks], sX1[kChunks];
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int tiles_n = (int)((g.C + kT - 1) / kT);
   const int logical = tile_remap(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(logical / tiles_n) * kT;
@@ -110,23 +115,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
 
-  // X DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (8 w + i) .. +7;
-  // lane L writes physical chunk L % 8 of row 8 (8 w + i) + L / 8, i.e. logical chunk
+  // X DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (4 w + i) .. +7;
+  // lane L writes physical chunk L % 8 of row 8 (4 w + i) + L / 8, i.e. logical chunk
   // (L % 8) ^ ((row >> 1) & 7) (the same swizzle as swzf).
-  uint32_t xoff[8];
+  uint32_t xoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (8 * wave + i) + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     xoff[i] = (uint32_t)(row * K * 2 + c * 16);
   }
-  const uint32_t coff = (uint32_t)(tid * (K / 2));
-  const uint32_t qoff = (uint32_t)(tid * kblk);
-  const int64_t sbase = (n0 + tid) * kblk;
+  // Decode ownership: weight row wr of the tile, elements 32 wh .. 32 wh + 31 of each step.
+  const int wr = tid >> 1, wh = tid & 1;
+  const uint32_t coff = (uint32_t)(wr * (K / 2) + wh * 16);
+  const uint32_t qoff = (uint32_t)(wr * kblk);
+  const int64_t sbase = (n0 + wr) * kblk;
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -134,15 +141,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
 
   auto dma_x = [&](int s, uint4 *sA) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rX, (__attribute__((address_space(3))) void *)(sA + (8 * wave + i) * 64), 16, xoff[i],
+          rX, (__attribute__((address_space(3))) void *)(sA + (4 * wave + i) * 64), 16, xoff[i],
           s * 128, 0, 0);
   };
-  constexpr int kCodeLoads = kDQ ? 4 : 3;   // loads issued by load_c
+  constexpr int kCodeLoads = kDQ ? 3 : 2;   // loads issued by load_c
   auto load_c = [&](int s, CStage &c) {
-    c.c0 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
-    c.c1 = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32 + 16, 0, 0);
+    c.c = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
     if (kDQ) {
       c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, qoff + s, 0, 0);
       c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)(((sbase + s) >> 8) * 4), 0, 0);
@@ -154,41 +160,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
     return kDQ ? int8_code(c.q) * __uint_as_float(c.sc) : __uint_as_float(c.q);
   };
   auto word = [](const CStage &c, int j) {
-    return j == 0 ? c.c0.x : j == 1 ? c.c0.y : j == 2 ? c.c0.z : j == 3 ? c.c0.w
-         : j == 4 ? c.c1.x : j == 5 ? c.c1.y : j == 6 ? c.c1.z : c.c1.w;
+    return j == 0 ? c.c.x : j == 1 ? c.c.y : j == 2 ? c.c.z : c.c.w;
   };
-  auto decode_all = [&](const CStage &c, uint4 *sB) {
+  auto decode_half = [&](const CStage &c, uint4 *sB) {
     const RowTable t = make_row_table(absmax_of(c), g.t);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
       decode8(t, word(c, j), o);
-      sB[swzf(tid, j)] = make_uint4(o[0], o[1], o[2], o[3]);
+      sB[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
-  auto read_frags = [&](const uint4 *sA, const uint4 *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
-    const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      af[t] = __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + t * 32 + (lane & 31), c)]);
-      bw[t] = __builtin_bit_cast(bf16x8, sB[swzf(wn * 128 + t * 32 + (lane & 31), c)]);
-    }
+  // k-slice kk: X fragments of rows wm*128 + 32 t (t < 4), W fragments of rows wn*64 + 32 t (t < 2)
+  auto afrag = [&](const uint4 *sA, int kk, int t) {
+    return __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + t * 32 + (lane & 31), kk * 2 + (lane >> 5))]);
+  };
+  auto bfrag = [&](const uint4 *sB, int kk, int t) {
+    return __builtin_bit_cast(bf16x8, sB[swzf(wn * 64 + t * 32 + (lane & 31), kk * 2 + (lane >> 5))]);
   };
   // Plain MFMA pass over one step (used for the LoRA steps).
   auto mma = [&](const uint4 *sA, const uint4 *sB) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[4], bw[4];
-      read_frags(sA, sB, kk, af, bw);
+      bf16x8 af[4], bw[2];
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
+      for (int t = 0; t < 4; ++t) af[t] = afrag(sA, kk, t);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) bw[t] = bfrag(sB, kk, t);
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32x32x16(bw[tn], af[tm], acc[tn][tm]);
     }
   };
 
   // One step: MFMAs on buffer P; the X tile of step s+1 arrives in buffer P^1 by DMA and the W
-  // rows of step s+1 (decoded from cn) are written there in between; codes of step s+2 go to cm.
+  // half-rows of step s+1 (decoded from cn) are written there in between; codes of step s+2 go to
+  // cm.
   auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
@@ -198,8 +206,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
     const uint4 *A = xbuf(P);
     const uint4 *B = wbuf(P);
     uint4 *Bn = wbuf(P ^ 1);
-    bf16x8 af[2][4], bw[2][4];
-    read_frags(A, B, 0, af[0], bw[0]);
+    bf16x8 af[2][4], bw[2][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) af[0][t] = afrag(A, 0, t);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) bw[0][t] = bfrag(B, 0, t);
 
     const float a = absmax_of(cn);
     uint32_t pk[8];
@@ -208,29 +219,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const int tn = i >> 2, tm = i & 3;
-        const int slot = kk * 16 + i;
+        const int slot = kk * 8 + i;
         acc[tn][tm] = mfma32x32x16(bw[kk & 1][tn], af[kk & 1][tm], acc[tn][tm]);
         // fragments of the next k-slice
-        if (kk < 3 && i < 4) {
-          const int c = (kk + 1) * 2 + (lane >> 5);
-          af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzf(wm * 128 + i * 32 + (lane & 31), c)]);
-          bw[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, B[swzf(wn * 128 + i * 32 + (lane & 31), c)]);
-        }
-        // decode table of step s+1 in slots 0..3, then chunk j = (slot - 4) / 7, piece (slot - 4) % 7
+        if (kk < 3 && i < 4) af[(kk + 1) & 1][i] = afrag(A, kk + 1, i);
+        if (kk < 3 && i >= 4 && i < 6) bw[(kk + 1) & 1][i - 4] = bfrag(B, kk + 1, i - 4);
+        // decode table of step s+1 in slots 0..3, then word j = (slot - 4) / 6, piece (slot - 4) % 6
         if (slot < 4) {
           pk[2 * slot] = pack_bf16x2(g.t.level[4 * slot] * a, g.t.level[4 * slot + 1] * a);
           pk[2 * slot + 1] = pack_bf16x2(g.t.level[4 * slot + 2] * a, g.t.level[4 * slot + 3] * a);
           t.L[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x06040200u);
           t.H[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x07050301u);
-        } else if (slot < 4 + 8 * 7) {
-          const int j = (slot - 4) / 7, p = (slot - 4) % 7;
+        } else if (slot < 4 + 4 * 6) {
+          const int j = (slot - 4) / 6, p = (slot - 4) % 6;
           if (p < 5) {
             if (p == 0) dx.d = word(cn, j);
             uint32_t o[4];
             dec_piece(t, dx, p, o);
-            if (p == 4) Bn[swzf(tid, j)] = make_uint4(o[0], o[1], o[2], o[3]);
+            if (p == 4) Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
       }
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   dma_x(0, xbuf(0));
   load_c(0, c0);
   load_c(kblk > 1 ? 1 : 0, c1);
-  decode_all(c0, wbuf(0));
+  decode_half(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int s = 0;
@@ -270,13 +278,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fused_kernel(GemmArgs g) {
   // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m
   // for each (tn, tm, group of 4 accumulator registers).
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
+  for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
       const int64_t m = m0 + wm * 128 + tm * 32 + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + tn * 32 + 8 * q + 4 * (lane >> 5);
+        const int64_t n = n0 + wn * 64 + tn * 32 + 8 * q + 4 * (lane >> 5);
         if (m < g.M && n < g.C) {
           const uint2 v = make_uint2(pack_bf16x2(acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1]),
                                      pack_bf16x2(acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3]));
