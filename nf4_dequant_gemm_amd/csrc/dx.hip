@@ -6,22 +6,26 @@
 // Unsloth kernels rewrite the backward pass]. As in the forward kernel, the NF4 weight is decoded
 // on the fly into LDS and the rank-r term runs as extra reduction steps into the same tile.
 //
-// Work split. One workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of dX (rows m, columns k) and
-// walks the reduction index n in steps of 64. The reduction runs over the weight's ROW index,
-// so the decoded weight tile is stored transposed in LDS (256 k-rows of 64 n). Thread t decodes
-// two weight rows (n, n+1) x 32 columns per step through two 16-entry bf16 tables (one per row
-// and block), pairs the rows per column with byte permutes and writes 4-byte (n, n+1) words.
+// Work split. One workgroup of 8 waves (2 x 4) owns a 256 x 256 tile of dX (rows m, columns k)
+// and walks the reduction index n in steps of 64; each wave accumulates 128 (m) x 64 (k) with
+// MFMA 16x16x32 (within 256 registers, so two waves share each SIMD and one wave's decode
+// overlaps the other's MFMAs). The reduction runs over the weight's ROW index, so the MFMA needs
+// the decoded tile transposed: the tile is stored in LDS as it is decoded (64 rows n x 256
+// columns k, 16-byte stores) and read with the gfx950 transposing LDS load ds_read_b64_tr_b16,
+// which hands each lane 4 consecutive rows of one column -- the operand layout with n as the
+// reduction index. Threads 8r .. 8r+7 decode weight row r of the step, 32 columns each, through
+// a register table of bf16(level_i * a) (byte permutes, no LDS lookups).
 //
 // Pipeline per step s: the dY tile of step s+1 goes straight to LDS buffer (s+1) & 1 by DMA
 // (buffer_load ... lds, issued at the start of the step, so its latency hides behind a whole
 // step) and the codes of step s+2 are loaded into registers; the 64 MFMAs of step s run on LDS
-// buffer s & 1 while the decoded, transposed weight of step s+1 is written to buffer (s+1) & 1
-// between MFMA issues.
+// buffer s & 1 while the weight rows of step s+1 are decoded into buffer (s+1) & 1 between MFMA
+// issues.
 //
 // LDS: the dY tile has rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot
-// c ^ ((r >> 1) & 7). The transposed weight tile pads its rows to 144 bytes (conflict-free for
-// both the 4-byte writes and the 16-byte fragment reads) and keeps column k in row
-// k ^ ((k / 32) & 1).
+// c ^ ((r >> 1) & 7). The weight tile has rows of 256 bf16 = 64 units of 8 bytes, unit u of row
+// r at u ^ (4 * ((r + 4 (r / 8)) % 8)): the XOR keeps 16-byte pairs together for the stores and
+// puts the 32 lanes of every transposing read on distinct banks.
 #include "common.h"
 #include "launch.h"
 
@@ -30,36 +34,62 @@ namespace {
 
 constexpr int kT = 256;
 constexpr int kS = 64;
-constexpr int kThreads = 256;
-constexpr int kChunks = kT * kS / 8;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kYChunks = kT * kS / 8;   // dY tile: 2048 chunks of 16 bytes
+constexpr int kWElems = kS * kT;        // weight tile: 64 x 256 bf16
 
 __device__ __forceinline__ int swzd(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
-// Transposed weight tile: row p(k) of column k (0..255) holds 64 n-values in 144 bytes (128 bytes
-// of data, 16 of padding). p(k) flips the lowest bit of k in odd groups of 32 columns, so the two
-// half-waves of a write (columns k and k + 32) land in different halves of the bank window.
-constexpr int kWRow = 36;    // 32-bit words per transposed row (144 bytes)
-__device__ __forceinline__ int prow(int k) { return k ^ ((k >> 5) & 1); }
+// bf16 index of 8-byte unit u of weight-tile row r
+__device__ __forceinline__ int wunit(int r, int u) {
+  return r * kT + ((u ^ (4 * ((r + 4 * (r >> 3)) & 7))) << 2);
+}
 
 __device__ __forceinline__ int tile_remap(int hw, int tiles) {
   const int per = tiles >> 3, rem = tiles & 7, x = hw & 7;
   return x * per + (x < rem ? x : rem) + (hw >> 3);
 }
 
-struct CStage2 {
-  u32x4 c[2];        // 16 bytes of codes (32 columns) of rows n and n+1
-  uint32_t q[2];     // block constants (int8 or float bits)
-  uint32_t sc[2];    // run scale bits (double quantisation)
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+
+struct CStage {
+  u32x4 c;           // 16 bytes of codes (32 columns) of the thread's weight row
+  uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
 };
 
-// LoRA step staging: A-side U columns jb..jb+63 (rows m), B-side s * A^T (rows k, columns j).
-__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sA, uint32_t *sB) {
+// LoRA step staging: the weight side gets s * A rows j = jb .. jb+63 (columns k0 ..), laid out
+// like a decoded weight tile; the dY side gets U columns jb .. jb+63 (rows m0 ..); zero-padded.
+__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sY,
+                              uint16_t *sW) {
   const int tid = threadIdx.x;
+  {
+    const int row = tid >> 3, seg = tid & 7;
+    const int j = jb + row;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = k0 + seg * 32 + q * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < g.r && k < g.C) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(g.lora_b + (int64_t)j * g.C + k);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g.s * bf16_lo(w[e]), g.s * bf16_hi(w[e]));
+        v = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+      *reinterpret_cast<uint4 *>(sW + wunit(row, seg * 8 + 2 * q)) = v;
+    }
+  }
 #pragma unroll 1
-  for (int i = 0; i < 8; ++i) {
-    const int q = tid + kThreads * i;
-    const int row = q >> 3, c = q & 7;
-    uint32_t wa[4], wb[4];
-    const int64_t m = m0 + row, k = k0 + row;
+  for (int i = 0; i < kYChunks / kThreads; ++i) {
+    const int qd = tid + kThreads * i;
+    const int row = qd >> 3, c = qd & 7;
+    const int64_t m = m0 + row;
+    uint32_t wa[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int j0 = jb + c * 8 + e, j1 = j0 + 1;
@@ -69,30 +99,25 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb,
         if (j1 < g.r) hi = g.lora_a[m * g.r + j1];
       }
       wa[e >> 1] = lo | (hi << 16);
-      float b0 = 0.f, b1 = 0.f;
-      if (k < g.C) {
-        if (j0 < g.r) b0 = bf16_to_f32(g.lora_b[(int64_t)j0 * g.C + k]);
-        if (j1 < g.r) b1 = bf16_to_f32(g.lora_b[(int64_t)j1 * g.C + k]);
-      }
-      wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
     }
-    sA[swzd(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-    reinterpret_cast<uint4 *>(sB)[prow(row) * (kWRow / 4) + c] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    sY[swzd(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
   }
 }
 
 template <bool kDQ>
-__global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
-  // dY tiles [m][n], two separate arrays: the compiler then knows that reads of one do not
-  // alias the DMA in flight into the other (one array of two would make it wait for the DMA)
-  __shared__ uint4 sY0[kChunks], sY1[kChunks];
+__global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
+  // separate LDS arrays per buffer: the compiler then knows that accesses to one do not alias
+  // the DMA in flight into another (one array of two would make it wait for the DMA)
+  __shared__ uint4 sY0[kYChunks], sY1[kYChunks];
+  __shared__ uint4 sW0[kWElems / 8], sW1[kWElems / 8];
   auto ybuf = [&](int P) { return P ? sY1 : sY0; };
-  __shared__ uint32_t sW[2][kT * kWRow];   // decoded weight tiles, transposed [p(k)][n], padded
+  auto wbuf = [&](int P) { return reinterpret_cast<uint16_t *>(P ? sW1 : sW0); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wk = wave & 1;
+  const int wm = wave >> 2, wk = wave & 3;
+  const int g16 = lane >> 4, l16 = lane & 15;
   const int tiles_k = (int)((g.C + kT - 1) / kT);
   const int logical = tile_remap(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(logical / tiles_k) * kT;
@@ -113,169 +138,169 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
   const int64_t nruns = (N * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
 
-  // dY DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (8 w + i) .. +7;
-  // lane L writes physical chunk L % 8 of row 8 (8 w + i) + L / 8, i.e. logical chunk
+  // dY DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (4 w + i) .. +7;
+  // lane L writes physical chunk L % 8 of row 8 (4 w + i) + L / 8, i.e. logical chunk
   // (L % 8) ^ ((row >> 1) & 7) (the same swizzle as swzd).
-  uint32_t yoff[8];
+  uint32_t yoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (8 * wave + i) + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     yoff[i] = (uint32_t)(row * N * 2 + c * 16);
   }
-  // Weight rows n = 64 s + 2 np + {0, 1}, columns k0 + 32 kq .. + 31.
-  const int np = tid & 31, kq = tid >> 5;
-  const int64_t kcol = k0 + kq * 32;
+  // Decode ownership: weight row n = 64 s + wr of step s, columns k0 + 32 seg .. + 31.
+  const int wr = tid >> 3, seg = tid & 7;
+  const int64_t kcol = k0 + seg * 32;
   const bool kvalid = kcol < K;
-  const uint32_t coff = (uint32_t)((2 * np) * (K / 2) + (kvalid ? kcol / 2 : 0));
-  const uint32_t crow = (uint32_t)(K / 2);
-  const uint32_t qoff = (uint32_t)((2 * np) * kblk + (kvalid ? kcol / 64 : 0));
+  const uint32_t coff = (uint32_t)(wr * (K / 2) + (kvalid ? kcol / 2 : 0));
+  const uint32_t cstep = (uint32_t)(kS * (K / 2));
+  const uint32_t qoff = (uint32_t)(wr * kblk + (kvalid ? kcol / 64 : 0));
+  const uint32_t qstep = (uint32_t)(kS * kblk);
 
-  f32x16 acc[4][4];
+  f32x4 acc[4][8];   // [k-tile][m-tile]
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto dma_y = [&](int s, uint4 *sA) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rY, (__attribute__((address_space(3))) void *)(sA + (8 * wave + i) * 64), 16, yoff[i],
+          rY, (__attribute__((address_space(3))) void *)(sA + (4 * wave + i) * 64), 16, yoff[i],
           s * 128, 0, 0);
   };
-  constexpr int kCodeLoads = 2 * (kDQ ? 3 : 2);   // loads issued by load_c
-  auto load_c = [&](int s, CStage2 &c) {
-    const uint32_t rowbase = (uint32_t)(s * kS);   // first weight row of the step
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      c.c[r] = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + (rowbase + r) * crow, 0, 0);
-      const uint32_t b = qoff + (rowbase + r) * (uint32_t)kblk;
-      if (kDQ) {
-        c.q[r] = __builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0);
-        c.sc[r] = __builtin_amdgcn_raw_buffer_load_b32(rS, (b >> 8) * 4, 0, 0);
-      } else {
-        c.q[r] = __builtin_amdgcn_raw_buffer_load_b32(rQ, b * 4, 0, 0);
-      }
+  constexpr int kCodeLoads = kDQ ? 3 : 2;   // loads issued by load_c
+  auto load_c = [&](int s, CStage &c) {
+    c.c = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * cstep, 0, 0);
+    const uint32_t b = qoff + s * qstep;
+    if (kDQ) {
+      c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0);
+      c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (b >> 8) * 4, 0, 0);
+    } else {
+      c.q = __builtin_amdgcn_raw_buffer_load_b32(rQ, b * 4, 0, 0);
     }
   };
-  auto absmax_of = [&](const CStage2 &c, int r) {
-    const float a = kDQ ? int8_code(c.q[r]) * __uint_as_float(c.sc[r]) : __uint_as_float(c.q[r]);
+  auto absmax_of = [&](const CStage &c) {
+    const float a = kDQ ? int8_code(c.q) * __uint_as_float(c.sc) : __uint_as_float(c.q);
     return kvalid ? a : 0.f;
   };
-  auto cword = [](const CStage2 &c, int r, int w) {
-    const u32x4 &v = c.c[r];
-    return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+  auto word = [](const CStage &c, int j) {
+    return j == 0 ? c.c.x : j == 1 ? c.c.y : j == 2 ? c.c.z : c.c.w;
   };
-  // Transposed weight write: the 4-byte word (n, n+1) of column k = kq * 32 + kl.
-  auto write_w = [&](uint32_t *sB, int kl, uint32_t v) { sB[prow(kq * 32 + kl) * kWRow + np] = v; };
-  auto decode_all = [&](const CStage2 &c, uint32_t *sB) {
-    RowTable t[2];
+  // columns 32 seg + 8 j .. +7 of the thread's weight row = 8-byte units 8 seg + 2 j, +1
+  auto wstore = [&](uint16_t *sW, int j, const uint32_t o[4]) {
+    *reinterpret_cast<uint4 *>(sW + wunit(wr, seg * 8 + 2 * j)) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  auto decode_all = [&](const CStage &c, uint16_t *sW) {
+    const RowTable t = make_row_table(absmax_of(c), g.t);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) t[r] = make_row_table(absmax_of(c, r), g.t);
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o[4];
+      decode8(t, word(c, j), o);
+      wstore(sW, j, o);
+    }
+  };
+  // MFMA operands of k-slice ks (32 rows n): the weight side, transposed on the fly -- lane
+  // (g16, l16) gets rows 32 ks + 8 g16 .. + 7 of column wk*64 + 16 kt + l16 -- and the dY side,
+  // row wm*128 + 16 mt + l16, reduction elements 32 ks + 8 g16 .. + 7.
+  auto wfrag = [&](const uint16_t *sW, int ks, int kt) {
+    const int row = ks * 32 + g16 * 8 + (l16 >> 2);
+    const int u = (wk * 64 + kt * 16) / 4 + (l16 & 3);
+    const s16x4 lo = lds_tr16(sW + wunit(row, u));
+    const s16x4 hi = lds_tr16(sW + wunit(row + 4, u));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  auto yfrag = [&](const uint4 *sA, int ks, int mt) {
+    return __builtin_bit_cast(bf16x8, sA[swzd(wm * 128 + mt * 16 + l16, ks * 4 + g16)]);
+  };
+  // Plain MFMA pass over one step (used for the LoRA steps).
+  auto mma = [&](const uint4 *sA, const uint16_t *sW) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t o[2][4];
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 aw[4];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) decode8(t[r], cword(c, r, w), o[r]);
+      for (int kt = 0; kt < 4; ++kt) aw[kt] = wfrag(sW, ks, kt);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        write_w(sB, w * 8 + 2 * q, perm(o[1][q], o[0][q], 0x05040100u));
-        write_w(sB, w * 8 + 2 * q + 1, perm(o[1][q], o[0][q], 0x07060302u));
+      for (int mt = 0; mt < 8; ++mt) {
+        const bf16x8 b = yfrag(sA, ks, mt);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[kt][mt] = mfma16x16x32(aw[kt], b, acc[kt][mt]);
       }
-    }
-  };
-  auto wfrag = [&](const uint32_t *sB, int t, int c) {
-    return __builtin_bit_cast(
-        bf16x8, reinterpret_cast<const uint4 *>(sB)[prow(wk * 128 + t * 32 + (lane & 31)) * (kWRow / 4) + c]);
-  };
-  auto read_frags = [&](const uint4 *sA, const uint32_t *sB, int kk, bf16x8 af[4], bf16x8 bw[4]) {
-    const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      af[t] = __builtin_bit_cast(bf16x8, sA[swzd(wm * 128 + t * 32 + (lane & 31), c)]);
-      bw[t] = wfrag(sB, t, c);
-    }
-  };
-  auto mma = [&](const uint4 *sA, const uint32_t *sB) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[4], bw[4];
-      read_frags(sA, sB, kk, af, bw);
-#pragma unroll
-      for (int tk = 0; tk < 4; ++tk)
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tk][tm] = mfma32x32x16(bw[tk], af[tm], acc[tk][tm]);
     }
   };
 
-  // One step: MFMAs on buffer P; dY chunks (yn) and the transposed weight (decoded from cn) of
-  // step s+1 go to buffer P^1 in between; loads of step s+2 go to ym / cm.
-  auto body = [&](int s, int P, CStage2 &cm, CStage2 &cn) {
+  // One step: MFMAs on buffer P; the dY tile of step s+1 arrives in buffer P^1 by DMA and the
+  // weight rows of step s+1 (decoded from cn) are written there in between; codes of step s+2
+  // go to cm. 16 groups (k-slice, m-tile) of 4 MFMAs; decode pieces go between groups.
+  auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
     dma_y(s1, ybuf(P ^ 1));
     __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
     load_c(s2, cm);
-    const uint4 *A = ybuf(P);
-    const uint32_t *B = sW[P];
-    uint32_t *Bn = sW[P ^ 1];
-    bf16x8 af[2][4], bw[2][4];
-    read_frags(A, B, 0, af[0], bw[0]);
+    const uint4 *Y = ybuf(P);
+    const uint16_t *W = wbuf(P);
+    uint16_t *Wn = wbuf(P ^ 1);
+    bf16x8 aw[4], yb[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) aw[kt] = wfrag(W, 0, kt);
+    yb[0] = yfrag(Y, 0, 0);
 
-    float a[2];
-    a[0] = absmax_of(cn, 0);
-    a[1] = absmax_of(cn, 1);
-    uint32_t pk[2][8];
-    RowTable t[2];
-    Dec8 dx[2];
-    uint32_t o[2][4];
+    const float a = absmax_of(cn);
+    uint32_t pk[8];
+    RowTable t;
+    Dec8 dx;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int grp = 0; grp < 16; ++grp) {
+      const int ks = grp >> 3, mt = grp & 7;
+      // the second k-slice's weight fragments replace the first's (one exposed LDS latency per
+      // step, which keeps the wave within 256 registers); the next m-tile's dY fragment is read
+      // one group ahead
+      if (grp == 8) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tk = i >> 2, tm = i & 3;
-        const int slot = kk * 16 + i;
-        acc[tk][tm] = mfma32x32x16(bw[kk & 1][tk], af[kk & 1][tm], acc[tk][tm]);
-        if (kk < 3 && i < 4) {
-          const int c = (kk + 1) * 2 + (lane >> 5);
-          af[(kk + 1) & 1][i] = __builtin_bit_cast(bf16x8, A[swzd(wm * 128 + i * 32 + (lane & 31), c)]);
-          bw[(kk + 1) & 1][i] = wfrag(B, i, c);
-        }
-        if (slot < 8) {
-          // tables: slot = 4 r + quarter
-          const int r = slot >> 2, qq = slot & 3;
-          pk[r][2 * qq] = pack_bf16x2(g.t.level[4 * qq] * a[r], g.t.level[4 * qq + 1] * a[r]);
-          pk[r][2 * qq + 1] = pack_bf16x2(g.t.level[4 * qq + 2] * a[r], g.t.level[4 * qq + 3] * a[r]);
-          t[r].L[qq] = perm(pk[r][2 * qq + 1], pk[r][2 * qq], 0x06040200u);
-          t[r].H[qq] = perm(pk[r][2 * qq + 1], pk[r][2 * qq], 0x07050301u);
+        for (int kt = 0; kt < 4; ++kt) aw[kt] = wfrag(W, 1, kt);
+      }
+      if (grp + 1 < 16) yb[(grp + 1) & 1] = yfrag(Y, (grp + 1) >> 3, (grp + 1) & 7);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) acc[kt][mt] = mfma16x16x32(aw[kt], yb[grp & 1], acc[kt][mt]);
+      // decode of step s+1: table in groups 0..3, then word j = (grp - 4) / 3 in pieces over
+      // three groups (pieces 0-1, 2-3, 4 + store)
+      if (grp < 4) {
+        pk[2 * grp] = pack_bf16x2(g.t.level[4 * grp] * a, g.t.level[4 * grp + 1] * a);
+        pk[2 * grp + 1] = pack_bf16x2(g.t.level[4 * grp + 2] * a, g.t.level[4 * grp + 3] * a);
+        t.L[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x06040200u);
+        t.H[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x07050301u);
+      } else {
+        const int j = (grp - 4) / 3, ph = (grp - 4) % 3;
+        uint32_t o[4];
+        if (ph == 0) {
+          dx.d = word(cn, j);
+          dec_piece(t, dx, 0, o);
+          dec_piece(t, dx, 1, o);
+        } else if (ph == 1) {
+          dec_piece(t, dx, 2, o);
+          dec_piece(t, dx, 3, o);
         } else {
-          // word w: slots 8 + 14 w .. : pieces of rows 0 and 1 interleaved (10 slots), then the
-          // 4 transposed pairs (4 slots)
-          const int w = (slot - 8) / 14, u = (slot - 8) % 14;
-          if (u < 10) {
-            const int r = u & 1, p = u >> 1;
-            if (p == 0) dx[r].d = cword(cn, r, w);
-            dec_piece(t[r], dx[r], p, o[r]);
-          } else {
-            const int q = u - 10;
-            write_w(Bn, w * 8 + 2 * q, perm(o[1][q], o[0][q], 0x05040100u));
-            write_w(Bn, w * 8 + 2 * q + 1, perm(o[1][q], o[0][q], 0x07060302u));
-          }
+          dec_piece(t, dx, 4, o);
+          wstore(Wn, j, o);
         }
       }
+      // keep each group's loads and decode work in place (hoisting them stretches register
+      // lifetimes past the 256 a wave may use with two waves per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // the dY DMA of step s+1 (older than the code loads of step s+2) has landed
+    // the dY DMA of step s+1 (older than the code loads of step s+2) has landed and this wave's
+    // LDS stores are done; the barrier publishes buffer P^1
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCodeLoads) : "memory");
   };
 
-  CStage2 c0, c1;
+  CStage c0, c1;
   dma_y(0, ybuf(0));
   load_c(0, c0);
   load_c(nsteps > 1 ? 1 : 0, c1);
-  decode_all(c0, sW[0]);
+  decode_all(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int s = 0;
@@ -291,26 +316,23 @@ __global__ __launch_bounds__(kThreads, 1) void dx_fused_kernel(GemmArgs g) {
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
-    stage_lora_dx(g, m0, k0, j * kS, ybuf(buf), sW[buf]);
+    stage_lora_dx(g, m0, k0, j * kS, ybuf(buf), wbuf(buf));
     __syncthreads();
-    mma(ybuf(buf), sW[buf]);
+    mma(ybuf(buf), wbuf(buf));
     __syncthreads();
   }
 
-  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns k..k+3 of row m.
+  // Epilogue: with the weight as the MFMA A operand, a lane holds columns k..k+3 of row m.
 #pragma unroll
-  for (int tk = 0; tk < 4; ++tk)
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-      const int64_t m = m0 + wm * 128 + tm * 32 + (lane & 31);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + wk * 128 + tk * 32 + 8 * q + 4 * (lane >> 5);
-        if (m < g.M && k < g.C) {
-          const uint2 v = make_uint2(pack_bf16x2(acc[tk][tm][4 * q], acc[tk][tm][4 * q + 1]),
-                                     pack_bf16x2(acc[tk][tm][4 * q + 2], acc[tk][tm][4 * q + 3]));
-          *reinterpret_cast<uint2 *>(g.out + m * g.ldo + k) = v;
-        }
+    for (int mt = 0; mt < 8; ++mt) {
+      const int64_t m = m0 + wm * 128 + mt * 16 + l16;
+      const int64_t k = k0 + wk * 64 + kt * 16 + 4 * g16;
+      if (m < g.M && k < g.C) {
+        const uint2 v = make_uint2(pack_bf16x2(acc[kt][mt][0], acc[kt][mt][1]),
+                                   pack_bf16x2(acc[kt][mt][2], acc[kt][mt][3]));
+        *reinterpret_cast<uint2 *>(g.out + m * g.ldo + k) = v;
       }
     }
 }
