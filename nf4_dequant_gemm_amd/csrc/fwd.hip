@@ -8,10 +8,10 @@
 // Unsloth Project" (no redundant buffers during dequantisation)].
 //
 // Work split. One workgroup of 8 waves (2 x 4) owns a 256 x 256 tile of Y and walks K in steps of
-// 64 = one NF4 block per weight row. Each wave accumulates 128 (m) x 64 (n) with 8 MFMA 32x32x16
-// tiles, which keeps it within 256 registers so that two waves share each SIMD: the NF4 decode of
-// one wave (vector ALU) then runs while the other wave's MFMAs execute (a lone wave overlaps only
-// a fraction of its own vector work with its MFMAs).
+// 64 = one NF4 block per weight row. Each wave accumulates 128 (m) x 64 (n) with MFMA 16x16x32
+// (32 tiles), which keeps it within 256 registers so that two waves share each SIMD: the NF4
+// decode of one wave (vector ALU) then runs while the other wave's MFMAs execute (a lone wave
+// overlaps only a fraction of its own vector work with its MFMAs).
 // Threads 2r and 2r+1 own weight row n0 + r of the tile, 32 elements each: per step they turn
 // 16 bytes of codes and the block constant into bf16 values through a 16-entry table of
 // bf16(level_i * a) held in registers (byte-select lookups, no LDS lookups, no per-element
@@ -21,8 +21,8 @@
 //   * the X tile of step s+1 is requested by DMA straight into LDS buffer (s+1) & 1
 //     (buffer_load ... lds: no registers, no LDS store instructions; its latency hides behind the
 //     whole step), and the codes and block constant of step s+2 are loaded into registers,
-//   * the 32 MFMAs of step s run on LDS buffer s & 1, with the fragments of the next k-slice read
-//     while the current one is multiplied,
+//   * the 64 MFMAs of step s run on LDS buffer s & 1 in 16 groups (k-slice, m-tile) of 4, the
+//     X fragment of the next group read while the current one is multiplied,
 //   * between MFMA issues, the W half-rows of step s+1 (codes loaded one step earlier) are decoded
 //     and written to LDS buffer (s+1) & 1.
 // LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
@@ -131,13 +131,12 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   const uint32_t qoff = (uint32_t)(wr * kblk);
   const int64_t sbase = (n0 + wr) * kblk;
 
-  f32x16 acc[2][4];
+  const int g16 = lane >> 4, l16 = lane & 15;
+  f32x4 acc[4][8];   // [n-tile][m-tile]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto dma_x = [&](int s, uint4 *sA) {
 #pragma unroll
@@ -171,32 +170,33 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
       sB[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
-  // k-slice kk: X fragments of rows wm*128 + 32 t (t < 4), W fragments of rows wn*64 + 32 t (t < 2)
-  auto afrag = [&](const uint4 *sA, int kk, int t) {
-    return __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + t * 32 + (lane & 31), kk * 2 + (lane >> 5))]);
+  // MFMA operands of k-slice ks (32 columns k): lane (g16, l16) takes 8 consecutive k
+  // (32 ks + 8 g16 ..) of weight row wn*64 + 16 nt + l16 or of X row wm*128 + 16 mt + l16.
+  auto wfrag = [&](const uint4 *sB, int ks, int nt) {
+    return __builtin_bit_cast(bf16x8, sB[swzf(wn * 64 + nt * 16 + l16, ks * 4 + g16)]);
   };
-  auto bfrag = [&](const uint4 *sB, int kk, int t) {
-    return __builtin_bit_cast(bf16x8, sB[swzf(wn * 64 + t * 32 + (lane & 31), kk * 2 + (lane >> 5))]);
+  auto xfrag = [&](const uint4 *sA, int ks, int mt) {
+    return __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + mt * 16 + l16, ks * 4 + g16)]);
   };
   // Plain MFMA pass over one step (used for the LoRA steps).
   auto mma = [&](const uint4 *sA, const uint4 *sB) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[4], bw[2];
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 aw[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) af[t] = afrag(sA, kk, t);
+      for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(sB, ks, nt);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) bw[t] = bfrag(sB, kk, t);
+      for (int mt = 0; mt < 8; ++mt) {
+        const bf16x8 b = xfrag(sA, ks, mt);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32x32x16(bw[tn], af[tm], acc[tn][tm]);
+        for (int nt = 0; nt < 4; ++nt) acc[nt][mt] = mfma16x16x32(aw[nt], b, acc[nt][mt]);
+      }
     }
   };
 
   // One step: MFMAs on buffer P; the X tile of step s+1 arrives in buffer P^1 by DMA and the W
   // half-rows of step s+1 (decoded from cn) are written there in between; codes of step s+2 go to
-  // cm.
+  // cm. 16 groups (k-slice, m-tile) of 4 MFMAs; decode pieces go between groups.
   auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
@@ -206,42 +206,52 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
     const uint4 *A = xbuf(P);
     const uint4 *B = wbuf(P);
     uint4 *Bn = wbuf(P ^ 1);
-    bf16x8 af[2][4], bw[2][2];
+    bf16x8 aw[4], xb[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) af[0][t] = afrag(A, 0, t);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) bw[0][t] = bfrag(B, 0, t);
+    for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(B, 0, nt);
+    xb[0] = xfrag(A, 0, 0);
 
     const float a = absmax_of(cn);
     uint32_t pk[8];
     RowTable t;
     Dec8 dx;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int grp = 0; grp < 16; ++grp) {
+      const int mt = grp & 7;
+      // the second k-slice's weight fragments replace the first's; the next m-tile's X fragment
+      // is read one group ahead
+      if (grp == 8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tn = i >> 2, tm = i & 3;
-        const int slot = kk * 8 + i;
-        acc[tn][tm] = mfma32x32x16(bw[kk & 1][tn], af[kk & 1][tm], acc[tn][tm]);
-        // fragments of the next k-slice
-        if (kk < 3 && i < 4) af[(kk + 1) & 1][i] = afrag(A, kk + 1, i);
-        if (kk < 3 && i >= 4 && i < 6) bw[(kk + 1) & 1][i - 4] = bfrag(B, kk + 1, i - 4);
-        // decode table of step s+1 in slots 0..3, then word j = (slot - 4) / 6, piece (slot - 4) % 6
-        if (slot < 4) {
-          pk[2 * slot] = pack_bf16x2(g.t.level[4 * slot] * a, g.t.level[4 * slot + 1] * a);
-          pk[2 * slot + 1] = pack_bf16x2(g.t.level[4 * slot + 2] * a, g.t.level[4 * slot + 3] * a);
-          t.L[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x06040200u);
-          t.H[slot] = perm(pk[2 * slot + 1], pk[2 * slot], 0x07050301u);
-        } else if (slot < 4 + 4 * 6) {
-          const int j = (slot - 4) / 6, p = (slot - 4) % 6;
-          if (p < 5) {
-            if (p == 0) dx.d = word(cn, j);
-            uint32_t o[4];
-            dec_piece(t, dx, p, o);
-            if (p == 4) Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
-          }
+        for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(B, 1, nt);
+      }
+      if (grp + 1 < 16) xb[(grp + 1) & 1] = xfrag(A, (grp + 1) >> 3, (grp + 1) & 7);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt][mt] = mfma16x16x32(aw[nt], xb[grp & 1], acc[nt][mt]);
+      // decode of step s+1: table in groups 0..3, then word j = (grp - 4) / 3 in pieces over
+      // three groups (pieces 0-1, 2-3, 4 + store)
+      if (grp < 4) {
+        pk[2 * grp] = pack_bf16x2(g.t.level[4 * grp] * a, g.t.level[4 * grp + 1] * a);
+        pk[2 * grp + 1] = pack_bf16x2(g.t.level[4 * grp + 2] * a, g.t.level[4 * grp + 3] * a);
+        t.L[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x06040200u);
+        t.H[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x07050301u);
+      } else {
+        const int j = (grp - 4) / 3, ph = (grp - 4) % 3;
+        uint32_t o[4];
+        if (ph == 0) {
+          dx.d = word(cn, j);
+          dec_piece(t, dx, 0, o);
+          dec_piece(t, dx, 1, o);
+        } else if (ph == 1) {
+          dec_piece(t, dx, 2, o);
+          dec_piece(t, dx, 3, o);
+        } else {
+          dec_piece(t, dx, 4, o);
+          Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
         }
       }
+      // keep each group's loads and decode work in place (hoisting them stretches register
+      // lifetimes past the 256 a wave may use with two waves per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // This wave's LDS writes are done and the X DMA of step s+1 (older than the code loads of
     // step s+2, which stay in flight) has landed; the barrier publishes buffer P^1.
@@ -275,21 +285,17 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m
-  // for each (tn, tm, group of 4 accumulator registers).
+  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m.
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn)
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-      const int64_t m = m0 + wm * 128 + tm * 32 + (lane & 31);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 64 + tn * 32 + 8 * q + 4 * (lane >> 5);
-        if (m < g.M && n < g.C) {
-          const uint2 v = make_uint2(pack_bf16x2(acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1]),
-                                     pack_bf16x2(acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3]));
-          *reinterpret_cast<uint2 *>(g.out + m * g.ldo + n) = v;
-        }
+    for (int mt = 0; mt < 8; ++mt) {
+      const int64_t m = m0 + wm * 128 + mt * 16 + l16;
+      const int64_t n = n0 + wn * 64 + nt * 16 + 4 * g16;
+      if (m < g.M && n < g.C) {
+        const uint2 v = make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                                   pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+        *reinterpret_cast<uint2 *>(g.out + m * g.ldo + n) = v;
       }
     }
 }
