@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COLD_BYTES = 512 << 20        # rotate weight copies until they add up to this
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"qlora_fwd_fused": "fwd.hip", "qlora_bwd_dx": "dx.hip",
-                  "qlora_fwd_fused (decode)": "decode.hip"}
+                  "qlora_fwd_fused (decode)": "decode16.hip"}
 
 
 def parse():

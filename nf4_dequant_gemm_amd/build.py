@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnf4qlora.so")
 ARCH = os.environ.get("NF4Q_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "quant.hip", "fwd.hip", "decode.hip", "dx.hip", "lora.hip"]
+SOURCES = ["api.cpp", "quant.hip", "fwd.hip", "decode.hip", "decode16.hip", "dx.hip", "lora.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

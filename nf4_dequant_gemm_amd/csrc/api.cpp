@@ -283,6 +283,8 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
   g.out = (uint16_t *)Y;
   g.ldo = W->n;
   g.t = tables();
+  if (m <= 16 && W->dq_block > 0 && W->k % 256 == 0)
+    return hip_status(nf4q::launch_decode16_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
   if (m <= nf4q::kDecodeMaxM && W->k % 256 == 0)
     return hip_status(nf4q::launch_decode_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
   return hip_status(nf4q::launch_gemm_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");

@@ -37,6 +37,9 @@ hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
 // decode of unscaled levels, block constant applied to the per-block partial sums.
 hipError_t launch_decode_fwd(const GemmArgs &g, hipStream_t st);
 constexpr int64_t kDecodeMaxM = 48;
+// Forward for M <= 16, double-quantised W and K % 256 == 0: codes, X and block constants all
+// staged by LDS DMA in whole lines, 112 weight rows per workgroup.
+hipError_t launch_decode16_fwd(const GemmArgs &g, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).

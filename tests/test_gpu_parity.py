@@ -159,6 +159,13 @@ DECODE_CASES = [
     (48, 3328, 520, 64, 0),
     (16, 576, 200, 16, 256),
     (9, 1600, 72, 8, 0),
+    # M <= 16 with double quantisation (the 112-row stage-ring kernel): one stage, stage counts
+    # around the 8-stage loop and its 4-stage code windows, ragged and multi-workgroup N
+    (1, 256, 8, 0, 256),
+    (3, 1792, 112, 1, 256),
+    (7, 2304, 120, 8, 256),
+    (16, 4352, 1000, 64, 256),
+    (16, 8192, 336, 16, 256),
 ]
 
 
