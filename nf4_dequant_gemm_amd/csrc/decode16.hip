@@ -23,7 +23,9 @@
 //   * MFMA 16x16x32 multiplies the unscaled levels by X; the block constant a (per weight row and
 //     64-element block) scales the fp32 block partial sum afterwards:
 //         Y[m][n] += a(n, b) * sum_{k in block b} X[m][k] * level(code[n][k]);
-//   * the two waves of a tile take blocks 0-1 and 2-3 of every stage; their sums meet in LDS.
+//   * wave (g, j) takes block j of every stage for tiles 4g .. 4g + 3 (3 tiles for g = 1), so each
+//     X fragment is read from LDS once per block and serves every tile of the wave; the four
+//     partial sums of a tile meet in LDS at the end.
 // LDS layouts are XOR-swizzled so the matrix-core reads hit distinct banks; the swizzle is applied
 // on the DMA source side (the DMA writes 1 KB contiguously).
 // Numerics: the NF4 level (not level * a) is rounded to bf16 before the product, as in the other
@@ -37,7 +39,7 @@ namespace {
 
 constexpr int kTiles = 7;
 constexpr int kRows = 16 * kTiles;           // weight rows per workgroup
-constexpr int kWaves = 2 * kTiles;           // wave (t, h): tile t, blocks 2h and 2h+1 of a stage
+constexpr int kWaves = 8;                    // wave (g, j): tiles 4g .. 4g+3 (< 7), block j of a stage
 constexpr int kThreads = kWaves * 64;
 constexpr int kCodeBytes = kRows * 128;      // a stage: 4 blocks x 32 bytes of each row
 constexpr int kXOff = kCodeBytes;            // X slice: 16 rows x 256 elements
@@ -133,38 +135,73 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const i32x4 rS = rsrc_words(g.w.scale + run0, (nruns - run0) * 4);
   const i32x4 rX = rsrc_words(g.X, g.M * K * 2);
 
-  // DMA roles, per stage: every wave copies 1 KB of codes: rows 8 w .. 8 w + 7, lane L -> row
-  // 8 w + L / 8, LDS chunk L % 8, which holds the row's 16-byte chunk (L % 8) ^ ((row / 2) % 8).
-  // Waves 0..7 copy 1 KB of X: rows 2 w, 2 w + 1, lane L -> row 2 w + L / 32, LDS chunk L % 32
-  // holding chunk (L % 32) ^ (row % 16) of the row's 512 bytes. Waves 10, 11 copy the run scale
-  // of the stage's group for rows 64 (w - 10) + L. Once every 4 stages, waves 8, 9 copy the int8
-  // codes of the next 4 groups (16 bytes) for rows 64 (w - 8) + L into a code window.
-  const int crow = 8 * wave + (lane >> 3);
-  const uint32_t cvoff = (uint32_t)(crow * (K / 2) + 16 * ((lane & 7) ^ ((crow >> 1) & 7)));
-  const int xrow = 2 * (wave & 7) + (lane >> 5);
+  // DMA roles, per stage (3 copies per wave): the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7;
+  // lane L -> row 8 i + L / 8, LDS chunk L % 8, which holds the row's 16-byte chunk
+  // (L % 8) ^ ((row / 2) % 8). Wave w copies pieces w and, for w < 6, w + 8. X is 8 pieces,
+  // rows 2 w, 2 w + 1: lane L -> row 2 w + L / 32, LDS chunk L % 32 holding chunk
+  // (L % 32) ^ (row % 16) of the row's 512 bytes; wave w copies piece w. Waves 6, 7 copy the run
+  // scale of the stage's group for rows 64 (w - 6) + L. Once every 4 stages, waves 0, 1 also copy
+  // the int8 codes of the next 4 groups (16 bytes) for rows 64 w + L into a code window.
+  auto code_voff = [&](int i) {
+    const int r = 8 * i + (lane >> 3);
+    return (uint32_t)(r * (K / 2) + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+  };
+  const uint32_t cvoff0 = code_voff(wave), cvoff1 = code_voff(wave < 6 ? wave + 8 : wave);
+  const int xrow = 2 * wave + (lane >> 5);
   const uint32_t xvoff = (uint32_t)(xrow * K * 2 + 16 * ((lane & 31) ^ (xrow & 15)));
-  const int krow = 64 * (wave & 1) + lane;          // waves 8..11: row of the constants
+  const int krow = 64 * (wave & 1) + lane;          // row of the block constants copied
   const uint32_t qvoff = (uint32_t)(krow * kblk);
-  const uint32_t cdst = 1024 * wave, xdst = kXOff + 1024 * (wave & 7), sdst = kSOff + 256 * (wave & 1);
-  const uint32_t qdst = 1024 * (wave & 1);
+  const uint32_t cdst0 = 1024 * wave, cdst1 = 1024 * (wave + 8), xdst = kXOff + 1024 * wave;
+  const uint32_t sdst = kSOff + 256 * (wave & 1), qdst = 1024 * (wave & 1);
 
+  // Workgroups start at different groups of K (in steps of 4, which keeps the code windows
+  // aligned): stage st reads group (st + rot) % nst. All workgroups walking K in step would send
+  // their requests to the same few memory channels at a time (measured: the DMA stream alone runs
+  // at 4.1 TB/s in step and 5.0 TB/s staggered).
+  const int rot = (nst >= 8 && nst % 4 == 0) ? (int)(blockIdx.x % (unsigned)(nst / 4)) * 4 : 0;
   // Copies of stage st into slot dst (look-ahead past the end re-reads the last stage into a slot
   // nobody reads any more); with the window flag, waves 8, 9 also copy the block codes of stages
-  // st .. st + 3 into window qw.
+  // st .. st + 3 into window qw. Stage numbers here are the workgroup's own order; the group of
+  // K they read is rotated by rot.
   auto dma = [&](int st, uint32_t dst, bool window, uint32_t qw) {
     st = st < nst ? st : nst - 1;
-    dma16(rC, dst + cdst, cvoff, (uint32_t)(st * 128));
-    if (wave < 8) {
-      dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
-    } else if (wave < 10) {
-      if (window) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
-    } else if (wave < 12) {
+    st += rot;
+    st = st < nst ? st : st - nst;
+    dma16(rC, dst + cdst0, cvoff0, (uint32_t)(st * 128));
+    dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
+    if (wave < 6) {
+      dma16(rC, dst + cdst1, cvoff1, (uint32_t)(st * 128));
+      if (window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
+    } else {
       const uint32_t run = (uint32_t)((boff + krow * kblk + 4 * st) >> 8);
       dma4(rS, dst + sdst, run * 4);
     }
   };
-  // Copies this wave issues in stage st's DMA (the count the stage waits below rely on).
-  auto ndma = [&](bool window) { return wave < 8 || (wave >= 10 && wave < 12) ? 2 : wave < 10 ? 1 + (int)window : 1; };
+  // Copies this wave issues in one stage's DMA (the count the stage waits below rely on).
+  auto ndma = [&](bool window) { return 3 + (int)(window && wave < 2); };
+
+  // LoRA operands of the tile this wave finishes (tile 4 g + j below, g = wave / 4,
+  // j = wave % 4), loaded now so that their latency hides under the main loop: rank steps of 32,
+  // lane (nl, gl) holds ranks 32 s + 8 gl .. + 7 of T row nl and of B row 16 t + nl (16-byte loads
+  // when r % 8 == 0; ranks at or past r, rows past M or N read as zero). Issued before the first
+  // copies, so the first stage wait covers them.
+  const int tfin = 4 * (wave >> 2) + (wave & 3);
+  const int nlf = lane & 15, glf = lane >> 4;
+  const bool lvec = g.r > 0 && g.r % 8 == 0 && tfin < kTiles;
+  u32x4 tpre[4], bpre[4];
+  {
+    // every load is issued (no branch, no register copies that would wait for them); those not
+    // needed read outside the buffers and return zero
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, lvec ? g.M * g.r * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (lvec ? n0 * g.r : 0), lvec ? rows * g.r * 2 : 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j0 = 32 * q + 8 * glf;
+      const uint32_t off = j0 < g.r ? 0u : 0x80000000u;   // ranks past r: outside both buffers
+      tpre[q] = __builtin_amdgcn_raw_buffer_load_b128(rT, (uint32_t)((nlf * g.r + j0) * 2) | off, 0, 0);
+      bpre[q] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(((16 * tfin + nlf) * g.r + j0) * 2) | off, 0, 0);
+    }
+  }
 
   dma(0, lds_addr(slot0), true, lds_addr(qwin0));
   dma(1, lds_addr(slot1), false, 0);
@@ -186,37 +223,39 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     reinterpret_cast<uint4 *>(stab)[i] = make_uint4(v, v, v, v);
   }
 
-  // This wave's operands: tile t, blocks jj = 2 h + b (b = 0, 1) of each stage. MFMA lanes:
-  // nl = column (weight row 16 t + nl) and X row, gl = k-group: the lane takes bytes
-  // 8 gl .. 8 gl + 7 of the row's block (elements 16 gl .. 16 gl + 15; the first 8 feed MFMA 0,
-  // the next 8 MFMA 1) and the same elements of X.
-  const int t = wave >> 1, h = wave & 1;
+  // This wave's operands: block jb of each stage for tiles t = 4 g + tt. MFMA lanes: nl = column
+  // (weight row 16 t + nl) and X row, gl = k-group: the lane takes bytes 8 gl .. 8 gl + 7 of the
+  // row's block (elements 16 gl .. 16 gl + 15; the first 8 feed MFMA 0, the next 8 MFMA 1) and the
+  // same elements of X.
+  const int grp = wave >> 2, jb = wave & 3;
+  const int ntiles = grp == 0 ? 4 : kTiles - 4;
   const int nl = lane & 15, gl = lane >> 4;
-  const int row = 16 * t + nl;
-  uint32_t caddr[2], xaddr[2][2], qaddr[2];
+  uint32_t caddr[4], qaddr[4], saddr[4], xaddr[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int jj = 2 * h + b;
-    caddr[b] = (uint32_t)(row * 128 + 16 * ((2 * jj + (gl >> 1)) ^ ((row >> 1) & 7)) + 8 * (gl & 1));
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      xaddr[b][hh] = (uint32_t)(kXOff + nl * 512 + 16 * ((8 * jj + 2 * gl + hh) ^ nl));
-    qaddr[b] = (uint32_t)(row * 16 + jj);        // in the window, + 4 * (stage % 4)
+  for (int tt = 0; tt < 4; ++tt) {
+    const int row = 16 * (4 * grp + tt) + nl;
+    caddr[tt] = (uint32_t)(row * 128 + 16 * ((2 * jb + (gl >> 1)) ^ ((row >> 1) & 7)) + 8 * (gl & 1));
+    qaddr[tt] = (uint32_t)(row * 16 + jb);          // in the window, + 4 * (stage % 4)
+    saddr[tt] = (uint32_t)(kSOff + row * 4);
   }
-  const uint32_t saddr = (uint32_t)(kSOff + row * 4);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+    xaddr[hh] = (uint32_t)(kXOff + nl * 512 + 16 * ((8 * jb + 2 * gl + hh) ^ nl));
   const uint32_t lane_off = (uint32_t)lane * 4;
   const char *ctab = reinterpret_cast<const char *>(stab);
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // One stage from slot base sb and window base qb (LDS byte addresses).
   auto consume = [&](uint32_t sb, uint32_t qb) {
-    const float sc = lds_ld<float>(sb + saddr);
+    const bf16x8 x0 = lds_ld<bf16x8>(sb + xaddr[0]);
+    const bf16x8 x1 = lds_ld<bf16x8>(sb + xaddr[1]);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const u32x2 cw = lds_ld<u32x2>(sb + caddr[b]);
-      const bf16x8 x0 = lds_ld<bf16x8>(sb + xaddr[b][0]);
-      const bf16x8 x1 = lds_ld<bf16x8>(sb + xaddr[b][1]);
-      const float a = float(lds_ld<int8_t>(qb + qaddr[b])) * sc;
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt == 3 && ntiles == 3) break;
+      const u32x2 cw = lds_ld<u32x2>(sb + caddr[tt]);
+      const float a = float(lds_ld<int8_t>(qb + qaddr[tt])) * lds_ld<float>(sb + saddr[tt]);
       uint32_t o[8];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -230,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       f32x4 part = mfma16x16x32(x0, w0, f32x4{0.f, 0.f, 0.f, 0.f});
       part = mfma16x16x32(x1, w1, part);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += a * part[v];
+      for (int v = 0; v < 4; ++v) acc[tt][v] += a * part[v];
     }
   };
 
@@ -244,12 +283,10 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     // copies of phases i + 1 and i + 2 = (i + 1) % 4, (i + 2) % 4; the window goes with phase 0)
     const bool w1 = ((i + 1) & 3) == 0, w2 = ((i + 2) & 3) == 0;
     const int pending = ndma(w1) + ndma(w2);
-    if (pending == 4)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (pending == 3)
-      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (pending == 7)
+      asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int in = (i + 3) & 3;                      // phase of stage st + 3
     dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
     consume(opaque(lds_addr(slot(i))), opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i));  // 4 codes of each row
@@ -267,16 +304,32 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // Every wave past its last stage (and every DMA landed: the look-ahead loads wrote into slots
   // nobody reads any more) before the table area is reused for the cross-wave sums.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Partial sums red[tile][block][lane]; wave (g, jb) then finishes tile 4 g + jb (7 tiles).
   f32x4 *red = reinterpret_cast<f32x4 *>(stab);
-  if (h == 1) red[t * 64 + lane] = acc;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+    if (tt < ntiles) red[((4 * grp + tt) * 4 + jb) * 64 + lane] = acc[tt];
   __syncthreads();
-  if (h == 1) return;
-  acc += red[t * 64 + lane];
+  const int t = 4 * grp + jb;
+  if (t >= kTiles) return;
+  const int row = 16 * t + nl;
+  f32x4 y = red[(t * 4) * 64 + lane];
+#pragma unroll
+  for (int jj = 1; jj < 4; ++jj) y += red[(t * 4 + jj) * 64 + lane];
 
   // LoRA term on the matrix cores: s * T[m][:] . B[n][:] for the tile's 16 columns, in steps of
-  // 32 ranks (A operand: T row m, B operand: B row n, both rank-contiguous; ranks at or past r,
-  // rows past M or N read as zero).
-  if (g.r > 0) {
+  // 32 ranks (A operand: T row m, B operand: B row n, both rank-contiguous). With r % 8 == 0 the
+  // operands were loaded before the main loop; otherwise they are read here element by element.
+  if (lvec) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (32 * q < g.r) {
+        const f32x4 lp = mfma16x16x32(__builtin_bit_cast(bf16x8, tpre[q]),
+                                      __builtin_bit_cast(bf16x8, bpre[q]), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) y[v] += g.s * lp[v];
+      }
+  } else if (g.r > 0) {
     const int r = g.r;
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, g.M * r * 2);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + n0 * r, rows * r * 2);
@@ -285,10 +338,10 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       uint32_t tb[8], bb[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = j0 + gl * 8 + e;
-        const bool in = j < r;
-        bb[e] = in ? __builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)((row * r + j) * 2), 0, 0) : 0u;
-        tb[e] = in ? __builtin_amdgcn_raw_buffer_load_b16(rT, (uint32_t)((nl * r + j) * 2), 0, 0) : 0u;
+        const int jr = j0 + gl * 8 + e;
+        const bool in = jr < r;
+        bb[e] = in ? __builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)((row * r + jr) * 2), 0, 0) : 0u;
+        tb[e] = in ? __builtin_amdgcn_raw_buffer_load_b16(rT, (uint32_t)((nl * r + jr) * 2), 0, 0) : 0u;
       }
       u32x4 bw, tw;
 #pragma unroll
@@ -299,16 +352,16 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       const f32x4 lp = mfma16x16x32(__builtin_bit_cast(bf16x8, tw), __builtin_bit_cast(bf16x8, bw),
                                     f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += g.s * lp[v];
+      for (int v = 0; v < 4; ++v) y[v] += g.s * lp[v];
     }
   }
 
-  // acc[v] = Y[m][n] for m = 4 gl + v, n = n0 + 16 t + nl
+  // y[v] = Y[m][n] for m = 4 gl + v, n = n0 + 16 t + nl
   const int64_t gn = n0 + row;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t m = 4 * gl + v;
-    if (m < g.M && gn < N) g.Y[m * N + gn] = (uint16_t)(pack_bf16x2(acc[v], 0.f) & 0xFFFFu);
+    if (m < g.M && gn < N) g.Y[m * N + gn] = (uint16_t)(pack_bf16x2(y[v], 0.f) & 0xFFFFu);
   }
 }
 
