@@ -21,8 +21,9 @@
 //   * the X tile of step s+1 is requested by DMA straight into LDS buffer (s+1) & 1
 //     (buffer_load ... lds: no registers, no LDS store instructions; its latency hides behind the
 //     whole step), and the codes and block constant of step s+2 are loaded into registers,
-//   * the 64 MFMAs of step s run on LDS buffer s & 1 in 16 groups (k-slice, m-tile) of 4, the
-//     X fragment of the next group read while the current one is multiplied,
+//   * the 64 MFMAs of step s run on LDS buffer s & 1 in 16 groups (k-slice, m-tile) of 4, each
+//     X fragment read two groups before its MFMAs and the second k-slice's weight fragments four
+//     groups before theirs,
 //   * between MFMA issues, the W half-rows of step s+1 (codes loaded one step earlier) are decoded
 //     and written to LDS buffer (s+1) & 1.
 // LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
@@ -206,36 +207,43 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
     const uint4 *A = xbuf(P);
     const uint4 *B = wbuf(P);
     uint4 *Bn = wbuf(P ^ 1);
-    bf16x8 aw[4], xb[2];
+    // LDS operands: the first k-slice's weight fragments and the first two X fragments now; the
+    // NF4 table of step s+1 is built while they arrive; later X fragments are read two groups
+    // ahead and the second k-slice's weight fragments four groups ahead, so an MFMA rarely waits
+    // for an LDS read.
+    bf16x8 aw0[4], aw1[4], xb[3];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(B, 0, nt);
+    for (int nt = 0; nt < 4; ++nt) aw0[nt] = wfrag(B, 0, nt);
     xb[0] = xfrag(A, 0, 0);
+    xb[1] = xfrag(A, 0, 1);
 
     const float a = absmax_of(cn);
     uint32_t pk[8];
     RowTable t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pk[2 * q] = pack_bf16x2(g.t.level[4 * q] * a, g.t.level[4 * q + 1] * a);
+      pk[2 * q + 1] = pack_bf16x2(g.t.level[4 * q + 2] * a, g.t.level[4 * q + 3] * a);
+      t.L[q] = perm(pk[2 * q + 1], pk[2 * q], 0x06040200u);
+      t.H[q] = perm(pk[2 * q + 1], pk[2 * q], 0x07050301u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     Dec8 dx;
 #pragma unroll
     for (int grp = 0; grp < 16; ++grp) {
-      const int mt = grp & 7;
-      // the second k-slice's weight fragments replace the first's; the next m-tile's X fragment
-      // is read one group ahead
-      if (grp == 8) {
+      const int mt = grp & 7, ks = grp >> 3;
+      if (grp == 4) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(B, 1, nt);
+        for (int nt = 0; nt < 4; ++nt) aw1[nt] = wfrag(B, 1, nt);
       }
-      if (grp + 1 < 16) xb[(grp + 1) & 1] = xfrag(A, (grp + 1) >> 3, (grp + 1) & 7);
+      if (grp + 2 < 16) xb[(grp + 2) % 3] = xfrag(A, (grp + 2) >> 3, (grp + 2) & 7);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt][mt] = mfma16x16x32(aw[nt], xb[grp & 1], acc[nt][mt]);
-      // decode of step s+1: table in groups 0..3, then word j = (grp - 4) / 3 in pieces over
-      // three groups (pieces 0-1, 2-3, 4 + store)
-      if (grp < 4) {
-        pk[2 * grp] = pack_bf16x2(g.t.level[4 * grp] * a, g.t.level[4 * grp + 1] * a);
-        pk[2 * grp + 1] = pack_bf16x2(g.t.level[4 * grp + 2] * a, g.t.level[4 * grp + 3] * a);
-        t.L[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x06040200u);
-        t.H[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x07050301u);
-      } else {
-        const int j = (grp - 4) / 3, ph = (grp - 4) % 3;
+      for (int nt = 0; nt < 4; ++nt)
+        acc[nt][mt] = mfma16x16x32(ks ? aw1[nt] : aw0[nt], xb[grp % 3], acc[nt][mt]);
+      // decode of step s+1: word j = grp / 3 in pieces over three groups (pieces 0-1, 2-3,
+      // 4 + store), groups 0..11
+      if (grp < 12) {
+        const int j = grp / 3, ph = grp % 3;
         uint32_t o[4];
         if (ph == 0) {
           dx.d = word(cn, j);
