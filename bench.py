@@ -132,6 +132,12 @@ class Layer:
         self.check(self.c.qlora_fwd_fused(p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["T"],
                                           p["B"], w.r, w.s, p["Y"], self.sp))
 
+    def fwd_whole(self, i):
+        """The whole forward call (T pre-pass and fused kernel), as a caller makes it."""
+        w, p = self.w, self.p
+        self.check(self.c.qlora_fwd(p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["A"], p["B"],
+                                    w.r, w.s, p["Y"], p["T"], p["ws_f"], self.fws, self.sp))
+
     def bwd_lora(self, i):
         """U (left at the start of the workspace), dA and dB: qlora_bwd without dX."""
         w, p = self.w, self.p
@@ -176,6 +182,22 @@ def time_layer(L, steps, warmup):
     return (t1 - t0) * 1e3 / steps, per
 
 
+def time_call(L, fn, steps, warmup):
+    """HIP-event times (ms) of one call over rotating weight copies: median, p10, p90."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, (a, b) in enumerate(ev):
+        a.record(L.stream)
+        fn(warmup + s)
+        b.record(L.stream)
+    torch.cuda.synchronize()
+    v = [a.elapsed_time(b) for a, b in ev]
+    return {"median": pct(v, 0.5), "p10": pct(v, 0.1), "p90": pct(v, 0.9)}
+
+
 def source_sha(name):
     path = os.path.join(ROOT, "nf4_dequant_gemm_amd", "csrc", KERNEL_SOURCES[name])
     with open(path, "rb") as f:
@@ -200,7 +222,7 @@ def run_weight_stream(dev, steps, warmup):
     w = wl.WORKLOADS["decode"]
     L = Layer(w, dev)
     _, per = time_layer(L, steps, warmup)
-    fwd_ms = per["lora_down"]["median"] + per["fwd_fused"]["median"]
+    fwd_ms = time_call(L, L.fwd_whole, steps, warmup)["median"]
     wb = w.weight_stream_bytes()
     gbs = wb / (fwd_ms * 1e-3) / 1e9
     kern = wb / (per["fwd_fused"]["median"] * 1e-3) / 1e9
@@ -335,6 +357,7 @@ def main():
     dev = torch.device("cuda:0")
     L = Layer(w, dev, args.wcopies)
     step_ms, per = time_layer(L, args.steps, args.warmup)
+    whole_fwd = time_call(L, L.fwd_whole, args.steps, args.warmup) if not w.backward else None
     ncopies = len(L.copies)
     context = None if args.no_context else run_context(L)
     del L
@@ -370,6 +393,11 @@ def main():
                    "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}},
         "roofline": roof,
     }
+    if whole_fwd:
+        out["config"]["qlora_fwd_ms"] = {q: round(x, 4) for q, x in whole_fwd.items()}
+        if M <= 64:
+            gbs = w.weight_stream_bytes() / (whole_fwd["median"] * 1e-3) / 1e9
+            out["config"]["weight_stream_GBps"] = round(gbs, 1)
     if context:
         ref = context.get("vendor_bf16_gemm", {}).get("TFLOP/s") or context.get("device_copy", {}).get("GB/s")
         if ref:

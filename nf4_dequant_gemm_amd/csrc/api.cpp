@@ -295,8 +295,43 @@ int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, cons
   int st = check_layer(X, m, W, A, B, r);
   if (st) return st;
   if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  // Decode shapes (the M <= 16 kernel): the split partials of T = X A^T are added inside the
+  // fused kernel (its prologue hides them under the first weight copies), saving the separate
+  // reduction launch; workgroup 0 of the fused kernel writes T.
+  const int64_t k = W->k;
+  if (r > 0 && m <= 16 && W->dq_block > 0 && k % 256 == 0 && r % 8 == 0) {
+    const FwdWs lay = fwd_ws(m, k, r);
+    if (lay.splits > 1 && (int64_t)r * lay.splits <= 1024) {
+      if (!T || !aligned16(T)) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
+      if (ws_bytes < lay.total || !ws)
+        return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                    lay.total);
+      if (!aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+      hipStream_t sm = (hipStream_t)stream;
+      hipError_t e = nf4q::launch_rowproj((const uint16_t *)X, k, (const uint16_t *)A, k, m, k, r,
+                                          lay.splits, (float *)ws, nullptr, sm);
+      if (e != hipSuccess) return hip_status(e, "qlora_fwd launch");
+      nf4q::GemmArgs g;
+      g.a_side = (const uint16_t *)X;
+      g.lda = k;
+      g.lora_a = nullptr;
+      g.lora_b = (const uint16_t *)B;
+      g.w = desc(W);
+      g.M = m;
+      g.C = W->n;
+      g.R = k;
+      g.r = r;
+      g.s = s;
+      g.out = (uint16_t *)Y;
+      g.ldo = W->n;
+      g.t = tables();
+      return hip_status(nf4q::launch_decode16_fwd_tpart(g, (const float *)ws, lay.splits,
+                                                        (uint16_t *)T, sm),
+                        "qlora_fwd launch");
+    }
+  }
   if (r > 0) {
-    st = qlora_lora_down(X, m, W->k, A, r, T, ws, ws_bytes, stream);
+    st = qlora_lora_down(X, m, k, A, r, T, ws, ws_bytes, stream);
     if (st) return st;
   }
   return qlora_fwd_fused(X, m, W, T, B, r, s, Y, stream);

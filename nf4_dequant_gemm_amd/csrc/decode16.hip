@@ -58,6 +58,9 @@ struct Dec16Args {
   float s;
   uint16_t *Y;
   Tables t;
+  const float *tpart;   // T = X A^T as split partials [M][r][tsplits] (NULL: T is given)
+  int tsplits;
+  uint16_t *tout;       // with tpart: T (bf16 [M][r]) written by workgroup 0
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   {
     // every load is issued (no branch, no register copies that would wait for them); those not
     // needed read outside the buffers and return zero
-    const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, lvec ? g.M * g.r * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, lvec && !g.tpart ? g.M * g.r * 2 : 0);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (lvec ? n0 * g.r : 0), lvec ? rows * g.r * 2 : 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -221,6 +224,43 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     const int e = i >> 4;
     const uint32_t v = pack_bf16x2(lv[e >> 4], lv[e & 15]);
     reinterpret_cast<uint4 *>(stab)[i] = make_uint4(v, v, v, v);
+  }
+
+  // T from split partials: every workgroup adds them (in split order, as the separate reduction
+  // does) into bf16 T in LDS (slot 3, after the levels), workgroup 0 also stores T, and the
+  // finishing waves take their LoRA operands from LDS. The partial loads wait for the copies
+  // issued above too (the compiler does not see those), which costs little: the first stage waits
+  // for them anyway.
+  if (g.tpart) {
+    uint16_t *tl = reinterpret_cast<uint16_t *>(slot3 + 1024);
+    const int r = g.r;
+    for (int idx = tid; idx < 16 * r; idx += kThreads) {
+      const int m = idx / r, j = idx - m * r;
+      float a = 0.f;
+      if (m < g.M) {
+        const float *pp = g.tpart + ((int64_t)m * r + j) * g.tsplits;
+        int q = 0;
+        for (; q + 8 <= g.tsplits; q += 8) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = pp[q + e];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a += v[e];
+        }
+        for (; q < g.tsplits; ++q) a += pp[q];
+      }
+      const uint16_t tb = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFFu);
+      tl[idx] = tb;
+      if (blockIdx.x == 0 && m < g.M) g.tout[idx] = tb;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (lvec) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * q + 8 * glf;
+        tpre[q] = j0 < r ? *reinterpret_cast<const u32x4 *>(tl + nlf * r + j0) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
   }
 
   // This wave's operands: block jb of each stage for tiles t = 4 g + tt. MFMA lanes: nl = column
@@ -378,7 +418,32 @@ hipError_t launch_decode16_fwd(const GemmArgs &ga, hipStream_t st) {
   g.s = ga.s;
   g.Y = ga.out;
   g.t = ga.t;
+  g.tpart = nullptr;
+  g.tsplits = 0;
+  g.tout = nullptr;
   if (ga.M > 16 || !ga.w.dq || ga.w.k % 256 != 0) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
+  decode16_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode16_fwd_tpart(const GemmArgs &ga, const float *tpart, int tsplits,
+                                     uint16_t *tout, hipStream_t st) {
+  Dec16Args g;
+  g.X = ga.a_side;
+  g.T = ga.lora_a;
+  g.B = ga.lora_b;
+  g.w = ga.w;
+  g.M = ga.M;
+  g.r = ga.r;
+  g.s = ga.s;
+  g.Y = ga.out;
+  g.t = ga.t;
+  g.tpart = tpart;
+  g.tsplits = tsplits;
+  g.tout = tout;
+  if (ga.M > 16 || !ga.w.dq || ga.w.k % 256 != 0 || ga.r % 8 != 0 || !tpart || tsplits < 1)
+    return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
   decode16_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();

@@ -40,11 +40,17 @@ constexpr int64_t kDecodeMaxM = 48;
 // Forward for M <= 16, double-quantised W and K % 256 == 0: codes, X and block constants all
 // staged by LDS DMA in whole lines, 112 weight rows per workgroup.
 hipError_t launch_decode16_fwd(const GemmArgs &g, hipStream_t st);
+// The same with T = X A^T given as split partials (float [M][r][tsplits], see launch_rowproj):
+// every workgroup adds them in split order for its LoRA term and workgroup 0 writes T (bf16) to
+// tout. Requires r % 8 == 0.
+hipError_t launch_decode16_fwd_tpart(const GemmArgs &g, const float *tpart, int tsplits,
+                                     uint16_t *tout, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).
-// With splits > 1 the partial sums go to part (float [splits][M][r]) and are reduced by
-// launch_rowproj_reduce into out.
+// With splits > 1 the partial sums go to part (float [M][r][splits], the splits of one output
+// contiguous) and a second launch adds them in split order into out; with out == NULL only the
+// partials are written (their consumer adds them in the same order).
 hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t ldp,
                           int64_t M, int64_t L, int r, int splits, float *part, uint16_t *out,
                           hipStream_t st);

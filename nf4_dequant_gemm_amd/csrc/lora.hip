@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
       const int64_t row = mbase + wave * 16 + 4 * (lane >> 4) + v;
       const int j = t * 16 + (lane & 15);
       if (row < M && j < r) {
-        if (part)
-          part[((int64_t)split * M + row) * r + j] = acc[t][v];
+        if (part)   // split-contiguous: the sum over splits reads one contiguous run
+          part[((int64_t)row * r + j) * gridDim.y + split] = acc[t][v];
         else
           out[row * r + j] = (uint16_t)(pack_bf16x2(acc[t][v], 0.f) & 0xFFFFu);
       }
@@ -129,16 +129,17 @@ __global__ void rowproj_reduce_kernel(const float *__restrict__ part, int64_t n,
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     // sequential sum over the splits (fixed order), its loads issued eight at a time
+    const float *pi = part + i * splits;
     float a = 0.f;
     int s = 0;
     for (; s + 8 <= splits; s += 8) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(s + j) * n + i];
+      for (int j = 0; j < 8; ++j) v[j] = pi[s + j];
 #pragma unroll
       for (int j = 0; j < 8; ++j) a += v[j];
     }
-    for (; s < splits; ++s) a += part[(int64_t)s * n + i];
+    for (; s < splits; ++s) a += pi[s];
     out[i] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFFu);
   }
 }
@@ -168,7 +169,7 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || splits == 1 || !out) return e;
   const int64_t n = M * r;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
