@@ -266,8 +266,14 @@ def run_cpu_baseline(w, target_s):
         dt = step(rows)
     flops = (w.fwd_flops() + (w.bwd_flops() if w.backward else 0)) * rows / w.M
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model, "wall_s": round(dt, 2),
             "sample": f"{rows} of {w.M} rows of the {w.name} workload, forward+backward in float64 "
                       f"(numpy/BLAS), {dt:.1f}s wall; W dequantised once outside the timing"}
 

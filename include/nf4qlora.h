@@ -130,7 +130,9 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
 /* Bytes of device workspace qlora_bwd needs for these sizes. */
 size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 
-/* Backward of the QLoRA layer, given the upstream gradient dY bf16 [m, n] and T from qlora_fwd:
+/* Backward of the QLoRA layer, given the upstream gradient dY bf16 [m, n] and T from qlora_fwd
+ * (T may be NULL: it is then recomputed as X A^T into the workspace, exactly as qlora_fwd and
+ * qlora_lora_down compute it):
  *   U  = bf16(dY B)                               (left in the workspace: see below)
  *   dX = bf16(dY deq(W) + s U A)      bf16 [m, k]  (skipped when dX is NULL)
  *   dA = bf16(s U^T X)                bf16 [r, k]

@@ -232,7 +232,8 @@ def qlora_bwd(dY: torch.Tensor, X: torch.Tensor, q: NF4Tensor, A: Optional[torch
     if r:
         _need(A, "A", torch.bfloat16, (r, q.k))
         _need(B, "B", torch.bfloat16, (q.n, r))
-        _need(T, "T", torch.bfloat16, (m, r))
+        if T is not None:                 # None: the library recomputes T = X A^T
+            _need(T, "T", torch.bfloat16, (m, r))
     dev = X.device
     dX = torch.empty(m, q.k, dtype=torch.bfloat16, device=dev) if need_dx else None
     dA = torch.empty(r, q.k, dtype=torch.bfloat16, device=dev) if r else None

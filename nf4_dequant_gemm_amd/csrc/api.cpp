@@ -176,8 +176,10 @@ FwdWs fwd_ws(int64_t m, int64_t k, int32_t r) {
 }
 
 struct BwdWs {
-  int splits_u = 1, splits_a = 1, splits_b = 1;
-  size_t u = 0, bt = 0, part = 0, total = 0;   // byte offsets: U at 0, Bt at u, partials at u+bt
+  int splits_u = 1, splits_a = 1, splits_b = 1, splits_t = 1;
+  // byte sizes: U at 0, Bt at u, T (recomputed when the caller passes none) at u + bt, partials
+  // at u + bt + t
+  size_t u = 0, bt = 0, t = 0, part = 0, total = 0;
 };
 
 BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
@@ -185,15 +187,18 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
   if (r <= 0) return w;
   w.u = align256((size_t)m * r * 2);
   w.bt = align256((size_t)r * n * 2);
+  w.t = align256((size_t)m * r * 2);
   w.splits_u = nf4q::rowproj_splits(m, n);
+  w.splits_t = nf4q::rowproj_splits(m, k);
   w.splits_a = nf4q::mreduce_splits(m, k);
   w.splits_b = nf4q::mreduce_splits(m, n);
   size_t p = 0;
   if (w.splits_u > 1) p = std::max(p, (size_t)w.splits_u * m * r * 4);
+  if (w.splits_t > 1) p = std::max(p, (size_t)w.splits_t * m * r * 4);
   p = std::max(p, (size_t)w.splits_a * r * k * 4);
   p = std::max(p, (size_t)w.splits_b * r * n * 4);
   w.part = align256(p);
-  w.total = w.u + w.bt + w.part;
+  w.total = w.u + w.bt + w.t + w.part;
   return w;
 }
 
@@ -350,8 +355,8 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
   if (!dY || !aligned16(dY)) return fail(NF4_EINVAL, "dY must be non-NULL and 16-byte aligned");
   if (dX && !aligned16(dX)) return fail(NF4_EINVAL, "dX must be 16-byte aligned");
   if (r > 0) {
-    if (!T || !dA || !dB) return fail(NF4_EINVAL, "T, dA and dB must be non-NULL when r > 0");
-    if (!aligned16(T) || !aligned16(dA) || !aligned16(dB))
+    if (!dA || !dB) return fail(NF4_EINVAL, "dA and dB must be non-NULL when r > 0");
+    if ((T && !aligned16(T)) || !aligned16(dA) || !aligned16(dB))
       return fail(NF4_EINVAL, "T, dA and dB must be 16-byte aligned");
   }
   if (!dX && r == 0) return ok();
@@ -365,9 +370,16 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
   char *base = (char *)ws;
   uint16_t *U = (uint16_t *)base;
   uint16_t *Bt = (uint16_t *)(base + lay.u);
-  float *part = (float *)(base + lay.u + lay.bt);
+  float *part = (float *)(base + lay.u + lay.bt + lay.t);
   const uint16_t *dy = (const uint16_t *)dY;
   hipError_t e;
+  if (r > 0 && !T) {   // T = X A^T recomputed into the workspace, as qlora_lora_down computes it
+    uint16_t *Tw = (uint16_t *)(base + lay.u + lay.bt);
+    e = nf4q::launch_rowproj((const uint16_t *)X, k, (const uint16_t *)A, k, m, k, r, lay.splits_t,
+                             part, Tw, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_bwd T launch");
+    T = Tw;
+  }
   if (r > 0) {
     e = nf4q::launch_transpose((const uint16_t *)B, n, r, Bt, sm);
     if (e != hipSuccess) return hip_status(e, "qlora_bwd transpose launch");

@@ -302,3 +302,38 @@ def test_bwd_split_matches_bwd(lib):
     assert torch.equal(dA.view(torch.int16), dA_full.view(torch.int16))
     assert torch.equal(dB.view(torch.int16), dB_full.view(torch.int16))
     check_close("U", f32(U), f32(dY).astype(np.float64) @ f32(B).astype(np.float64))
+
+
+@pytest.mark.parametrize("M,K,N,r", [(16, 8192, 336, 16), (7, 2304, 120, 8), (1, 768, 232, 64)])
+def test_decode_qlora_fwd_matches_two_calls(lib, M, K, N, r):
+    """On decode shapes qlora_fwd adds the split partials of T inside the fused kernel; Y and T
+    equal those of qlora_lora_down followed by qlora_fwd_fused bit for bit (same partials, same
+    summation order), and T matches X A^T from the oracle."""
+    s = 2.0
+    X, W, A, _, _ = rand_layer(M, K, N, r, seed=M * 7 + K + N)
+    B = wl.normal_bf16(M + K + N + 5, (N, r), 0.1)
+    qg = lib.nf4_quantize(W.to(DEV), 256)
+    Xd, Ad, Bd = X.to(DEV), A.to(DEV), B.to(DEV)
+    Y1, T1 = lib.qlora_fwd(Xd, qg, Ad, Bd, s)
+    T2 = lib.qlora_lora_down(Xd, Ad)
+    Y2 = lib.qlora_fwd_fused(Xd, qg, T2, Bd, s)
+    torch.cuda.synchronize()
+    assert torch.equal(T1.view(torch.int16), T2.view(torch.int16))
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    check_close("T", f32(T1), f32(X).astype(np.float64) @ f32(A).astype(np.float64).T)
+
+
+@pytest.mark.parametrize("M,K,N,r", [(200, 512, 264, 16), (16, 2304, 120, 8)])
+def test_bwd_recomputes_missing_T(lib, M, K, N, r):
+    """qlora_bwd with T = NULL recomputes T = X A^T in its workspace: dX, dA and dB equal those of
+    a call given the T of qlora_fwd, bit for bit."""
+    s = 0.5
+    X, W, A, B, dY = rand_layer(M, K, N, r, seed=M + 3 * K + N)
+    qg = lib.nf4_quantize(W.to(DEV), 256)
+    Xd, Ad, Bd, dYd = X.to(DEV), A.to(DEV), B.to(DEV), dY.to(DEV)
+    _, T = lib.qlora_fwd(Xd, qg, Ad, Bd, s)
+    g1 = lib.qlora_bwd(dYd, Xd, qg, Ad, Bd, s, T)
+    g2 = lib.qlora_bwd(dYd, Xd, qg, Ad, Bd, s, None)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

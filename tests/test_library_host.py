@@ -125,7 +125,8 @@ def test_layer_calls_reject_bad_arguments():
                                       kw.get("ws", FAKE), kw.get("wsb", wsb), None)
     assert bwd(wsb=wsb - 1) == m.NF4_EINVAL
     assert bwd(ws=None) == m.NF4_EINVAL
-    assert bwd(T=None) == m.NF4_EINVAL
+    assert bwd(T=None, wsb=wsb - 1) == m.NF4_EINVAL       # T may be NULL (recomputed), ws still checked
+    assert bwd(T=ctypes.c_void_p(4100)) == m.NF4_EINVAL  # misaligned T
     assert bwd(dA=None) == m.NF4_EINVAL
     assert bwd(r=200) == m.NF4_EINVAL
     assert "workspace" in lib.nf4_last_error().decode() or lib.nf4_last_error()
