@@ -61,42 +61,63 @@ struct CStage {
   uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
 };
 
-// LoRA step staging: the weight side gets s * A rows j = jb .. jb+63 (columns k0 ..), laid out
-// like a decoded weight tile; the dY side gets U columns jb .. jb+63 (rows m0 ..); zero-padded.
-__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int jb, uint4 *sY,
-                              uint16_t *sW) {
+// LoRA step staging: the weight side gets s * A rows j = jb .. jb + nrows - 1 (columns k0 ..),
+// laid out like a decoded weight tile; the dY side gets U columns jb .. (rows m0 ..), chunks of 8
+// columns 0 .. nch - 1; both zero-padded (the MFMAs of the step read no further). U chunks are
+// one 16-byte buffer load each when r is a multiple of 8 and U is 16-byte aligned (rows past the
+// tile edge and chunks past r read as zero), single values otherwise.
+__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t rows_m, int jb,
+                              int nrows, int nch, uint4 *sY, uint16_t *sW) {
   const int tid = threadIdx.x;
   {
     const int row = tid >> 3, seg = tid & 7;
     const int j = jb + row;
+    if (row < nrows) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t k = k0 + seg * 32 + q * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < g.r && k < g.C) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(g.lora_b + (int64_t)j * g.C + k);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-        uint32_t o[4];
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + seg * 32 + q * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < g.r && k < g.C) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(g.lora_b + (int64_t)j * g.C + k);
+          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+          uint32_t o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g.s * bf16_lo(w[e]), g.s * bf16_hi(w[e]));
-        v = make_uint4(o[0], o[1], o[2], o[3]);
+          for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g.s * bf16_lo(w[e]), g.s * bf16_hi(w[e]));
+          v = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        *reinterpret_cast<uint4 *>(sW + wunit(row, seg * 8 + 2 * q)) = v;
       }
-      *reinterpret_cast<uint4 *>(sW + wunit(row, seg * 8 + 2 * q)) = v;
     }
+  }
+  const int c = tid & 7, row0 = tid >> 3;
+  if (c >= nch) return;
+  const int j0 = jb + c * 8;
+  if ((g.r & 7) == 0 && (reinterpret_cast<uintptr_t>(g.lora_a) & 15) == 0) {
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(g.lora_a + m0 * g.r, rows_m * g.r * 2);
+    u32x4 u[kYChunks / kThreads];
+#pragma unroll
+    for (int i = 0; i < kYChunks / kThreads; ++i) {
+      const int row = row0 + 64 * i;
+      const uint32_t off = j0 < g.r ? (uint32_t)(row * g.r + j0) * 2 : 0x80000000u;
+      u[i] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kYChunks / kThreads; ++i)
+      sY[swzd(row0 + 64 * i, c)] = make_uint4(u[i][0], u[i][1], u[i][2], u[i][3]);
+    return;
   }
 #pragma unroll 1
   for (int i = 0; i < kYChunks / kThreads; ++i) {
-    const int qd = tid + kThreads * i;
-    const int row = qd >> 3, c = qd & 7;
+    const int row = row0 + 64 * i;
     const int64_t m = m0 + row;
     uint32_t wa[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const int j0 = jb + c * 8 + e, j1 = j0 + 1;
+      const int ja = j0 + e, jc = ja + 1;
       uint32_t lo = 0, hi = 0;
       if (m < g.M) {
-        if (j0 < g.r) lo = g.lora_a[m * g.r + j0];
-        if (j1 < g.r) hi = g.lora_a[m * g.r + j1];
+        if (ja < g.r) lo = g.lora_a[m * g.r + ja];
+        if (jc < g.r) hi = g.lora_a[m * g.r + jc];
       }
       wa[e >> 1] = lo | (hi << 16);
     }
@@ -215,19 +236,16 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   auto yfrag = [&](const uint4 *sA, int ks, int mt) {
     return __builtin_bit_cast(bf16x8, sA[swzd(wm * 128 + mt * 16 + l16, ks * 4 + g16)]);
   };
-  // Plain MFMA pass over one step (used for the LoRA steps).
-  auto mma = [&](const uint4 *sA, const uint16_t *sW) {
+  // Plain MFMA pass over k-slice ks of one step (used for the LoRA steps).
+  auto mma = [&](const uint4 *sA, const uint16_t *sW, int ks) {
+    bf16x8 aw[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 aw[4];
+    for (int kt = 0; kt < 4; ++kt) aw[kt] = wfrag(sW, ks, kt);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) aw[kt] = wfrag(sW, ks, kt);
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 b = yfrag(sA, ks, mt);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 b = yfrag(sA, ks, mt);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc[kt][mt] = mfma16x16x32(aw[kt], b, acc[kt][mt]);
-      }
+      for (int kt = 0; kt < 4; ++kt) acc[kt][mt] = mfma16x16x32(aw[kt], b, acc[kt][mt]);
     }
   };
 
@@ -312,17 +330,51 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   if (s < nsteps) body(s, 0, c0, c1);
   __syncthreads();
 
+  // LoRA steps; a k-slice of 32 rows j that lies wholly past r is skipped.
   const int nlora = (g.r + kS - 1) / kS;
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
-    stage_lora_dx(g, m0, k0, j * kS, ybuf(buf), wbuf(buf));
+    const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
+    stage_lora_dx(g, m0, k0, rows_m, j * kS, 32 * nks, 4 * nks, ybuf(buf), wbuf(buf));
     __syncthreads();
-    mma(ybuf(buf), wbuf(buf));
+    mma(ybuf(buf), wbuf(buf), 0);
+    if (nks > 1) mma(ybuf(buf), wbuf(buf), 1);
     __syncthreads();
   }
 
-  // Epilogue: with the weight as the MFMA A operand, a lane holds columns k..k+3 of row m.
+  // Epilogue. With the weight as the MFMA A operand, a lane holds columns k..k+3 of row m. When
+  // rows of dX are 16-byte aligned and the column count is a multiple of 8, each wave packs its
+  // 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as whole 128-byte row
+  // pieces, 16 bytes per lane, with non-temporal stores (dX is not read again by this kernel, and
+  // streaming it out measured faster than write-back cached stores); otherwise lanes store their
+  // 8 bytes directly.
+  const bool wide = ((g.ldo | g.C) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+  if (wide) {
+    uint4 *blk = (wave >> 1) == 0 ? sY0 : (wave >> 1) == 1 ? sY1 : (wave >> 1) == 2 ? sW0 : sW1;
+    blk += (wave & 1) * (kYChunks / 2);
+    uint2 *b2 = reinterpret_cast<uint2 *>(blk);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        b2[swzd(mt * 16 + l16, 2 * kt + (g16 >> 1)) * 2 + (g16 & 1)] =
+            make_uint2(pack_bf16x2(acc[kt][mt][0], acc[kt][mt][1]),
+                       pack_bf16x2(acc[kt][mt][2], acc[kt][mt][3]));
+    __syncthreads();
+    const int c = lane & 7;
+    const int64_t k = k0 + wk * 64 + c * 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int64_t m = m0 + wm * 128 + row;
+      const uint4 v = blk[swzd(row, c)];
+      if (m < g.M && k < g.C)
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4 *>(g.out + m * g.ldo + k));
+    }
+    return;
+  }
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll

@@ -55,28 +55,59 @@ struct CStage {
   uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
 };
 
-// LoRA step staging: A-side T columns jb..jb+63, B-side s * B (rows n), both zero-padded.
-__device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int jb, uint4 *sA, uint4 *sB) {
+// LoRA step staging: A side T columns jb..jb+63, B side s * B (rows n), zero-padded; only the
+// first nch 8-column chunks are written (the MFMAs of the step read no further). Thread t stages
+// chunk t % 8 of rows t / 8 + 64 i. When r is a multiple of 8 and T and B are 16-byte aligned,
+// each chunk is one 16-byte buffer load (rows past the tile edge and chunks past r read as zero);
+// otherwise values are read one at a time.
+__device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t rows_m, int64_t rows_n,
+                           int jb, int nch, uint4 *sA, uint4 *sB) {
   const int tid = threadIdx.x;
+  const int c = tid & 7, row0 = tid >> 3;
+  if (c >= nch) return;
+  const int j0 = jb + c * 8;
+  const bool vec = (g.r & 7) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(g.lora_a) | reinterpret_cast<uintptr_t>(g.lora_b)) & 15) == 0;
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.lora_a + m0 * g.r, rows_m * g.r * 2);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.lora_b + n0 * g.r, rows_n * g.r * 2);
+    u32x4 ta[kChunks / kThreads], tb[kChunks / kThreads];
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+      const int row = row0 + 64 * i;
+      const uint32_t off = j0 < g.r ? (uint32_t)(row * g.r + j0) * 2 : 0x80000000u;
+      ta[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+      tb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+      const int row = row0 + 64 * i;
+      uint32_t wb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wb[e] = pack_bf16x2(g.s * bf16_lo(tb[i][e]), g.s * bf16_hi(tb[i][e]));
+      sA[swzf(row, c)] = make_uint4(ta[i][0], ta[i][1], ta[i][2], ta[i][3]);
+      sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    }
+    return;
+  }
 #pragma unroll 1
   for (int i = 0; i < kChunks / kThreads; ++i) {
-    const int q = tid + kThreads * i;
-    const int row = q >> 3, c = q & 7;
+    const int row = row0 + 64 * i;
     uint32_t wa[4], wb[4];
     const int64_t m = m0 + row, n = n0 + row;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const int j0 = jb + c * 8 + e, j1 = j0 + 1;
+      const int ja = j0 + e, jc = ja + 1;
       uint32_t lo = 0, hi = 0;
       if (m < g.M) {
-        if (j0 < g.r) lo = g.lora_a[m * g.r + j0];
-        if (j1 < g.r) hi = g.lora_a[m * g.r + j1];
+        if (ja < g.r) lo = g.lora_a[m * g.r + ja];
+        if (jc < g.r) hi = g.lora_a[m * g.r + jc];
       }
       wa[e >> 1] = lo | (hi << 16);
       float b0 = 0.f, b1 = 0.f;
       if (n < g.C) {
-        if (j0 < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + j0]);
-        if (j1 < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + j1]);
+        if (ja < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + ja]);
+        if (jc < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + jc]);
       }
       wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
     }
@@ -179,19 +210,16 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   auto xfrag = [&](const uint4 *sA, int ks, int mt) {
     return __builtin_bit_cast(bf16x8, sA[swzf(wm * 128 + mt * 16 + l16, ks * 4 + g16)]);
   };
-  // Plain MFMA pass over one step (used for the LoRA steps).
-  auto mma = [&](const uint4 *sA, const uint4 *sB) {
+  // Plain MFMA pass over k-slice ks of one step (used for the LoRA steps).
+  auto mma = [&](const uint4 *sA, const uint4 *sB, int ks) {
+    bf16x8 aw[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 aw[4];
+    for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(sB, ks, nt);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) aw[nt] = wfrag(sB, ks, nt);
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 b = xfrag(sA, ks, mt);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 b = xfrag(sA, ks, mt);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[nt][mt] = mfma16x16x32(aw[nt], b, acc[nt][mt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) acc[nt][mt] = mfma16x16x32(aw[nt], b, acc[nt][mt]);
     }
   };
 
@@ -282,18 +310,50 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   if (s < kblk) body(s, 0, c0, c1);
   __syncthreads();
 
-  // LoRA steps: [T | s B] as extra reduction steps of the same tile.
+  // LoRA steps: [T | s B] as extra reduction steps of the same tile; a k-slice of 32 columns
+  // that lies wholly past r is skipped.
   const int nlora = (g.r + kS - 1) / kS;
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
-    stage_lora(g, m0, n0, j * kS, xbuf(buf), wbuf(buf));
+    const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
+    stage_lora(g, m0, n0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
     __syncthreads();
-    mma(xbuf(buf), wbuf(buf));
+    mma(xbuf(buf), wbuf(buf), 0);
+    if (nks > 1) mma(xbuf(buf), wbuf(buf), 1);
     __syncthreads();
   }
 
-  // Epilogue: with the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m.
+  // Epilogue. With the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m.
+  // When rows of Y are 16-byte aligned and the column count is a multiple of 8, each wave packs
+  // its 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as whole
+  // 128-byte row pieces, 16 bytes per lane, with non-temporal stores (Y is not read again by this
+  // kernel, and streaming it out measured faster than write-back cached stores);
+  // otherwise lanes store their 8 bytes directly.
+  const bool wide = ((g.ldo | g.C) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+  if (wide) {
+    uint4 *blk = (wave >> 1) == 0 ? sX0 : (wave >> 1) == 1 ? sX1 : (wave >> 1) == 2 ? sW0 : sW1;
+    blk += (wave & 1) * (kChunks / 2);
+    uint2 *b2 = reinterpret_cast<uint2 *>(blk);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        b2[swzf(mt * 16 + l16, 2 * nt + (g16 >> 1)) * 2 + (g16 & 1)] =
+            make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                       pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+    __syncthreads();
+    const int c = lane & 7;
+    const int64_t n = n0 + wn * 64 + c * 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int64_t m = m0 + wm * 128 + row;
+      const uint4 v = blk[swzf(row, c)];
+      if (m < g.M && n < g.C) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
