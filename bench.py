@@ -323,6 +323,7 @@ def run_context(L):
         out["unfused_fwd"] = {"what": "nf4_dequantize + vendor GEMM + LoRA GEMMs (forward)",
                               "ms": round(ms_u, 4),
                               "TFLOP/s": round(w.fwd_flops() / (ms_u * 1e-3) / 1e12, 2)}
+        out["mfma_loop"] = run_mfma_loop(Wd, L.X)
         del Wd, Wt, At, Bt
     else:
         n = 1 << 30
@@ -334,6 +335,37 @@ def run_context(L):
         del src, dst
     torch.cuda.empty_cache()
     return out
+
+
+def run_mfma_loop(a, b, workgroups=2048, iters=2048):
+    """The dense bf16 MFMA rate this chip sustains: libnf4probe's loop of back-to-back MFMA
+    16x16x32 on register operands (values taken from the dequantised weight and from X, since the
+    rate under the power limit depends on the data), 8 workgroups of 4 waves per CU."""
+    import ctypes
+    import torch
+    from nf4_dequant_gemm_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError(f"{PROBE_LIB} is not built; run python -m nf4_dequant_gemm_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.nf4probe_mfma_loop.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    lib.nf4probe_mfma_loop.restype = ctypes.c_int
+    lib.nf4probe_mfma_loop_flops.argtypes = [i64, i32]
+    lib.nf4probe_mfma_loop_flops.restype = ctypes.c_double
+    nbytes = min(a.numel() * a.element_size(), b.numel() * b.element_size())
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device=a.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.nf4probe_mfma_loop(a.data_ptr(), b.data_ptr(), nbytes, workgroups, iters,
+                                    out.data_ptr(), st)
+        if rc != 0:
+            raise RuntimeError(f"nf4probe_mfma_loop returned {rc}")
+    ms = _median_ms(launch, 5)
+    flops = lib.nf4probe_mfma_loop_flops(workgroups, iters)
+    return {"what": "bf16 MFMA 16x16x32 loop on register operands (values of deq(W) and X), "
+                    f"{workgroups} workgroups x 4 waves x {iters} x 8 MFMAs",
+            "ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
 def copy_calibration():
@@ -408,6 +440,9 @@ def main():
         ref = context.get("vendor_bf16_gemm", {}).get("TFLOP/s") or context.get("device_copy", {}).get("GB/s")
         if ref:
             roof["frac_of_measured_achievable"] = round(roof["achieved"] / ref, 4)
+        loop = context.get("mfma_loop", {}).get("TFLOP/s")
+        if loop:
+            roof["frac_of_mfma_loop"] = round(roof["achieved"] / loop, 4)
         out["context"] = context
     if not args.no_weight_stream and w.name != "decode":
         out["weight_stream"] = run_weight_stream(dev, 20, 5)

@@ -3,7 +3,8 @@
     python -m nf4_dequant_gemm_amd.build
 
 Sources are compiled in parallel into _build/ and linked into
-nf4_dequant_gemm_amd/libnf4qlora.so. Every HIP source is compiled with the packed-fp32
+nf4_dequant_gemm_amd/libnf4qlora.so; the measurement aid csrc/probe.hip (a matrix-core loop that
+bench.py times as the measured-achievable MFMA rate) is linked on its own into libnf4probe.so. Every HIP source is compiled with the packed-fp32
 instructions disabled and without fast-math (float division stays correctly rounded, which the
 bit-exact quantiser relies on).
 """
@@ -20,9 +21,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnf4qlora.so")
+PROBE_LIB = os.path.join(PKG, "libnf4probe.so")
 ARCH = os.environ.get("NF4Q_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "quant.hip", "fwd.hip", "decode.hip", "decode16.hip", "dx.hip", "lora.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -45,18 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

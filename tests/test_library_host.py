@@ -155,3 +155,25 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(m, "_LIB_PATH", "/nonexistent/libnf4qlora.so")
     with pytest.raises(ImportError):
         m.library()
+
+
+def test_probe_library_exports_its_header():
+    """libnf4probe.so (the matrix-core loop bench.py times) exports what include/nf4probe.h
+    declares; its argument checks run on the host and its flop count is closed-form."""
+    from nf4_dequant_gemm_amd.build import PROBE_LIB
+    hdr = os.path.join(os.path.dirname(HEADER), "nf4probe.h")
+    src = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+    assert names == {"nf4probe_mfma_loop", "nf4probe_mfma_loop_flops"}
+    lib = ctypes.CDLL(PROBE_LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.nf4probe_mfma_loop.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    lib.nf4probe_mfma_loop_flops.argtypes = [i64, i32]
+    lib.nf4probe_mfma_loop_flops.restype = ctypes.c_double
+    assert lib.nf4probe_mfma_loop(None, None, 1024, 8, 8, None, None) == -1
+    assert lib.nf4probe_mfma_loop(ctypes.c_void_p(64), ctypes.c_void_p(64), 8, 8, 8, ctypes.c_void_p(64), None) == -1
+    assert lib.nf4probe_mfma_loop(ctypes.c_void_p(64), ctypes.c_void_p(64), 64, 8, 0, ctypes.c_void_p(64), None) == -1
+    # 4 waves x iters x 8 MFMAs x 16*16*32 multiply-adds per workgroup
+    assert lib.nf4probe_mfma_loop_flops(3, 5) == 3 * 4 * 5 * 8 * 16 * 16 * 32 * 2
