@@ -13,7 +13,7 @@
 // the decoded tile transposed: the tile is stored in LDS as it is decoded (64 rows n x 256
 // columns k, 16-byte stores) and read with the gfx950 transposing LDS load ds_read_b64_tr_b16,
 // which hands each lane 4 consecutive rows of one column -- the operand layout with n as the
-// reduction index. Threads 8r .. 8r+7 decode weight row r of the step, 32 columns each, through
+// reduction index. Eight threads decode each weight row of the step, 32 columns each, through
 // a register table of bf16(level_i * a) (byte permutes, no LDS lookups).
 //
 // Pipeline per step s: the dY tile of step s+1 goes straight to LDS buffer (s+1) & 1 by DMA
@@ -24,8 +24,12 @@
 //
 // LDS: the dY tile has rows of 64 bf16 = 8 chunks of 16 bytes, chunk c of row r at slot
 // c ^ ((r >> 1) & 7). The weight tile has rows of 256 bf16 = 64 units of 8 bytes, unit u of row
-// r at u ^ (4 * ((r + 4 (r / 8)) % 8)): the XOR keeps 16-byte pairs together for the stores and
-// puts the 32 lanes of every transposing read on distinct banks.
+// r at u ^ (4 ((r + 4 (r / 8)) % 8) + 2 ((r / 4) % 2)). Measured on gfx950, a transposing 8-byte
+// read serves 32 lanes per 256-byte bank window and a 16-byte write 8 lanes per 128 bytes. The
+// multiple of 4 units puts the 8 rows x 32 bytes of every transposing read on distinct banks; the
+// 2-unit term (which only permutes units inside a 32-byte group, so reads keep their banks) and
+// the decode ownership (the 8 lanes of a write pass take 8 different rows) put every decode write
+// on distinct banks. (Eight lanes of one row, the plain mapping, conflicted 4 ways.)
 #include "common.h"
 #include "launch.h"
 
@@ -42,8 +46,12 @@ constexpr int kWElems = kS * kT;        // weight tile: 64 x 256 bf16
 __device__ __forceinline__ int swzd(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 // bf16 index of 8-byte unit u of weight-tile row r
 __device__ __forceinline__ int wunit(int r, int u) {
-  return r * kT + ((u ^ (4 * ((r + 4 * (r >> 3)) & 7))) << 2);
+  return r * kT + ((u ^ (4 * ((r + 4 * (r >> 3)) & 7) + 2 * ((r >> 2) & 1))) << 2);
 }
+// Weight-tile ownership of thread t: row 8 (t / 64) + t % 8, 32-column segment (t / 8) % 8, so
+// that the 8 lanes of a write pass hold 8 different rows.
+__device__ __forceinline__ int own_row(int t) { return ((t >> 6) << 3) | (t & 7); }
+__device__ __forceinline__ int own_seg(int t) { return (t >> 3) & 7; }
 
 __device__ __forceinline__ int tile_remap(int hw, int tiles) {
   const int per = tiles >> 3, rem = tiles & 7, x = hw & 7;
@@ -70,7 +78,7 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t
                               int nrows, int nch, uint4 *sY, uint16_t *sW) {
   const int tid = threadIdx.x;
   {
-    const int row = tid >> 3, seg = tid & 7;
+    const int row = own_row(tid), seg = own_seg(tid);
     const int j = jb + row;
     if (row < nrows) {
 #pragma unroll
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
     yoff[i] = (uint32_t)(row * N * 2 + c * 16);
   }
   // Decode ownership: weight row n = 64 s + wr of step s, columns k0 + 32 seg .. + 31.
-  const int wr = tid >> 3, seg = tid & 7;
+  const int wr = own_row(tid), seg = own_seg(tid);
   const int64_t kcol = k0 + seg * 32;
   const bool kvalid = kcol < K;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + (kvalid ? kcol / 2 : 0));

@@ -26,9 +26,12 @@
 //     groups before theirs,
 //   * between MFMA issues, the W half-rows of step s+1 (codes loaded one step earlier) are decoded
 //     and written to LDS buffer (s+1) & 1.
-// LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot
-// c ^ ((r >> 1) & 7), which keeps 16 consecutive rows on distinct slots of the 256-byte bank
-// window that a 16-byte LDS access covers per pass on gfx950.
+// LDS rows hold 64 bf16 as 8 chunks of 16 bytes; chunk c of row r sits at slot c ^ x(r) with
+// x(r) = ((r >> 1) ^ 2 (r & 1)) & 7. Measured on gfx950, a 16-byte LDS read serves 16 lanes per
+// 256-byte bank window and a 16-byte write 8 lanes per 128 bytes: x keeps the 16 consecutive rows
+// of a fragment read on distinct slots of the 256-byte window, and the 4 rows x 2 chunks of a
+// decode write on distinct slots of the 128-byte window (the plain (r >> 1) & 7 left those writes
+// 2-way conflicted).
 #include "common.h"
 #include "launch.h"
 
@@ -41,7 +44,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kChunks = kT * kS / 8;
 
-__device__ __forceinline__ int swzf(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+__device__ __forceinline__ int rowx(int row) { return ((row >> 1) ^ ((row & 1) << 1)) & 7; }
+__device__ __forceinline__ int swzf(int row, int c) { return row * 8 + (c ^ rowx(row)); }
 
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of tiles so
 // the n-tiles of one m-block (which share X) run on one XCD and share its L2.
@@ -149,12 +153,12 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
 
   // X DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (4 w + i) .. +7;
   // lane L writes physical chunk L % 8 of row 8 (4 w + i) + L / 8, i.e. logical chunk
-  // (L % 8) ^ ((row >> 1) & 7) (the same swizzle as swzf).
+  // (L % 8) ^ rowx(row) (the same swizzle as swzf).
   uint32_t xoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 8 * (4 * wave + i) + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int c = (lane & 7) ^ rowx(row);
     xoff[i] = (uint32_t)(row * K * 2 + c * 16);
   }
   // Decode ownership: weight row wr of the tile, elements 32 wh .. 32 wh + 31 of each step.
