@@ -112,20 +112,24 @@ __device__ __forceinline__ void decode8(const RowTable &t, uint32_t d, uint32_t 
 }
 
 // decode8 split into five pieces of about six VALU instructions each, so the decode of a chunk
-// can be spread between MFMA issues.
+// can be spread between MFMA issues. The select masks come from byte permutes of (mhi, mlo) by
+// selector bytes 0 / 4 (bit 3 of the code clear / set): (0xFFFFFFFF, 0) gives 0xFF where the code
+// is >= 8 (the table's upper half sits in L[2..3], H[2..3]); (0, 0xFFFFFFFF) gives the complement,
+// for a table whose halves are stored the other way round.
 struct Dec8 {
   uint32_t d, se7, so7, me, mo, Le, He, Lo, Ho, E01, E23;
 };
 
-__device__ __forceinline__ void dec_piece(const RowTable &t, Dec8 &x, int piece, uint32_t out[4]) {
+__device__ __forceinline__ void dec_piece(const RowTable &t, Dec8 &x, int piece, uint32_t out[4],
+                                          uint32_t mhi, uint32_t mlo) {
   switch (piece) {
     case 0:
       x.se7 = (x.d >> 4) & 0x07070707u;
       x.so7 = x.d & 0x07070707u;
-      x.me = perm(0u, 0u, ((x.d >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
+      x.me = perm(mhi, mlo, (x.d >> 5) & 0x04040404u);
       break;
     case 1:
-      x.mo = perm(0u, 0u, ((x.d >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+      x.mo = perm(mhi, mlo, (x.d >> 1) & 0x04040404u);
       x.Le = lookup4(t.L, x.se7, x.me);
       break;
     case 2:
@@ -145,6 +149,15 @@ __device__ __forceinline__ void dec_piece(const RowTable &t, Dec8 &x, int piece,
       out[3] = perm(O23, x.E23, 0x07060302u);
     }
   }
+}
+
+// Value of v in lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+// Value of v in lane l ^ 8 within each row of 16 lanes (DPP row rotation by 8).
+__device__ __forceinline__ uint32_t swap_lane_octets(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {

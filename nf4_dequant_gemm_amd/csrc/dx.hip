@@ -139,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   // the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sY0[kYChunks], sY1[kYChunks];
   __shared__ uint4 sW0[kWElems / 8], sW1[kWElems / 8];
+  __shared__ __attribute__((aligned(16))) float sLv[16];
   auto ybuf = [&](int P) { return P ? sY1 : sY0; };
   auto wbuf = [&](int P) { return reinterpret_cast<uint16_t *>(P ? sW1 : sW0); };
 
@@ -179,6 +180,16 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   }
   // Decode ownership: weight row n = 64 s + wr of step s, columns k0 + 32 seg .. + 31.
   const int wr = own_row(tid), seg = own_seg(tid);
+  // In the pipelined steps the two threads of a 64-column block (segments 2b and 2b + 1, lanes l
+  // and l ^ 8) split its table: the thread with segment parity h builds entries 8 h .. 8 h + 7
+  // (levels lvh) and takes the other half from the partner lane; the select masks of the decode
+  // are complemented for h = 1, whose own half is the upper one.
+  // The levels are read from LDS four at a time when the table is built (eight per-lane
+  // registers held across the loop would not fit beside the accumulators).
+  const int sh = seg & 1;
+  const uint32_t mhi = sh ? 0u : 0xFFFFFFFFu, mlo = sh ? 0xFFFFFFFFu : 0u;
+  if (tid < 16) sLv[tid] = g.t.level[tid];
+  const f32x4 *lvq = reinterpret_cast<const f32x4 *>(sLv) + 2 * sh;
   const int64_t kcol = k0 + seg * 32;
   const bool kvalid = kcol < K;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + (kvalid ? kcol / 2 : 0));
@@ -275,7 +286,6 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
     yb[0] = yfrag(Y, 0, 0);
 
     const float a = absmax_of(cn);
-    uint32_t pk[8];
     RowTable t;
     Dec8 dx;
 #pragma unroll
@@ -294,22 +304,31 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
       // decode of step s+1: table in groups 0..3, then word j = (grp - 4) / 3 in pieces over
       // three groups (pieces 0-1, 2-3, 4 + store)
       if (grp < 4) {
-        pk[2 * grp] = pack_bf16x2(g.t.level[4 * grp] * a, g.t.level[4 * grp + 1] * a);
-        pk[2 * grp + 1] = pack_bf16x2(g.t.level[4 * grp + 2] * a, g.t.level[4 * grp + 3] * a);
-        t.L[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x06040200u);
-        t.H[grp] = perm(pk[2 * grp + 1], pk[2 * grp], 0x07050301u);
+        // this thread's half of the table in L[0..1], H[0..1] (groups 0, 1); the partner lane's
+        // half by DPP (groups 1, 2)
+        if (grp < 2) {
+          const f32x4 lv = lvq[grp];
+          const uint32_t p0 = pack_bf16x2(lv[0] * a, lv[1] * a);
+          const uint32_t p1 = pack_bf16x2(lv[2] * a, lv[3] * a);
+          t.L[grp] = perm(p1, p0, 0x06040200u);
+          t.H[grp] = perm(p1, p0, 0x07050301u);
+        }
+        if (grp == 1 || grp == 2) {
+          t.L[grp + 1] = swap_lane_octets(t.L[grp - 1]);
+          t.H[grp + 1] = swap_lane_octets(t.H[grp - 1]);
+        }
       } else {
         const int j = (grp - 4) / 3, ph = (grp - 4) % 3;
         uint32_t o[4];
         if (ph == 0) {
           dx.d = word(cn, j);
-          dec_piece(t, dx, 0, o);
-          dec_piece(t, dx, 1, o);
+          dec_piece(t, dx, 0, o, mhi, mlo);
+          dec_piece(t, dx, 1, o, mhi, mlo);
         } else if (ph == 1) {
-          dec_piece(t, dx, 2, o);
-          dec_piece(t, dx, 3, o);
+          dec_piece(t, dx, 2, o, mhi, mlo);
+          dec_piece(t, dx, 3, o, mhi, mlo);
         } else {
-          dec_piece(t, dx, 4, o);
+          dec_piece(t, dx, 4, o, mhi, mlo);
           wstore(Wn, j, o);
         }
       }

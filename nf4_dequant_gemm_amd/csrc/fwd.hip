@@ -163,6 +163,13 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   }
   // Decode ownership: weight row wr of the tile, elements 32 wh .. 32 wh + 31 of each step.
   const int wr = tid >> 1, wh = tid & 1;
+  // In the pipelined steps the two threads of a row split its table: thread wh builds entries
+  // 8 wh .. 8 wh + 7 (levels lvh) and takes the other half from the partner lane; the select masks
+  // of the decode are complemented for wh = 1, whose own half is the upper one.
+  float lvh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lvh[i] = wh ? g.t.level[8 + i] : g.t.level[i];
+  const uint32_t mhi = wh ? 0u : 0xFFFFFFFFu, mlo = wh ? 0xFFFFFFFFu : 0u;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + wh * 16);
   const uint32_t qoff = (uint32_t)(wr * kblk);
   const int64_t sbase = (n0 + wr) * kblk;
@@ -249,15 +256,20 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
     xb[0] = xfrag(A, 0, 0);
     xb[1] = xfrag(A, 0, 1);
 
+    // this thread's half of the table in L[0..1], H[0..1]; the partner lane's half by DPP
     const float a = absmax_of(cn);
-    uint32_t pk[8];
     RowTable t;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pk[2 * q] = pack_bf16x2(g.t.level[4 * q] * a, g.t.level[4 * q + 1] * a);
-      pk[2 * q + 1] = pack_bf16x2(g.t.level[4 * q + 2] * a, g.t.level[4 * q + 3] * a);
-      t.L[q] = perm(pk[2 * q + 1], pk[2 * q], 0x06040200u);
-      t.H[q] = perm(pk[2 * q + 1], pk[2 * q], 0x07050301u);
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t p0 = pack_bf16x2(lvh[4 * q] * a, lvh[4 * q + 1] * a);
+      const uint32_t p1 = pack_bf16x2(lvh[4 * q + 2] * a, lvh[4 * q + 3] * a);
+      t.L[q] = perm(p1, p0, 0x06040200u);
+      t.H[q] = perm(p1, p0, 0x07050301u);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      t.L[2 + q] = swap_adjacent_lanes(t.L[q]);
+      t.H[2 + q] = swap_adjacent_lanes(t.H[q]);
     }
     __builtin_amdgcn_sched_barrier(0);
     Dec8 dx;
@@ -279,13 +291,13 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
         uint32_t o[4];
         if (ph == 0) {
           dx.d = word(cn, j);
-          dec_piece(t, dx, 0, o);
-          dec_piece(t, dx, 1, o);
+          dec_piece(t, dx, 0, o, mhi, mlo);
+          dec_piece(t, dx, 1, o, mhi, mlo);
         } else if (ph == 1) {
-          dec_piece(t, dx, 2, o);
-          dec_piece(t, dx, 3, o);
+          dec_piece(t, dx, 2, o, mhi, mlo);
+          dec_piece(t, dx, 3, o, mhi, mlo);
         } else {
-          dec_piece(t, dx, 4, o);
+          dec_piece(t, dx, 4, o, mhi, mlo);
           Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
         }
       }
