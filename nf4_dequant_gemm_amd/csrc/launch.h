@@ -48,9 +48,9 @@ hipError_t launch_decode16_fwd_tpart(const GemmArgs &g, const float *tpart, int 
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).
-// With splits > 1 the partial sums go to part (float [M][r][splits], the splits of one output
-// contiguous) and a second launch adds them in split order into out; with out == NULL only the
-// partials are written (their consumer adds them in the same order).
+// With splits > 1 the partial sums go to part and are added in split order: by a second launch
+// into out, from split-major partials (float [splits][M][r]); or, with out == NULL, by their
+// consumer, from partials with the splits of one output contiguous (float [M][r][splits]).
 hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t ldp,
                           int64_t M, int64_t L, int r, int splits, float *part, uint16_t *out,
                           hipStream_t st);

@@ -26,7 +26,7 @@ template <int TN>
 __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict__ in, int64_t ldin,
                                                       const uint16_t *__restrict__ p, int64_t ldp,
                                                       int64_t M, int64_t L, int r, int64_t lsplit,
-                                                      float *__restrict__ part,
+                                                      float *__restrict__ part, int smajor,
                                                       uint16_t *__restrict__ out) {
   constexpr int PCH = TN * 16 * 8;                 // p-tile chunks per step
   constexpr int PPT = (PCH + 255) / 256;           // p-tile chunks per thread
@@ -116,7 +116,9 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
       const int64_t row = mbase + wave * 16 + 4 * (lane >> 4) + v;
       const int j = t * 16 + (lane & 15);
       if (row < M && j < r) {
-        if (part)   // split-contiguous: the sum over splits reads one contiguous run
+        if (part && smajor)   // [split][M][r]: a workgroup's partials form one contiguous block
+          part[((int64_t)split * M + row) * r + j] = acc[t][v];
+        else if (part)        // [M][r][split]: the splits of one output form one contiguous run
           part[((int64_t)row * r + j) * gridDim.y + split] = acc[t][v];
         else
           out[row * r + j] = (uint16_t)(pack_bf16x2(acc[t][v], 0.f) & 0xFFFFu);
@@ -128,18 +130,19 @@ __global__ void rowproj_reduce_kernel(const float *__restrict__ part, int64_t n,
                                       uint16_t *__restrict__ out) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    // sequential sum over the splits (fixed order), its loads issued eight at a time
-    const float *pi = part + i * splits;
+    // sequential sum over the splits (fixed order) of the split-major partials, its loads issued
+    // eight at a time
+    const float *pi = part + i;
     float a = 0.f;
     int s = 0;
     for (; s + 8 <= splits; s += 8) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = pi[s + j];
+      for (int j = 0; j < 8; ++j) v[j] = pi[(int64_t)(s + j) * n];
 #pragma unroll
       for (int j = 0; j < 8; ++j) a += v[j];
     }
-    for (; s < splits; ++s) a += pi[s];
+    for (; s < splits; ++s) a += pi[(int64_t)s * n];
     out[i] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFFu);
   }
 }
@@ -160,10 +163,11 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
   lsplit = (lsplit + 63) / 64 * 64;
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)splits);
   float *pp = splits > 1 ? part : nullptr;
+  const int smajor = out != nullptr;   // a reduction launch follows: split-major partials
   const int tn = (r + 15) / 16;
   switch (tn) {
 #define RP_CASE(T) \
-  case T: rowproj_kernel<T><<<grid, dim3(256), 0, st>>>(in, ldin, p, ldp, M, L, r, lsplit, pp, out); break;
+  case T: rowproj_kernel<T><<<grid, dim3(256), 0, st>>>(in, ldin, p, ldp, M, L, r, lsplit, pp, smajor, out); break;
     RP_CASE(1) RP_CASE(2) RP_CASE(3) RP_CASE(4) RP_CASE(5) RP_CASE(6) RP_CASE(7) RP_CASE(8)
 #undef RP_CASE
     default: return hipErrorInvalidValue;
