@@ -42,6 +42,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kYChunks = kT * kS / 8;   // dY tile: 2048 chunks of 16 bytes
 constexpr int kWElems = kS * kT;        // weight tile: 64 x 256 bf16
+constexpr int kGroupM = 4;              // row blocks per tile group (see the tile order)
 
 __device__ __forceinline__ int swzd(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 // bf16 index of 8-byte unit u of weight-tile row r
@@ -149,9 +150,16 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   const int wm = wave >> 2, wk = wave & 3;
   const int g16 = lane >> 4, l16 = lane & 15;
   const int tiles_k = (int)((g.C + kT - 1) / kT);
+  // Tiles in groups of kGroupM row blocks: consecutive logical tiles walk the row blocks of a group
+  // first, so the 32 workgroups an XCD runs at once cover 4 row blocks x 8 column tiles and
+  // share 4 dY row blocks and 8 weight column tiles in its L2 (one row block x 32 column tiles
+  // re-fetched the whole weight from beyond L2 once per row block).
   const int logical = tile_remap(blockIdx.x, gridDim.x);
-  const int64_t m0 = (int64_t)(logical / tiles_k) * kT;
-  const int64_t k0 = (int64_t)(logical % tiles_k) * kT;
+  const int tiles_m = (int)((g.M + kT - 1) / kT);
+  const int gsz = kGroupM * tiles_k, grp0 = logical / gsz, gin = logical % gsz;
+  const int gm = tiles_m - grp0 * kGroupM < kGroupM ? tiles_m - grp0 * kGroupM : kGroupM;
+  const int64_t m0 = (int64_t)(grp0 * kGroupM + gin % gm) * kT;
+  const int64_t k0 = (int64_t)(gin / gm) * kT;
   const int64_t K = g.w.k, N = g.w.n;
   const int64_t rows_m = (g.M - m0 < kT) ? g.M - m0 : kT;
   const int kblk = (int)(K / kS);
