@@ -240,6 +240,14 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       if (m < g.M) {
         const float *pp = g.tpart + ((int64_t)m * r + j) * g.tsplits;
         int q = 0;
+        // loads issued 32 (then 8) at a time, added in split order
+        for (; q + 32 <= g.tsplits; q += 32) {
+          float v[32];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) v[e] = pp[q + e];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) a += v[e];
+        }
         for (; q + 8 <= g.tsplits; q += 8) {
           float v[8];
 #pragma unroll

@@ -126,6 +126,75 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
     }
 }
 
+// The same product for at most 16 rows (decode shapes), where the reduction is short and a
+// workgroup has little to stream: latency, not bandwidth, sets the time. Each wave takes 32-column
+// slices 4 u + wave of its split and issues all of its loads (straight into MFMA operand registers,
+// 16 bytes per lane) before its MFMAs: one memory round trip per workgroup. The four waves' sums
+// are added in wave order in LDS. Rows past M and ranks past r read as zero (buffer bounds).
+template <int TN>
+__global__ __launch_bounds__(256) void rowproj16_kernel(const uint16_t *__restrict__ in, int64_t ldin,
+                                                        const uint16_t *__restrict__ p, int64_t ldp,
+                                                        int64_t M, int64_t L, int r, int64_t lsplit,
+                                                        float *__restrict__ part, int smajor,
+                                                        uint16_t *__restrict__ out) {
+  __shared__ f32x4 red[4][TN][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int64_t lb = split * lsplit;
+  const int64_t le = (lb + lsplit < L) ? lb + lsplit : L;
+  const __amdgpu_buffer_rsrc_t rI = make_rsrc(in, M * ldin * 2);
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(p, (int64_t)r * ldp * 2);
+  const int nl = lane & 15, kg = lane >> 4;
+  f32x4 acc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int64_t k0 = lb + 32 * wave; k0 < le; k0 += 256) {
+    // two slices per pass: k0 and k0 + 128 (the second may lie past the split: reads as zero)
+    const int64_t k1 = k0 + 128;
+    const uint32_t oob = 0x80000000u;
+    const uint32_t xo0 = (uint32_t)((nl * ldin + k0 + 8 * kg) * 2);
+    const uint32_t xo1 = k1 < le ? (uint32_t)((nl * ldin + k1 + 8 * kg) * 2) : oob;
+    const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rI, xo0, 0, 0);
+    const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rI, xo1, 0, 0);
+    u32x4 a0[TN], a1[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int64_t j = 16 * t + nl;
+      a0[t] = __builtin_amdgcn_raw_buffer_load_b128(rP, (uint32_t)((j * ldp + k0 + 8 * kg) * 2), 0, 0);
+      a1[t] = __builtin_amdgcn_raw_buffer_load_b128(
+          rP, k1 < le ? (uint32_t)((j * ldp + k1 + 8 * kg) * 2) : oob, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      acc[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, x0), __builtin_bit_cast(bf16x8, a0[t]), acc[t]);
+      acc[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, x1), __builtin_bit_cast(bf16x8, a1[t]), acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TN; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  // D[m][j]: lane l holds column j = l % 16 and rows 4 (l / 16) + v; wave w finishes tiles w, w + 4
+  for (int t = wave; t < TN; t += 4) {
+    f32x4 v4 = red[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v4 += red[w][t][lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = 4 * kg + v;
+      const int j = 16 * t + nl;
+      if (row < M && j < r) {
+        if (part && smajor)
+          part[((int64_t)split * M + row) * r + j] = v4[v];
+        else if (part)
+          part[((int64_t)row * r + j) * gridDim.x + split] = v4[v];
+        else
+          out[row * r + j] = (uint16_t)(pack_bf16x2(v4[v], 0.f) & 0xFFFFu);
+      }
+    }
+  }
+}
+
 __global__ void rowproj_reduce_kernel(const float *__restrict__ part, int64_t n, int splits,
                                       uint16_t *__restrict__ out) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -165,12 +234,22 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
   float *pp = splits > 1 ? part : nullptr;
   const int smajor = out != nullptr;   // a reduction launch follows: split-major partials
   const int tn = (r + 15) / 16;
-  switch (tn) {
+  if (M <= 16) {
+    switch (tn) {
+#define RP_CASE(T) \
+  case T: rowproj16_kernel<T><<<dim3((unsigned)splits), dim3(256), 0, st>>>(in, ldin, p, ldp, M, L, r, lsplit, pp, smajor, out); break;
+      RP_CASE(1) RP_CASE(2) RP_CASE(3) RP_CASE(4) RP_CASE(5) RP_CASE(6) RP_CASE(7) RP_CASE(8)
+#undef RP_CASE
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (tn) {
 #define RP_CASE(T) \
   case T: rowproj_kernel<T><<<grid, dim3(256), 0, st>>>(in, ldin, p, ldp, M, L, r, lsplit, pp, smajor, out); break;
-    RP_CASE(1) RP_CASE(2) RP_CASE(3) RP_CASE(4) RP_CASE(5) RP_CASE(6) RP_CASE(7) RP_CASE(8)
+      RP_CASE(1) RP_CASE(2) RP_CASE(3) RP_CASE(4) RP_CASE(5) RP_CASE(6) RP_CASE(7) RP_CASE(8)
 #undef RP_CASE
-    default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || !out) return e;
