@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
 // workgroup has little to stream: latency, not bandwidth, sets the time. Each wave takes 32-column
 // slices 4 u + wave of its split and issues all of its loads (straight into MFMA operand registers,
 // 16 bytes per lane) before its MFMAs: one memory round trip per workgroup. The four waves' sums
-// are added in wave order in LDS. Rows past M and ranks past r read as zero (buffer bounds).
+// are added in wave order in LDS. Rows past M and ranks past r read as zero (buffer bounds);
+// requires L % 8 == 0 (every reduction length here: K % 64 == 0, N % 8 == 0).
 template <int TN>
 __global__ __launch_bounds__(256) void rowproj16_kernel(const uint16_t *__restrict__ in, int64_t ldin,
                                                         const uint16_t *__restrict__ p, int64_t ldp,
@@ -150,20 +151,21 @@ __global__ __launch_bounds__(256) void rowproj16_kernel(const uint16_t *__restri
   for (int t = 0; t < TN; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int64_t k0 = lb + 32 * wave; k0 < le; k0 += 256) {
-    // two slices per pass: k0 and k0 + 128 (the second may lie past the split: reads as zero)
-    const int64_t k1 = k0 + 128;
+    // two slices per pass: k0 and k0 + 128. A lane reads 8 columns from c = k + 8 kg; L (and so
+    // le) is a multiple of 8, so such a chunk lies wholly inside or wholly past the split, and a
+    // chunk past it (which would otherwise read the next row's values) reads as zero.
+    const int64_t c0 = k0 + 8 * kg, c1 = k0 + 128 + 8 * kg;
     const uint32_t oob = 0x80000000u;
-    const uint32_t xo0 = (uint32_t)((nl * ldin + k0 + 8 * kg) * 2);
-    const uint32_t xo1 = k1 < le ? (uint32_t)((nl * ldin + k1 + 8 * kg) * 2) : oob;
+    const uint32_t xo0 = c0 < le ? (uint32_t)((nl * ldin + c0) * 2) : oob;
+    const uint32_t xo1 = c1 < le ? (uint32_t)((nl * ldin + c1) * 2) : oob;
     const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rI, xo0, 0, 0);
     const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rI, xo1, 0, 0);
     u32x4 a0[TN], a1[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int64_t j = 16 * t + nl;
-      a0[t] = __builtin_amdgcn_raw_buffer_load_b128(rP, (uint32_t)((j * ldp + k0 + 8 * kg) * 2), 0, 0);
-      a1[t] = __builtin_amdgcn_raw_buffer_load_b128(
-          rP, k1 < le ? (uint32_t)((j * ldp + k1 + 8 * kg) * 2) : oob, 0, 0);
+      a0[t] = __builtin_amdgcn_raw_buffer_load_b128(rP, c0 < le ? (uint32_t)((j * ldp + c0) * 2) : oob, 0, 0);
+      a1[t] = __builtin_amdgcn_raw_buffer_load_b128(rP, c1 < le ? (uint32_t)((j * ldp + c1) * 2) : oob, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {

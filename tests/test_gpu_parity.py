@@ -113,6 +113,11 @@ LAYER_CASES = [
     (33, 128, 16, 128, 0, 0.25),
     (513, 640, 776, 0, 256, 1.0),
     (200, 1024, 96, 64, 256, 2.0),
+    # at most 16 rows (the short-reduction row projection) with N not a multiple of 32, so the
+    # U = dY B reduction ends inside a 32-column slice
+    (12, 256, 200, 16, 256, 1.5),
+    (16, 320, 72, 8, 0, -0.5),
+    (3, 128, 40, 24, 256, 2.0),
 ]
 
 
