@@ -378,14 +378,12 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Epilogue. With the weight as the MFMA A operand, a lane holds columns k..k+3 of row m. When
-  // rows of dX are 16-byte aligned and the column count is a multiple of 8, each wave packs its
-  // 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as whole 128-byte row
-  // pieces, 16 bytes per lane, with non-temporal stores (dX is not read again by this kernel, and
-  // streaming it out measured faster than write-back cached stores); otherwise lanes store their
-  // 8 bytes directly.
-  const bool wide = ((g.ldo | g.C) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
-  if (wide) {
+  // Epilogue. With the weight as the MFMA A operand, a lane holds columns k..k+3 of row m. Each
+  // wave packs its 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as whole
+  // 128-byte row pieces, 16 bytes per lane, with non-temporal stores (dX is not read again by this
+  // kernel, and streaming it out measured faster than write-back cached stores). Rows of dX are
+  // 16-byte aligned and the column count is a multiple of 8 (checked at launch).
+  {
     uint4 *blk = (wave >> 1) == 0 ? sY0 : (wave >> 1) == 1 ? sY1 : (wave >> 1) == 2 ? sW0 : sW1;
     blk += (wave & 1) * (kYChunks / 2);
     uint2 *b2 = reinterpret_cast<uint2 *>(blk);
@@ -408,25 +406,14 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<u32x4 *>(g.out + m * g.ldo + k));
     }
-    return;
   }
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int64_t m = m0 + wm * 128 + mt * 16 + l16;
-      const int64_t k = k0 + wk * 64 + kt * 16 + 4 * g16;
-      if (m < g.M && k < g.C) {
-        const uint2 v = make_uint2(pack_bf16x2(acc[kt][mt][0], acc[kt][mt][1]),
-                                   pack_bf16x2(acc[kt][mt][2], acc[kt][mt][3]));
-        *reinterpret_cast<uint2 *>(g.out + m * g.ldo + k) = v;
-      }
-    }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st) {
+  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0)
+    return hipErrorInvalidValue;   // the epilogue writes 16-byte pieces of 8 columns
   const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
   if (g.w.dq)
     dx_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);

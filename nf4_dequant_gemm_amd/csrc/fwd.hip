@@ -341,13 +341,12 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   }
 
   // Epilogue. With the weight tile as the MFMA A operand, a lane holds columns n..n+3 of row m.
-  // When rows of Y are 16-byte aligned and the column count is a multiple of 8, each wave packs
-  // its 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as whole
-  // 128-byte row pieces, 16 bytes per lane, with non-temporal stores (Y is not read again by this
-  // kernel, and streaming it out measured faster than write-back cached stores);
-  // otherwise lanes store their 8 bytes directly.
-  const bool wide = ((g.ldo | g.C) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
-  if (wide) {
+  // Each wave packs its 128 x 64 block to bf16 in 16 KB of the (now idle) LDS and writes it out as
+  // whole 128-byte row pieces, 16 bytes per lane, with non-temporal stores (Y is not read again by
+  // this kernel, and streaming it out measured faster than write-back cached stores). Rows of Y
+  // are 16-byte aligned and the column count is a multiple of 8 (checked at launch), so a 16-byte
+  // piece lies wholly inside or wholly past the last column.
+  {
     uint4 *blk = (wave >> 1) == 0 ? sX0 : (wave >> 1) == 1 ? sX1 : (wave >> 1) == 2 ? sW0 : sW1;
     blk += (wave & 1) * (kChunks / 2);
     uint2 *b2 = reinterpret_cast<uint2 *>(blk);
@@ -366,27 +365,18 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
       const int row = 8 * i + (lane >> 3);
       const int64_t m = m0 + wm * 128 + row;
       const uint4 v = blk[swzf(row, c)];
-      if (m < g.M && n < g.C) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
+      if (m < g.M && n < g.C)
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
     }
-    return;
   }
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int64_t m = m0 + wm * 128 + mt * 16 + l16;
-      const int64_t n = n0 + wn * 64 + nt * 16 + 4 * g16;
-      if (m < g.M && n < g.C) {
-        const uint2 v = make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
-                                   pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
-        *reinterpret_cast<uint2 *>(g.out + m * g.ldo + n) = v;
-      }
-    }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st) {
+  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0)
+    return hipErrorInvalidValue;   // the epilogue writes 16-byte pieces of 8 columns
   const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
   if (g.w.dq)
     fwd_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
