@@ -8,10 +8,11 @@ live only inside this test (pytest's monkeypatch undoes them).
 import numpy as np
 import pytest
 
-from oracle import nf4, qlora
+from oracle import nf4, qlora, swiglu
 from tests import test_oracle_codebook as tc
 from tests import test_oracle_gemm as tg
 from tests import test_oracle_quant as tq
+from tests import test_oracle_swiglu as ts
 
 PINS = [
     tc.test_codebook_structure,
@@ -33,6 +34,11 @@ PINS = [
     tg.test_rank_zero_equals_b_zero_equals_plain_gemm,
     tg.test_zero_base_leaves_lora_term,
     tg.test_identity_input_returns_dequantised_weight,
+    ts.test_silu_matches_scipy_logistic,
+    lambda: ts.test_forward_is_the_gated_composition(5, 128, 7, 3, 0, 1.5),
+    lambda: ts.test_backward_matches_finite_differences(5, 2.0),
+    ts.test_stacked_form_equals_the_pair,
+    ts.test_zero_up_projection,
 ]
 
 _fwd, _bwd = qlora.forward, qlora.backward
@@ -80,6 +86,30 @@ def bwd_da_uses_t(dY, X, Wd, A, B, s):
 def bwd_dx_transposed_weight_rows(dY, X, Wd, A, B, s):
     dX, dA, dB = _bwd(dY, X, _f64(Wd)[::-1], A, B, s)
     return dX, dA, dB
+
+
+_sfwd, _sbwd = swiglu.forward, swiglu.backward
+
+
+def swiglu_gate_up_swapped(X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s):
+    H, Yg, Yu, Tg, Tu = _sfwd(X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s)
+    return swiglu.silu(Yu) * Yg, Yg, Yu, Tg, Tu
+
+
+def swiglu_dyu_without_silu(dH, X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s):
+    Yg, _ = qlora.forward(X, Wd_g, Ag, Bg, s)
+    Yu, _ = qlora.forward(X, Wd_u, Au, Bu, s)
+    dYg = _f64(dH) * Yu * swiglu.silu_grad(Yg)
+    dXg, dAg, dBg = qlora.backward(dYg, X, Wd_g, Ag, Bg, s)
+    dXu, dAu, dBu = qlora.backward(_f64(dH) * Yg, X, Wd_u, Au, Bu, s)
+    return dXg + dXu, dAg, dAu, dBg, dBu
+
+
+def swiglu_dx_gate_only(dH, X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s):
+    dX, dAg, dAu, dBg, dBu = _sbwd(dH, X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s)
+    Yg, _ = qlora.forward(X, Wd_g, Ag, Bg, s)
+    dXu, _, _ = qlora.backward(_f64(dH) * swiglu.silu(Yg), X, Wd_u, Au, Bu, s)
+    return dX - dXu, dAg, dAu, dBg, dBu
 
 
 _encode = nf4.encode
@@ -175,6 +205,10 @@ MUTATIONS = {
     "bwd dB uses U instead of T": [(qlora, "backward", bwd_db_uses_u)],
     "bwd dA uses T instead of U": [(qlora, "backward", bwd_da_uses_t)],
     "bwd dX reads weight rows reversed": [(qlora, "backward", bwd_dx_transposed_weight_rows)],
+    "swiglu: silu derivative misses x (1 - sigma)": [(swiglu, "silu_grad", swiglu.sigmoid)],
+    "swiglu: gate and up swapped": [(swiglu, "forward", swiglu_gate_up_swapped)],
+    "swiglu: dYu uses Yg instead of silu(Yg)": [(swiglu, "backward", swiglu_dyu_without_silu)],
+    "swiglu: dX drops the up projection": [(swiglu, "backward", swiglu_dx_gate_only)],
     "encode ties go up": [(nf4, "encode", encode_ties_up)],
     "encode by rounded-to-nearest midpoints": [(nf4, "encode", encode_rne_midpoints)],
     "nibble order swapped": [(nf4, "pack", pack_swapped), (nf4, "unpack", unpack_swapped)],
