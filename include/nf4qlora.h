@@ -155,6 +155,44 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
 int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,
                  int32_t r, float s, void *dX, void *stream);
 
+/* ---- Gate/up pair with SwiGLU -------------------------------------------------------------
+ * The gated MLP's gate and up projections, two QLoRA layers on the same input, joined by the
+ * SwiGLU activation (the pages name a fused gated-MLP activation kernel beside the fused LoRA
+ * matmul [pyshine Unsloth code tour, "Why You Need This"; "Inside Unsloth" listing, "What You'll
+ * Learn", "Triton Kernel Internals"]; the activation is read as the Llama gated MLP):
+ *   Yg = X deq(Wg)^T + s (X Ag^T) Bg^T,   Yu = X deq(Wu)^T + s (X Au^T) Bu^T,
+ *   H  = silu(Yg) * Yu,                   silu(x) = x / (1 + exp(-x)).
+ * Layout: Wgu is ONE NF4 tensor [2n, k] quantised from the stacked weight [Wg; Wu] (rows 0 .. n-1
+ * gate, n .. 2n-1 up: the usual fused gate_up layout); Agu bf16 [2r, k] is [Ag; Au]; Bg and Bu
+ * are bf16 [n, r] each. The pair runs as one stacked QLoRA layer with the block-diagonal up
+ * projection [[Bg, 0], [0, Bu]] (built in the workspace), so its GEMMs are qlora_fwd's and
+ * qlora_bwd's kernels on [2n, k]. Requires n % 8 == 0 and 0 <= r <= 64 (2r <= 128).
+ *
+ * Bytes of device workspace qlora_swiglu_fwd and qlora_swiglu_bwd need (the same for both). */
+size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
+
+/* Forward: H bf16 [m, n] = bf16(silu(Yg) * Yu), computed in float32 from the bf16 Yg, Yu that are
+ * also returned in Ygu bf16 [m, 2n] (each row: Yg then Yu), kept for the backward; Tgu bf16
+ * [m, 2r] = [X Ag^T | X Au^T] (may be NULL: the backward then recomputes it). Agu, Bg, Bu, Tgu
+ * NULL when r == 0. ws: at least qlora_swiglu_workspace_bytes(m, n, k, r) bytes, 16-byte aligned.
+ * Errors: as qlora_fwd; NF4_EINVAL also when Wgu->n is odd, r > 64 or H / Ygu is NULL. */
+int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
+                     const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
+                     void *Tgu, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward for the upstream gradient dH bf16 [m, n], given Ygu and Tgu from the forward (Tgu may
+ * be NULL: recomputed):
+ *   dYg = dH * Yu * silu'(Yg),  dYu = dH * silu(Yg)      (float32, rounded to bf16)
+ *   dX  bf16 [m, k]  = the sum of both projections' input gradients  (skipped when NULL)
+ *   dAgu bf16 [2r, k] = [dAg; dAu],  dBg, dBu bf16 [n, r]
+ * computed as qlora_bwd of the stacked layer with dY = [dYg | dYu]; sums in a fixed order
+ * (deterministic). dAgu, dBg, dBu are ignored when r == 0.
+ * Errors: as qlora_bwd; NF4_EINVAL also when dH or Ygu is NULL. */
+int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor *Wgu,
+                     const void *Agu, const void *Bg, const void *Bu, int32_t r, float s,
+                     const void *Ygu, const void *Tgu, void *dX, void *dAgu, void *dBg, void *dBu,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);
 

@@ -8,6 +8,9 @@ torch fallback: if the library is not built, every call raises.
     Y, T = qlora_fwd(X, q, A, B, s)                  # Y = X deq(W)^T + s (X A^T) B^T
     dX, dA, dB = qlora_bwd(dY, X, q, A, B, s, T)
     Y = QLoRALinearFunction.apply(X, q, A, B, s)     # autograd: gradients for X, A, B
+    qgu = nf4_quantize(torch.cat([Wg, Wu]))           # gate/up pair, stacked [2n, k]
+    H, Ygu, Tgu = qlora_swiglu_fwd(X, qgu, Agu, Bg, Bu, s)   # H = silu(Yg) * Yu
+    dX, dAgu, dBg, dBu = qlora_swiglu_bwd(dH, X, qgu, Agu, Bg, Bu, s, Ygu, Tgu)
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ NF4_BF16, NF4_F32 = 0, 1
 
 EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
-            "qlora_bwd", "qlora_bwd_dx", "nf4_last_error")
+            "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
+            "qlora_swiglu_bwd", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -62,6 +66,10 @@ def library() -> ctypes.CDLL:
         "qlora_bwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
         "qlora_bwd_dx": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
+        "qlora_swiglu_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "qlora_swiglu_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "qlora_swiglu_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]),
         "nf4_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -263,6 +271,63 @@ def qlora_bwd_dx(dY: torch.Tensor, q: NF4Tensor, U: Optional[torch.Tensor], A: O
     return dX
 
 
+def _swiglu_args(X, q: NF4Tensor, Agu, Bg, Bu):
+    if q.n % 2:
+        raise ValueError("the gate/up weight must hold 2n rows (gate rows, then up rows)")
+    m, n = X.shape[0], q.n // 2
+    r = 0 if Agu is None else Agu.shape[0] // 2
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    if r:
+        _need(Agu, "Agu", torch.bfloat16, (2 * r, q.k))
+        _need(Bg, "Bg", torch.bfloat16, (n, r))
+        _need(Bu, "Bu", torch.bfloat16, (n, r))
+    return m, n, r
+
+
+def qlora_swiglu_fwd(X: torch.Tensor, q: NF4Tensor, Agu: Optional[torch.Tensor],
+                     Bg: Optional[torch.Tensor], Bu: Optional[torch.Tensor], s: float):
+    """(H, Ygu, Tgu) of the gate/up pair: q is the stacked NF4 weight [Wg; Wu] [2n, k], Agu the
+    stacked [Ag; Au] [2r, k]; H = silu(Yg) * Yu [m, n], Ygu = [Yg | Yu] [m, 2n], Tgu [m, 2r]."""
+    m, n, r = _swiglu_args(X, q, Agu, Bg, Bu)
+    dev = X.device
+    H = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    Ygu = torch.empty(m, 2 * n, dtype=torch.bfloat16, device=dev)
+    Tgu = torch.empty(m, 2 * r, dtype=torch.bfloat16, device=dev) if r else None
+    lib = library()
+    wsb = lib.qlora_swiglu_workspace_bytes(m, n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.c_struct()
+    _check(lib.qlora_swiglu_fwd(_ptr(X), m, ctypes.byref(st), _ptr(Agu), _ptr(Bg), _ptr(Bu), r,
+                                float(s), _ptr(H), _ptr(Ygu), _ptr(Tgu), _ptr(ws), wsb,
+                                _stream(dev)))
+    return H, Ygu, Tgu
+
+
+def qlora_swiglu_bwd(dH: torch.Tensor, X: torch.Tensor, q: NF4Tensor, Agu: Optional[torch.Tensor],
+                     Bg: Optional[torch.Tensor], Bu: Optional[torch.Tensor], s: float,
+                     Ygu: torch.Tensor, Tgu: Optional[torch.Tensor], need_dx: bool = True):
+    """(dX, dAgu, dBg, dBu) of the gate/up pair for the upstream gradient dH [m, n]."""
+    m, n, r = _swiglu_args(X, q, Agu, Bg, Bu)
+    _need(dH, "dH", torch.bfloat16, (m, n))
+    _need(Ygu, "Ygu", torch.bfloat16, (m, 2 * n))
+    if r and Tgu is not None:
+        _need(Tgu, "Tgu", torch.bfloat16, (m, 2 * r))
+    dev = X.device
+    dX = torch.empty(m, q.k, dtype=torch.bfloat16, device=dev) if need_dx else None
+    dAgu = torch.empty(2 * r, q.k, dtype=torch.bfloat16, device=dev) if r else None
+    dBg = torch.empty(n, r, dtype=torch.bfloat16, device=dev) if r else None
+    dBu = torch.empty(n, r, dtype=torch.bfloat16, device=dev) if r else None
+    lib = library()
+    wsb = lib.qlora_swiglu_workspace_bytes(m, n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.c_struct()
+    _check(lib.qlora_swiglu_bwd(_ptr(dH), _ptr(X), m, ctypes.byref(st), _ptr(Agu), _ptr(Bg),
+                                _ptr(Bu), r, float(s), _ptr(Ygu), _ptr(Tgu if r else None),
+                                _ptr(dX), _ptr(dAgu), _ptr(dBg), _ptr(dBu), _ptr(ws), wsb,
+                                _stream(dev)))
+    return dX, dAgu, dBg, dBu
+
+
 class QLoRALinearFunction(torch.autograd.Function):
     """Y = X deq(W)^T + s (X A^T) B^T with W frozen; gradients flow to X, A and B."""
 
@@ -279,3 +344,22 @@ class QLoRALinearFunction(torch.autograd.Function):
         dX, dA, dB = qlora_bwd(dY.contiguous(), X, ctx.q, A, B, ctx.s, T,
                                need_dx=ctx.needs_input_grad[0])
         return dX, None, dA, dB, None
+
+
+class QLoRASwiGLUFunction(torch.autograd.Function):
+    """H = silu(X deq(Wg)^T + s (X Ag^T) Bg^T) * (X deq(Wu)^T + s (X Au^T) Bu^T) with the bases frozen
+    (q = stacked NF4 [Wg; Wu]); gradients flow to X, Agu = [Ag; Au], Bg and Bu."""
+
+    @staticmethod
+    def forward(ctx, X, q: NF4Tensor, Agu, Bg, Bu, s: float):
+        H, Ygu, Tgu = qlora_swiglu_fwd(X, q, Agu, Bg, Bu, s)
+        ctx.q, ctx.s = q, s
+        ctx.save_for_backward(X, Agu, Bg, Bu, Ygu, Tgu)
+        return H
+
+    @staticmethod
+    def backward(ctx, dH):
+        X, Agu, Bg, Bu, Ygu, Tgu = ctx.saved_tensors
+        dX, dAgu, dBg, dBu = qlora_swiglu_bwd(dH.contiguous(), X, ctx.q, Agu, Bg, Bu, ctx.s, Ygu, Tgu,
+                                              need_dx=ctx.needs_input_grad[0])
+        return dX, None, dAgu, dBg, dBu, None

@@ -202,6 +202,49 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
   return w;
 }
 
+// Gate/up SwiGLU pair: B2 [2n, 2r] (block-diagonal up projection) first; then, for the forward,
+// T (when the caller keeps none) and qlora_fwd's workspace of the stacked layer; for the
+// backward, dY2 [m, 2n], dB2 [2n, 2r] and qlora_bwd's workspace of the stacked layer.
+struct SwiWs {
+  size_t b2 = 0, t = 0, fwd = 0, dy2 = 0, db2 = 0, bwd = 0, total = 0;
+};
+
+SwiWs swi_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
+  SwiWs w;
+  if (r > 0) {
+    w.b2 = align256((size_t)(2 * n) * (2 * r) * 2);
+    w.t = align256((size_t)m * (2 * r) * 2);
+    w.fwd = fwd_ws(m, k, 2 * r).total;
+    w.db2 = w.b2;
+  }
+  w.dy2 = align256((size_t)m * (2 * n) * 2);
+  w.bwd = bwd_ws(m, 2 * n, k, 2 * r).total;
+  w.total = w.b2 + std::max(w.t + w.fwd, w.dy2 + w.db2 + w.bwd);
+  return w;
+}
+
+int check_swiglu(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu, const void *Bg,
+                 const void *Bu, int32_t r, void *ws, size_t ws_bytes, size_t *need) {
+  int st = check_weight(Wgu);
+  if (st) return st;
+  if (Wgu->n % 2) return fail(NF4_EINVAL, "Wgu must hold 2n rows (got %lld)", (long long)Wgu->n);
+  const int64_t n = Wgu->n / 2;
+  if (n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)n);
+  if (r < 0 || r > 64) return fail(NF4_EINVAL, "r must lie in [0, 64] (got %d)", r);
+  st = check_layer(X, m, Wgu, Agu, Agu, 2 * r);   // X, the stacked weight, Agu
+  if (st) return st;
+  if (r > 0) {
+    if (!Bg || !Bu) return fail(NF4_EINVAL, "Bg and Bu must be non-NULL when r > 0");
+    if (!aligned16(Bg) || !aligned16(Bu)) return fail(NF4_EINVAL, "Bg and Bu must be 16-byte aligned");
+  }
+  *need = swi_ws(m, n, Wgu->k, r).total;
+  if (ws_bytes < *need || !ws)
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                *need);
+  if (!aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  return NF4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -398,6 +441,75 @@ int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, con
                              (uint16_t *)dB, true, sm);
     if (e != hipSuccess) return hip_status(e, "qlora_bwd dB launch");
   }
+  return ok();
+}
+
+size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  if (m < 1 || n < 1 || k < 1 || r < 0) return 0;
+  return swi_ws(m, n, k, r).total;
+}
+
+int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
+                     const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
+                     void *Tgu, void *ws, size_t ws_bytes, void *stream) {
+  size_t need = 0;
+  int st = check_swiglu(X, m, Wgu, Agu, Bg, Bu, r, ws, ws_bytes, &need);
+  if (st) return st;
+  if (!H || !aligned16(H) || !Ygu || !aligned16(Ygu))
+    return fail(NF4_EINVAL, "H and Ygu must be non-NULL and 16-byte aligned");
+  if (Tgu && !aligned16(Tgu)) return fail(NF4_EINVAL, "Tgu must be 16-byte aligned");
+  const int64_t n = Wgu->n / 2;
+  const SwiWs lay = swi_ws(m, n, Wgu->k, r);
+  hipStream_t sm = (hipStream_t)stream;
+  char *base = (char *)ws;
+  uint16_t *B2 = r > 0 ? (uint16_t *)base : nullptr;
+  void *T = r > 0 ? (Tgu ? Tgu : (void *)(base + lay.b2)) : nullptr;
+  if (r > 0) {
+    hipError_t e = nf4q::launch_blockdiag((const uint16_t *)Bg, (const uint16_t *)Bu, n, r, B2, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_swiglu_fwd launch");
+  }
+  st = qlora_fwd(X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, Ygu, T,
+                 lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd, stream);
+  if (st) return st;
+  return hip_status(nf4q::launch_swiglu_fwd((const uint16_t *)Ygu, m, n, (uint16_t *)H, sm),
+                    "qlora_swiglu_fwd launch");
+}
+
+int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor *Wgu,
+                     const void *Agu, const void *Bg, const void *Bu, int32_t r, float s,
+                     const void *Ygu, const void *Tgu, void *dX, void *dAgu, void *dBg, void *dBu,
+                     void *ws, size_t ws_bytes, void *stream) {
+  size_t need = 0;
+  int st = check_swiglu(X, m, Wgu, Agu, Bg, Bu, r, ws, ws_bytes, &need);
+  if (st) return st;
+  if (!dH || !aligned16(dH) || !Ygu || !aligned16(Ygu))
+    return fail(NF4_EINVAL, "dH and Ygu must be non-NULL and 16-byte aligned");
+  if (dX && !aligned16(dX)) return fail(NF4_EINVAL, "dX must be 16-byte aligned");
+  if (r > 0) {
+    if (!dAgu || !dBg || !dBu) return fail(NF4_EINVAL, "dAgu, dBg and dBu must be non-NULL when r > 0");
+    if ((Tgu && !aligned16(Tgu)) || !aligned16(dAgu) || !aligned16(dBg) || !aligned16(dBu))
+      return fail(NF4_EINVAL, "Tgu, dAgu, dBg and dBu must be 16-byte aligned");
+  }
+  if (!dX && r == 0) return ok();
+  const int64_t n = Wgu->n / 2;
+  const SwiWs lay = swi_ws(m, n, Wgu->k, r);
+  hipStream_t sm = (hipStream_t)stream;
+  char *base = (char *)ws;
+  uint16_t *B2 = r > 0 ? (uint16_t *)base : nullptr;
+  uint16_t *dY2 = (uint16_t *)(base + lay.b2);
+  uint16_t *dB2 = r > 0 ? (uint16_t *)(base + lay.b2 + lay.dy2) : nullptr;
+  hipError_t e = nf4q::launch_swiglu_bwd((const uint16_t *)dH, (const uint16_t *)Ygu, m, n, dY2, sm);
+  if (e != hipSuccess) return hip_status(e, "qlora_swiglu_bwd launch");
+  if (r > 0) {
+    e = nf4q::launch_blockdiag((const uint16_t *)Bg, (const uint16_t *)Bu, n, r, B2, sm);
+    if (e != hipSuccess) return hip_status(e, "qlora_swiglu_bwd launch");
+  }
+  st = qlora_bwd(dY2, X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, r > 0 ? Tgu : nullptr, dX,
+                 r > 0 ? dAgu : nullptr, dB2, base + lay.b2 + lay.dy2 + lay.db2, lay.bwd, stream);
+  if (st) return st;
+  if (r > 0)
+    return hip_status(nf4q::launch_diagblocks(dB2, n, r, (uint16_t *)dBg, (uint16_t *)dBu, sm),
+                      "qlora_swiglu_bwd launch");
   return ok();
 }
 

@@ -66,4 +66,13 @@ int mreduce_splits(int64_t M, int64_t C);
 // dst[j][l] = src[l][j] for a bf16 [L][r] matrix.
 hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst, hipStream_t st);
 
+// Gate/up SwiGLU pair (swiglu.hip). ygu / dygu rows: the gate block then the up block, 2n columns.
+hipError_t launch_swiglu_fwd(const uint16_t *ygu, int64_t m, int64_t n, uint16_t *h, hipStream_t st);
+hipError_t launch_swiglu_bwd(const uint16_t *dh, const uint16_t *ygu, int64_t m, int64_t n,
+                             uint16_t *dygu, hipStream_t st);
+hipError_t launch_blockdiag(const uint16_t *bg, const uint16_t *bu, int64_t n, int r, uint16_t *b2,
+                            hipStream_t st);
+hipError_t launch_diagblocks(const uint16_t *db2, int64_t n, int r, uint16_t *dbg, uint16_t *dbu,
+                             hipStream_t st);
+
 }  // namespace nf4q

@@ -1,0 +1,114 @@
+"""GPU parity of the gate/up SwiGLU pair (qlora_swiglu_fwd / qlora_swiglu_bwd) against the oracle.
+
+The stacked NF4 weight [Wg; Wu] is bit-exact against the oracle's quantisation of the same
+stacked weight (double-quant runs may straddle the gate/up boundary on both sides alike); H, the
+saved Ygu and Tgu, and dX, dAgu, dBg, dBu are within max|got - ref| / max|ref| <= 1e-2 of the
+float64 oracle (oracle/swiglu.py). Shapes span several 256-wide tiles with ragged tails, the
+M <= 16 kernels, r = 0 and the largest rank (2r = 128).
+
+The pair rounds twice where one layer rounds once (Yg, Yu are bf16 before the activation; dYg,
+dYu are bf16 before the backward GEMMs), so its errors sit near twice the one-rounding floor:
+the warning level for a bug hiding under the bar is 8e-3 here (4e-3 for one layer).
+"""
+import numpy as np
+import pytest
+import torch
+
+import nf4_dequant_gemm_amd as lib_mod
+import workloads as wl
+from oracle import nf4, swiglu
+from tests.gpu_helpers import assert_quant_equal, check_close as _check_close, f32, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def check_close(name, got, ref):
+    return _check_close(name, got, ref, warn_above=8e-3)
+
+CASES = [
+    # M, K, N, r, dq, s
+    (64, 256, 128, 8, 256, 2.0),
+    (200, 320, 72, 16, 0, -0.5),
+    (7, 512, 264, 8, 256, 1.0),        # M <= 16: the stacked forward takes the decode kernel
+    (12, 256, 40, 16, 0, 1.5),         # M <= 16 without double quantisation
+    (33, 256, 40, 0, 256, 1.0),        # no adapters
+    (300, 1024, 520, 64, 256, 0.5),    # 2r = 128, the layer's largest rank
+]
+
+
+def rand_pair(M, K, N, r, seed):
+    X = wl.normal_bf16(seed + 1, (M, K), 1.0)
+    Wgu = wl.normal_bf16(seed + 2, (2 * N, K), 0.02)
+    Agu = wl.normal_bf16(seed + 3, (2 * r, K), K ** -0.5)
+    # adapters large enough that the LoRA terms are visible in H
+    Bg = wl.normal_bf16(seed + 4, (N, r), 0.1)
+    Bu = wl.normal_bf16(seed + 5, (N, r), 0.1)
+    dH = wl.normal_bf16(seed + 6, (M, N), 1.0)
+    return X, Wgu, Agu, Bg, Bu, dH
+
+
+def run_pair(lib, M, K, N, r, dq, s, seed):
+    X, Wgu, Agu, Bg, Bu, dH = rand_pair(M, K, N, r, seed)
+    qo = nf4.quantize(Wgu.float().numpy(), dq)
+    Wd = nf4.dequantize_f32(qo)
+    f = lambda t: t.float().numpy()
+    Ag, Au = (f(Agu[:r]), f(Agu[r:])) if r else (np.zeros((0, K)), np.zeros((0, K)))
+    Bgo, Buo = (f(Bg), f(Bu)) if r else (np.zeros((N, 0)), np.zeros((N, 0)))
+    ref_fwd = swiglu.forward(f(X), Wd[:N], Wd[N:], Ag, Au, Bgo, Buo, s)
+    ref_bwd = swiglu.backward(f(dH), f(X), Wd[:N], Wd[N:], Ag, Au, Bgo, Buo, s)
+    qg = lib.nf4_quantize(Wgu.to(DEV), dq)
+    d = lambda t: t.to(DEV) if r else None
+    H, Ygu, Tgu = lib.qlora_swiglu_fwd(X.to(DEV), qg, d(Agu), d(Bg), d(Bu), s)
+    dX, dAgu, dBg, dBu = lib.qlora_swiglu_bwd(dH.to(DEV), X.to(DEV), qg, d(Agu), d(Bg), d(Bu), s, Ygu, Tgu)
+    torch.cuda.synchronize()
+    assert_quant_equal(qg, qo)
+    return (H, Ygu, Tgu, dX, dAgu, dBg, dBu), ref_fwd, ref_bwd
+
+
+@pytest.mark.parametrize("M,K,N,r,dq,s", CASES)
+def test_swiglu_pair_parity(lib, M, K, N, r, dq, s):
+    say(f"swiglu pair M={M} K={K} N={N} r={r} dq={dq} s={s}")
+    (H, Ygu, Tgu, dX, dAgu, dBg, dBu), (Hr, Yg, Yu, Tg, Tu), (dXr, dAg, dAu, dBgr, dBur) = \
+        run_pair(lib, M, K, N, r, dq, s, seed=M * 11 + N)
+    check_close("H", f32(H), Hr)
+    check_close("Ygu", f32(Ygu), np.concatenate([Yg, Yu], axis=1))
+    check_close("dX", f32(dX), dXr)
+    if r:
+        check_close("Tgu", f32(Tgu), np.concatenate([Tg, Tu], axis=1))
+        check_close("dAgu", f32(dAgu), np.concatenate([dAg, dAu]))
+        check_close("dBg", f32(dBg), dBgr)
+        check_close("dBu", f32(dBu), dBur)
+    else:
+        assert Tgu is None and dAgu is None and dBg is None and dBu is None
+
+
+def test_swiglu_recomputes_missing_tgu(lib):
+    """Tgu = None in the backward recomputes it exactly as the forward computes it."""
+    M, K, N, r, s = 40, 256, 64, 8, 1.0
+    X, Wgu, Agu, Bg, Bu, dH = rand_pair(M, K, N, r, 77)
+    qg = lib.nf4_quantize(Wgu.to(DEV), 256)
+    X, Agu, Bg, Bu, dH = (t.to(DEV) for t in (X, Agu, Bg, Bu, dH))
+    H, Ygu, Tgu = lib.qlora_swiglu_fwd(X, qg, Agu, Bg, Bu, s)
+    a = lib.qlora_swiglu_bwd(dH, X, qg, Agu, Bg, Bu, s, Ygu, Tgu)
+    b = lib.qlora_swiglu_bwd(dH, X, qg, Agu, Bg, Bu, s, Ygu, None)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_swiglu_autograd_function(lib):
+    M, K, N, r, s = 48, 256, 64, 8, 0.5
+    X, Wgu, Agu, Bg, Bu, dH = rand_pair(M, K, N, r, 91)
+    qg = lib.nf4_quantize(Wgu.to(DEV), 256)
+    Xd = X.to(DEV).requires_grad_(True)
+    Ad, Bgd, Bud = (t.to(DEV).requires_grad_(True) for t in (Agu, Bg, Bu))
+    H = lib_mod.QLoRASwiGLUFunction.apply(Xd, qg, Ad, Bgd, Bud, s)
+    H.backward(dH.to(DEV))
+    H2, Ygu, Tgu = lib.qlora_swiglu_fwd(X.to(DEV), qg, Agu.to(DEV), Bg.to(DEV), Bu.to(DEV), s)
+    ref = lib.qlora_swiglu_bwd(dH.to(DEV), X.to(DEV), qg, Agu.to(DEV), Bg.to(DEV), Bu.to(DEV), s, Ygu, Tgu)
+    torch.cuda.synchronize()
+    assert torch.equal(H.detach(), H2)
+    for got, want in zip((Xd.grad, Ad.grad, Bgd.grad, Bud.grad), ref):
+        assert torch.equal(got, want)

@@ -142,12 +142,51 @@ def test_layer_calls_reject_bad_arguments():
     assert dx(q=wdesc(n=60, k=128)) == m.NF4_EUNSUPPORTED
 
 
+def test_swiglu_calls_reject_bad_arguments():
+    """The gate/up pair validates on the host: stacked weight rows, r range, outputs, workspace."""
+    lib = m.library()
+    q = wdesc(n=128, k=128)                      # stacked [Wg; Wu]: n = 64 per projection
+    wsb = lib.qlora_swiglu_workspace_bytes(100, 64, 128, 8)
+    assert wsb > 0
+    fwd = lambda **kw: lib.qlora_swiglu_fwd(kw.get("X", FAKE), kw.get("m", 100), ctypes.byref(kw.get("q", q)),
+                                             kw.get("A", FAKE), kw.get("Bg", FAKE), kw.get("Bu", FAKE),
+                                             kw.get("r", 8), 1.0, kw.get("H", FAKE), kw.get("Y", FAKE),
+                                             kw.get("T", FAKE), kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert fwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert fwd(ws=None) == m.NF4_EINVAL
+    assert fwd(m=0) == m.NF4_EINVAL
+    assert fwd(r=65) == m.NF4_EINVAL           # 2r must fit the layer's 128
+    assert fwd(r=-1) == m.NF4_EINVAL
+    assert fwd(Bu=None) == m.NF4_EINVAL
+    assert fwd(A=None) == m.NF4_EINVAL
+    assert fwd(H=None) == m.NF4_EINVAL
+    assert fwd(Y=None) == m.NF4_EINVAL
+    assert fwd(T=ctypes.c_void_p(4100)) == m.NF4_EINVAL
+    assert fwd(q=wdesc(n=129, k=128)) == m.NF4_EINVAL         # odd row count: not a stacked pair
+    assert fwd(q=wdesc(n=120, k=128)) == m.NF4_EUNSUPPORTED   # n = 60 per projection
+    bwd = lambda **kw: lib.qlora_swiglu_bwd(kw.get("dH", FAKE), FAKE, 100, ctypes.byref(q), FAKE, FAKE, FAKE,
+                                             kw.get("r", 8), 1.0, kw.get("Y", FAKE), kw.get("T", FAKE), FAKE,
+                                             kw.get("dA", FAKE), kw.get("dBg", FAKE), FAKE,
+                                             kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert bwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert bwd(dH=None) == m.NF4_EINVAL
+    assert bwd(Y=None) == m.NF4_EINVAL
+    assert bwd(dA=None) == m.NF4_EINVAL
+    assert bwd(dBg=ctypes.c_void_p(4104)) == m.NF4_EINVAL
+    assert bwd(r=100) == m.NF4_EINVAL
+    assert bwd(T=None, wsb=wsb - 1) == m.NF4_EINVAL          # Tgu may be NULL, ws still checked
+
+
 def test_workspace_sizes_are_consistent():
     lib = m.library()
     assert lib.qlora_fwd_workspace_bytes(100, 64, 128, 0) == 0
     assert lib.qlora_bwd_workspace_bytes(100, 64, 128, 0) == 0
     # bwd workspace holds at least U (bf16 [m, r]) and B^T (bf16 [r, n])
     assert lib.qlora_bwd_workspace_bytes(16384, 4096, 14336, 32) >= 16384 * 32 * 2 + 32 * 4096 * 2
+    # the gate/up pair holds at least the stacked dY (bf16 [m, 2n]) and the stacked layer's
+    # backward workspace
+    assert lib.qlora_swiglu_workspace_bytes(8192, 11008, 4096, 64) >= (
+        8192 * 2 * 11008 * 2 + lib.qlora_bwd_workspace_bytes(8192, 2 * 11008, 4096, 128))
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
