@@ -26,6 +26,9 @@ matrix-core-bound shapes, a device copy for the HBM-bound one.
 
     python bench.py [--steps K] [--warmup W] [--workload down] [--no-cpu-baseline]
                     [--no-weight-stream] [--copy-calibration]
+
+--workload mlp_swiglu measures the gate/up SwiGLU pair instead (a step: qlora_swiglu_fwd +
+qlora_swiglu_bwd on the mlp_up shape, two projections).
 """
 from __future__ import annotations
 
@@ -37,6 +40,7 @@ import math
 import os
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -278,6 +282,140 @@ def run_cpu_baseline(w, target_s):
                       f"(numpy/BLAS), {dt:.1f}s wall; W dequantised once outside the timing"}
 
 
+def run_pair(args, pw, dev):
+    """The gate/up SwiGLU pair (qlora_swiglu_fwd + qlora_swiglu_bwd per step) on pair workload pw."""
+    import torch
+    import nf4_dequant_gemm_amd as lib
+    import workloads as wl
+    c = lib.library()
+    M, K, N, r, s = pw.M, pw.K, pw.N, pw.r, pw.s
+    host = {t: wl.pair_tensor(pw, t) for t in ("X", "Wgu", "Agu", "Bg", "Bu", "dH")}
+    d = {t: v.to(dev) for t, v in host.items() if t != "Wgu"}
+    q = lib.nf4_quantize(host["Wgu"].to(dev), pw.dq_block)
+    del host
+    ncopies = args.wcopies or max(1, min(64, math.ceil(COLD_BYTES / pw.weight_stream_bytes())))
+    copies = [q] + [q.clone() for _ in range(ncopies - 1)]
+    qs = [x.c_struct() for x in copies]
+    bf = torch.bfloat16
+    H = torch.empty(M, N, dtype=bf, device=dev)
+    Ygu = torch.empty(M, 2 * N, dtype=bf, device=dev)
+    Tgu = torch.empty(M, 2 * r, dtype=bf, device=dev)
+    dX = torch.empty(M, K, dtype=bf, device=dev)
+    dAgu = torch.empty(2 * r, K, dtype=bf, device=dev)
+    dBg = torch.empty(N, r, dtype=bf, device=dev)
+    dBu = torch.empty(N, r, dtype=bf, device=dev)
+    wsb = c.qlora_swiglu_workspace_bytes(M, N, K, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(c.nf4_last_error().decode())
+
+    def fwd(i):
+        check(c.qlora_swiglu_fwd(P(d["X"]), M, ctypes.byref(qs[i % ncopies]), P(d["Agu"]), P(d["Bg"]),
+                                 P(d["Bu"]), r, s, P(H), P(Ygu), P(Tgu), P(ws), wsb, sp))
+
+    def bwd(i):
+        check(c.qlora_swiglu_bwd(P(d["dH"]), P(d["X"]), M, ctypes.byref(qs[i % ncopies]), P(d["Agu"]),
+                                 P(d["Bg"]), P(d["Bu"]), r, s, P(Ygu), P(Tgu), P(dX), P(dAgu), P(dBg),
+                                 P(dBu), P(ws), wsb, sp))
+
+    calls = (fwd, bwd)
+    for i in range(args.warmup):
+        for f in calls:
+            f(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        ev[st][0].record(stream)
+        for j, f in enumerate(calls):
+            f(args.warmup + st)
+            ev[st][j + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {}
+    for j, name in enumerate(("swiglu_fwd", "swiglu_bwd")):
+        v = [ev[st][j].elapsed_time(ev[st][j + 1]) for st in range(args.steps)]
+        per[name] = {"mean": sum(v) / len(v), "median": pct(v, 0.5), "p10": pct(v, 0.1), "p90": pct(v, 0.9)}
+    # The dominant launch: the fused forward of the stacked layer ([Wg; Wu] with the block-diagonal
+    # up projection), the kernel qlora_swiglu_fwd runs; timed on its own with T from the forward.
+    B2 = torch.zeros(2 * N, 2 * r, dtype=bf, device=dev)
+    B2[:N, :r] = d["Bg"]
+    B2[N:, r:] = d["Bu"]
+
+    def fused(i):
+        check(c.qlora_fwd_fused(P(d["X"]), M, ctypes.byref(qs[i % ncopies]), P(Tgu), P(B2), 2 * r, s,
+                                P(Ygu), sp))
+    t = time_call(types.SimpleNamespace(stream=stream), fused, args.steps, args.warmup)
+    work = 2 * M * (2 * N) * K + 2 * M * (2 * N) * (2 * r)
+    achieved = work / (t["median"] * 1e-3) / 1e12
+    roof = {"kernel": "qlora_fwd_fused (stacked gate/up)", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in t.items()}, "traffic": None}
+    context = None
+    if not args.no_context:
+        Wd = lib.nf4_dequantize(q, torch.bfloat16)
+        context = {"mfma_loop": run_mfma_loop(Wd, d["X"])}
+        roof["frac_of_mfma_loop"] = round(achieved / context["mfma_loop"]["TFLOP/s"], 4)
+        del Wd
+    del copies, qs, d, H, Ygu, Tgu, dX, dAgu, dBg, dBu, ws, B2
+    torch.cuda.empty_cache()
+    flops = pw.fwd_flops() + pw.bwd_flops()
+    out = {
+        "metric": METRIC, "value": round(flops / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{pw.name}: gate/up pair, X [{M},{K}] bf16, W NF4 [{N},{K}] x 2 (stacked) "
+                               f"double-quant int8/256, LoRA r={r} x 2 s={s}, H = silu(Yg) * Yu, fwd+bwd",
+                   "M": M, "K": K, "N": N, "r": r, "weight_copies": ncopies,
+                   "phase_ms": {k: {x: round(y, 4) for x, y in v.items()} for k, v in per.items()}},
+        "roofline": roof,
+    }
+    if context:
+        out["context"] = context
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_pair_cpu_baseline(pw, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def run_pair_cpu_baseline(pw, target_s):
+    """The oracle's gate/up pair (float64) on a row sample of the same step."""
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import nf4, swiglu
+    Wd = nf4.dequantize_f32(nf4.quantize(wl.pair_tensor(pw, "Wgu").float().numpy(), pw.dq_block))
+    N, r = pw.N, pw.r
+    Agu = wl.pair_tensor(pw, "Agu").float().numpy()
+    Bg, Bu = wl.pair_tensor(pw, "Bg").float().numpy(), wl.pair_tensor(pw, "Bu").float().numpy()
+    Xall = wl.pair_tensor(pw, "X").float().numpy()
+    dHall = wl.pair_tensor(pw, "dH").float().numpy()
+
+    def step(rows):
+        t = time.perf_counter()
+        swiglu.forward(Xall[:rows], Wd[:N], Wd[N:], Agu[:r], Agu[r:], Bg, Bu, pw.s)
+        swiglu.backward(dHall[:rows], Xall[:rows], Wd[:N], Wd[N:], Agu[:r], Agu[r:], Bg, Bu, pw.s)
+        return time.perf_counter() - t
+
+    rows = 64
+    dt = step(rows)
+    while dt < 0.4 * target_s and rows < pw.M:
+        rows = int(min(pw.M, max(2 * rows, rows * target_s / max(dt, 1e-3))))
+        rows = max(64, rows // 64 * 64)
+        dt = step(rows)
+    flops = (pw.fwd_flops() + pw.bwd_flops()) * rows / pw.M
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "wall_s": round(dt, 2),
+            "sample": f"{rows} of {pw.M} rows of the {pw.name} pair, forward+backward in float64 "
+                      f"(numpy/BLAS), {dt:.1f}s wall; the weights dequantised once outside the timing"}
+
+
 def _median_ms(fn, reps, warmup=2):
     import torch
     for _ in range(warmup):
@@ -391,8 +529,11 @@ def main():
         return
     import torch
     import workloads as wl
-    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.workload in wl.PAIRS:
+        run_pair(args, wl.PAIRS[args.workload], dev)
+        return
+    w = wl.WORKLOADS[args.workload]
     L = Layer(w, dev, args.wcopies)
     step_ms, per = time_layer(L, args.steps, args.warmup)
     whole_fwd = time_call(L, L.fwd_whole, args.steps, args.warmup) if not w.backward else None

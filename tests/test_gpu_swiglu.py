@@ -112,3 +112,51 @@ def test_swiglu_autograd_function(lib):
     assert torch.equal(H.detach(), H2)
     for got, want in zip((Xd.grad, Ad.grad, Bgd.grad, Bud.grad), ref):
         assert torch.equal(got, want)
+
+
+def test_swiglu_pair_full_size(lib):
+    """The mlp_swiglu pair at full size, as bench.py launches it: the stacked weight bit for bit;
+    H, Ygu, Tgu and dX on sampled rows, dAgu on sampled columns, dBg and dBu on sampled rows,
+    against the float64 oracle on the same seeded inputs."""
+    from tests.test_gpu_workloads import sample, t_full
+    p = wl.PAIRS["mlp_swiglu"]
+    M, K, N, r, s = p.M, p.K, p.N, p.r, p.s
+    say(f"pair {p.name}: M={M} K={K} N={N} r={r} s={s}")
+    Wgu = wl.pair_tensor(p, "Wgu")
+    X, Agu, Bg, Bu, dH = (wl.pair_tensor(p, t) for t in ("X", "Agu", "Bg", "Bu", "dH"))
+    qg = lib.nf4_quantize(Wgu.to(DEV), p.dq_block)
+    Xd, Ad, Bgd, Bud = X.to(DEV), Agu.to(DEV), Bg.to(DEV), Bu.to(DEV)
+    H, Ygu, Tgu = lib.qlora_swiglu_fwd(Xd, qg, Ad, Bgd, Bud, s)
+    dX, dAgu, dBgg, dBug = lib.qlora_swiglu_bwd(dH.to(DEV), Xd, qg, Ad, Bgd, Bud, s, Ygu, Tgu)
+    torch.cuda.synchronize()
+    say("  fwd + bwd done")
+    qo = nf4.quantize(Wgu.float().numpy(), p.dq_block)
+    assert_quant_equal(qg, qo)
+    del Wgu
+    Wd = nf4.dequantize_f32(qo).astype(np.float64)
+    Xf, Af, Bgf, Buf, dHf = (f32(t).astype(np.float64) for t in (X, Agu, Bg, Bu, dH))
+    Ag, Au = Af[:r], Af[r:]
+    Tg, Tu = t_full(f32(X), f32(Agu)[:r]), t_full(f32(X), f32(Agu)[r:])
+    # full gate and up outputs in float64 (the gradients of the adapters sum over every row)
+    Yg = np.empty((M, N))
+    Yu = np.empty((M, N))
+    for lo in range(0, M, 1024):
+        Yg[lo:lo + 1024] = Xf[lo:lo + 1024] @ Wd[:N].T + s * (Tg[lo:lo + 1024] @ Bgf.T)
+        Yu[lo:lo + 1024] = Xf[lo:lo + 1024] @ Wd[N:].T + s * (Tu[lo:lo + 1024] @ Buf.T)
+    sg = swiglu.sigmoid(Yg)
+    dYg = dHf * Yu * (sg * (1 + Yg * (1 - sg)))
+    dYu = dHf * Yg * sg
+    rows = sample(M, 48, p.index)
+    rt = torch.from_numpy(rows).to(DEV)
+    check_close("H", f32(H[rt]), (Yg * sg * Yu)[rows])
+    check_close("Ygu", f32(Ygu[rt]), np.concatenate([Yg[rows], Yu[rows]], axis=1))
+    check_close("Tgu", f32(Tgu[rt]), np.concatenate([Tg[rows], Tu[rows]], axis=1))
+    Ug, Uu = dYg @ Bgf, dYu @ Buf
+    dXs = dYg[rows] @ Wd[:N] + dYu[rows] @ Wd[N:] + s * (Ug[rows] @ Ag + Uu[rows] @ Au)
+    check_close("dX", f32(dX[rt]), dXs)
+    cols = sample(K, 64, p.index + 1)
+    dAs = s * np.concatenate([Ug.T @ Xf[:, cols], Uu.T @ Xf[:, cols]])
+    check_close("dAgu", f32(dAgu)[:, cols], dAs)
+    nrows = sample(N, 64, p.index + 2)
+    check_close("dBg", f32(dBgg)[nrows], s * (dYg[:, nrows].T @ Tg))
+    check_close("dBu", f32(dBug)[nrows], s * (dYu[:, nrows].T @ Tu))

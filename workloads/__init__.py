@@ -14,6 +14,10 @@ the Unsloth pages' "About the Unsloth Project" section):
   decode  M=16    K=8192   N=28672  r=16  s=2   absmax int8/256     fwd (weight-stream bound)
   down    M=16384 K=14336  N=4096   r=32  s=1   absmax int8/256     fwd+bwd
 
+and one gate/up pair (two projections on the same X joined by SwiGLU, PAIRS below):
+
+  mlp_swiglu  M=8192  K=4096  N=11008 (x2)  r=64 (x2)  s=0.5  absmax int8/256  fwd+bwd
+
 Distributions (std is the standard deviation of a normal): X ~ N(0,1); W ~ N(0,0.02) (0.015 for
 decode); A ~ N(0, 1/K) read as variance 1/K, i.e. std K**-0.5; B ~ N(0,0.01); dY ~ N(0,1)
 (N(0,1e-2) for down). Workloads that name no A/B distribution use the mlp_up one.
@@ -90,6 +94,60 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
 ]}
 
 
+@dataclasses.dataclass(frozen=True)
+class PairWorkload:
+    """A gate/up pair of QLoRA projections on the same X, joined by SwiGLU (H = silu(Yg) * Yu).
+
+    Tensors: X [M,K]; Wgu [2N,K] (gate rows, then up rows: the stacked base weight); Agu [2r,K]
+    (gate A, then up A); Bg, Bu [N,r]; dH [M,N]. Seeds 1000*index + t (X=1, Wgu=2, Agu=3, Bg=4,
+    dH=5, Bu=6); distributions as the single-layer workloads.
+    """
+    name: str
+    index: int
+    M: int
+    K: int
+    N: int
+    r: int
+    s: float
+    dq_block: int
+    std_x: float
+    std_w: float
+    std_b: float
+    std_dh: float
+
+    def shape(self, tensor: str) -> Tuple[int, int]:
+        M, K, N, r = self.M, self.K, self.N, self.r
+        return {"X": (M, K), "Wgu": (2 * N, K), "Agu": (2 * r, K), "Bg": (N, r), "Bu": (N, r),
+                "dH": (M, N)}[tensor]
+
+    def std(self, tensor: str) -> float:
+        return {"X": self.std_x, "Wgu": self.std_w, "Agu": self.K ** -0.5, "Bg": self.std_b,
+                "Bu": self.std_b, "dH": self.std_dh}[tensor]
+
+    def seed(self, tensor: str) -> int:
+        return 1000 * self.index + {"X": 1, "Wgu": 2, "Agu": 3, "Bg": 4, "dH": 5, "Bu": 6}[tensor]
+
+    def projection(self) -> Workload:
+        """One of the two projections as a single-layer workload (for its flop counts)."""
+        return Workload(self.name, self.index, self.M, self.K, self.N, self.r, self.s, self.dq_block,
+                        self.std_x, self.std_w, self.std_b, self.std_dh, True)
+
+    def fwd_flops(self) -> int:
+        return 2 * self.projection().fwd_flops()
+
+    def bwd_flops(self) -> int:
+        return 2 * self.projection().bwd_flops()
+
+    def weight_stream_bytes(self) -> int:
+        return 2 * self.projection().weight_stream_bytes()
+
+
+# The mlp_up shape as the Llama MLP's gate/up pair (the step straight after the single layer).
+PAIRS: Dict[str, PairWorkload] = {p.name: p for p in [
+    PairWorkload("mlp_swiglu", 6, 8192, 4096, 11008, 64, 0.5, 256, 1.0, 0.02, 0.01, 1.0),
+]}
+
+
 def normal_bf16(seed: int, shape, std: float) -> torch.Tensor:
     """float32 standard normals from PCG64(seed), times std (float32), rounded to bf16 (CPU)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -102,6 +160,14 @@ def uniform_f32(seed: int, shape, lo: float, hi: float) -> torch.Tensor:
     """float32 uniforms on [lo, hi) from PCG64(seed) (CPU)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return torch.from_numpy(rng.uniform(lo, hi, size=tuple(shape)).astype(np.float32))
+
+
+def pair_tensor(p: PairWorkload, name: str, rows: int | None = None) -> torch.Tensor:
+    """The named input of pair workload p as a bf16 CPU tensor (rows: X and dH only)."""
+    t = normal_bf16(p.seed(name), p.shape(name), p.std(name))
+    if rows is not None:
+        t = t[:rows].contiguous()
+    return t
 
 
 def tensor(w: Workload, name: str, rows: int | None = None) -> torch.Tensor:
