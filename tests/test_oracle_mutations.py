@@ -8,9 +8,10 @@ live only inside this test (pytest's monkeypatch undoes them).
 import numpy as np
 import pytest
 
-from oracle import nf4, qlora, swiglu
+from oracle import merge, nf4, qlora, swiglu
 from tests import test_oracle_codebook as tc
 from tests import test_oracle_gemm as tg
+from tests import test_oracle_merge as tm
 from tests import test_oracle_quant as tq
 from tests import test_oracle_swiglu as ts
 
@@ -39,6 +40,9 @@ PINS = [
     lambda: ts.test_backward_matches_finite_differences(5, 2.0),
     ts.test_stacked_form_equals_the_pair,
     ts.test_zero_up_projection,
+    tm.test_merged_layer_equals_the_qlora_layer,
+    tm.test_merge_brute_force,
+    tm.test_merge_special_cases,
 ]
 
 _fwd, _bwd = qlora.forward, qlora.backward
@@ -110,6 +114,17 @@ def swiglu_dx_gate_only(dH, X, Wd_g, Wd_u, Ag, Au, Bg, Bu, s):
     Yg, _ = qlora.forward(X, Wd_g, Ag, Bg, s)
     dXu, _, _ = qlora.backward(_f64(dH) * swiglu.silu(Yg), X, Wd_u, Au, Bu, s)
     return dX - dXu, dAg, dAu, dBg, dBu
+
+
+_merge = merge.merge
+
+
+def merge_transposed_product(Wd, A, B, s):
+    return _f64(Wd) + s * (_f64(B)[:, ::-1] @ _f64(A))     # adapter ranks paired in reverse
+
+
+def merge_without_s(Wd, A, B, s):
+    return _merge(Wd, A, B, 1.0)
 
 
 _encode = nf4.encode
@@ -209,6 +224,8 @@ MUTATIONS = {
     "swiglu: gate and up swapped": [(swiglu, "forward", swiglu_gate_up_swapped)],
     "swiglu: dYu uses Yg instead of silu(Yg)": [(swiglu, "backward", swiglu_dyu_without_silu)],
     "swiglu: dX drops the up projection": [(swiglu, "backward", swiglu_dx_gate_only)],
+    "merge pairs ranks in reverse": [(merge, "merge", merge_transposed_product)],
+    "merge drops s": [(merge, "merge", merge_without_s)],
     "encode ties go up": [(nf4, "encode", encode_ties_up)],
     "encode by rounded-to-nearest midpoints": [(nf4, "encode", encode_rne_midpoints)],
     "nibble order swapped": [(nf4, "pack", pack_swapped), (nf4, "unpack", unpack_swapped)],
