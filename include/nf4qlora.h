@@ -193,6 +193,19 @@ int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor 
                      const void *Ygu, const void *Tgu, void *dX, void *dAgu, void *dBg, void *dBu,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* ---- LoRA merge ----------------------------------------------------------------------------
+ * The adapters folded into the base for a merged save [pyshine Unsloth code tour, the save.py
+ * walkthrough; NVFP4 update article, "A More Flexible Quantization Export Pipeline"]:
+ *   Wout bf16 [n, k] = bf16(deq(W) + s B A)       W NF4 [n, k], A bf16 [r, k], B bf16 [n, r]
+ * so that X Wout^T is the layer's X deq(W)^T + s (X A^T) B^T up to the rounding of Wout. One
+ * launch: the rank-r product on the matrix cores, deq(W) = fl32(level * a') added in float32,
+ * rounded once to bf16. With r == 0 (A, B NULL) Wout equals nf4_dequantize's bf16 output bit for
+ * bit. Re-quantising for export is nf4_quantize of Wout (a new NF4 tensor [n, k]).
+ * Errors: NF4_EINVAL for NULL/misaligned pointers or r outside [0, 128]; NF4_EUNSUPPORTED for the
+ * NF4 format limits of nf4_quantize or n*k >= 2^32. */
+int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, float s, void *Wout,
+                void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);
 

@@ -11,6 +11,7 @@ torch fallback: if the library is not built, every call raises.
     qgu = nf4_quantize(torch.cat([Wg, Wu]))           # gate/up pair, stacked [2n, k]
     H, Ygu, Tgu = qlora_swiglu_fwd(X, qgu, Agu, Bg, Bu, s)   # H = silu(Yg) * Yu
     dX, dAgu, dBg, dBu = qlora_swiglu_bwd(dH, X, qgu, Agu, Bg, Bu, s, Ygu, Tgu)
+    W_merged = qlora_merge(q, A, B, s)                # bf16 deq(W) + s B A (requantize=256: NF4)
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ NF4_BF16, NF4_F32 = 0, 1
 EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
             "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
-            "qlora_swiglu_bwd", "nf4_last_error")
+            "qlora_swiglu_bwd", "qlora_merge", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -66,6 +67,7 @@ def library() -> ctypes.CDLL:
         "qlora_bwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
         "qlora_bwd_dx": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
+        "qlora_merge": (ctypes.c_int, [P, vp, vp, i32, f32, vp, vp]),
         "qlora_swiglu_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_swiglu_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_swiglu_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
@@ -269,6 +271,22 @@ def qlora_bwd_dx(dY: torch.Tensor, q: NF4Tensor, U: Optional[torch.Tensor], A: O
     _check(library().qlora_bwd_dx(_ptr(dY), m, ctypes.byref(st), _ptr(U), _ptr(A), r, float(s),
                                   _ptr(dX), _stream(dY.device)))
     return dX
+
+
+def qlora_merge(q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tensor], s: float,
+                requantize: Optional[int] = None):
+    """W' = bf16(deq(W) + s B A) [n, k]; with requantize = dq_block, nf4_quantize(W') instead."""
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, "A", torch.bfloat16, (r, q.k))
+        _need(B, "B", torch.bfloat16, (q.n, r))
+    out = torch.empty(q.n, q.k, dtype=torch.bfloat16, device=q.device)
+    st = q.c_struct()
+    _check(library().qlora_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(s), _ptr(out),
+                                 _stream(q.device)))
+    if requantize is None:
+        return out
+    return nf4_quantize(out, requantize)
 
 
 def _swiglu_args(X, q: NF4Tensor, Agu, Bg, Bu):

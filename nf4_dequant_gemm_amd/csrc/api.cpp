@@ -513,6 +513,23 @@ int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor 
   return ok();
 }
 
+int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, float s, void *Wout,
+                void *stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (W->n * W->k >= (int64_t(1) << 32))
+    return fail(NF4_EUNSUPPORTED, "n*k must be below 2^32 for qlora_merge");
+  if (r < 0 || r > 128) return fail(NF4_EINVAL, "r must lie in [0, 128] (got %d)", r);
+  if (r > 0) {
+    if (!A || !B) return fail(NF4_EINVAL, "A and B must be non-NULL when r > 0");
+    if (!aligned16(A) || !aligned16(B)) return fail(NF4_EINVAL, "A and B must be 16-byte aligned");
+  }
+  if (!Wout || !aligned16(Wout)) return fail(NF4_EINVAL, "Wout must be non-NULL and 16-byte aligned");
+  return hip_status(nf4q::launch_merge(desc(W), (const uint16_t *)A, (const uint16_t *)B, r, s,
+                                       tables(), (uint16_t *)Wout, (hipStream_t)stream),
+                    "qlora_merge launch");
+}
+
 int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,
                  int32_t r, float s, void *dX, void *stream) {
   // dY [m, n] plays the part of X in the layer checks, U [m, r] and A [r, k] that of A and B

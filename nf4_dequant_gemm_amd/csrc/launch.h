@@ -75,4 +75,8 @@ hipError_t launch_blockdiag(const uint16_t *bg, const uint16_t *bu, int64_t n, i
 hipError_t launch_diagblocks(const uint16_t *db2, int64_t n, int r, uint16_t *dbg, uint16_t *dbu,
                              hipStream_t st);
 
+// LoRA merge (merge.hip): out bf16 [n, k] = bf16(deq(W) + s B A), 0 <= r <= 128, k % 64 == 0.
+hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, int r, float s,
+                        const Tables &t, uint16_t *out, hipStream_t st);
+
 }  // namespace nf4q

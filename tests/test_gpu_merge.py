@@ -1,0 +1,63 @@
+"""GPU parity of the LoRA merge (qlora_merge) against the oracle.
+
+W' = bf16(deq(W) + s B A) is compared element by element with the float64 oracle (oracle/merge.py):
+every element within one bf16 unit in the last place of the exact value (one rounding of a
+float32 sum). With r = 0 it equals nf4_dequantize's bf16 output exactly. Re-quantising W' with
+nf4_quantize equals the oracle's quantisation of the same values bit for bit. Shapes are ragged
+against the 64 x 128 tile, ranks span the rank-term padding (1, 5, 16, 33, 64, 128).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import merge, nf4
+from tests.gpu_helpers import assert_quant_equal, f32, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """bf16 spacing at |x| (the normal range; the smallest normal's spacing below it)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+@pytest.mark.parametrize("n,k,r,dq,s", [
+    (64, 128, 16, 256, 2.0),
+    (200, 320, 5, 0, -0.5),
+    (129, 576, 1, 256, 1.0),
+    (70, 1024, 33, 256, 0.25),
+    (256, 256, 64, 0, 1.5),
+    (40, 192, 128, 256, -2.0),
+])
+def test_merge_parity(lib, n, k, r, dq, s):
+    say(f"merge n={n} k={k} r={r} dq={dq} s={s}")
+    W = wl.normal_bf16(500 + n, (n, k), 0.02)
+    A = wl.normal_bf16(501 + n, (r, k), k ** -0.5)
+    B = wl.normal_bf16(502 + n, (n, r), 0.05)
+    qg = lib.nf4_quantize(W.to(DEV), dq)
+    Wm = lib.qlora_merge(qg, A.to(DEV), B.to(DEV), s)
+    q2 = lib.nf4_quantize(Wm, 256)
+    torch.cuda.synchronize()
+    qo = nf4.quantize(W.float().numpy(), dq)
+    assert_quant_equal(qg, qo)
+    ref = merge.merge(nf4.dequantize_f32(qo), f32(A), f32(B), s)
+    got = f32(Wm).astype(np.float64)
+    ulps = np.abs(got - ref) / bf16_ulp(ref)
+    say(f"  max error {ulps.max():.3f} bf16 ulp")
+    assert ulps.max() <= 1.0
+    # re-quantised merged weight: bit for bit the oracle's quantisation of the same values
+    assert_quant_equal(q2, nf4.quantize(f32(Wm), 256))
+
+
+def test_merge_rank_zero_equals_dequantize(lib):
+    W = wl.normal_bf16(610, (136, 448), 0.02)
+    for dq in (0, 256):
+        qg = lib.nf4_quantize(W.to(DEV), dq)
+        Wm = lib.qlora_merge(qg, None, None, 3.0)
+        Wd = lib.nf4_dequantize(qg, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(f32(Wm), f32(Wd))

@@ -177,6 +177,21 @@ def test_swiglu_calls_reject_bad_arguments():
     assert bwd(T=None, wsb=wsb - 1) == m.NF4_EINVAL          # Tgu may be NULL, ws still checked
 
 
+def test_merge_rejects_bad_arguments():
+    lib = m.library()
+    q = wdesc(n=64, k=128)
+    mg = lambda **kw: lib.qlora_merge(ctypes.byref(kw.get("q", q)), kw.get("A", FAKE), kw.get("B", FAKE),
+                                       kw.get("r", 8), 1.0, kw.get("W", FAKE), None)
+    assert mg(W=None) == m.NF4_EINVAL
+    assert mg(W=ctypes.c_void_p(4104)) == m.NF4_EINVAL
+    assert mg(A=None) == m.NF4_EINVAL
+    assert mg(B=ctypes.c_void_p(4098)) == m.NF4_EINVAL
+    assert mg(r=129) == m.NF4_EINVAL
+    assert mg(r=-1) == m.NF4_EINVAL
+    assert mg(q=wdesc(n=64, k=100)) == m.NF4_EUNSUPPORTED
+    assert mg(q=wdesc(n=1 << 20, k=1 << 12)) == m.NF4_EUNSUPPORTED      # n*k = 2^32
+
+
 def test_workspace_sizes_are_consistent():
     lib = m.library()
     assert lib.qlora_fwd_workspace_bytes(100, 64, 128, 0) == 0
