@@ -240,6 +240,25 @@ def run_weight_stream(dev, steps, warmup):
     return out
 
 
+def run_merge(L, steps, warmup):
+    """LoRA merge of the workload's weight (qlora_merge, W' = bf16(deq(W) + s B A)), cold weights:
+    bytes moved (weight stream + A, B read; W' written) / HIP-event time, against HBM."""
+    import torch
+    w, c = L.w, L.c
+    out = torch.empty(w.N, w.K, dtype=torch.bfloat16, device=L.X.device)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def fn(i):
+        L.check(c.qlora_merge(ctypes.byref(L.qs[i % len(L.qs)]), P(L.A), P(L.B), w.r, w.s, P(out), L.sp))
+    t = time_call(L, fn, steps, warmup)
+    nbytes = w.weight_stream_bytes() + 2 * w.r * w.K + 2 * w.N * w.r + 2 * w.N * w.K
+    gbs = nbytes / (t["median"] * 1e-3) / 1e9
+    del out
+    return {"what": f"qlora_merge of the {w.name} weight [{w.N},{w.K}], r={w.r}: W' = bf16(deq(W) + s B A)",
+            "us": round(t["median"] * 1e3, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def run_cpu_baseline(w, target_s):
     """The oracle (float64 numpy/BLAS) on a row sample of the same step."""
     from threadpoolctl import threadpool_info
@@ -538,6 +557,7 @@ def main():
     step_ms, per = time_layer(L, args.steps, args.warmup)
     whole_fwd = time_call(L, L.fwd_whole, args.steps, args.warmup) if not w.backward else None
     ncopies = len(L.copies)
+    merge = run_merge(L, args.steps, args.warmup) if w.M > 64 else None
     context = None if args.no_context else run_context(L)
     del L
     torch.cuda.empty_cache()
@@ -572,6 +592,8 @@ def main():
                    "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}},
         "roofline": roof,
     }
+    if merge:
+        out["merge"] = merge
     if whole_fwd:
         out["config"]["qlora_fwd_ms"] = {q: round(x, 4) for q, x in whole_fwd.items()}
         if M <= 64:

@@ -3,13 +3,15 @@
 // [pyshine Unsloth code tour, the save.py walkthrough: merged saves, LoRA weights merged layer by
 // layer; NVFP4 update article, "A More Flexible Quantization Export Pipeline"].
 //
-// One workgroup (4 waves) owns a 64 (n) x 128 (k) tile of W'. The rank-r product B A runs on the
+// One workgroup (4 waves) owns a 32 (n) x 128 (k) tile of W'. The rank-r product B A runs on the
 // matrix cores with MFMA 16x16x32 over r (zero-padded to a multiple of 32): A [r, k] is staged in
 // LDS row-major and read with the transposing LDS load ds_read_b64_tr_b16 (each lane receives 4
 // consecutive rows r of one column k, the operand layout with r as the reduction index), B [n, r]
-// is staged row-major and read 16 bytes per lane. With A as the first operand, a lane holds 4
-// consecutive columns k of one row n; it adds fl32(level * a') of those 4 elements (the codes, the
-// block constant and a 16-entry level table in LDS) to s times the fp32 sum, rounds to bf16 and
+// is staged row-major and read 16 bytes per lane. The tile's codes (one 16-byte load per thread)
+// and its block constants are staged in LDS as well: loaded per lane, 2 bytes at a time, they
+// made the kernel request-bound (1.35 TB/s). With A as the first operand, a lane holds 4
+// consecutive columns k of one row n; it adds fl32(level * a') of those 4 elements (codes, block
+// constant and a 16-entry level table from LDS) to s times the fp32 sum, rounds to bf16 and
 // stages the tile in LDS, from which rows leave in 16-byte pieces. The work is the weight stream:
 // 0.52 bytes read and 2 bytes written per element.
 #include "common.h"
@@ -18,9 +20,9 @@
 namespace nf4q {
 namespace {
 
-constexpr int kTN = 64, kTK = 128, kThreads = 256;
+constexpr int kTN = 32, kTK = 128, kThreads = 256;
+constexpr int kNT = kTN / 16;     // 16-row MFMA tiles per workgroup tile
 constexpr int kMaxR = 128;
-constexpr int kBStride = kMaxR + 8;   // bf16 per staged B row (16 bytes of padding)
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 __device__ __forceinline__ s16x4 lds_tr16(const uint16_t *p) {
@@ -35,17 +37,41 @@ __device__ __forceinline__ int aunit(int j, int u) {
 __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, int r,
                                                          float s, Tables t, uint16_t *__restrict__ out) {
-  __shared__ __align__(16) uint16_t sA[kMaxR * kTK];
-  __shared__ __align__(16) uint16_t sB[kTN * kBStride];
-  __shared__ __align__(16) uint16_t sO[kTN * kTK];
-  __shared__ float sLv[16];
+  // LDS sized to the rank (dynamic): the output tile, codes, block constants and levels, then A
+  // (rp rows of 128 columns) and B (32 rows of rp + 8 ranks); 21 KB at r <= 32, seven workgroups
+  // per CU. The kernel is latency-bound (each workgroup loads, computes and stores in turn), so
+  // occupancy sets its rate: on a 4096 x 14336 weight, r = 32, a fixed 128-rank layout with 64-row
+  // tiles (2 workgroups per CU) ran 93 us, rank-sized 64-row tiles 64 us, 32-row tiles 61 us.
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int rp = (r + 31) / 32 * 32;
+  const int bstride = rp + 8;
+  uint16_t *sO = reinterpret_cast<uint16_t *>(smem);                    // kTN * kTK bf16
+  uint8_t *sC = smem + kTN * kTK * 2;                                    // kTN * kTK / 2 bytes
+  float *sAbs = reinterpret_cast<float *>(sC + kTN * kTK / 2);          // 2 per row
+  float *sLv = sAbs + kTN * kTK / 64;                                    // 16 levels
+  uint16_t *sA = reinterpret_cast<uint16_t *>(sLv + 16);                 // rp * kTK bf16
+  uint16_t *sB = sA + rp * kTK;                                          // kTN * bstride bf16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int64_t N = w.n, K = w.k;
   const int64_t n0 = (int64_t)blockIdx.y * kTN, k0 = (int64_t)blockIdx.x * kTK;
-  const int rp = (r + 31) / 32 * 32;
   if (tid < 16) sLv[tid] = t.level[tid];
-  // stage A rows 0 .. rp-1, columns k0 .. k0+127 (zero past r and past K) and B rows n0 .. n0+63,
+  // the tile's codes (one 16-byte load per thread of the first 128; rows past N read as zero) and
+  // block constants
+  {
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(w.codes, N * K / 2);
+    const int row = tid >> 2, piece = tid & 3;
+    const int64_t n = n0 + row;
+    const uint32_t off = row < kTN && n < N ? (uint32_t)((n * K + k0) / 2 + 16 * piece) : 0x80000000u;
+    if (row < kTN)
+      *reinterpret_cast<u32x4 *>(sC + row * (kTK / 2) + 16 * piece) =
+          __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
+    if (tid < kTN * kTK / 64) {
+      const int64_t bn = n0 + (tid >> 1), bk = k0 + 64 * (tid & 1);
+      sAbs[tid] = (bn < N && bk < K) ? block_absmax(w, (bn * K + bk) / 64) : 0.f;
+    }
+  }
+  // stage A rows 0 .. rp-1, columns k0 .. k0+127 (zero past r and past K) and B rows n0 .. n0+31,
   // ranks 0 .. rp-1 (zero past r and past N), 16 bytes at a time
   for (int i = tid; i < rp * (kTK / 8); i += kThreads) {
     const int j = i / (kTK / 8), c = i % (kTK / 8);
@@ -70,16 +96,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
         v = make_uint4(e[0], e[1], e[2], e[3]);
       }
     }
-    *reinterpret_cast<uint4 *>(sB + row * kBStride + 8 * c) = v;
+    *reinterpret_cast<uint4 *>(sB + row * bstride + 8 * c) = v;
   }
   __syncthreads();
 
-  // wave w: columns 32 w .. 32 w + 31 (2 tiles of 16) x rows 0 .. 63 (4 tiles of 16)
-  f32x4 acc[2][4];
+  // wave w: columns 32 w .. 32 w + 31 (2 tiles of 16) x the tile's rows (kNT tiles of 16)
+  f32x4 acc[2][kNT];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kNT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int ks = 0; ks < rp / 32; ++ks) {
     bf16x8 af[2];
 #pragma unroll
@@ -92,28 +118,28 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
       af[kt] = __builtin_bit_cast(bf16x8, v8);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
       const bf16x8 bf = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4 *>(sB + (16 * nt + l16) * kBStride + 32 * ks + 8 * g16));
+          bf16x8, *reinterpret_cast<const uint4 *>(sB + (16 * nt + l16) * bstride + 32 * ks + 8 * g16));
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) acc[kt][nt] = mfma16x16x32(af[kt], bf, acc[kt][nt]);
     }
   }
 
   // lane: row n = n0 + 16 nt + l16, columns k .. k+3 with k = k0 + 32 w + 16 kt + 4 g16
-  const __amdgpu_buffer_rsrc_t rC = make_rsrc(w.codes, N * K / 2);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t n = n0 + 16 * nt + l16;
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int row = 16 * nt + l16;
+    const int64_t n = n0 + row;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int kk = 32 * wave + 16 * kt + 4 * g16;
       const int64_t k = k0 + kk;
       uint32_t o[2] = {0, 0};
       if (n < N && k < K) {
-        const int64_t e0 = n * K + k;                 // even: codes of k, k+1 in one byte
-        const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b16(rC, (uint32_t)(e0 / 2), 0, 0);
-        const float a = block_absmax(w, e0 / 64);
+        // codes of k .. k+3 (two bytes, high nibble first) and the constant of their block
+        const uint32_t cw = *reinterpret_cast<const uint16_t *>(sC + row * (kTK / 2) + kk / 2);
+        const float a = sAbs[2 * row + kk / 64];
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -144,7 +170,15 @@ hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, in
                         const Tables &t, uint16_t *out, hipStream_t st) {
   if (r < 0 || r > kMaxR || w.k % 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((w.k + kTK - 1) / kTK), (unsigned)((w.n + kTN - 1) / kTN));
-  merge_kernel<<<grid, dim3(kThreads), 0, st>>>(w, A, B, r, s, t, out);
+  const int rp = (r + 31) / 32 * 32;
+  const size_t lds = (size_t)kTN * kTK * 2 + kTN * kTK / 2 + 4 * (kTN * kTK / 64 + 16) +
+                     2 * ((size_t)rp * kTK + (size_t)kTN * (rp + 8));
+  if (lds > 65536) {   // above the default dynamic-LDS limit: opt in (gfx950 has 160 KB per CU)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(merge_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  merge_kernel<<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
   return hipGetLastError();
 }
 
