@@ -61,3 +61,23 @@ def test_merge_rank_zero_equals_dequantize(lib):
         Wd = lib.nf4_dequantize(qg, torch.bfloat16)
         torch.cuda.synchronize()
         assert np.array_equal(f32(Wm), f32(Wd))
+
+
+def test_merge_full_size_down_weight(lib):
+    """The merge bench.py times: the down workload's weight [4096, 14336], r = 32, s = 1, on
+    sampled rows (all columns) against the oracle, within one bf16 ulp."""
+    from tests.test_gpu_workloads import sample
+    w = wl.WORKLOADS["down"]
+    W, A, B = wl.tensor(w, "W"), wl.tensor(w, "A"), wl.tensor(w, "B")
+    qg = lib.nf4_quantize(W.to(DEV), w.dq_block)
+    Wm = lib.qlora_merge(qg, A.to(DEV), B.to(DEV), w.s)
+    torch.cuda.synchronize()
+    qo = nf4.quantize(W.float().numpy(), w.dq_block)
+    assert_quant_equal(qg, qo)
+    rows = sample(w.N, 64, 55)
+    Wd = nf4.dequantize_f32(qo)
+    ref = merge.merge(Wd[rows], f32(A), f32(B)[rows], w.s)
+    got = f32(Wm[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    ulps = np.abs(got - ref) / bf16_ulp(ref)
+    say(f"  full-size merge: max error {ulps.max():.3f} bf16 ulp")
+    assert ulps.max() <= 1.0
