@@ -8,10 +8,11 @@ live only inside this test (pytest's monkeypatch undoes them).
 import numpy as np
 import pytest
 
-from oracle import merge, nf4, qlora, swiglu
+from oracle import merge, moe, nf4, qlora, swiglu
 from tests import test_oracle_codebook as tc
 from tests import test_oracle_gemm as tg
 from tests import test_oracle_merge as tm
+from tests import test_oracle_moe as to
 from tests import test_oracle_quant as tq
 from tests import test_oracle_swiglu as ts
 
@@ -43,6 +44,10 @@ PINS = [
     tm.test_merged_layer_equals_the_qlora_layer,
     tm.test_merge_brute_force,
     tm.test_merge_special_cases,
+    to.test_one_expert_is_the_single_layer,
+    to.test_brute_force_rows,
+    to.test_empty_expert,
+    to.test_expert_reordering,
 ]
 
 _fwd, _bwd = qlora.forward, qlora.backward
@@ -125,6 +130,31 @@ def merge_transposed_product(Wd, A, B, s):
 
 def merge_without_s(Wd, A, B, s):
     return _merge(Wd, A, B, 1.0)
+
+
+_mfwd, _mbwd = moe.forward, moe.backward
+
+
+def moe_next_experts_weights(X, counts, Wd, A, B, s):
+    E = len(counts)
+    N = _f64(Wd).shape[0] // E
+    return _mfwd(X, counts, np.roll(_f64(Wd), -N, axis=0), A, B, s)
+
+
+def moe_offsets_shifted(counts):
+    off = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
+    off[1:-1] += 1
+    return np.minimum(off, off[-1])
+
+
+def moe_db_over_all_rows(dY, X, counts, Wd, A, B, s):
+    dX, dA, dB = _mbwd(dY, X, counts, Wd, A, B, s)
+    E = len(counts)
+    N, r = _f64(Wd).shape[0] // E, _f64(A).shape[0] // E
+    T = _f64(X) @ _f64(A)[:r].T
+    dB = dB.copy()
+    dB[:N] = s * _f64(dY).T @ T
+    return dX, dA, dB
 
 
 _encode = nf4.encode
@@ -226,6 +256,9 @@ MUTATIONS = {
     "swiglu: dX drops the up projection": [(swiglu, "backward", swiglu_dx_gate_only)],
     "merge pairs ranks in reverse": [(merge, "merge", merge_transposed_product)],
     "merge drops s": [(merge, "merge", merge_without_s)],
+    "moe: rows use the next expert's weight": [(moe, "forward", moe_next_experts_weights)],
+    "moe: expert boundaries shifted by a row": [(moe, "offsets", moe_offsets_shifted)],
+    "moe: dB summed over every row": [(moe, "backward", moe_db_over_all_rows)],
     "encode ties go up": [(nf4, "encode", encode_ties_up)],
     "encode by rounded-to-nearest midpoints": [(nf4, "encode", encode_rne_midpoints)],
     "nibble order swapped": [(nf4, "pack", pack_swapped), (nf4, "unpack", unpack_swapped)],
