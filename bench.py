@@ -28,7 +28,9 @@ matrix-core-bound shapes, a device copy for the HBM-bound one.
                     [--no-weight-stream] [--copy-calibration]
 
 --workload mlp_swiglu measures the gate/up SwiGLU pair instead (a step: qlora_swiglu_fwd +
-qlora_swiglu_bwd on the mlp_up shape, two projections).
+qlora_swiglu_bwd on the mlp_up shape, two projections); --workload moe_mlp_up the grouped
+mixture-of-experts layer (a step: qlora_moe_fwd + qlora_moe_bwd, 8 experts of the mlp_up shape,
+16384 routed rows).
 """
 from __future__ import annotations
 
@@ -402,6 +404,140 @@ def run_pair(args, pw, dev):
     print(json.dumps(out), flush=True)
 
 
+def run_moe(args, mw, dev):
+    """The grouped MoE layer (qlora_moe_fwd + qlora_moe_bwd per step) on MoE workload mw."""
+    import torch
+    import nf4_dequant_gemm_amd as lib
+    import workloads as wl
+    c = lib.library()
+    E, M, K, N, r, s = mw.E, mw.M, mw.K, mw.N, mw.r, mw.s
+    counts = mw.counts()
+    cnt = (ctypes.c_int64 * E)(*counts)
+    host = {t: wl.moe_tensor(mw, t) for t in ("X", "W", "A", "B", "dY")}
+    d = {t: v.to(dev) for t, v in host.items() if t != "W"}
+    q = lib.nf4_quantize(host["W"].to(dev), mw.dq_block)
+    del host
+    ncopies = args.wcopies or max(1, min(64, math.ceil(COLD_BYTES / mw.weight_stream_bytes())))
+    copies = [q] + [q.clone() for _ in range(ncopies - 1)]
+    qs = [x.c_struct() for x in copies]
+    bf = torch.bfloat16
+    Y = torch.empty(M, N, dtype=bf, device=dev)
+    T = torch.empty(M, r, dtype=bf, device=dev)
+    dX = torch.empty(M, K, dtype=bf, device=dev)
+    dA = torch.empty(E * r, K, dtype=bf, device=dev)
+    dB = torch.empty(E * N, r, dtype=bf, device=dev)
+    wsb = c.qlora_moe_workspace_bytes(cnt, E, N, K, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(c.nf4_last_error().decode())
+
+    def fwd(i):
+        check(c.qlora_moe_fwd(P(d["X"]), cnt, E, ctypes.byref(qs[i % ncopies]), P(d["A"]), P(d["B"]), r, s,
+                              P(Y), P(T), P(ws), wsb, sp))
+
+    def bwd(i):
+        check(c.qlora_moe_bwd(P(d["dY"]), P(d["X"]), cnt, E, ctypes.byref(qs[i % ncopies]), P(d["A"]),
+                              P(d["B"]), r, s, P(T), P(dX), P(dA), P(dB), P(ws), wsb, sp))
+
+    calls = (fwd, bwd)
+    for i in range(args.warmup):
+        for f in calls:
+            f(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        ev[st][0].record(stream)
+        for j, f in enumerate(calls):
+            f(args.warmup + st)
+            ev[st][j + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {}
+    for j, name in enumerate(("moe_fwd", "moe_bwd")):
+        v = [ev[st][j].elapsed_time(ev[st][j + 1]) for st in range(args.steps)]
+        per[name] = {"mean": sum(v) / len(v), "median": pct(v, 0.5), "p10": pct(v, 0.1), "p90": pct(v, 0.9)}
+
+    # The dominant forward launch: the grouped fused kernel (every expert's tiles), given T.
+    def fused(i):
+        check(c.qlora_moe_fwd_fused(P(d["X"]), cnt, E, ctypes.byref(qs[i % ncopies]), P(T), P(d["B"]), r, s,
+                                    P(Y), sp))
+    t = time_call(types.SimpleNamespace(stream=stream), fused, args.steps, args.warmup)
+    work = 2 * M * N * K + 2 * M * N * r
+    achieved = work / (t["median"] * 1e-3) / 1e12
+    roof = {"kernel": "qlora_moe_fwd_fused (grouped)", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in t.items()}, "traffic": None}
+    context = None
+    if not args.no_context:
+        Wd = lib.nf4_dequantize(q, torch.bfloat16)[:N]
+        context = {"mfma_loop": run_mfma_loop(Wd, d["X"])}
+        roof["frac_of_mfma_loop"] = round(achieved / context["mfma_loop"]["TFLOP/s"], 4)
+        del Wd
+    del copies, qs, d, Y, T, dX, dA, dB, ws
+    torch.cuda.empty_cache()
+    flops = mw.fwd_flops() + mw.bwd_flops()
+    out = {
+        "metric": METRIC, "value": round(flops / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{mw.name}: {E} experts, {mw.tokens} tokens x top-{mw.top_k} = {M} rows "
+                               f"grouped by expert, X [{M},{K}] bf16, W NF4 [{E}x{N},{K}] double-quant "
+                               f"int8/256, LoRA r={r} per expert s={s}, fwd+bwd",
+                   "E": E, "M": M, "K": K, "N": N, "r": r, "counts": counts, "weight_copies": ncopies,
+                   "phase_ms": {k: {x: round(y, 4) for x, y in v.items()} for k, v in per.items()}},
+        "roofline": roof,
+    }
+    if context:
+        out["context"] = context
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_moe_cpu_baseline(mw, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def run_moe_cpu_baseline(mw, target_s):
+    """The oracle's grouped layer (float64) on a sample: the first rows of every expert's group,
+    in proportion to its count."""
+    from threadpoolctl import threadpool_info
+
+    import numpy as np
+    import workloads as wl
+    from oracle import moe, nf4
+    counts = mw.counts()
+    off = moe.offsets(counts)
+    Wd = nf4.dequantize_f32(nf4.quantize(wl.moe_tensor(mw, "W").float().numpy(), mw.dq_block))
+    A, B = wl.moe_tensor(mw, "A").float().numpy(), wl.moe_tensor(mw, "B").float().numpy()
+    Xall, dYall = wl.moe_tensor(mw, "X").float().numpy(), wl.moe_tensor(mw, "dY").float().numpy()
+
+    def step(frac):
+        cs = [int(c * frac) for c in counts]
+        rows = np.concatenate([np.arange(off[e], off[e] + cs[e]) for e in range(mw.E)])
+        X, dY = Xall[rows], dYall[rows]
+        t = time.perf_counter()
+        moe.forward(X, cs, Wd, A, B, mw.s)
+        moe.backward(dY, X, cs, Wd, A, B, mw.s)
+        return time.perf_counter() - t, sum(cs)
+
+    frac = 64 / mw.M * mw.E
+    dt, rows = step(frac)
+    while dt < 0.4 * target_s and frac < 1:
+        frac = min(1.0, max(2 * frac, frac * target_s / max(dt, 1e-3)))
+        dt, rows = step(frac)
+    flops = (mw.fwd_flops() + mw.bwd_flops()) * rows / mw.M
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "wall_s": round(dt, 2),
+            "sample": f"{rows} of {mw.M} rows of the {mw.name} layer (the first rows of each expert's group, "
+                      f"in proportion), forward+backward in float64 (numpy/BLAS), {dt:.1f}s wall; the weights "
+                      f"dequantised once outside the timing"}
+
+
 def run_pair_cpu_baseline(pw, target_s):
     """The oracle's gate/up pair (float64) on a row sample of the same step."""
     from threadpoolctl import threadpool_info
@@ -551,6 +687,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload in wl.PAIRS:
         run_pair(args, wl.PAIRS[args.workload], dev)
+        return
+    if args.workload in wl.MOES:
+        run_moe(args, wl.MOES[args.workload], dev)
         return
     w = wl.WORKLOADS[args.workload]
     L = Layer(w, dev, args.wcopies)

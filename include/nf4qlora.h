@@ -206,6 +206,43 @@ int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor 
 int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, float s, void *Wout,
                 void *stream);
 
+/* ---- Grouped (mixture-of-experts) layer -------------------------------------------------------
+ * E experts (1 <= E <= 64), each a QLoRA layer with its own frozen NF4 base and adapters
+ * [NVFP4 update article, "Comprehensive Improvements in Training Performance and Stability":
+ * grouped MoE, LoRA on the experts' MLP layers; pyshine Unsloth code tour, "Why You Need This":
+ * the grouped-GEMM interface for MoE experts]. The routing is given: the rows of X (and of Y, T,
+ * dY, dX) are grouped by expert in expert order, counts[e] >= 0 of them for expert e (a HOST
+ * array of E values), and
+ *   Y[rows of e] = X[rows of e] deq(W_e)^T + s (X[rows of e] A_e^T) B_e^T.
+ * The experts' tensors are stacked in expert order: W ONE NF4 tensor [E n, k] (quantised from the
+ * stacked bf16 weights), A bf16 [E r, k], B bf16 [E n, r]; T bf16 [sum(counts), r].
+ *
+ * Bytes of device workspace qlora_moe_fwd and qlora_moe_bwd need for these counts. */
+size_t qlora_moe_workspace_bytes(const int64_t *counts, int32_t E, int64_t n, int64_t k, int32_t r);
+
+/* Forward: T (per expert rows, one row projection per expert with rows) and Y [sum(counts), n]
+ * in ONE launch of the fused kernel for all experts (each workgroup finds its expert's rows and
+ * weight). T must be non-NULL when r > 0. Errors: as qlora_fwd; NF4_EINVAL also for E out of
+ * range, a negative count, W->n not a multiple of E. */
+int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                  const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* The grouped fused launch alone, given T [sum(counts), r] (NULL when r == 0): what qlora_moe_fwd
+ * runs after its row projections. No workspace. Errors: as qlora_moe_fwd. */
+int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                        const void *T, const void *B, int32_t r, float s, void *Y, void *stream);
+
+/* Backward for dY [sum(counts), n]: dX [sum(counts), k] (skipped when NULL), dA [E r, k] and
+ * dB [E n, r], each expert's adapter gradients summed over its own rows (zero for an expert with
+ * no rows); T from the forward or NULL (recomputed). dX of every expert comes from ONE launch of
+ * the fused dX kernel; U = dY_e B_e, dA and dB are per-expert launches of the layer's kernels.
+ * Errors: as qlora_bwd and qlora_moe_fwd. */
+int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
+                  const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
+                  const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
+                  void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);
 

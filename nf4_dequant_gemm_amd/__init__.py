@@ -12,6 +12,7 @@ torch fallback: if the library is not built, every call raises.
     H, Ygu, Tgu = qlora_swiglu_fwd(X, qgu, Agu, Bg, Bu, s)   # H = silu(Yg) * Yu
     dX, dAgu, dBg, dBu = qlora_swiglu_bwd(dH, X, qgu, Agu, Bg, Bu, s, Ygu, Tgu)
     W_merged = qlora_merge(q, A, B, s)                # bf16 deq(W) + s B A (requantize=256: NF4)
+    Y, T = qlora_moe_fwd(X, counts, qe, Ae, Be, s)    # experts: rows grouped, tensors stacked
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ NF4_BF16, NF4_F32 = 0, 1
 EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
             "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
-            "qlora_swiglu_bwd", "qlora_merge", "nf4_last_error")
+            "qlora_swiglu_bwd", "qlora_merge", "qlora_moe_workspace_bytes", "qlora_moe_fwd",
+            "qlora_moe_fwd_fused", "qlora_moe_bwd", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -68,6 +70,10 @@ def library() -> ctypes.CDLL:
         "qlora_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
         "qlora_bwd_dx": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
         "qlora_merge": (ctypes.c_int, [P, vp, vp, i32, f32, vp, vp]),
+        "qlora_moe_workspace_bytes": (sz, [vp, i32, i64, i64, i32]),
+        "qlora_moe_fwd": (ctypes.c_int, [vp, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_moe_fwd_fused": (ctypes.c_int, [vp, vp, i32, P, vp, vp, i32, f32, vp, vp]),
+        "qlora_moe_bwd": (ctypes.c_int, [vp, vp, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
         "qlora_swiglu_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_swiglu_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_swiglu_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
@@ -287,6 +293,78 @@ def qlora_merge(q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tenso
     if requantize is None:
         return out
     return nf4_quantize(out, requantize)
+
+
+def _moe_args(X, counts, q: NF4Tensor, A, B):
+    E = len(counts)
+    if E < 1 or q.n % E:
+        raise ValueError("the stacked weight must hold E*n rows for E = len(counts) experts")
+    n = q.n // E
+    r = 0 if A is None else A.shape[0] // E
+    M = int(sum(counts))
+    _need(X, "X", torch.bfloat16, (M, q.k))
+    if r:
+        _need(A, "A", torch.bfloat16, (E * r, q.k))
+        _need(B, "B", torch.bfloat16, (E * n, r))
+    c = (ctypes.c_int64 * E)(*[int(x) for x in counts])
+    return E, n, r, M, c
+
+
+def qlora_moe_fwd(X: torch.Tensor, counts, q: NF4Tensor, A: Optional[torch.Tensor],
+                  B: Optional[torch.Tensor], s: float):
+    """(Y, T) of the grouped layer: rows of X grouped by expert (counts[e] rows for expert e), q the
+    stacked NF4 weight [E*n, k], A [E*r, k], B [E*n, r]; T is None when r == 0."""
+    E, n, r, M, c = _moe_args(X, counts, q, A, B)
+    dev = X.device
+    Y = torch.empty(M, n, dtype=torch.bfloat16, device=dev)
+    T = torch.empty(M, r, dtype=torch.bfloat16, device=dev) if r else None
+    lib = library()
+    wsb = lib.qlora_moe_workspace_bytes(c, E, n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.c_struct()
+    _check(lib.qlora_moe_fwd(_ptr(X), c, E, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
+                             _ptr(T), _ptr(ws), wsb, _stream(dev)))
+    return Y, T
+
+
+def qlora_moe_fwd_fused(X: torch.Tensor, counts, q: NF4Tensor, T: Optional[torch.Tensor],
+                        B: Optional[torch.Tensor], s: float) -> torch.Tensor:
+    """Y of the grouped layer in one launch, given T (the experts' X_e A_e^T, rows grouped)."""
+    E = len(counts)
+    if E < 1 or q.n % E:
+        raise ValueError("the stacked weight must hold E*n rows for E = len(counts) experts")
+    n, M = q.n // E, int(sum(counts))
+    r = 0 if T is None else T.shape[1]
+    _need(X, "X", torch.bfloat16, (M, q.k))
+    if r:
+        _need(T, "T", torch.bfloat16, (M, r))
+        _need(B, "B", torch.bfloat16, (E * n, r))
+    c = (ctypes.c_int64 * E)(*[int(x) for x in counts])
+    Y = torch.empty(M, n, dtype=torch.bfloat16, device=X.device)
+    st = q.c_struct()
+    _check(library().qlora_moe_fwd_fused(_ptr(X), c, E, ctypes.byref(st), _ptr(T), _ptr(B), r, float(s),
+                                         _ptr(Y), _stream(X.device)))
+    return Y
+
+
+def qlora_moe_bwd(dY: torch.Tensor, X: torch.Tensor, counts, q: NF4Tensor, A: Optional[torch.Tensor],
+                  B: Optional[torch.Tensor], s: float, T: Optional[torch.Tensor], need_dx: bool = True):
+    """(dX, dA, dB) of the grouped layer; dA [E*r, k], dB [E*n, r] (None when r == 0)."""
+    E, n, r, M, c = _moe_args(X, counts, q, A, B)
+    _need(dY, "dY", torch.bfloat16, (M, n))
+    if r and T is not None:
+        _need(T, "T", torch.bfloat16, (M, r))
+    dev = X.device
+    dX = torch.empty(M, q.k, dtype=torch.bfloat16, device=dev) if need_dx else None
+    dA = torch.empty(E * r, q.k, dtype=torch.bfloat16, device=dev) if r else None
+    dB = torch.empty(E * n, r, dtype=torch.bfloat16, device=dev) if r else None
+    lib = library()
+    wsb = lib.qlora_moe_workspace_bytes(c, E, n, q.k, r)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.c_struct()
+    _check(lib.qlora_moe_bwd(_ptr(dY), _ptr(X), c, E, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s),
+                             _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(dev)))
+    return dX, dA, dB
 
 
 def _swiglu_args(X, q: NF4Tensor, Agu, Bg, Bu):

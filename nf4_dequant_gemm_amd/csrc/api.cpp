@@ -245,6 +245,77 @@ int check_swiglu(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Ag
   return NF4_OK;
 }
 
+// Mixture of experts: E experts, counts[e] rows each (grouped in expert order), stacked tensors
+// W [E n, k], A [E r, k], B [E n, r].
+struct Moe {
+  int64_t off[nf4q::kMaxExperts + 1];
+  int64_t n = 0, mtotal = 0;
+};
+
+int check_moe(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W, const void *A,
+              const void *B, int32_t r, Moe *mo) {
+  if (E < 1 || E > nf4q::kMaxExperts)
+    return fail(NF4_EINVAL, "E must lie in [1, %d] (got %d)", nf4q::kMaxExperts, E);
+  if (!counts) return fail(NF4_EINVAL, "counts is NULL");
+  int st = check_weight(W);
+  if (st) return st;
+  if (W->n % E) return fail(NF4_EINVAL, "W must hold E*n rows (got %lld for E = %d)", (long long)W->n, E);
+  mo->n = W->n / E;
+  if (mo->n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)mo->n);
+  mo->off[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    if (counts[e] < 0) return fail(NF4_EINVAL, "counts[%d] is negative", e);
+    mo->off[e + 1] = mo->off[e] + counts[e];
+  }
+  mo->mtotal = mo->off[E];
+  st = check_layer(X, mo->mtotal, W, A, B, r);   // m >= 1, the GEMM limits, X, A, B
+  if (st) return st;
+  return NF4_OK;
+}
+
+// Workspace of the grouped layer. Forward: the largest expert's row-projection partials.
+// Backward: U [sum(counts), r] at 0, the transposed stacked B [r, E n] at u, T (recomputed when
+// the caller passes none) at u + bt, then the largest expert's partials (experts run in stream
+// order, so they share them).
+struct MoeWs {
+  size_t u = 0, bt = 0, t = 0, part = 0, total = 0;
+};
+
+MoeWs moe_ws_layout(const Moe &mo, int32_t E, int64_t k, int32_t r) {
+  MoeWs w;
+  if (r <= 0) return w;
+  w.u = align256((size_t)mo.mtotal * r * 2);
+  w.bt = align256((size_t)r * E * mo.n * 2);
+  w.t = w.u;
+  for (int e = 0; e < E; ++e) {
+    const int64_t me = mo.off[e + 1] - mo.off[e];
+    if (me < 1) continue;
+    w.part = std::max(w.part, fwd_ws(me, k, r).part);
+    w.part = std::max(w.part, bwd_ws(me, mo.n, k, r).part);
+  }
+  w.total = w.u + w.bt + w.t + w.part;
+  return w;
+}
+
+size_t moe_ws(const Moe &mo, int32_t E, int64_t k, int32_t r) {
+  return moe_ws_layout(mo, E, k, r).total;
+}
+
+// Groups of the grouped launches: experts' row offsets and the first tile of each expert (its
+// rows in 256-row blocks times `tiles_c` column tiles).
+int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr) {
+  gr->E = E;
+  gr->tile_off[0] = 0;
+  for (int e = 0; e <= E; ++e) gr->m_off[e] = mo.off[e];
+  for (int e = 0; e < E; ++e) {
+    const int64_t me = mo.off[e + 1] - mo.off[e];
+    const int64_t t = gr->tile_off[e] + (me + 255) / 256 * tiles_c;
+    if (t >= (int64_t(1) << 31)) return fail(NF4_EUNSUPPORTED, "too many tiles");
+    gr->tile_off[e + 1] = (int32_t)t;
+  }
+  return NF4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -528,6 +599,163 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
   return hip_status(nf4q::launch_merge(desc(W), (const uint16_t *)A, (const uint16_t *)B, r, s,
                                        tables(), (uint16_t *)Wout, (hipStream_t)stream),
                     "qlora_merge launch");
+}
+
+size_t qlora_moe_workspace_bytes(const int64_t *counts, int32_t E, int64_t n, int64_t k, int32_t r) {
+  if (!counts || E < 1 || E > nf4q::kMaxExperts || n < 1 || k < 1 || r < 0) return 0;
+  Moe mo;
+  mo.n = n;
+  mo.off[0] = 0;
+  for (int e = 0; e < E; ++e) mo.off[e + 1] = mo.off[e] + std::max<int64_t>(counts[e], 0);
+  mo.mtotal = mo.off[E];
+  return moe_ws(mo, E, k, r);
+}
+
+int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                        const void *T, const void *B, int32_t r, float s, void *Y, void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, T, B, r, &mo);   // T [sum(counts), r] in A's place
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  const int64_t k = W->k, n = mo.n;
+  // every expert's tiles in one launch of the fused kernel
+  nf4q::GroupArgs gr;
+  st = moe_groups(mo, E, (n + 255) / 256, &gr);
+  if (st) return st;
+  nf4q::GemmArgs g;
+  g.a_side = (const uint16_t *)X;
+  g.lda = k;
+  g.lora_a = r > 0 ? (const uint16_t *)T : nullptr;
+  g.lora_b = (const uint16_t *)B;
+  g.w = desc(W);
+  g.M = mo.mtotal;
+  g.C = n;
+  g.R = k;
+  g.r = r;
+  g.s = s;
+  g.out = (uint16_t *)Y;
+  g.ldo = n;
+  g.t = tables();
+  return hip_status(nf4q::launch_gemm_fwd_grouped(g, gr, (hipStream_t)stream),
+                    "qlora_moe_fwd_fused launch");
+}
+
+int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                  const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
+                  size_t ws_bytes, void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  if (r > 0 && (!T || !aligned16(T))) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
+  const int64_t k = W->k;
+  const size_t need = moe_ws(mo, E, k, r);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+  if (need && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  // T = X_e A_e^T for each expert's rows (one row projection per expert with rows)
+  if (r > 0)
+    for (int e = 0; e < E; ++e) {
+      const int64_t me = mo.off[e + 1] - mo.off[e];
+      if (me < 1) continue;
+      st = qlora_lora_down((const uint16_t *)X + mo.off[e] * k, me, k,
+                           (const uint16_t *)A + (int64_t)e * r * k, r,
+                           (uint16_t *)T + mo.off[e] * r, ws, ws_bytes, stream);
+      if (st) return st;
+    }
+  return qlora_moe_fwd_fused(X, counts, E, W, T, B, r, s, Y, stream);
+}
+
+int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
+                  const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
+                  const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
+                  void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  if (!dY || !aligned16(dY)) return fail(NF4_EINVAL, "dY must be non-NULL and 16-byte aligned");
+  if (dX && !aligned16(dX)) return fail(NF4_EINVAL, "dX must be 16-byte aligned");
+  if (r > 0) {
+    if (!dA || !dB) return fail(NF4_EINVAL, "dA and dB must be non-NULL when r > 0");
+    if ((T && !aligned16(T)) || !aligned16(dA) || !aligned16(dB))
+      return fail(NF4_EINVAL, "T, dA and dB must be 16-byte aligned");
+  }
+  const int64_t k = W->k, n = mo.n;
+  const MoeWs lay = moe_ws_layout(mo, E, k, r);
+  if (ws_bytes < lay.total || (lay.total && !ws))
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                lay.total);
+  if (lay.total && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  if (!dX && r == 0) return ok();
+  hipStream_t sm = (hipStream_t)stream;
+  char *base = (char *)ws;
+  uint16_t *U = (uint16_t *)base;
+  uint16_t *Bt = (uint16_t *)(base + lay.u);
+  float *part = (float *)(base + lay.u + lay.bt + lay.t);
+  const uint16_t *dy = (const uint16_t *)dY, *x = (const uint16_t *)X;
+  const uint16_t *a = (const uint16_t *)A;
+  hipError_t he;
+  // U = dY_e B_e for each expert's rows (and T = X_e A_e^T when the caller keeps none), from one
+  // transpose of the stacked B: Bt [r, E n], expert e's columns e n .. e n + n - 1
+  if (r > 0) {
+    he = nf4q::launch_transpose((const uint16_t *)B, E * n, r, Bt, sm);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd transpose launch");
+    uint16_t *Tw = T ? nullptr : (uint16_t *)(base + lay.u + lay.bt);
+    for (int e = 0; e < E; ++e) {
+      const int64_t me = mo.off[e + 1] - mo.off[e];
+      if (me < 1) continue;
+      if (Tw) {
+        he = nf4q::launch_rowproj(x + mo.off[e] * k, k, a + (int64_t)e * r * k, k, me, k, r,
+                                  nf4q::rowproj_splits(me, k), part, Tw + mo.off[e] * r, sm);
+        if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd T launch");
+      }
+      he = nf4q::launch_rowproj(dy + mo.off[e] * n, n, Bt + e * n, E * n, me, n, r,
+                                nf4q::rowproj_splits(me, n), part, U + mo.off[e] * r, sm);
+      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd U launch");
+    }
+    if (Tw) T = Tw;
+  }
+  // dX of every expert in one launch
+  if (dX) {
+    nf4q::GroupArgs gr;
+    st = moe_groups(mo, E, (k + 255) / 256, &gr);
+    if (st) return st;
+    nf4q::GemmArgs g;
+    g.a_side = dy;
+    g.lda = n;
+    g.lora_a = U;
+    g.lora_b = a;
+    g.w = desc(W);
+    g.M = mo.mtotal;
+    g.C = k;
+    g.R = n;
+    g.r = r;
+    g.s = s;
+    g.out = (uint16_t *)dX;
+    g.ldo = k;
+    g.t = tables();
+    he = nf4q::launch_gemm_dx_grouped(g, gr, sm);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dX launch");
+  }
+  // dA_e = s U_e^T X_e, dB_e = s dY_e^T T_e (zero for an expert with no rows)
+  for (int e = 0; e < E && r > 0; ++e) {
+    const int64_t me = mo.off[e + 1] - mo.off[e];
+    uint16_t *dAe = (uint16_t *)dA + (int64_t)e * r * k;
+    uint16_t *dBe = (uint16_t *)dB + (int64_t)e * n * r;
+    if (me < 1) {
+      he = nf4q::launch_zero(dAe, (int64_t)r * k * 2, sm);
+      if (he == hipSuccess) he = nf4q::launch_zero(dBe, n * r * 2, sm);
+      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd launch");
+      continue;
+    }
+    he = nf4q::launch_mreduce(U + mo.off[e] * r, x + mo.off[e] * k, k, me, k, r, s,
+                              nf4q::mreduce_splits(me, k), part, dAe, false, sm);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dA launch");
+    he = nf4q::launch_mreduce((const uint16_t *)T + mo.off[e] * r, dy + mo.off[e] * n, n, me, n, r,
+                              s, nf4q::mreduce_splits(me, n), part, dBe, true, sm);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dB launch");
+  }
+  return ok();
 }
 
 int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,

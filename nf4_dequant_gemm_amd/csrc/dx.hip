@@ -75,8 +75,8 @@ struct CStage {
 // columns 0 .. nch - 1; both zero-padded (the MFMAs of the step read no further). U chunks are
 // one 16-byte buffer load each when r is a multiple of 8 and U is 16-byte aligned (rows past the
 // tile edge and chunks past r read as zero), single values otherwise.
-__device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t rows_m, int jb,
-                              int nrows, int nch, uint4 *sY, uint16_t *sW) {
+__device__ void stage_lora_dx(const GemmArgs &g, const uint16_t *A, int64_t m0, int64_t k0,
+                              int64_t rows_m, int jb, int nrows, int nch, uint4 *sY, uint16_t *sW) {
   const int tid = threadIdx.x;
   {
     const int row = own_row(tid), seg = own_seg(tid);
@@ -87,7 +87,7 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t
         const int64_t k = k0 + seg * 32 + q * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (j < g.r && k < g.C) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(g.lora_b + (int64_t)j * g.C + k);
+          const uint4 a = *reinterpret_cast<const uint4 *>(A + (int64_t)j * g.C + k);
           const uint32_t w[4] = {a.x, a.y, a.z, a.w};
           uint32_t o[4];
 #pragma unroll
@@ -124,7 +124,7 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t
     for (int e = 0; e < 8; e += 2) {
       const int ja = j0 + e, jc = ja + 1;
       uint32_t lo = 0, hi = 0;
-      if (m < g.M) {
+      if (row < rows_m) {
         if (ja < g.r) lo = g.lora_a[m * g.r + ja];
         if (jc < g.r) hi = g.lora_a[m * g.r + jc];
       }
@@ -134,8 +134,12 @@ __device__ void stage_lora_dx(const GemmArgs &g, int64_t m0, int64_t k0, int64_t
   }
 }
 
-template <bool kDQ>
-__global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
+// kGrp: the grouped (mixture-of-experts) form. The weight holds E experts' [N, K] blocks stacked
+// ([E N, K]), A their [r, K] blocks ([E r, K]); the rows of dY, U and dX are grouped by expert
+// (rows m_off[e] .. m_off[e+1] - 1 belong to expert e), and expert e's tiles are the logical
+// tiles tile_off[e] .. tile_off[e+1] - 1 of the launch.
+template <bool kDQ, bool kGrp>
+__device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) {
   // separate LDS arrays per buffer: the compiler then knows that accesses to one do not alias
   // the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sY0[kYChunks], sY1[kYChunks];
@@ -154,27 +158,40 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
   // first, so the 32 workgroups an XCD runs at once cover 4 row blocks x 8 column tiles and
   // share 4 dY row blocks and 8 weight column tiles in its L2 (one row block x 32 column tiles
   // re-fetched the whole weight from beyond L2 once per row block).
-  const int logical = tile_remap(blockIdx.x, gridDim.x);
-  const int tiles_m = (int)((g.M + kT - 1) / kT);
+  int logical = tile_remap(blockIdx.x, gridDim.x);
+  int64_t m_lo = 0, m_hi = g.M, wbase = 0;
+  if (kGrp) {
+    int e = 0;
+    while (e + 1 < gr.E && logical >= gr.tile_off[e + 1]) ++e;
+    logical -= gr.tile_off[e];
+    m_lo = gr.m_off[e];
+    m_hi = gr.m_off[e + 1];
+    wbase = (int64_t)e * g.R;
+  }
+  const int tiles_m = (int)((m_hi - m_lo + kT - 1) / kT);
   const int gsz = kGroupM * tiles_k, grp0 = logical / gsz, gin = logical % gsz;
   const int gm = tiles_m - grp0 * kGroupM < kGroupM ? tiles_m - grp0 * kGroupM : kGroupM;
-  const int64_t m0 = (int64_t)(grp0 * kGroupM + gin % gm) * kT;
+  const int64_t m0 = m_lo + (int64_t)(grp0 * kGroupM + gin % gm) * kT;
   const int64_t k0 = (int64_t)(gin / gm) * kT;
-  const int64_t K = g.w.k, N = g.w.n;
-  const int64_t rows_m = (g.M - m0 < kT) ? g.M - m0 : kT;
+  const int64_t K = g.w.k, N = g.R;   // N: the reduction length (one expert's rows of the weight)
+  const int64_t rows_m = (m_hi - m0 < kT) ? m_hi - m0 : kT;
   const int kblk = (int)(K / kS);
   const int nsteps = (int)((N + kS - 1) / kS);
   const int last = nsteps - 1;
 
   // dY rows m0.. (reduction index n contiguous). Chunks past n = N read the next row's values
   // (finite) and meet weight rows past N, which decode to exact zeros (codes and constants read
-  // past the end of their buffers are 0), so they add nothing.
-  const __amdgpu_buffer_rsrc_t rY = make_rsrc(g.a_side + m0 * N, rows_m * N * 2);
-  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes, N * (K / 2));
+  // past the end of the expert's part of their buffers are 0), so they add nothing. The run
+  // scales of the double quantisation are indexed by the block's place in the whole tensor
+  // (qb0 + block), since a run may straddle two experts.
+  const int64_t qb0 = wbase * kblk;
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wbase * (K / 2), N * (K / 2));
   const __amdgpu_buffer_rsrc_t rQ =
-      kDQ ? make_rsrc(g.w.absmax, N * kblk) : make_rsrc(g.w.absmax, N * kblk * 4);
-  const int64_t nruns = (N * kblk + 255) / 256;
+      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + qb0, N * kblk)
+          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + qb0, N * kblk * 4);
+  const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(g.a_side + m0 * N, rows_m * N * 2);
 
   // dY DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (4 w + i) .. +7;
   // lane L writes physical chunk L % 8 of row 8 (4 w + i) + L / 8, i.e. logical chunk
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
     const uint32_t b = qoff + s * qstep;
     if (kDQ) {
       c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0);
-      c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (b >> 8) * 4, 0, 0);
+      c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)((qb0 + b) >> 8) * 4, 0, 0);
     } else {
       c.q = __builtin_amdgcn_raw_buffer_load_b32(rQ, b * 4, 0, 0);
     }
@@ -367,11 +384,12 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
 
   // LoRA steps; a k-slice of 32 rows j that lies wholly past r is skipped.
   const int nlora = (g.r + kS - 1) / kS;
+  const uint16_t *Ae = g.lora_b + (kGrp ? (wbase / g.R) * g.r * K : 0);   // the expert's A
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
-    stage_lora_dx(g, m0, k0, rows_m, j * kS, 32 * nks, 4 * nks, ybuf(buf), wbuf(buf));
+    stage_lora_dx(g, Ae, m0, k0, rows_m, j * kS, 32 * nks, 4 * nks, ybuf(buf), wbuf(buf));
     __syncthreads();
     mma(ybuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(ybuf(buf), wbuf(buf), 1);
@@ -402,17 +420,39 @@ __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
       const int row = 8 * i + (lane >> 3);
       const int64_t m = m0 + wm * 128 + row;
       const uint4 v = blk[swzd(row, c)];
-      if (m < g.M && k < g.C)
+      if (m < m_hi && k < g.C)
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<u32x4 *>(g.out + m * g.ldo + k));
     }
   }
 }
 
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
+  dx_body<kDQ, false>(g, GroupArgs{});
+}
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void dx_grouped_kernel(GemmArgs g, GroupArgs gr) {
+  dx_body<kDQ, true>(g, gr);
+}
+
 }  // namespace
 
+hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st) {
+  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || gr.E < 1 ||
+      gr.E > kMaxExperts || g.w.n != (int64_t)gr.E * g.R)
+    return hipErrorInvalidValue;
+  const int tiles = gr.tile_off[gr.E];
+  if (tiles < 1) return hipSuccess;
+  if (g.w.dq)
+    dx_grouped_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  else
+    dx_grouped_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st) {
-  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0)
+  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || g.R != g.w.n)
     return hipErrorInvalidValue;   // the epilogue writes 16-byte pieces of 8 columns
   const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
   if (g.w.dq)

@@ -66,6 +66,7 @@ struct CStage {
 // otherwise values are read one at a time.
 __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t rows_m, int64_t rows_n,
                            int jb, int nch, uint4 *sA, uint4 *sB) {
+  // m0: first row of T; n0: first row of B (rows past rows_m / rows_n are zero)
   const int tid = threadIdx.x;
   const int c = tid & 7, row0 = tid >> 3;
   if (c >= nch) return;
@@ -103,13 +104,13 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t ro
     for (int e = 0; e < 8; e += 2) {
       const int ja = j0 + e, jc = ja + 1;
       uint32_t lo = 0, hi = 0;
-      if (m < g.M) {
+      if (row < rows_m) {
         if (ja < g.r) lo = g.lora_a[m * g.r + ja];
         if (jc < g.r) hi = g.lora_a[m * g.r + jc];
       }
       wa[e >> 1] = lo | (hi << 16);
       float b0 = 0.f, b1 = 0.f;
-      if (n < g.C) {
+      if (row < rows_n) {
         if (ja < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + ja]);
         if (jc < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + jc]);
       }
@@ -120,8 +121,12 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t ro
   }
 }
 
-template <bool kDQ>
-__global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
+// The kernel body, shared by the plain launch and the grouped (mixture-of-experts) launch. With
+// kGrp, the tiles of every expert follow one another: the workgroup finds its expert e from the
+// first-tile table, takes rows m_off[e] .. m_off[e+1] of X, T and Y, and rows e N .. of the stacked
+// weight and of the stacked B (N = g.C); everything else is the plain kernel.
+template <bool kDQ, bool kGrp>
+__device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr) {
   // X and W tiles as separate arrays: the compiler then knows that LDS accesses to one do not
   // alias the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sX0[kChunks], sX1[kChunks];
@@ -134,20 +139,30 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int tiles_n = (int)((g.C + kT - 1) / kT);
-  const int logical = tile_remap(blockIdx.x, gridDim.x);
-  const int64_t m0 = (int64_t)(logical / tiles_n) * kT;
-  const int64_t n0 = (int64_t)(logical % tiles_n) * kT;
+  int local = tile_remap(blockIdx.x, gridDim.x);
+  int64_t m_lo = 0, m_hi = g.M, wbase = 0;
+  if (kGrp) {
+    int e = 0;
+    while (e + 1 < gr.E && local >= gr.tile_off[e + 1]) ++e;
+    local -= gr.tile_off[e];
+    m_lo = gr.m_off[e];
+    m_hi = gr.m_off[e + 1];
+    wbase = (int64_t)e * g.C;
+  }
+  const int64_t m0 = m_lo + (int64_t)(local / tiles_n) * kT;
+  const int64_t n0 = (int64_t)(local % tiles_n) * kT;    // columns of Y
+  const int64_t wn0 = wbase + n0;                         // rows of the (stacked) weight and B
   const int64_t K = g.w.k;
-  const int64_t rows_m = (g.M - m0 < kT) ? g.M - m0 : kT;
+  const int64_t rows_m = (m_hi - m0 < kT) ? m_hi - m0 : kT;
   const int64_t rows_n = (g.C - n0 < kT) ? g.C - n0 : kT;
   const int kblk = (int)(K / kS);
   const int last = kblk - 1;
 
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.a_side + m0 * K, rows_m * K * 2);
-  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + n0 * (K / 2), rows_n * (K / 2));
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wn0 * (K / 2), rows_n * (K / 2));
   const __amdgpu_buffer_rsrc_t rQ =
-      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows_n * kblk)
-          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + n0 * kblk, rows_n * kblk * 4);
+      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + wn0 * kblk, rows_n * kblk)
+          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + wn0 * kblk, rows_n * kblk * 4);
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
 
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   const uint32_t mhi = wh ? 0u : 0xFFFFFFFFu, mlo = wh ? 0xFFFFFFFFu : 0u;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + wh * 16);
   const uint32_t qoff = (uint32_t)(wr * kblk);
-  const int64_t sbase = (n0 + wr) * kblk;
+  const int64_t sbase = (wn0 + wr) * kblk;
 
   const int g16 = lane >> 4, l16 = lane & 15;
   f32x4 acc[4][8];   // [n-tile][m-tile]
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
-    stage_lora(g, m0, n0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
+    stage_lora(g, m0, wn0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
     __syncthreads();
     mma(xbuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(xbuf(buf), wbuf(buf), 1);
@@ -365,11 +380,21 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
       const int row = 8 * i + (lane >> 3);
       const int64_t m = m0 + wm * 128 + row;
       const uint4 v = blk[swzf(row, c)];
-      if (m < g.M && n < g.C)
+      if (wm * 128 + row < rows_m && n < g.C)
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
     }
   }
+}
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
+  fwd_body<kDQ, false>(g, GroupArgs{});
+}
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(GemmArgs g, GroupArgs gr) {
+  fwd_body<kDQ, true>(g, gr);
 }
 
 }  // namespace
@@ -382,6 +407,19 @@ hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st) {
     fwd_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   else
     fwd_fused_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st) {
+  if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || gr.E < 1 ||
+      gr.E > kMaxExperts)
+    return hipErrorInvalidValue;
+  const int64_t tiles = gr.tile_off[gr.E];
+  if (tiles < 1) return hipSuccess;
+  if (g.w.dq)
+    fwd_grouped_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  else
+    fwd_grouped_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   return hipGetLastError();
 }
 

@@ -33,6 +33,18 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
+
+// Grouped (mixture-of-experts) forward: E experts, rows m_off[e] .. m_off[e+1] of X, T and Y
+// belong to expert e, whose weight rows are e N .. e N + N - 1 of the stacked weight g.w and whose
+// B rows are the same rows of g.lora_b (N = g.C). tile_off[e] = sum over e' < e of
+// ceil(rows_e' / 256) * ceil(N / 256): one launch runs every expert's tiles.
+constexpr int kMaxExperts = 64;
+struct GroupArgs {
+  int E;
+  int64_t m_off[kMaxExperts + 1];
+  int32_t tile_off[kMaxExperts + 1];
+};
+hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st);
 // Forward for M <= 48 and K % 256 == 0 (weight-stream bound): codes streamed by LDS DMA, table
 // decode of unscaled levels, block constant applied to the per-block partial sums.
 hipError_t launch_decode_fwd(const GemmArgs &g, hipStream_t st);
@@ -46,6 +58,10 @@ hipError_t launch_decode16_fwd(const GemmArgs &g, hipStream_t st);
 hipError_t launch_decode16_fwd_tpart(const GemmArgs &g, const float *tpart, int tsplits,
                                      uint16_t *tout, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
+// dX of every expert in one launch: g.R = N (one expert's rows of the stacked weight, the
+// reduction), g.w.n = E N, g.lora_b = the stacked A [E r, K]; rows of dY, U, dX grouped by
+// expert as gr.m_off says; gr.tile_off[e] = sum over e' < e of ceil(rows_e' / 256) * ceil(K / 256).
+hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).
 // With splits > 1 the partial sums go to part and are added in split order: by a second launch
@@ -78,5 +94,8 @@ hipError_t launch_diagblocks(const uint16_t *db2, int64_t n, int r, uint16_t *db
 // LoRA merge (merge.hip): out bf16 [n, k] = bf16(deq(W) + s B A), 0 <= r <= 128, k % 64 == 0.
 hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, int r, float s,
                         const Tables &t, uint16_t *out, hipStream_t st);
+
+// Zero `bytes` (a multiple of 16) at the 16-byte aligned p with a fill kernel.
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t st);
 
 }  // namespace nf4q

@@ -490,4 +490,23 @@ hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------ zeroing
+// A plain fill kernel (16-byte stores) rather than a memset, so that callers may capture the
+// calls that use it in a graph.
+__global__ __launch_bounds__(256) void zero_kernel(uint4 *__restrict__ p, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t st) {
+  if (bytes % 16 || (reinterpret_cast<uintptr_t>(p) & 15)) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(reinterpret_cast<uint4 *>(p), n16);
+  return hipGetLastError();
+}
+
 }  // namespace nf4q

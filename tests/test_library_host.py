@@ -192,6 +192,43 @@ def test_merge_rejects_bad_arguments():
     assert mg(q=wdesc(n=1 << 20, k=1 << 12)) == m.NF4_EUNSUPPORTED      # n*k = 2^32
 
 
+def test_moe_calls_reject_bad_arguments():
+    """The grouped layer validates on the host: expert count, counts, stacked shapes, outputs and
+    workspace."""
+    lib = m.library()
+    q = wdesc(n=4 * 64, k=128)                    # 4 experts of 64 rows
+    cnt = lambda *c: (ctypes.c_int64 * len(c))(*c)
+    c4 = cnt(10, 0, 300, 7)
+    wsb = lib.qlora_moe_workspace_bytes(c4, 4, 64, 128, 8)
+    assert wsb > 0
+    assert lib.qlora_moe_workspace_bytes(c4, 0, 64, 128, 8) == 0
+    assert lib.qlora_moe_workspace_bytes(None, 4, 64, 128, 8) == 0
+    # at least U and T [sum(counts), r] and the transposed stacked B [r, E n] (bf16)
+    assert wsb >= 2 * 317 * 8 * 2 + 8 * 4 * 64 * 2
+    fwd = lambda **kw: lib.qlora_moe_fwd(FAKE, kw.get("c", c4), kw.get("E", 4), ctypes.byref(kw.get("q", q)),
+                                         kw.get("A", FAKE), FAKE, kw.get("r", 8), 1.0, kw.get("Y", FAKE),
+                                         kw.get("T", FAKE), kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert fwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert fwd(ws=None) == m.NF4_EINVAL
+    assert fwd(E=0) == m.NF4_EINVAL
+    assert fwd(E=65, c=cnt(*([1] * 65)), q=wdesc(n=65 * 8, k=128)) == m.NF4_EINVAL   # at most 64 experts
+    assert fwd(E=3, c=cnt(1, 2, 3)) == m.NF4_EINVAL          # 256 rows are not 3 experts
+    assert fwd(c=cnt(10, -1, 300, 7)) == m.NF4_EINVAL        # negative count
+    assert fwd(c=cnt(0, 0, 0, 0)) == m.NF4_EINVAL            # no rows at all
+    assert fwd(c=None) == m.NF4_EINVAL
+    assert fwd(E=8, c=cnt(*([1] * 8)), q=wdesc(n=8 * 36, k=128)) == m.NF4_EUNSUPPORTED   # n = 36
+    assert fwd(T=None) == m.NF4_EINVAL
+    assert fwd(Y=None) == m.NF4_EINVAL
+    assert fwd(A=None) == m.NF4_EINVAL
+    assert fwd(r=129) == m.NF4_EINVAL
+    bwd = lambda **kw: lib.qlora_moe_bwd(kw.get("dY", FAKE), FAKE, c4, 4, ctypes.byref(kw.get("q", q)), FAKE,
+                                         FAKE, 8, 1.0, FAKE, FAKE, kw.get("dA", FAKE), FAKE,
+                                         kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert bwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert bwd(dY=None) == m.NF4_EINVAL
+    assert bwd(dA=None) == m.NF4_EINVAL
+
+
 def test_workspace_sizes_are_consistent():
     lib = m.library()
     assert lib.qlora_fwd_workspace_bytes(100, 64, 128, 0) == 0

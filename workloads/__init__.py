@@ -18,6 +18,11 @@ and one gate/up pair (two projections on the same X joined by SwiGLU, PAIRS belo
 
   mlp_swiglu  M=8192  K=4096  N=11008 (x2)  r=64 (x2)  s=0.5  absmax int8/256  fwd+bwd
 
+and one grouped mixture-of-experts layer (MOES below):
+
+  moe_mlp_up  E=8 experts of K=4096 N=11008, 8192 tokens x top-2 = 16384 rows, r=16, s=2,
+              absmax int8/256, fwd+bwd
+
 Distributions (std is the standard deviation of a normal): X ~ N(0,1); W ~ N(0,0.02) (0.015 for
 decode); A ~ N(0, 1/K) read as variance 1/K, i.e. std K**-0.5; B ~ N(0,0.01); dY ~ N(0,1)
 (N(0,1e-2) for down). Workloads that name no A/B distribution use the mlp_up one.
@@ -146,6 +151,82 @@ class PairWorkload:
 PAIRS: Dict[str, PairWorkload] = {p.name: p for p in [
     PairWorkload("mlp_swiglu", 6, 8192, 4096, 11008, 64, 0.5, 256, 1.0, 0.02, 0.01, 1.0),
 ]}
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    """A grouped (mixture-of-experts) QLoRA layer: E experts, each with its own NF4 base [N,K] and
+    adapters, over `tokens` tokens routed to top_k experts each (M = tokens * top_k rows, grouped by
+    expert).
+
+    Routing: counts[e] = the rows of expert e, a multinomial draw of M over expert probabilities
+    p_e = exp(z_e) / sum exp(z), z ~ N(0, skew^2), both from PCG64(1000*index + 7) (a seeded,
+    uneven load across experts, as a learned router produces). Tensors: X [M,K]; W [E*N,K] (the
+    experts' weights stacked); A [E*r,K]; B [E*N,r]; dY [M,N]; seeds 1000*index + t (X=1, W=2,
+    A=3, B=4, dY=5); distributions as the single-layer workloads.
+    """
+    name: str
+    index: int
+    E: int
+    tokens: int
+    top_k: int
+    K: int
+    N: int
+    r: int
+    s: float
+    dq_block: int
+    skew: float
+    std_x: float
+    std_w: float
+    std_b: float
+    std_dy: float
+
+    @property
+    def M(self) -> int:
+        return self.tokens * self.top_k
+
+    def counts(self):
+        rng = np.random.Generator(np.random.PCG64(1000 * self.index + 7))
+        z = rng.standard_normal(self.E) * self.skew
+        p = np.exp(z) / np.exp(z).sum()
+        return [int(c) for c in rng.multinomial(self.M, p)]
+
+    def shape(self, tensor: str) -> Tuple[int, int]:
+        M, E, K, N, r = self.M, self.E, self.K, self.N, self.r
+        return {"X": (M, K), "W": (E * N, K), "A": (E * r, K), "B": (E * N, r), "dY": (M, N)}[tensor]
+
+    def std(self, tensor: str) -> float:
+        return {"X": self.std_x, "W": self.std_w, "A": self.K ** -0.5, "B": self.std_b,
+                "dY": self.std_dy}[tensor]
+
+    def seed(self, tensor: str) -> int:
+        return 1000 * self.index + TENSOR_IDS[tensor]
+
+    def rows_workload(self) -> Workload:
+        """The layer's flop counts over all M rows (every term is linear in the rows)."""
+        return Workload(self.name, self.index, self.M, self.K, self.N, self.r, self.s, self.dq_block,
+                        self.std_x, self.std_w, self.std_b, self.std_dy, True)
+
+    def fwd_flops(self) -> int:
+        return self.rows_workload().fwd_flops()
+
+    def bwd_flops(self) -> int:
+        return self.rows_workload().bwd_flops()
+
+    def weight_stream_bytes(self) -> int:
+        return self.E * Workload(self.name, self.index, 1, self.K, self.N, self.r, self.s, self.dq_block,
+                                 self.std_x, self.std_w, self.std_b, self.std_dy, True).weight_stream_bytes()
+
+
+# Eight experts of the mlp_up projection's shape, 8192 tokens routed to two experts each.
+MOES: Dict[str, MoeWorkload] = {m.name: m for m in [
+    MoeWorkload("moe_mlp_up", 7, 8, 8192, 2, 4096, 11008, 16, 2.0, 256, 0.5, 1.0, 0.02, 0.01, 1.0),
+]}
+
+
+def moe_tensor(w: MoeWorkload, name: str) -> torch.Tensor:
+    """The named input of MoE workload w as a bf16 CPU tensor."""
+    return normal_bf16(w.seed(name), w.shape(name), w.std(name))
 
 
 def normal_bf16(seed: int, shape, std: float) -> torch.Tensor:
