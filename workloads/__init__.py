@@ -160,10 +160,10 @@ class MoeWorkload:
     expert).
 
     Routing: counts[e] = the rows of expert e, a multinomial draw of M over expert probabilities
-    p_e = exp(z_e) / sum exp(z), z normal with standard deviation skew, both from PCG64(1000*index + 7) (a seeded,
-    uneven load across experts, as a learned router produces). Tensors: X [M,K]; W [E*N,K] (the
-    experts' weights stacked); A [E*r,K]; B [E*N,r]; dY [M,N]; seeds 1000*index + t (X=1, W=2,
-    A=3, B=4, dY=5); distributions as the single-layer workloads.
+    p_e = exp(z_e) / sum exp(z), z normal with standard deviation `skew`, both from
+    PCG64(1000*index + 7) (a seeded, uneven load across experts, as a learned router produces).
+    Tensors: X [M,K]; W [E*N,K] (the experts' weights stacked); A [E*r,K]; B [E*N,r]; dY [M,N];
+    seeds 1000*index + t (X=1, W=2, A=3, B=4, dY=5); distributions as the single-layer workloads.
     """
     name: str
     index: int
