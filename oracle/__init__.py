@@ -4,7 +4,8 @@ A plain, slow, obviously-correct numpy implementation of what the HIP library co
 codebook, blockwise absmax quantisation with double quantisation, dequantisation, and the QLoRA
 layer Y = X deq(W)^T + s (X A^T) B^T with its backward dX, dA, dB, all products in float64, and
 the gate/up pair of such layers joined by the SwiGLU activation (swiglu.py), the LoRA merge
-W' = deq(W) + s B A (merge.py) and the grouped mixture-of-experts layer (moe.py).
+W' = deq(W) + s B A (merge.py), the grouped mixture-of-experts layer (moe.py) and the 4-bit
+floating-point (E2M1) variant of the weight format with FP8 group scales (fp4.py).
 
 Only the test suite, the smoke check in __graft_entry__ and the CPU-baseline leg of bench.py may
 import or run anything in this package. The product path (nf4_dequant_gemm_amd) never does: it
@@ -23,4 +24,4 @@ Parity status: every function here is pinned by tests/test_oracle_*.py against c
 library routines (scipy's normal quantile, torch's bf16 conversion), brute force on tiny inputs,
 exact identities (adjoints, linearity) and planted-mistake checks. No function is unpinned.
 """
-from . import merge, moe, nf4, qlora, swiglu  # noqa: F401
+from . import fp4, merge, moe, nf4, qlora, swiglu  # noqa: F401

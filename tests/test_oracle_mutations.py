@@ -8,8 +8,9 @@ live only inside this test (pytest's monkeypatch undoes them).
 import numpy as np
 import pytest
 
-from oracle import merge, moe, nf4, qlora, swiglu
+from oracle import fp4, merge, moe, nf4, qlora, swiglu
 from tests import test_oracle_codebook as tc
+from tests import test_oracle_fp4 as tf
 from tests import test_oracle_gemm as tg
 from tests import test_oracle_merge as tm
 from tests import test_oracle_moe as to
@@ -48,6 +49,15 @@ PINS = [
     to.test_brute_force_rows,
     to.test_empty_expert,
     to.test_expert_reordering,
+    tf.test_e2m1_codebook_matches_the_page,
+    tf.test_e4m3_grid_matches_torch,
+    tf.test_e4m3_rounding_matches_torch,
+    tf.test_group_scales_match_torch,
+    tf.test_encode_brute_force_random,
+    tf.test_encode_brute_force_at_midpoints,
+    tf.test_special_cases,
+    tf.test_pack_known_pattern,
+    tf.test_dequantize_definition_and_bound,
 ]
 
 _fwd, _bwd = qlora.forward, qlora.backward
@@ -240,7 +250,50 @@ def decode_absmax_next_run(wq):
     return (q * S).astype(np.float32)
 
 
+_fp4_round, _fp4_encode = fp4.round_to_grid, fp4.encode
+
+
+def fp4_round_ties_up(x, grid):
+    x = np.asarray(x, dtype=np.float64)
+    mids = (grid[1:] + grid[:-1]) / 2.0
+    return np.searchsorted(mids, x, side="right")
+
+
+def fp4_encode_ties_up(w, scales, S):
+    fp4.round_to_grid = fp4_round_ties_up
+    try:
+        return _fp4_encode(w, scales, S)
+    finally:
+        fp4.round_to_grid = _fp4_round
+
+
+def fp4_scales_truncated(w, S):
+    g = np.abs(w.astype(np.float32)).reshape(-1, fp4.GROUP).max(axis=1)
+    if S == 0:
+        return np.zeros(g.shape, np.uint8)
+    t = (g / np.float32(np.float32(6.0) * S)).astype(np.float32)
+    return np.clip(np.searchsorted(fp4.e4m3_grid(), t, side="right") - 1, 0, 126).astype(np.uint8)
+
+
+def fp4_deq_without_tensor_scale(q):
+    codes = fp4.unpack(q.codes).reshape(-1, fp4.GROUP)
+    s = fp4.e4m3_grid()[q.scales].astype(np.float32)[:, None]
+    return (fp4.e2m1_codebook()[codes].astype(np.float32) * s).astype(np.float32).reshape(q.n, q.k)
+
+
+def fp4_value_bias_zero(code):
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = m / 2.0 if e == 0 else 2.0 ** e * (1.0 + m / 2.0)
+    return -mag if s else mag
+
+
 MUTATIONS = {
+    "fp4: E2M1 ties go up": [(fp4, "encode", fp4_encode_ties_up)],
+    "fp4: group scales truncated": [(fp4, "group_scales", fp4_scales_truncated)],
+    "fp4: tensor scale divides by 448": [(fp4, "TSCALE_DIV", 448.0)],
+    "fp4: dequant drops the tensor scale": [(fp4, "dequantize_f32", fp4_deq_without_tensor_scale)],
+    "fp4: nibble order swapped": [(fp4, "pack", pack_swapped), (fp4, "unpack", unpack_swapped)],
+    "fp4: exponent bias 0": [(fp4, "e2m1_value", fp4_value_bias_zero)],
     "fwd drops the LoRA term": [(qlora, "forward", fwd_no_lora)],
     "fwd flips the LoRA sign": [(qlora, "forward", fwd_wrong_sign)],
     "fwd applies s twice": [(qlora, "forward", fwd_s_twice)],
