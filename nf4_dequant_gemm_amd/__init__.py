@@ -116,27 +116,32 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None):
 
 @dataclasses.dataclass
 class NF4Tensor:
-    """An NF4-quantised weight [n, k]: packed codes, block constants and (double quant) scales."""
+    """A 4-bit quantised weight [n, k]: packed codes, block constants and their scales.
+
+    block 64 (NF4): absmax float32 [n*k/64] (dq_block 0) or int8 [n*k/64] with float32 run
+    scales [ceil(n*k/64/256)] (dq_block 256). block 16 (E2M1): absmax holds the uint8 E4M3 group
+    scales [n*k/16] and scale the float32 tensor scale [1]."""
     n: int
     k: int
     dq_block: int
     codes: torch.Tensor                   # uint8 [n*k/2]
-    absmax: torch.Tensor                  # float32 or int8 [n*k/64]
-    scale: Optional[torch.Tensor] = None  # float32 [ceil(n*k/64/256)] when dq_block
+    absmax: torch.Tensor                  # block constants (see above)
+    scale: Optional[torch.Tensor] = None  # run scales or the tensor scale (see above)
+    block: int = 64
 
     @property
     def device(self) -> torch.device:
         return self.codes.device
 
     def c_struct(self) -> _NF4TensorC:
-        return _NF4TensorC(self.n, self.k, 64, self.dq_block, self.codes.data_ptr(),
+        return _NF4TensorC(self.n, self.k, self.block, self.dq_block, self.codes.data_ptr(),
                            self.absmax.data_ptr(),
                            self.scale.data_ptr() if self.scale is not None else None)
 
     def clone(self) -> "NF4Tensor":
         """A copy in new device buffers (same values, different addresses)."""
         return NF4Tensor(self.n, self.k, self.dq_block, self.codes.clone(), self.absmax.clone(),
-                         self.scale.clone() if self.scale is not None else None)
+                         self.scale.clone() if self.scale is not None else None, self.block)
 
     @staticmethod
     def empty(n: int, k: int, dq_block: int, device) -> "NF4Tensor":
@@ -173,6 +178,27 @@ def nf4_quantize(w: torch.Tensor, dq_block: int = 256) -> NF4Tensor:
     st = q.c_struct()
     _check(library().nf4_quantize(_ptr(w), NF4_F32 if w.dtype == torch.float32 else NF4_BF16,
                                   ctypes.byref(st), _stream(w.device)))
+    return q
+
+
+def fp4_quantize(w: torch.Tensor) -> NF4Tensor:
+    """Quantise a bf16 or float32 device weight [n, k] to the E2M1 format: 4-bit floats in groups
+    of 16 with one E4M3 scale each and a float32 tensor scale (block 16 of the descriptor)."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [n, k]")
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be bfloat16 or float32")
+    _need(w, "w", w.dtype)
+    n, k = w.shape
+    if k % 64:
+        raise NF4Error(NF4_EUNSUPPORTED, "k must be a multiple of 64")
+    dev = w.device
+    q = NF4Tensor(n, k, 0, torch.empty(n * k // 2, dtype=torch.uint8, device=dev),
+                  torch.empty(n * k // 16, dtype=torch.uint8, device=dev),
+                  torch.empty(4, dtype=torch.float32, device=dev), block=16)
+    st = q.c_struct()
+    _check(library().nf4_quantize(_ptr(w), NF4_F32 if w.dtype == torch.float32 else NF4_BF16,
+                                  ctypes.byref(st), _stream(dev)))
     return q
 
 

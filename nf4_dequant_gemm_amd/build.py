@@ -25,7 +25,7 @@ PROBE_LIB = os.path.join(PKG, "libnf4probe.so")
 ARCH = os.environ.get("NF4Q_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "quant.hip", "fwd.hip", "decode.hip", "decode16.hip", "dx.hip", "lora.hip",
-           "swiglu.hip", "merge.hip"]
+           "swiglu.hip", "merge.hip", "fp4.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

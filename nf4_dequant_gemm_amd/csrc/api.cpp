@@ -97,14 +97,18 @@ int check_weight(const nf4_tensor *q) {
   if (q->k < 64 || q->k % 64)
     return fail(NF4_EUNSUPPORTED, "weight k must be a positive multiple of 64 (got %lld)",
                 (long long)q->k);
-  if (q->block != 64) return fail(NF4_EUNSUPPORTED, "block must be 64 (got %d)", q->block);
+  if (q->block != 64 && q->block != 16)
+    return fail(NF4_EUNSUPPORTED, "block must be 64 (NF4) or 16 (E2M1) (got %d)", q->block);
+  if (q->block == 16 && q->dq_block != 0)
+    return fail(NF4_EUNSUPPORTED, "the E2M1 format (block 16) takes dq_block 0 (got %d)", q->dq_block);
   if (q->dq_block != 0 && q->dq_block != 256)
     return fail(NF4_EUNSUPPORTED, "dq_block must be 0 or 256 (got %d)", q->dq_block);
   if (q->n > (int64_t(1) << 40) / q->k)
     return fail(NF4_EUNSUPPORTED, "n*k must be below 2^40");
   if (!q->codes || !q->absmax) return fail(NF4_EINVAL, "codes/absmax pointer is NULL");
-  if (q->dq_block && !q->absmax_scale) return fail(NF4_EINVAL, "absmax_scale is NULL");
-  if (!aligned16(q->codes) || !aligned16(q->absmax) || (q->dq_block && !aligned16(q->absmax_scale)))
+  const bool scale_used = q->dq_block || q->block == 16;
+  if (scale_used && !q->absmax_scale) return fail(NF4_EINVAL, "absmax_scale is NULL");
+  if (!aligned16(q->codes) || !aligned16(q->absmax) || (scale_used && !aligned16(q->absmax_scale)))
     return fail(NF4_EINVAL, "weight buffers must be 16-byte aligned");
   return NF4_OK;
 }
@@ -117,6 +121,7 @@ nf4q::WDesc desc(const nf4_tensor *q) {
   w.n = q->n;
   w.k = q->k;
   w.dq = q->dq_block ? 1 : 0;
+  w.fp4 = q->block == 16 ? 1 : 0;
   return w;
 }
 
@@ -337,6 +342,11 @@ int nf4_quantize(const void *w, int w_dtype, const nf4_tensor *q, void *stream) 
   if (!w) return fail(NF4_EINVAL, "w is NULL");
   if (!aligned16(w)) return fail(NF4_EINVAL, "w must be 16-byte aligned");
   if (w_dtype != NF4_BF16 && w_dtype != NF4_F32) return fail(NF4_EINVAL, "unknown w_dtype %d", w_dtype);
+  if (q->block == 16)
+    return hip_status(nf4q::launch_fp4_quantize(w, w_dtype == NF4_F32, q->n * q->k, q->codes,
+                                                (uint8_t *)q->absmax, q->absmax_scale,
+                                                (hipStream_t)stream),
+                      "nf4_quantize launch");
   const int64_t nblk = q->n * q->k / 64;
   return hip_status(nf4q::launch_quantize(w, w_dtype == NF4_F32, q->codes, q->absmax,
                                           q->absmax_scale, nblk, q->dq_block ? 1 : 0, tables(),
@@ -351,6 +361,10 @@ int nf4_dequantize(const nf4_tensor *q, void *out, int out_dtype, void *stream) 
   if (!aligned16(out)) return fail(NF4_EINVAL, "out must be 16-byte aligned");
   if (out_dtype != NF4_BF16 && out_dtype != NF4_F32)
     return fail(NF4_EINVAL, "unknown out_dtype %d", out_dtype);
+  if (q->block == 16)
+    return hip_status(nf4q::launch_fp4_dequantize(desc(q), out, out_dtype == NF4_F32,
+                                                  (hipStream_t)stream),
+                      "nf4_dequantize launch");
   return hip_status(nf4q::launch_dequantize(desc(q), out, out_dtype == NF4_F32, tables(),
                                             (hipStream_t)stream),
                     "nf4_dequantize launch");
@@ -404,7 +418,7 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
   g.t = tables();
   if (m <= 16 && W->dq_block > 0 && W->k % 256 == 0)
     return hip_status(nf4q::launch_decode16_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
-  if (m <= nf4q::kDecodeMaxM && W->k % 256 == 0)
+  if (m <= nf4q::kDecodeMaxM && W->k % 256 == 0 && W->block == 64)
     return hip_status(nf4q::launch_decode_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
   return hip_status(nf4q::launch_gemm_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
 }
@@ -588,6 +602,9 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
                 void *stream) {
   int st = check_weight(W);
   if (st) return st;
+  if (W->block != 64)
+    return fail(NF4_EUNSUPPORTED, "qlora_merge takes NF4 weights (block 64) only (got block %d)",
+                W->block);
   if (W->n * W->k >= (int64_t(1) << 32))
     return fail(NF4_EUNSUPPORTED, "n*k must be below 2^32 for qlora_merge");
   if (r < 0 || r > 128) return fail(NF4_EINVAL, "r must lie in [0, 128] (got %d)", r);

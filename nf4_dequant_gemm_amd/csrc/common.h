@@ -27,6 +27,8 @@ struct WDesc {
   const float *scale;     // [ceil(nblk/256)] when dq
   int64_t n, k;
   int dq;                 // 0 or 1 (runs of 256)
+  int fp4;                // 1: E2M1 codes, absmax = uint8 E4M3 scale per group of 16,
+                          //    scale = float[1] tensor scale (see fp4.hip)
 };
 
 // Two floats -> packed bf16 pair (low half = lo), round-to-nearest-even (v_cvt_pk_bf16_f32).
@@ -149,6 +151,33 @@ __device__ __forceinline__ void dec_piece(const RowTable &t, Dec8 &x, int piece,
       out[3] = perm(O23, x.E23, 0x07060302u);
     }
   }
+}
+
+// ---- 4-bit float (E2M1) weights with FP8 (E4M3) group scales --------------------------------
+// Value of a non-negative E4M3 byte (bias 7, exponent field 0 subnormal: m * 2^-9). The sign bit
+// is ignored (group scales are never negative).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u;
+  return e ? __uint_as_float(((b & 0x7Fu) << 20) + (120u << 23)) : float(b & 7u) * 0x1p-9f;
+}
+
+// Decode table of one group of 16: the 16 values bf16(e2m1[c] * s) in the RowTable byte-plane
+// layout. The products are exact (at most 6 significant bits), so the bf16 conversion does not
+// round. Entries 8..15 are entries 0..7 with the sign bit set: the same low bytes, high bytes with
+// bit 7 flipped.
+__device__ __forceinline__ RowTable make_e2m1_table(float s) {
+  const uint32_t p0 = pack_bf16x2(0.f, 0.5f * s), p1 = pack_bf16x2(s, 1.5f * s);
+  const uint32_t p2 = pack_bf16x2(2.f * s, 3.f * s), p3 = pack_bf16x2(4.f * s, 6.f * s);
+  RowTable r;
+  r.L[0] = perm(p1, p0, 0x06040200u);
+  r.H[0] = perm(p1, p0, 0x07050301u);
+  r.L[1] = perm(p3, p2, 0x06040200u);
+  r.H[1] = perm(p3, p2, 0x07050301u);
+  r.L[2] = r.L[0];
+  r.L[3] = r.L[1];
+  r.H[2] = r.H[0] ^ 0x80808080u;
+  r.H[3] = r.H[1] ^ 0x80808080u;
+  return r;
 }
 
 // Value of v in lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).

@@ -75,7 +75,7 @@ struct CStage {
 // columns 0 .. nch - 1; both zero-padded (the MFMAs of the step read no further). U chunks are
 // one 16-byte buffer load each when r is a multiple of 8 and U is 16-byte aligned (rows past the
 // tile edge and chunks past r read as zero), single values otherwise.
-__device__ void stage_lora_dx(const GemmArgs &g, const uint16_t *A, int64_t m0, int64_t k0,
+__device__ void stage_lora_dx(const GemmArgs &g, float sa, const uint16_t *A, int64_t m0, int64_t k0,
                               int64_t rows_m, int jb, int nrows, int nch, uint4 *sY, uint16_t *sW) {
   const int tid = threadIdx.x;
   {
@@ -91,7 +91,7 @@ __device__ void stage_lora_dx(const GemmArgs &g, const uint16_t *A, int64_t m0, 
           const uint32_t w[4] = {a.x, a.y, a.z, a.w};
           uint32_t o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g.s * bf16_lo(w[e]), g.s * bf16_hi(w[e]));
+          for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(sa * bf16_lo(w[e]), sa * bf16_hi(w[e]));
           v = make_uint4(o[0], o[1], o[2], o[3]);
         }
         *reinterpret_cast<uint4 *>(sW + wunit(row, seg * 8 + 2 * q)) = v;
@@ -138,8 +138,13 @@ __device__ void stage_lora_dx(const GemmArgs &g, const uint16_t *A, int64_t m0, 
 // ([E N, K]), A their [r, K] blocks ([E r, K]); the rows of dY, U and dX are grouped by expert
 // (rows m_off[e] .. m_off[e+1] - 1 belong to expert e), and expert e's tiles are the logical
 // tiles tile_off[e] .. tile_off[e+1] - 1 of the launch.
-template <bool kDQ, bool kGrp>
+// kFmt: 0 NF4 with float32 block constants, 1 NF4 double-quantised, 2 E2M1 with E4M3 group
+// scales of 16 (a thread's 32 columns are two groups, each with its own whole table; the operand
+// is exact in bf16) and a float32 tensor scale applied in the epilogue (the LoRA steps stage
+// s / S times A).
+template <int kFmt, bool kGrp>
 __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) {
+  constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
   // separate LDS arrays per buffer: the compiler then knows that accesses to one do not alias
   // the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sY0[kYChunks], sY1[kYChunks];
@@ -187,8 +192,15 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   const int64_t qb0 = wbase * kblk;
   const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wbase * (K / 2), N * (K / 2));
   const __amdgpu_buffer_rsrc_t rQ =
-      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + qb0, N * kblk)
-          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + qb0, N * kblk * 4);
+      kFP4  ? make_rsrc(reinterpret_cast<const uint8_t *>(g.w.absmax) + wbase * (K / 16), N * (K / 16))
+      : kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + qb0, N * kblk)
+            : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + qb0, N * kblk * 4);
+  // E2M1: the tensor scale (1 for an all-zero weight, whose group scales are all 0), read where
+  // it is used so that no register holds it through the main loop
+  auto tscale = [&]() {
+    const float S = *g.w.scale;
+    return S > 0.f ? S : 1.f;
+  };
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
   const __amdgpu_buffer_rsrc_t rY = make_rsrc(g.a_side + m0 * N, rows_m * N * 2);
@@ -211,7 +223,7 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   // are complemented for h = 1, whose own half is the upper one.
   // The levels are read from LDS four at a time when the table is built (eight per-lane
   // registers held across the loop would not fit beside the accumulators).
-  const int sh = seg & 1;
+  const int sh = kFP4 ? 0 : (seg & 1);
   const uint32_t mhi = sh ? 0u : 0xFFFFFFFFu, mlo = sh ? 0xFFFFFFFFu : 0u;
   if (tid < 16) sLv[tid] = g.t.level[tid];
   const f32x4 *lvq = reinterpret_cast<const f32x4 *>(sLv) + 2 * sh;
@@ -219,8 +231,10 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   const bool kvalid = kcol < K;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + (kvalid ? kcol / 2 : 0));
   const uint32_t cstep = (uint32_t)(kS * (K / 2));
-  const uint32_t qoff = (uint32_t)(wr * kblk + (kvalid ? kcol / 64 : 0));
-  const uint32_t qstep = (uint32_t)(kS * kblk);
+  // E2M1: the two group scales of the thread's 32 columns, bytes kcol / 16 and + 1 of its row
+  const uint32_t qoff = kFP4 ? (uint32_t)(wr * (K / 16) + (kvalid ? kcol / 16 : 0))
+                             : (uint32_t)(wr * kblk + (kvalid ? kcol / 64 : 0));
+  const uint32_t qstep = kFP4 ? (uint32_t)(kS * (K / 16)) : (uint32_t)(kS * kblk);
 
   f32x4 acc[4][8];   // [k-tile][m-tile]
 #pragma unroll
@@ -239,7 +253,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   auto load_c = [&](int s, CStage &c) {
     c.c = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * cstep, 0, 0);
     const uint32_t b = qoff + s * qstep;
-    if (kDQ) {
+    if (kFP4) {
+      c.q = __builtin_amdgcn_raw_buffer_load_b16(rQ, b, 0, 0);
+    } else if (kDQ) {
       c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0);
       c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)((qb0 + b) >> 8) * 4, 0, 0);
     } else {
@@ -257,11 +273,16 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   auto wstore = [&](uint16_t *sW, int j, const uint32_t o[4]) {
     *reinterpret_cast<uint4 *>(sW + wunit(wr, seg * 8 + 2 * j)) = make_uint4(o[0], o[1], o[2], o[3]);
   };
+  // E2M1 table of the thread's group h (0, 1); zero past K
+  auto fp4_table = [&](const CStage &c, int h) {
+    return make_e2m1_table(kvalid ? e4m3_to_f32((c.q >> (8 * h)) & 0xFFu) : 0.f);
+  };
   auto decode_all = [&](const CStage &c, uint16_t *sW) {
-    const RowTable t = make_row_table(absmax_of(c), g.t);
+    RowTable t = kFP4 ? fp4_table(c, 0) : make_row_table(absmax_of(c), g.t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
+      if (kFP4 && j == 2) t = fp4_table(c, 1);
       decode8(t, word(c, j), o);
       wstore(sW, j, o);
     }
@@ -328,7 +349,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
       for (int kt = 0; kt < 4; ++kt) acc[kt][mt] = mfma16x16x32(aw[kt], yb[grp & 1], acc[kt][mt]);
       // decode of step s+1: table in groups 0..3, then word j = (grp - 4) / 3 in pieces over
       // three groups (pieces 0-1, 2-3, 4 + store)
-      if (grp < 4) {
+      if (kFP4 && grp < 4) {
+        if (grp == 0) t = fp4_table(cn, 0);       // the whole table of the first group
+      } else if (grp < 4) {
         // this thread's half of the table in L[0..1], H[0..1] (groups 0, 1); the partner lane's
         // half by DPP (groups 1, 2)
         if (grp < 2) {
@@ -355,6 +378,7 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
         } else {
           dec_piece(t, dx, 4, o, mhi, mlo);
           wstore(Wn, j, o);
+          if (kFP4 && j == 1) t = fp4_table(cn, 1);   // words 2, 3: the second group
         }
       }
       // keep each group's loads and decode work in place (hoisting them stretches register
@@ -389,7 +413,8 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
-    stage_lora_dx(g, Ae, m0, k0, rows_m, j * kS, 32 * nks, 4 * nks, ybuf(buf), wbuf(buf));
+    stage_lora_dx(g, kFP4 ? g.s / tscale() : g.s, Ae, m0, k0, rows_m, j * kS, 32 * nks, 4 * nks, ybuf(buf),
+                  wbuf(buf));
     __syncthreads();
     mma(ybuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(ybuf(buf), wbuf(buf), 1);
@@ -405,13 +430,16 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
     uint4 *blk = (wave >> 1) == 0 ? sY0 : (wave >> 1) == 1 ? sY1 : (wave >> 1) == 2 ? sW0 : sW1;
     blk += (wave & 1) * (kYChunks / 2);
     uint2 *b2 = reinterpret_cast<uint2 *>(blk);
+    const float tsc = kFP4 ? tscale() : 1.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
         b2[swzd(mt * 16 + l16, 2 * kt + (g16 >> 1)) * 2 + (g16 & 1)] =
-            make_uint2(pack_bf16x2(acc[kt][mt][0], acc[kt][mt][1]),
-                       pack_bf16x2(acc[kt][mt][2], acc[kt][mt][3]));
+            kFP4 ? make_uint2(pack_bf16x2(tsc * acc[kt][mt][0], tsc * acc[kt][mt][1]),
+                              pack_bf16x2(tsc * acc[kt][mt][2], tsc * acc[kt][mt][3]))
+                 : make_uint2(pack_bf16x2(acc[kt][mt][0], acc[kt][mt][1]),
+                              pack_bf16x2(acc[kt][mt][2], acc[kt][mt][3]));
     __syncthreads();
     const int c = lane & 7;
     const int64_t k = k0 + wk * 64 + c * 8;
@@ -427,13 +455,13 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   }
 }
 
-template <bool kDQ>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void dx_fused_kernel(GemmArgs g) {
-  dx_body<kDQ, false>(g, GroupArgs{});
+  dx_body<kFmt, false>(g, GroupArgs{});
 }
-template <bool kDQ>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void dx_grouped_kernel(GemmArgs g, GroupArgs gr) {
-  dx_body<kDQ, true>(g, gr);
+  dx_body<kFmt, true>(g, gr);
 }
 
 }  // namespace
@@ -444,10 +472,12 @@ hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStr
     return hipErrorInvalidValue;
   const int tiles = gr.tile_off[gr.E];
   if (tiles < 1) return hipSuccess;
-  if (g.w.dq)
-    dx_grouped_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  if (g.w.fp4)
+    dx_grouped_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  else if (g.w.dq)
+    dx_grouped_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   else
-    dx_grouped_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+    dx_grouped_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   return hipGetLastError();
 }
 
@@ -455,10 +485,12 @@ hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st) {
   if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || g.R != g.w.n)
     return hipErrorInvalidValue;   // the epilogue writes 16-byte pieces of 8 columns
   const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
-  if (g.w.dq)
-    dx_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  if (g.w.fp4)
+    dx_fused_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else if (g.w.dq)
+    dx_fused_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   else
-    dx_fused_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+    dx_fused_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
 }
 

@@ -64,9 +64,10 @@ struct CStage {
 // chunk t % 8 of rows t / 8 + 64 i. When r is a multiple of 8 and T and B are 16-byte aligned,
 // each chunk is one 16-byte buffer load (rows past the tile edge and chunks past r read as zero);
 // otherwise values are read one at a time.
-__device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t rows_m, int64_t rows_n,
-                           int jb, int nch, uint4 *sA, uint4 *sB) {
-  // m0: first row of T; n0: first row of B (rows past rows_m / rows_n are zero)
+__device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, int64_t rows_m,
+                           int64_t rows_n, int jb, int nch, uint4 *sA, uint4 *sB) {
+  // m0: first row of T; n0: first row of B (rows past rows_m / rows_n are zero); B is staged
+  // times sb
   const int tid = threadIdx.x;
   const int c = tid & 7, row0 = tid >> 3;
   if (c >= nch) return;
@@ -89,7 +90,7 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t ro
       const int row = row0 + 64 * i;
       uint32_t wb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wb[e] = pack_bf16x2(g.s * bf16_lo(tb[i][e]), g.s * bf16_hi(tb[i][e]));
+      for (int e = 0; e < 4; ++e) wb[e] = pack_bf16x2(sb * bf16_lo(tb[i][e]), sb * bf16_hi(tb[i][e]));
       sA[swzf(row, c)] = make_uint4(ta[i][0], ta[i][1], ta[i][2], ta[i][3]);
       sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
     }
@@ -114,7 +115,7 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t ro
         if (ja < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + ja]);
         if (jc < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + jc]);
       }
-      wb[e >> 1] = pack_bf16x2(g.s * b0, g.s * b1);
+      wb[e >> 1] = pack_bf16x2(sb * b0, sb * b1);
     }
     sA[swzf(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
     sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
@@ -125,8 +126,14 @@ __device__ void stage_lora(const GemmArgs &g, int64_t m0, int64_t n0, int64_t ro
 // kGrp, the tiles of every expert follow one another: the workgroup finds its expert e from the
 // first-tile table, takes rows m_off[e] .. m_off[e+1] of X, T and Y, and rows e N .. of the stacked
 // weight and of the stacked B (N = g.C); everything else is the plain kernel.
-template <bool kDQ, bool kGrp>
+// kFmt: 0 NF4 with float32 block constants, 1 NF4 with double-quantised constants, 2 E2M1 with
+// E4M3 group scales (groups of 16: the two groups of a thread's 32 elements get a table each) and
+// a float32 tensor scale S. E2M1 values times group scales are exact in bf16, so the weight
+// operand is decoded without rounding and S multiplies the accumulators in the epilogue; the
+// LoRA steps stage B times s / S to share the accumulators.
+template <int kFmt, bool kGrp>
 __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr) {
+  constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
   // X and W tiles as separate arrays: the compiler then knows that LDS accesses to one do not
   // alias the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sX0[kChunks], sX1[kChunks];
@@ -161,10 +168,17 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.a_side + m0 * K, rows_m * K * 2);
   const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wn0 * (K / 2), rows_n * (K / 2));
   const __amdgpu_buffer_rsrc_t rQ =
-      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + wn0 * kblk, rows_n * kblk)
-          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + wn0 * kblk, rows_n * kblk * 4);
+      kFP4  ? make_rsrc(reinterpret_cast<const uint8_t *>(g.w.absmax) + wn0 * (K / 16), rows_n * (K / 16))
+      : kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + wn0 * kblk, rows_n * kblk)
+            : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + wn0 * kblk, rows_n * kblk * 4);
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
+  // E2M1: the tensor scale (1 for an all-zero weight, whose group scales are all 0), read where
+  // it is used so that no register holds it through the main loop
+  auto tscale = [&]() {
+    const float S = *g.w.scale;
+    return S > 0.f ? S : 1.f;
+  };
 
   // X DMA: instruction i of wave w fills the 1 KB of the tile holding rows 8 (4 w + i) .. +7;
   // lane L writes physical chunk L % 8 of row 8 (4 w + i) + L / 8, i.e. logical chunk
@@ -184,9 +198,10 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   float lvh[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) lvh[i] = wh ? g.t.level[8 + i] : g.t.level[i];
-  const uint32_t mhi = wh ? 0u : 0xFFFFFFFFu, mlo = wh ? 0xFFFFFFFFu : 0u;
+  const uint32_t mhi = (wh && !kFP4) ? 0u : 0xFFFFFFFFu, mlo = (wh && !kFP4) ? 0xFFFFFFFFu : 0u;
   const uint32_t coff = (uint32_t)(wr * (K / 2) + wh * 16);
-  const uint32_t qoff = (uint32_t)(wr * kblk);
+  // E2M1: the two group scales of the thread's 32 elements (bytes 4 s + 2 wh, + 1 of its row)
+  const uint32_t qoff = kFP4 ? (uint32_t)(wr * (K / 16) + 2 * wh) : (uint32_t)(wr * kblk);
   const int64_t sbase = (wn0 + wr) * kblk;
 
   const int g16 = lane >> 4, l16 = lane & 15;
@@ -206,7 +221,9 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   constexpr int kCodeLoads = kDQ ? 3 : 2;   // loads issued by load_c
   auto load_c = [&](int s, CStage &c) {
     c.c = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
-    if (kDQ) {
+    if (kFP4) {
+      c.q = __builtin_amdgcn_raw_buffer_load_b16(rQ, qoff + 4 * s, 0, 0);
+    } else if (kDQ) {
       c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, qoff + s, 0, 0);
       c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)(((sbase + s) >> 8) * 4), 0, 0);
     } else {
@@ -220,10 +237,11 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     return j == 0 ? c.c.x : j == 1 ? c.c.y : j == 2 ? c.c.z : c.c.w;
   };
   auto decode_half = [&](const CStage &c, uint4 *sB) {
-    const RowTable t = make_row_table(absmax_of(c), g.t);
+    RowTable t = kFP4 ? make_e2m1_table(e4m3_to_f32(c.q & 0xFFu)) : make_row_table(absmax_of(c), g.t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
+      if (kFP4 && j == 2) t = make_e2m1_table(e4m3_to_f32((c.q >> 8) & 0xFFu));
       decode8(t, word(c, j), o);
       sB[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -272,19 +290,24 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     xb[1] = xfrag(A, 0, 1);
 
     // this thread's half of the table in L[0..1], H[0..1]; the partner lane's half by DPP
-    const float a = absmax_of(cn);
+    // (E2M1: the whole table of the thread's first group)
     RowTable t;
+    if (kFP4) {
+      t = make_e2m1_table(e4m3_to_f32(cn.q & 0xFFu));
+    } else {
+      const float a = absmax_of(cn);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t p0 = pack_bf16x2(lvh[4 * q] * a, lvh[4 * q + 1] * a);
-      const uint32_t p1 = pack_bf16x2(lvh[4 * q + 2] * a, lvh[4 * q + 3] * a);
-      t.L[q] = perm(p1, p0, 0x06040200u);
-      t.H[q] = perm(p1, p0, 0x07050301u);
-    }
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t p0 = pack_bf16x2(lvh[4 * q] * a, lvh[4 * q + 1] * a);
+        const uint32_t p1 = pack_bf16x2(lvh[4 * q + 2] * a, lvh[4 * q + 3] * a);
+        t.L[q] = perm(p1, p0, 0x06040200u);
+        t.H[q] = perm(p1, p0, 0x07050301u);
+      }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      t.L[2 + q] = swap_adjacent_lanes(t.L[q]);
-      t.H[2 + q] = swap_adjacent_lanes(t.H[q]);
+      for (int q = 0; q < 2; ++q) {
+        t.L[2 + q] = swap_adjacent_lanes(t.L[q]);
+        t.H[2 + q] = swap_adjacent_lanes(t.H[q]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     Dec8 dx;
@@ -314,6 +337,8 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
         } else {
           dec_piece(t, dx, 4, o, mhi, mlo);
           Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
+          // E2M1: words 2 and 3 belong to the thread's second group
+          if (kFP4 && j == 1) t = make_e2m1_table(e4m3_to_f32((cn.q >> 8) & 0xFFu));
         }
       }
       // keep each group's loads and decode work in place (hoisting them stretches register
@@ -348,7 +373,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
-    stage_lora(g, m0, wn0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
+    stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, wn0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
     __syncthreads();
     mma(xbuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(xbuf(buf), wbuf(buf), 1);
@@ -365,13 +390,16 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     uint4 *blk = (wave >> 1) == 0 ? sX0 : (wave >> 1) == 1 ? sX1 : (wave >> 1) == 2 ? sW0 : sW1;
     blk += (wave & 1) * (kChunks / 2);
     uint2 *b2 = reinterpret_cast<uint2 *>(blk);
+    const float tsc = kFP4 ? tscale() : 1.f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
         b2[swzf(mt * 16 + l16, 2 * nt + (g16 >> 1)) * 2 + (g16 & 1)] =
-            make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
-                       pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+            kFP4 ? make_uint2(pack_bf16x2(tsc * acc[nt][mt][0], tsc * acc[nt][mt][1]),
+                              pack_bf16x2(tsc * acc[nt][mt][2], tsc * acc[nt][mt][3]))
+                 : make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                              pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
     __syncthreads();
     const int c = lane & 7;
     const int64_t n = n0 + wn * 64 + c * 8;
@@ -387,14 +415,14 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   }
 }
 
-template <bool kDQ>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
-  fwd_body<kDQ, false>(g, GroupArgs{});
+  fwd_body<kFmt, false>(g, GroupArgs{});
 }
 
-template <bool kDQ>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(GemmArgs g, GroupArgs gr) {
-  fwd_body<kDQ, true>(g, gr);
+  fwd_body<kFmt, true>(g, gr);
 }
 
 }  // namespace
@@ -403,10 +431,12 @@ hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st) {
   if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0)
     return hipErrorInvalidValue;   // the epilogue writes 16-byte pieces of 8 columns
   const int64_t tiles = ((g.C + kT - 1) / kT) * ((g.M + kT - 1) / kT);
-  if (g.w.dq)
-    fwd_fused_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  if (g.w.fp4)
+    fwd_fused_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else if (g.w.dq)
+    fwd_fused_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   else
-    fwd_fused_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+    fwd_fused_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
 }
 
@@ -416,10 +446,12 @@ hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipSt
     return hipErrorInvalidValue;
   const int64_t tiles = gr.tile_off[gr.E];
   if (tiles < 1) return hipSuccess;
-  if (g.w.dq)
-    fwd_grouped_kernel<true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  if (g.w.fp4)
+    fwd_grouped_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  else if (g.w.dq)
+    fwd_grouped_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   else
-    fwd_grouped_kernel<false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+    fwd_grouped_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   return hipGetLastError();
 }
 

@@ -12,6 +12,11 @@ hipError_t launch_quantize(const void *w, bool f32_in, uint8_t *codes, void *abs
                            int64_t nblk, int dq, const Tables &t, hipStream_t st);
 hipError_t launch_dequantize(const WDesc &w, void *out, bool f32_out, const Tables &t,
                              hipStream_t st);
+// The E2M1 variant (fp4.hip): codes, E4M3 group scales (one per 16 elements) and the float32
+// tensor scale of nelem values; nelem % 16 == 0.
+hipError_t launch_fp4_quantize(const void *w, bool f32_in, int64_t nelem, uint8_t *codes,
+                               uint8_t *scales, float *tscale, hipStream_t st);
+hipError_t launch_fp4_dequantize(const WDesc &w, void *out, bool f32_out, hipStream_t st);
 
 // out[m][c] = bf16( sum_red a_side[m][red] * deq-side[c][red] + sum_j lora_a[m][j] * s*lora_b(c, j) )
 //   fwd: a_side = X [M,K], weight rows c = n (reduction over k), lora_a = T [M,r], lora_b = B [N,r]

@@ -80,6 +80,9 @@ def wdesc(n=64, k=128, block=64, dq=0, codes=FAKE, absmax=FAKE, scale=None):
     (dict(codes=None), m.NF4_EINVAL),
     (dict(dq=256, scale=None), m.NF4_EINVAL),
     (dict(codes=ctypes.c_void_p(4100)), m.NF4_EINVAL),
+    (dict(block=16, dq=256, scale=FAKE), m.NF4_EUNSUPPORTED),   # E2M1 takes no double quant
+    (dict(block=16, scale=None), m.NF4_EINVAL),                 # E2M1 needs its tensor scale
+    (dict(block=16, scale=ctypes.c_void_p(4104)), m.NF4_EINVAL),
 ])
 def test_quantize_rejects_bad_weight(desc, status):
     lib = m.library()
@@ -190,6 +193,7 @@ def test_merge_rejects_bad_arguments():
     assert mg(r=-1) == m.NF4_EINVAL
     assert mg(q=wdesc(n=64, k=100)) == m.NF4_EUNSUPPORTED
     assert mg(q=wdesc(n=1 << 20, k=1 << 12)) == m.NF4_EUNSUPPORTED      # n*k = 2^32
+    assert mg(q=wdesc(block=16, scale=FAKE)) == m.NF4_EUNSUPPORTED     # E2M1 weights: NF4 only
 
 
 def test_moe_calls_reject_bad_arguments():
