@@ -103,7 +103,8 @@ class Layer:
         self.A = host["A"].to(dev)
         self.B = host["B"].to(dev)
         self.dY = host["dY"].to(dev) if w.backward else None
-        q = lib.nf4_quantize(host["W"].to(dev), w.dq_block)
+        q = (lib.fp4_quantize(host["W"].to(dev)) if w.fmt == "e2m1"
+             else lib.nf4_quantize(host["W"].to(dev), w.dq_block))
         del host
         n = wcopies or max(1, min(64, math.ceil(COLD_BYTES / w.weight_stream_bytes())))
         self.copies = [q] + [q.clone() for _ in range(n - 1)]
@@ -268,7 +269,11 @@ def run_cpu_baseline(w, target_s):
     import workloads as wl
     from oracle import nf4, qlora
     W = wl.tensor(w, "W").float().numpy()
-    Wd = nf4.dequantize_f32(nf4.quantize(W, w.dq_block))
+    if w.fmt == "e2m1":
+        from oracle import fp4
+        Wd = fp4.dequantize_f32(fp4.quantize(W))
+    else:
+        Wd = nf4.dequantize_f32(nf4.quantize(W, w.dq_block))
     A, B = wl.tensor(w, "A").float().numpy(), wl.tensor(w, "B").float().numpy()
 
     Xall = wl.tensor(w, "X").float().numpy()
@@ -696,7 +701,7 @@ def main():
     step_ms, per = time_layer(L, args.steps, args.warmup)
     whole_fwd = time_call(L, L.fwd_whole, args.steps, args.warmup) if not w.backward else None
     ncopies = len(L.copies)
-    merge = run_merge(L, args.steps, args.warmup) if w.M > 64 else None
+    merge = run_merge(L, args.steps, args.warmup) if w.M > 64 and w.fmt == "nf4" else None
     context = None if args.no_context else run_context(L)
     del L
     torch.cuda.empty_cache()
@@ -724,8 +729,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: X [{M},{K}] bf16, W NF4 [{N},{K}] block 64"
-                               f"{' double-quant int8/256' if w.dq_block else ' fp32 absmax'}, "
+        "config": {"workload": f"{w.name}: X [{M},{K}] bf16, "
+                               + (f"W E2M1 [{N},{K}] E4M3 scale per 16 + fp32 tensor scale, " if w.fmt == "e2m1"
+                                  else f"W NF4 [{N},{K}] block 64"
+                                  f"{' double-quant int8/256' if w.dq_block else ' fp32 absmax'}, ") +
                                f"LoRA r={r} s={w.s}, {'fwd+bwd' if w.backward else 'fwd'}",
                    "M": M, "K": K, "N": N, "r": r, "weight_copies": ncopies,
                    "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}},

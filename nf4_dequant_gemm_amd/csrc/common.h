@@ -161,10 +161,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return e ? __uint_as_float(((b & 0x7Fu) << 20) + (120u << 23)) : float(b & 7u) * 0x1p-9f;
 }
 
-// Decode table of one group of 16: the 16 values bf16(e2m1[c] * s) in the RowTable byte-plane
-// layout. The products are exact (at most 6 significant bits), so the bf16 conversion does not
-// round. Entries 8..15 are entries 0..7 with the sign bit set: the same low bytes, high bytes with
-// bit 7 flipped.
+// Decode table of one group of 16: the 8 magnitudes bf16(e2m1[i] * s), i = 0..7, as byte planes
+// (L[0..1] low bytes, H[0..1] high bytes, four entries per word). The products are exact (at most
+// 6 significant bits), so the bf16 conversion does not round. The sign (code bit 3) is not in the
+// table: decode_e2m1 sets the bf16 sign bit from the code. L[2..3], H[2..3] are unused.
 __device__ __forceinline__ RowTable make_e2m1_table(float s) {
   const uint32_t p0 = pack_bf16x2(0.f, 0.5f * s), p1 = pack_bf16x2(s, 1.5f * s);
   const uint32_t p2 = pack_bf16x2(2.f * s, 3.f * s), p3 = pack_bf16x2(4.f * s, 6.f * s);
@@ -173,11 +173,47 @@ __device__ __forceinline__ RowTable make_e2m1_table(float s) {
   r.H[0] = perm(p1, p0, 0x07050301u);
   r.L[1] = perm(p3, p2, 0x06040200u);
   r.H[1] = perm(p3, p2, 0x07050301u);
-  r.L[2] = r.L[0];
-  r.L[3] = r.L[1];
-  r.H[2] = r.H[0] ^ 0x80808080u;
-  r.H[3] = r.H[1] ^ 0x80808080u;
+  r.L[2] = r.L[3] = r.H[2] = r.H[3] = 0u;
   return r;
+}
+
+// decode8 / dec_piece for E2M1 codes (same five-piece split and output order): one byte permute
+// per plane looks up the magnitude of 4 codes at once (3-bit index into 8 bytes), and the code's
+// sign bit is moved onto bit 7 of the high byte (the bf16 sign): bit 7 of each code byte for the
+// even elements, bit 3 (shifted left by 4) for the odd ones.
+__device__ __forceinline__ void dec_piece_e2m1(const RowTable &t, Dec8 &x, int piece, uint32_t out[4]) {
+  switch (piece) {
+    case 0:
+      x.se7 = (x.d >> 4) & 0x07070707u;
+      x.so7 = x.d & 0x07070707u;
+      break;
+    case 1:
+      x.Le = perm(t.L[1], t.L[0], x.se7);
+      x.He = perm(t.H[1], t.H[0], x.se7) | (x.d & 0x80808080u);
+      break;
+    case 2:
+      x.Lo = perm(t.L[1], t.L[0], x.so7);
+      x.Ho = perm(t.H[1], t.H[0], x.so7) | ((x.d << 4) & 0x80808080u);
+      break;
+    case 3:
+      x.E01 = perm(x.He, x.Le, 0x05010400u);
+      x.E23 = perm(x.He, x.Le, 0x07030602u);
+      break;
+    default: {
+      const uint32_t O01 = perm(x.Ho, x.Lo, 0x05010400u), O23 = perm(x.Ho, x.Lo, 0x07030602u);
+      out[0] = perm(O01, x.E01, 0x05040100u);
+      out[1] = perm(O01, x.E01, 0x07060302u);
+      out[2] = perm(O23, x.E23, 0x05040100u);
+      out[3] = perm(O23, x.E23, 0x07060302u);
+    }
+  }
+}
+
+__device__ __forceinline__ void decode8_e2m1(const RowTable &t, uint32_t d, uint32_t out[4]) {
+  Dec8 x;
+  x.d = d;
+#pragma unroll
+  for (int p = 0; p < 5; ++p) dec_piece_e2m1(t, x, p, out);
 }
 
 // Value of v in lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).

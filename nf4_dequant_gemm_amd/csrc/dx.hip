@@ -283,7 +283,7 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
     for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
       if (kFP4 && j == 2) t = fp4_table(c, 1);
-      decode8(t, word(c, j), o);
+      if (kFP4) decode8_e2m1(t, word(c, j), o); else decode8(t, word(c, j), o);
       wstore(sW, j, o);
     }
   };
@@ -370,13 +370,13 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
         uint32_t o[4];
         if (ph == 0) {
           dx.d = word(cn, j);
-          dec_piece(t, dx, 0, o, mhi, mlo);
-          dec_piece(t, dx, 1, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 0, o) : dec_piece(t, dx, 0, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 1, o) : dec_piece(t, dx, 1, o, mhi, mlo);
         } else if (ph == 1) {
-          dec_piece(t, dx, 2, o, mhi, mlo);
-          dec_piece(t, dx, 3, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 2, o) : dec_piece(t, dx, 2, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 3, o) : dec_piece(t, dx, 3, o, mhi, mlo);
         } else {
-          dec_piece(t, dx, 4, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 4, o) : dec_piece(t, dx, 4, o, mhi, mlo);
           wstore(Wn, j, o);
           if (kFP4 && j == 1) t = fp4_table(cn, 1);   // words 2, 3: the second group
         }

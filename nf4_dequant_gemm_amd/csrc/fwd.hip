@@ -242,7 +242,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
       if (kFP4 && j == 2) t = make_e2m1_table(e4m3_to_f32((c.q >> 8) & 0xFFu));
-      decode8(t, word(c, j), o);
+      if (kFP4) decode8_e2m1(t, word(c, j), o); else decode8(t, word(c, j), o);
       sB[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
@@ -329,16 +329,21 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
         uint32_t o[4];
         if (ph == 0) {
           dx.d = word(cn, j);
-          dec_piece(t, dx, 0, o, mhi, mlo);
-          dec_piece(t, dx, 1, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 0, o) : dec_piece(t, dx, 0, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 1, o) : dec_piece(t, dx, 1, o, mhi, mlo);
         } else if (ph == 1) {
-          dec_piece(t, dx, 2, o, mhi, mlo);
-          dec_piece(t, dx, 3, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 2, o) : dec_piece(t, dx, 2, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 3, o) : dec_piece(t, dx, 3, o, mhi, mlo);
         } else {
-          dec_piece(t, dx, 4, o, mhi, mlo);
+          kFP4 ? dec_piece_e2m1(t, dx, 4, o) : dec_piece(t, dx, 4, o, mhi, mlo);
           Bn[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
-          // E2M1: words 2 and 3 belong to the thread's second group
-          if (kFP4 && j == 1) t = make_e2m1_table(e4m3_to_f32((cn.q >> 8) & 0xFFu));
+          // E2M1: words 2 and 3 belong to the thread's second group. The empty asm keeps this
+          // table from being hoisted above the groups before (two live tables spill registers).
+          if (kFP4 && j == 1) {
+            uint32_t q2 = cn.q;
+            asm volatile("" : "+v"(q2));
+            t = make_e2m1_table(e4m3_to_f32((q2 >> 8) & 0xFFu));
+          }
         }
       }
       // keep each group's loads and decode work in place (hoisting them stretches register

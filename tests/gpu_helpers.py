@@ -9,7 +9,7 @@ import warnings
 import numpy as np
 import torch
 
-from oracle import nf4, qlora
+from oracle import fp4, nf4, qlora
 
 TOL = 1e-2   # max |got - ref| / max |ref| for Y, dX, dA, dB (bf16 outputs, fp32 accumulation)
 
@@ -43,6 +43,18 @@ def assert_quant_equal(qg, qo: nf4.NF4Weight):
     else:
         am = qg.absmax.cpu().numpy()
         assert np.array_equal(am.view(np.uint32), qo.absmax.view(np.uint32)), "absmax differs"
+
+
+def assert_fp4_equal(qg, qo: fp4.FP4Weight):
+    """GPU E2M1 tensor == oracle FP4Weight, bit for bit (codes, group scales, tensor scale)."""
+    codes = qg.codes.cpu().numpy()
+    bad = np.nonzero(codes != qo.codes)[0]
+    assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:5]}"
+    sc = qg.absmax.cpu().numpy()
+    bad = np.nonzero(sc != qo.scales)[0]
+    assert bad.size == 0, f"{bad.size} group scales differ, first at {bad[:5]}"
+    S = qg.scale.cpu().numpy()[0]
+    assert np.float32(S).view(np.uint32) == np.float32(qo.tscale).view(np.uint32), (S, qo.tscale)
 
 
 def check_close(name: str, got, ref, tol: float = TOL, warn_above: float = 4e-3):

@@ -17,22 +17,11 @@ import torch
 
 import workloads as wl
 from oracle import fp4, moe, nf4, qlora, swiglu
-from tests.gpu_helpers import check_close, f32, say, u16
+from tests.gpu_helpers import assert_fp4_equal, check_close, f32, say, u16
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-
-
-def assert_fp4_equal(qg, qo: fp4.FP4Weight):
-    codes = qg.codes.cpu().numpy()
-    bad = np.nonzero(codes != qo.codes)[0]
-    assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:5]}"
-    sc = qg.absmax.cpu().numpy()
-    bad = np.nonzero(sc != qo.scales)[0]
-    assert bad.size == 0, f"{bad.size} group scales differ, first at {bad[:5]}"
-    S = qg.scale.cpu().numpy()[0]
-    assert np.float32(S).view(np.uint32) == np.float32(qo.tscale).view(np.uint32), (S, qo.tscale)
 
 
 @pytest.mark.parametrize("n,k,std,f32_in", [

@@ -1,4 +1,5 @@
-"""GPU parity on the five full-size workloads (small, q_proj, mlp_up, decode, down).
+"""GPU parity on the full-size workloads (small, q_proj, mlp_up, decode, down, and mlp_up with an
+E2M1 base weight).
 
 The HIP path runs at full size, exactly as bench.py launches it. The quantised weight is compared
 bit for bit in full. Y, T and dX are compared on sampled rows (first, last and random rows), dA
@@ -10,8 +11,8 @@ import pytest
 import torch
 
 import workloads as wl
-from oracle import nf4, qlora
-from tests.gpu_helpers import assert_quant_equal, check_close, f32, say
+from oracle import fp4, nf4, qlora
+from tests.gpu_helpers import assert_fp4_equal, assert_quant_equal, check_close, f32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,14 +45,20 @@ def test_workload(lib, name):
     X = wl.tensor(w, "X")
     A = wl.tensor(w, "A")
     B = wl.tensor(w, "B")
-    qg = lib.nf4_quantize(W.to(DEV), w.dq_block)
+    e2m1 = w.fmt == "e2m1"
+    qg = lib.fp4_quantize(W.to(DEV)) if e2m1 else lib.nf4_quantize(W.to(DEV), w.dq_block)
     Xd, Ad, Bd = X.to(DEV), A.to(DEV), B.to(DEV)
     Yg, Tg = lib.qlora_fwd(Xd, qg, Ad, Bd, w.s)
     torch.cuda.synchronize()
     say("  fwd done")
-    qo = nf4.quantize(W.float().numpy(), w.dq_block)
-    assert_quant_equal(qg, qo)
-    Wd = nf4.dequantize_f32(qo)
+    if e2m1:
+        qo = fp4.quantize(W.float().numpy())
+        assert_fp4_equal(qg, qo)
+        Wd = fp4.dequantize_f32(qo)
+    else:
+        qo = nf4.quantize(W.float().numpy(), w.dq_block)
+        assert_quant_equal(qg, qo)
+        Wd = nf4.dequantize_f32(qo)
     del W
     Xf, Af, Bf = f32(X), f32(A), f32(B)
     rows = sample(w.M, 48, w.index)

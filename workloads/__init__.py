@@ -13,6 +13,7 @@ the Unsloth pages' "About the Unsloth Project" section):
   mlp_up  M=8192  K=4096   N=11008  r=64  s=0.5 absmax int8/256     fwd+bwd
   decode  M=16    K=8192   N=28672  r=16  s=2   absmax int8/256     fwd (weight-stream bound)
   down    M=16384 K=14336  N=4096   r=32  s=1   absmax int8/256     fwd+bwd
+  mlp_up_e2m1  the mlp_up shape with an E2M1 base (E4M3 scale per 16)  fwd+bwd
 
 and one gate/up pair (two projections on the same X joined by SwiGLU, PAIRS below):
 
@@ -57,6 +58,7 @@ class Workload:
     std_b: float
     std_dy: float
     backward: bool
+    fmt: str = "nf4"    # "nf4", or "e2m1": 4-bit floats, E4M3 scale per 16, float32 tensor scale
 
     @property
     def std_a(self) -> float:
@@ -85,6 +87,8 @@ class Workload:
     def weight_stream_bytes(self) -> int:
         nblk = self.N * self.K // 64
         codes = self.N * self.K // 2
+        if self.fmt == "e2m1":
+            return codes + self.N * self.K // 16 + 4
         if self.dq_block:
             return codes + nblk + 4 * ((nblk + self.dq_block - 1) // self.dq_block)
         return codes + 4 * nblk
@@ -96,6 +100,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("mlp_up", 3, 8192, 4096, 11008, 64, 0.5, 256, 1.0, 0.02, 0.01, 1.0, True),
     Workload("decode", 4, 16, 8192, 28672, 16, 2.0, 256, 1.0, 0.015, 0.01, 1.0, False),
     Workload("down", 5, 16384, 14336, 4096, 32, 1.0, 256, 1.0, 0.02, 0.01, 1e-2, True),
+    # the mlp_up shape with the E2M1 base weight (the 4-bit float variant of the format)
+    Workload("mlp_up_e2m1", 8, 8192, 4096, 11008, 64, 0.5, 0, 1.0, 0.02, 0.01, 1.0, True, "e2m1"),
 ]}
 
 
