@@ -43,6 +43,18 @@
  *     blocks decode with a' = fl32(q * S_j). Codes are always taken against the exact a.
  *   - dequantised element: w' = fl32(level[code] * a'); the GEMMs consume w' rounded to bf16
  *     (round-to-nearest-even) and accumulate in float32.
+ *
+ * E2M1 format (block == 16), the 4-bit floating-point variant of the same layer [NVFP4 update
+ * article, "NVFP4: A Quantization Format for the Next Generation of Hardware": E2M1 elements with
+ * 1 sign, 2 exponent and 1 mantissa bits up to +-6, groups of 16 or 32 sharing an FP8 scale]:
+ *   - element values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; code = sign << 3 | index.
+ *   - groups of 16 consecutive elements (k % 64 == 0 as for NF4); `absmax` holds one FP8 E4M3 byte
+ *     per group (bias 7, largest value 448), `absmax_scale` points to ONE float32 tensor scale.
+ *   - S = fl32(max |w| / 2688); group scale s = E4M3(fl32(max_g |w| / fl32(6 S))), nearest, ties
+ *     to even, saturating at 448 (S == 0: every s and code 0); code = E2M1(fl32(w / fl32(s S))),
+ *     nearest, ties to the even mantissa, saturating at 6, sign bit set for negative values.
+ *   - packing as NF4 (first element in the high nibble); dequantised w' = fl32(fl32(e2m1 * s) * S).
+ *   - the GEMMs consume e2m1 * s, which is exact in bf16, and multiply the float32 sums by S.
  */
 #ifndef NF4QLORA_H
 #define NF4QLORA_H
@@ -67,19 +79,23 @@ typedef enum { NF4_BF16 = 0, NF4_F32 = 1 } nf4_dtype;
  * pointers owned by the caller. */
 typedef struct {
   int64_t n, k;         /* logical shape of W; n >= 1, k >= 64, k % 64 == 0                  */
-  int32_t block;        /* absmax block length: must be 64                                   */
-  int32_t dq_block;     /* 0 (float32 absmax) or 256 (int8 absmax + float32 scale per run)   */
+  int32_t block;        /* 64: NF4; 16: E2M1 (see above)                                     */
+  int32_t dq_block;     /* NF4: 0 (float32 absmax) or 256 (int8 absmax + float32 run scale);
+                           E2M1: 0                                                            */
   uint8_t *codes;       /* [n*k/2] packed codes                                              */
-  void *absmax;         /* float[n*k/64] if dq_block == 0, else int8_t[n*k/64]               */
-  float *absmax_scale;  /* float[ceil(n*k/64/dq_block)] if dq_block > 0, else ignored         */
+  void *absmax;         /* NF4: float[n*k/64] if dq_block == 0, else int8_t[n*k/64];
+                           E2M1: uint8_t[n*k/16] E4M3 group scales                           */
+  float *absmax_scale;  /* NF4: float[ceil(n*k/64/dq_block)] if dq_block > 0, else ignored;
+                           E2M1: float[1], the tensor scale (written by nf4_quantize)        */
 } nf4_tensor;
 
-/* Quantise W (bf16 or float32, [q->n, q->k]) into the buffers of *q, as described above.
- * One kernel launch; no workspace. Bit-exact: the codes, absmax and scales equal those of the
+/* Quantise W (bf16 or float32, [q->n, q->k]) into the buffers of *q, as described above (NF4
+ * for block 64, E2M1 for block 16). NF4: one kernel launch; E2M1: four (the tensor maximum, then
+ * the groups). No workspace. Bit-exact: the codes, block constants and scales equal those of the
  * definition for every finite input.
  * Errors: NF4_EINVAL for a NULL pointer, a misaligned pointer or n < 1;
- *         NF4_EUNSUPPORTED for k % 64 != 0, block != 64, dq_block not in {0, 256}, or
- *         n*k >= 2^40. */
+ *         NF4_EUNSUPPORTED for k % 64 != 0, block not in {64, 16}, dq_block not in {0, 256}
+ *         (0 for E2M1), or n*k >= 2^40. */
 int nf4_quantize(const void *w, int w_dtype, const nf4_tensor *q, void *stream);
 
 /* Write deq(W) to out [n,k] as float32 (w', exact) or bf16 (w' rounded to nearest-even).
@@ -202,7 +218,8 @@ int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor 
  * rounded once to bf16. With r == 0 (A, B NULL) Wout equals nf4_dequantize's bf16 output bit for
  * bit. Re-quantising for export is nf4_quantize of Wout (a new NF4 tensor [n, k]).
  * Errors: NF4_EINVAL for NULL/misaligned pointers or r outside [0, 128]; NF4_EUNSUPPORTED for the
- * NF4 format limits of nf4_quantize or n*k >= 2^32. */
+ * NF4 format limits of nf4_quantize, an E2M1 weight (block 16: not implemented for the merge) or
+ * n*k >= 2^32. */
 int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, float s, void *Wout,
                 void *stream);
 
