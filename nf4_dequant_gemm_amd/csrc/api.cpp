@@ -278,10 +278,38 @@ int check_moe(const void *X, const int64_t *counts, int32_t E, const nf4_tensor 
   return NF4_OK;
 }
 
-// Workspace of the grouped layer. Forward: the largest expert's row-projection partials.
-// Backward: U [sum(counts), r] at 0, the transposed stacked B [r, E n] at u, T (recomputed when
-// the caller passes none) at u + bt, then the largest expert's partials (experts run in stream
-// order, so they share them).
+// Launch plan of the grouped layer's rank-r products: the row projections (T = X_e A_e^T,
+// U = dY_e B_e) run over every expert's 64-row blocks in one launch, split over the reduction
+// like the single layer's; the M-reductions (dA_e, dB_e) run over (expert, column tile, split)
+// in one launch, with the same split count for every expert, aiming at about 1024 workgroups.
+struct MoePlan {
+  int64_t blocks64 = 0, maxrows = 0;
+  int sp_k = 1, sp_n = 1, sa = 1, sb = 1;
+};
+
+MoePlan moe_plan(const Moe &mo, int32_t E, int64_t k) {
+  MoePlan pl;
+  for (int e = 0; e < E; ++e) {
+    const int64_t me = mo.off[e + 1] - mo.off[e];
+    pl.blocks64 += (me + 63) / 64;
+    pl.maxrows = std::max(pl.maxrows, me);
+  }
+  pl.sp_k = nf4q::rowproj_splits(pl.blocks64 * 64, k);
+  pl.sp_n = nf4q::rowproj_splits(pl.blocks64 * 64, mo.n);
+  auto mr = [&](int64_t C) {
+    const int64_t ct = (C + 127) / 128;
+    int64_t sp = (1024 + ct * E - 1) / (ct * E);
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, (pl.maxrows + 63) / 64));
+    return (int)std::max<int64_t>(sp, 1);
+  };
+  pl.sa = mr(k);
+  pl.sb = mr(mo.n);
+  return pl;
+}
+
+// Workspace of the grouped layer: U [sum(counts), r] at 0, the transposed stacked B [r, E n] at
+// u, T (recomputed when the caller passes none) at u + bt, then float partials of the row
+// projections or of the M-reductions (never both at once).
 struct MoeWs {
   size_t u = 0, bt = 0, t = 0, part = 0, total = 0;
 };
@@ -289,15 +317,16 @@ struct MoeWs {
 MoeWs moe_ws_layout(const Moe &mo, int32_t E, int64_t k, int32_t r) {
   MoeWs w;
   if (r <= 0) return w;
+  const MoePlan pl = moe_plan(mo, E, k);
   w.u = align256((size_t)mo.mtotal * r * 2);
   w.bt = align256((size_t)r * E * mo.n * 2);
   w.t = w.u;
-  for (int e = 0; e < E; ++e) {
-    const int64_t me = mo.off[e + 1] - mo.off[e];
-    if (me < 1) continue;
-    w.part = std::max(w.part, fwd_ws(me, k, r).part);
-    w.part = std::max(w.part, bwd_ws(me, mo.n, k, r).part);
-  }
+  size_t p = 0;
+  if (pl.sp_k > 1) p = std::max(p, (size_t)pl.sp_k * mo.mtotal * r * 4);
+  if (pl.sp_n > 1) p = std::max(p, (size_t)pl.sp_n * mo.mtotal * r * 4);
+  p = std::max(p, (size_t)E * pl.sa * r * k * 4);
+  p = std::max(p, (size_t)E * pl.sb * r * mo.n * 4);
+  w.part = align256(p);
   w.total = w.u + w.bt + w.t + w.part;
   return w;
 }
@@ -307,14 +336,14 @@ size_t moe_ws(const Moe &mo, int32_t E, int64_t k, int32_t r) {
 }
 
 // Groups of the grouped launches: experts' row offsets and the first tile of each expert (its
-// rows in 256-row blocks times `tiles_c` column tiles).
-int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr) {
+// rows in blocks of `rows` times `tiles_c` column tiles).
+int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr, int64_t rows = 256) {
   gr->E = E;
   gr->tile_off[0] = 0;
   for (int e = 0; e <= E; ++e) gr->m_off[e] = mo.off[e];
   for (int e = 0; e < E; ++e) {
     const int64_t me = mo.off[e + 1] - mo.off[e];
-    const int64_t t = gr->tile_off[e] + (me + 255) / 256 * tiles_c;
+    const int64_t t = gr->tile_off[e] + (me + rows - 1) / rows * tiles_c;
     if (t >= (int64_t(1) << 31)) return fail(NF4_EUNSUPPORTED, "too many tiles");
     gr->tile_off[e + 1] = (int32_t)t;
   }
@@ -670,16 +699,18 @@ int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_ten
   if (ws_bytes < need || (need && !ws))
     return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
   if (need && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
-  // T = X_e A_e^T for each expert's rows (one row projection per expert with rows)
-  if (r > 0)
-    for (int e = 0; e < E; ++e) {
-      const int64_t me = mo.off[e + 1] - mo.off[e];
-      if (me < 1) continue;
-      st = qlora_lora_down((const uint16_t *)X + mo.off[e] * k, me, k,
-                           (const uint16_t *)A + (int64_t)e * r * k, r,
-                           (uint16_t *)T + mo.off[e] * r, ws, ws_bytes, stream);
-      if (st) return st;
-    }
+  // T = X_e A_e^T for every expert's rows in one grouped row projection
+  if (r > 0) {
+    nf4q::GroupArgs g64;
+    st = moe_groups(mo, E, 1, &g64, 64);
+    if (st) return st;
+    const MoePlan pl = moe_plan(mo, E, k);
+    const MoeWs lay = moe_ws_layout(mo, E, k, r);
+    hipError_t he = nf4q::launch_rowproj_grouped(
+        (const uint16_t *)X, k, (const uint16_t *)A, (int64_t)r * k, k, mo.mtotal, k, r, pl.sp_k,
+        (float *)((char *)ws + lay.u + lay.bt + lay.t), (uint16_t *)T, g64, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_fwd T launch");
+  }
   return qlora_moe_fwd_fused(X, counts, E, W, T, B, r, s, Y, stream);
 }
 
@@ -712,25 +743,25 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
   const uint16_t *dy = (const uint16_t *)dY, *x = (const uint16_t *)X;
   const uint16_t *a = (const uint16_t *)A;
   hipError_t he;
-  // U = dY_e B_e for each expert's rows (and T = X_e A_e^T when the caller keeps none), from one
-  // transpose of the stacked B: Bt [r, E n], expert e's columns e n .. e n + n - 1
+  // U = dY_e B_e for every expert's rows in one grouped row projection (and T = X_e A_e^T the
+  // same way when the caller keeps none), B_e from one transpose of the stacked B: Bt [r, E n],
+  // expert e's columns e n .. e n + n - 1
+  const MoePlan pl = moe_plan(mo, E, k);
+  nf4q::GroupArgs g64;
+  st = moe_groups(mo, E, 1, &g64, 64);
+  if (st) return st;
   if (r > 0) {
     he = nf4q::launch_transpose((const uint16_t *)B, E * n, r, Bt, sm);
     if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd transpose launch");
-    uint16_t *Tw = T ? nullptr : (uint16_t *)(base + lay.u + lay.bt);
-    for (int e = 0; e < E; ++e) {
-      const int64_t me = mo.off[e + 1] - mo.off[e];
-      if (me < 1) continue;
-      if (Tw) {
-        he = nf4q::launch_rowproj(x + mo.off[e] * k, k, a + (int64_t)e * r * k, k, me, k, r,
-                                  nf4q::rowproj_splits(me, k), part, Tw + mo.off[e] * r, sm);
-        if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd T launch");
-      }
-      he = nf4q::launch_rowproj(dy + mo.off[e] * n, n, Bt + e * n, E * n, me, n, r,
-                                nf4q::rowproj_splits(me, n), part, U + mo.off[e] * r, sm);
-      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd U launch");
+    if (!T) {
+      uint16_t *Tw = (uint16_t *)(base + lay.u + lay.bt);
+      he = nf4q::launch_rowproj_grouped(x, k, a, (int64_t)r * k, k, mo.mtotal, k, r, pl.sp_k, part, Tw,
+                                        g64, sm);
+      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd T launch");
+      T = Tw;
     }
-    if (Tw) T = Tw;
+    he = nf4q::launch_rowproj_grouped(dy, n, Bt, n, E * n, mo.mtotal, n, r, pl.sp_n, part, U, g64, sm);
+    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd U launch");
   }
   // dX of every expert in one launch
   if (dX) {
@@ -754,22 +785,13 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
     he = nf4q::launch_gemm_dx_grouped(g, gr, sm);
     if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dX launch");
   }
-  // dA_e = s U_e^T X_e, dB_e = s dY_e^T T_e (zero for an expert with no rows)
-  for (int e = 0; e < E && r > 0; ++e) {
-    const int64_t me = mo.off[e + 1] - mo.off[e];
-    uint16_t *dAe = (uint16_t *)dA + (int64_t)e * r * k;
-    uint16_t *dBe = (uint16_t *)dB + (int64_t)e * n * r;
-    if (me < 1) {
-      he = nf4q::launch_zero(dAe, (int64_t)r * k * 2, sm);
-      if (he == hipSuccess) he = nf4q::launch_zero(dBe, n * r * 2, sm);
-      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd launch");
-      continue;
-    }
-    he = nf4q::launch_mreduce(U + mo.off[e] * r, x + mo.off[e] * k, k, me, k, r, s,
-                              nf4q::mreduce_splits(me, k), part, dAe, false, sm);
+  // dA_e = s U_e^T X_e, dB_e = s dY_e^T T_e over each expert's own rows, every expert in one
+  // launch each (an expert with no rows sums nothing: zero gradients)
+  if (r > 0) {
+    he = nf4q::launch_mreduce_grouped(U, x, k, k, r, s, pl.sa, part, (uint16_t *)dA, false, g64, sm);
     if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dA launch");
-    he = nf4q::launch_mreduce((const uint16_t *)T + mo.off[e] * r, dy + mo.off[e] * n, n, me, n, r,
-                              s, nf4q::mreduce_splits(me, n), part, dBe, true, sm);
+    he = nf4q::launch_mreduce_grouped((const uint16_t *)T, dy, n, n, r, s, pl.sb, part, (uint16_t *)dB,
+                                      true, g64, sm);
     if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dB launch");
   }
   return ok();

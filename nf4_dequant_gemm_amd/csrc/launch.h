@@ -86,6 +86,16 @@ int mreduce_splits(int64_t M, int64_t C);
 
 // dst[j][l] = src[l][j] for a bf16 [L][r] matrix.
 hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst, hipStream_t st);
+// Grouped forms (rows grouped by expert as gr.m_off says). Row projection: expert e's p is
+// p + e * pstride, gr.tile_off[e] = its first 64-row block, partials need splits * M * r floats.
+// M-reduction: one [r][C] sum per expert over its own rows, written at out + e r C (transposed:
+// [C][r] there); partials need E * splits * r * C floats.
+hipError_t launch_rowproj_grouped(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t pstride,
+                                  int64_t ldp, int64_t M, int64_t L, int r, int splits, float *part,
+                                  uint16_t *out, const GroupArgs &gr, hipStream_t st);
+hipError_t launch_mreduce_grouped(const uint16_t *P, const uint16_t *Q, int64_t ldq, int64_t C, int r,
+                                  float s, int splits, float *part, uint16_t *out,
+                                  bool transposed_out, const GroupArgs &gr, hipStream_t st);
 
 // Gate/up SwiGLU pair (swiglu.hip). ygu / dygu rows: the gate block then the up block, 2n columns.
 hipError_t launch_swiglu_fwd(const uint16_t *ygu, int64_t m, int64_t n, uint16_t *h, hipStream_t st);
@@ -99,8 +109,5 @@ hipError_t launch_diagblocks(const uint16_t *db2, int64_t n, int r, uint16_t *db
 // LoRA merge (merge.hip): out bf16 [n, k] = bf16(deq(W) + s B A), 0 <= r <= 128, k % 64 == 0.
 hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, int r, float s,
                         const Tables &t, uint16_t *out, hipStream_t st);
-
-// Zero `bytes` (a multiple of 16) at the 16-byte aligned p with a fill kernel.
-hipError_t launch_zero(void *p, int64_t bytes, hipStream_t st);
 
 }  // namespace nf4q

@@ -22,18 +22,29 @@ namespace nf4q {
 // c ^ ((i >> 1) & 7)), from where the fragments are read.
 __device__ __forceinline__ int swzr(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 
-template <int TN>
-__global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict__ in, int64_t ldin,
-                                                      const uint16_t *__restrict__ p, int64_t ldp,
-                                                      int64_t M, int64_t L, int r, int64_t lsplit,
-                                                      float *__restrict__ part, int smajor,
-                                                      uint16_t *__restrict__ out) {
+// kGrp: rows grouped by expert (rows gr.m_off[e] .. gr.m_off[e+1] - 1 of `in` and `out` belong
+// to expert e, whose p is p + e * pstride); the launch's 64-row blocks are every expert's blocks
+// in turn (expert e's first block is gr.tile_off[e]). The partial-sum layout is over all M rows.
+template <int TN, bool kGrp>
+__device__ __forceinline__ void rowproj_body(const uint16_t *__restrict__ in, int64_t ldin,
+                                             const uint16_t *__restrict__ p, int64_t ldp, int64_t M,
+                                             int64_t L, int r, int64_t lsplit,
+                                             float *__restrict__ part, int smajor,
+                                             uint16_t *__restrict__ out, const GroupArgs &gr,
+                                             int64_t pstride) {
   constexpr int PCH = TN * 16 * 8;                 // p-tile chunks per step
   constexpr int PPT = (PCH + 255) / 256;           // p-tile chunks per thread
   __shared__ uint4 sI[2][64 * 8];
   __shared__ uint4 sP[2][TN * 16 * 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t mbase = (int64_t)blockIdx.x * 64;
+  int64_t mbase = (int64_t)blockIdx.x * 64, mhi = M;
+  if (kGrp) {
+    int e = 0;
+    while (e + 1 < gr.E && (int)blockIdx.x >= gr.tile_off[e + 1]) ++e;
+    mbase = gr.m_off[e] + (int64_t)((int)blockIdx.x - gr.tile_off[e]) * 64;
+    mhi = gr.m_off[e + 1];
+    p += e * pstride;
+  }
   const int split = blockIdx.y;
   const int64_t lb = split * lsplit;
   const int64_t le = (lb + lsplit < L) ? lb + lsplit : L;
@@ -52,7 +63,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
       const int qd = tid + 256 * i;
       const int row = qd >> 3, c = qd & 7;
       const int64_t m = mbase + row, l = l0 + c * 8;
-      st.x[i] = (m < M && l < le) ? *reinterpret_cast<const uint4 *>(in + m * ldin + l) : make_uint4(0, 0, 0, 0);
+      st.x[i] = (m < mhi && l < le) ? *reinterpret_cast<const uint4 *>(in + m * ldin + l) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
     for (int v = 0; v < 4; ++v) {
       const int64_t row = mbase + wave * 16 + 4 * (lane >> 4) + v;
       const int j = t * 16 + (lane & 15);
-      if (row < M && j < r) {
+      if (row < mhi && j < r) {
         if (part && smajor)   // [split][M][r]: a workgroup's partials form one contiguous block
           part[((int64_t)split * M + row) * r + j] = acc[t][v];
         else if (part)        // [M][r][split]: the splits of one output form one contiguous run
@@ -124,6 +135,23 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict
           out[row * r + j] = (uint16_t)(pack_bf16x2(acc[t][v], 0.f) & 0xFFFFu);
       }
     }
+}
+
+template <int TN>
+__global__ __launch_bounds__(256) void rowproj_kernel(const uint16_t *__restrict__ in, int64_t ldin,
+                                                      const uint16_t *__restrict__ p, int64_t ldp,
+                                                      int64_t M, int64_t L, int r, int64_t lsplit,
+                                                      float *__restrict__ part, int smajor,
+                                                      uint16_t *__restrict__ out) {
+  rowproj_body<TN, false>(in, ldin, p, ldp, M, L, r, lsplit, part, smajor, out, GroupArgs{}, 0);
+}
+
+template <int TN>
+__global__ __launch_bounds__(256) void rowproj_grouped_kernel(
+    const uint16_t *__restrict__ in, int64_t ldin, const uint16_t *__restrict__ p, int64_t ldp,
+    int64_t M, int64_t L, int r, int64_t lsplit, float *__restrict__ part, int smajor,
+    uint16_t *__restrict__ out, GroupArgs gr, int64_t pstride) {
+  rowproj_body<TN, true>(in, ldin, p, ldp, M, L, r, lsplit, part, smajor, out, gr, pstride);
 }
 
 // The same product for at most 16 rows (decode shapes), where the reduction is short and a
@@ -262,6 +290,32 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
   return hipGetLastError();
 }
 
+hipError_t launch_rowproj_grouped(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t pstride,
+                                  int64_t ldp, int64_t M, int64_t L, int r, int splits, float *part,
+                                  uint16_t *out, const GroupArgs &gr, hipStream_t st) {
+  const int blocks = gr.tile_off[gr.E];
+  if (blocks < 1) return hipSuccess;
+  int64_t lsplit = (L + splits - 1) / splits;
+  lsplit = (lsplit + 63) / 64 * 64;
+  const dim3 grid((unsigned)blocks, (unsigned)splits);
+  float *pp = splits > 1 ? part : nullptr;
+  const int tn = (r + 15) / 16;
+  switch (tn) {
+#define RP_CASE(T) \
+  case T: rowproj_grouped_kernel<T><<<grid, dim3(256), 0, st>>>(in, ldin, p, ldp, M, L, r, lsplit, pp, 1, out, gr, pstride); break;
+    RP_CASE(1) RP_CASE(2) RP_CASE(3) RP_CASE(4) RP_CASE(5) RP_CASE(6) RP_CASE(7) RP_CASE(8)
+#undef RP_CASE
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n = M * r;
+  int64_t nb = (n + 255) / 256;
+  if (nb > 4096) nb = 4096;
+  rowproj_reduce_kernel<<<dim3((unsigned)nb), dim3(256), 0, st>>>(part, n, splits, out);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------ mreduce
 // out[j][c] = sum over m of P[m][j] * Q[m][c]  (dA: P = U, Q = X;  dB: P = T, Q = dY).
 // Workgroup: 128 columns c x all r (<= 128) rows j, over one split of the M rows in stages of 64,
@@ -281,19 +335,29 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint16_t *p) {
       (__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-template <int TJ>
-__global__ __launch_bounds__(256) void mreduce_kernel(const uint16_t *__restrict__ P,
-                                                      const uint16_t *__restrict__ Q, int64_t ldq,
-                                                      int64_t M, int64_t C, int r, int64_t msplit,
-                                                      float *__restrict__ part) {
+// kGrp: one sum per expert over its own rows (expert blockIdx.z: rows gr.m_off[z] ..
+// gr.m_off[z+1] - 1, cut into gridDim.y splits of whole 64-row stages); partials
+// [expert][split][r][C].
+template <int TJ, bool kGrp>
+__device__ __forceinline__ void mreduce_body(const uint16_t *__restrict__ P,
+                                             const uint16_t *__restrict__ Q, int64_t ldq, int64_t M,
+                                             int64_t C, int r, int64_t msplit,
+                                             float *__restrict__ part, const GroupArgs &gr) {
   constexpr int PROW = TJ * 16 + 16;          // P row stride in bf16 (padded by 32 bytes)
   __shared__ uint16_t sQ[2][kMR_BM * kMR_QROW];
   __shared__ uint16_t sP[2][kMR_BM * PROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kMR_BC;
   const int split = blockIdx.y;
-  const int64_t mb = split * msplit;
-  const int64_t me = (mb + msplit < M) ? mb + msplit : M;
+  int64_t lo = 0, hi = M;
+  if (kGrp) {
+    lo = gr.m_off[blockIdx.z];
+    hi = gr.m_off[blockIdx.z + 1];
+    msplit = (hi - lo + gridDim.y - 1) / gridDim.y;
+    msplit = (msplit + kMR_BM - 1) / kMR_BM * kMR_BM;
+  }
+  const int64_t mb = lo + split * msplit;
+  const int64_t me = (mb + msplit < hi) ? mb + msplit : hi;
   const bool pvec = (r & 7) == 0;
 
   f32x4 acc[TJ][2];
@@ -410,29 +474,50 @@ __global__ __launch_bounds__(256) void mreduce_kernel(const uint16_t *__restrict
       for (int v = 0; v < 4; ++v) {
         const int j = t * 16 + 4 * g16 + v;
         const int64_t c = c0 + wave * 32 + u * 16 + l16;
-        if (j < r && c < C) part[((int64_t)split * r + j) * C + c] = acc[t][u][v];
+        if (j < r && c < C)
+          part[(((int64_t)blockIdx.z * gridDim.y + split) * r + j) * C + c] = acc[t][u][v];
       }
 }
 
+template <int TJ>
+__global__ __launch_bounds__(256) void mreduce_kernel(const uint16_t *__restrict__ P,
+                                                      const uint16_t *__restrict__ Q, int64_t ldq,
+                                                      int64_t M, int64_t C, int r, int64_t msplit,
+                                                      float *__restrict__ part) {
+  mreduce_body<TJ, false>(P, Q, ldq, M, C, r, msplit, part, GroupArgs{});
+}
+
+template <int TJ>
+__global__ __launch_bounds__(256) void mreduce_grouped_kernel(const uint16_t *__restrict__ P,
+                                                              const uint16_t *__restrict__ Q,
+                                                              int64_t ldq, int64_t C, int r,
+                                                              float *__restrict__ part, GroupArgs gr) {
+  mreduce_body<TJ, true>(P, Q, ldq, gr.m_off[gr.E], C, r, 0, part, gr);
+}
+
+// out = s * (sum over splits of part), for E blocks of [r][C] (E = 1 unless grouped); block e of
+// the output is [r][C] at out + e r C, or [C][r] there when transposed.
 __global__ void mreduce_final_kernel(const float *__restrict__ part, int64_t C, int r, int splits,
-                                     float s, bool transposed, uint16_t *__restrict__ out) {
+                                     int E, float s, bool transposed, uint16_t *__restrict__ out) {
   const int64_t n = (int64_t)r * C;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n * E;
        i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / n, ie = i - e * n;
+    const float *pe = part + e * splits * n + ie;
     float a = 0.f;
     int sp = 0;
     for (; sp + 8 <= splits; sp += 8) {   // fixed-order sum, loads issued eight at a time
       float v8[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v8[j] = part[(int64_t)(sp + j) * n + i];
+      for (int j = 0; j < 8; ++j) v8[j] = pe[(int64_t)(sp + j) * n];
 #pragma unroll
       for (int j = 0; j < 8; ++j) a += v8[j];
     }
-    for (; sp < splits; ++sp) a += part[(int64_t)sp * n + i];
+    for (; sp < splits; ++sp) a += pe[(int64_t)sp * n];
     const uint16_t v = (uint16_t)(pack_bf16x2(s * a, 0.f) & 0xFFFFu);
-    const int64_t j = i / C, c = i % C;
+    const int64_t j = ie / C, c = ie % C;
     if (transposed)
-      out[c * r + j] = v;
+      out[e * n + c * r + j] = v;
     else
       out[i] = v;
   }
@@ -466,7 +551,29 @@ hipError_t launch_mreduce(const uint16_t *P, const uint16_t *Q, int64_t ldq, int
   const int64_t n = (int64_t)r * C;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  mreduce_final_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(part, C, r, splits, s,
+  mreduce_final_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(part, C, r, splits, 1, s,
+                                                                     transposed_out, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mreduce_grouped(const uint16_t *P, const uint16_t *Q, int64_t ldq, int64_t C, int r,
+                                  float s, int splits, float *part, uint16_t *out,
+                                  bool transposed_out, const GroupArgs &gr, hipStream_t st) {
+  const dim3 grid((unsigned)((C + kMR_BC - 1) / kMR_BC), (unsigned)splits, (unsigned)gr.E);
+  const int tj = (r + 15) / 16;
+  switch (tj) {
+#define MR_CASE(T) \
+  case T: mreduce_grouped_kernel<T><<<grid, dim3(256), 0, st>>>(P, Q, ldq, C, r, part, gr); break;
+    MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4) MR_CASE(5) MR_CASE(6) MR_CASE(7) MR_CASE(8)
+#undef MR_CASE
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)gr.E * r * C;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  mreduce_final_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(part, C, r, splits, gr.E, s,
                                                                      transposed_out, out);
   return hipGetLastError();
 }
@@ -487,25 +594,6 @@ hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   transpose_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(src, L, r, dst);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------ zeroing
-// A plain fill kernel (16-byte stores) rather than a memset, so that callers may capture the
-// calls that use it in a graph.
-__global__ __launch_bounds__(256) void zero_kernel(uint4 *__restrict__ p, int64_t n16) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = make_uint4(0, 0, 0, 0);
-}
-
-hipError_t launch_zero(void *p, int64_t bytes, hipStream_t st) {
-  if (bytes % 16 || (reinterpret_cast<uintptr_t>(p) & 15)) return hipErrorInvalidValue;
-  const int64_t n16 = bytes / 16;
-  if (n16 == 0) return hipSuccess;
-  int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(reinterpret_cast<uint4 *>(p), n16);
   return hipGetLastError();
 }
 
