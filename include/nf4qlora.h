@@ -217,9 +217,10 @@ int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor 
  * launch: the rank-r product on the matrix cores, deq(W) = fl32(level * a') added in float32,
  * rounded once to bf16. With r == 0 (A, B NULL) Wout equals nf4_dequantize's bf16 output bit for
  * bit. Re-quantising for export is nf4_quantize of Wout (a new NF4 tensor [n, k]).
+ * An E2M1 weight (block 16) merges the same way with w' its E2M1 dequantisation; re-quantising
+ * Wout with block 16 gives a compressed FP4 export of the merged layer.
  * Errors: NF4_EINVAL for NULL/misaligned pointers or r outside [0, 128]; NF4_EUNSUPPORTED for the
- * NF4 format limits of nf4_quantize, an E2M1 weight (block 16: not implemented for the merge) or
- * n*k >= 2^32. */
+ * format limits of nf4_quantize or n*k >= 2^32. */
 int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, float s, void *Wout,
                 void *stream);
 

@@ -306,8 +306,9 @@ def qlora_bwd_dx(dY: torch.Tensor, q: NF4Tensor, U: Optional[torch.Tensor], A: O
 
 
 def qlora_merge(q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tensor], s: float,
-                requantize: Optional[int] = None):
-    """W' = bf16(deq(W) + s B A) [n, k]; with requantize = dq_block, nf4_quantize(W') instead."""
+                requantize=None):
+    """W' = bf16(deq(W) + s B A) [n, k] (NF4 or E2M1 base); with requantize = a dq_block (0, 256),
+    nf4_quantize(W') instead, with requantize = "e2m1", fp4_quantize(W')."""
     r = 0 if A is None else A.shape[0]
     if r:
         _need(A, "A", torch.bfloat16, (r, q.k))
@@ -318,6 +319,8 @@ def qlora_merge(q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tenso
                                  _stream(q.device)))
     if requantize is None:
         return out
+    if requantize == "e2m1":
+        return fp4_quantize(out)
     return nf4_quantize(out, requantize)
 
 

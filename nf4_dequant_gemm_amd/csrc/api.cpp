@@ -631,9 +631,6 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
                 void *stream) {
   int st = check_weight(W);
   if (st) return st;
-  if (W->block != 64)
-    return fail(NF4_EUNSUPPORTED, "qlora_merge takes NF4 weights (block 64) only (got block %d)",
-                W->block);
   if (W->n * W->k >= (int64_t(1) << 32))
     return fail(NF4_EUNSUPPORTED, "n*k must be below 2^32 for qlora_merge");
   if (r < 0 || r > 128) return fail(NF4_EINVAL, "r must lie in [0, 128] (got %d)", r);

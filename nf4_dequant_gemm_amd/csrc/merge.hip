@@ -9,7 +9,9 @@
 // consecutive rows r of one column k, the operand layout with r as the reduction index), B [n, r]
 // is staged row-major and read 16 bytes per lane. The tile's codes (one 16-byte load per thread)
 // and its block constants are staged in LDS as well: loaded per lane, 2 bytes at a time, they
-// made the kernel request-bound (1.35 TB/s). With A as the first operand, a lane holds 4
+// made the kernel request-bound (1.35 TB/s). For an E2M1 weight the constants are the tile's E4M3
+// group scales (8 per row), the levels the E2M1 values, and the dequantised element is
+// fl32(fl32(e2m1 * s_g) * S) with S the tensor scale. With A as the first operand, a lane holds 4
 // consecutive columns k of one row n; it adds fl32(level * a') of those 4 elements (codes, block
 // constant and a 16-entry level table from LDS) to s times the fp32 sum, rounds to bf16 and
 // stages the tile in LDS, from which rows leave in 16-byte pieces. The work is the weight stream:
@@ -34,6 +36,7 @@ __device__ __forceinline__ int aunit(int j, int u) {
   return j * kTK + ((u ^ (4 * ((j + 4 * (j >> 3)) & 7))) << 2);
 }
 
+template <bool kFP4>
 __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, int r,
                                                          float s, Tables t, uint16_t *__restrict__ out) {
@@ -47,15 +50,24 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
   const int bstride = rp + 8;
   uint16_t *sO = reinterpret_cast<uint16_t *>(smem);                    // kTN * kTK bf16
   uint8_t *sC = smem + kTN * kTK * 2;                                    // kTN * kTK / 2 bytes
-  float *sAbs = reinterpret_cast<float *>(sC + kTN * kTK / 2);          // 2 per row
-  float *sLv = sAbs + kTN * kTK / 64;                                    // 16 levels
+  float *sAbs = reinterpret_cast<float *>(sC + kTN * kTK / 2);          // 2 (NF4) or 8 per row
+  float *sLv = sAbs + kTN * kTK / 16;                                    // 16 levels
   uint16_t *sA = reinterpret_cast<uint16_t *>(sLv + 16);                 // rp * kTK bf16
   uint16_t *sB = sA + rp * kTK;                                          // kTN * bstride bf16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int64_t N = w.n, K = w.k;
   const int64_t n0 = (int64_t)blockIdx.y * kTN, k0 = (int64_t)blockIdx.x * kTK;
-  if (tid < 16) sLv[tid] = t.level[tid];
+  if (tid < 16) {
+    if (kFP4) {   // E2M1 value of code tid: sign bit 3, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
+      const int mi = tid & 7;
+      const float mag = mi < 4 ? 0.5f * float(mi) : (mi == 4 ? 2.f : mi == 5 ? 3.f : mi == 6 ? 4.f : 6.f);
+      sLv[tid] = (tid & 8) ? -mag : mag;
+    } else {
+      sLv[tid] = t.level[tid];
+    }
+  }
+  const float tsc = kFP4 ? *w.scale : 1.f;
   // the tile's codes (one 16-byte load per thread of the first 128; rows past N read as zero) and
   // block constants
   {
@@ -66,7 +78,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
     if (row < kTN)
       *reinterpret_cast<u32x4 *>(sC + row * (kTK / 2) + 16 * piece) =
           __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
-    if (tid < kTN * kTK / 64) {
+    if (kFP4) {
+      // 8 group scales per row: thread t takes row t / 8, group t % 8
+      const int64_t bn = n0 + (tid >> 3), bk = k0 + 16 * (tid & 7);
+      sAbs[tid] = (tid < kTN * kTK / 16 && bn < N && bk < K)
+                      ? e4m3_to_f32(reinterpret_cast<const uint8_t *>(w.absmax)[(bn * K + bk) / 16])
+                      : 0.f;
+    } else if (tid < kTN * kTK / 64) {
       const int64_t bn = n0 + (tid >> 1), bk = k0 + 64 * (tid & 1);
       sAbs[tid] = (bn < N && bk < K) ? block_absmax(w, (bn * K + bk) / 64) : 0.f;
     }
@@ -139,13 +157,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
       if (n < N && k < K) {
         // codes of k .. k+3 (two bytes, high nibble first) and the constant of their block
         const uint32_t cw = *reinterpret_cast<const uint16_t *>(sC + row * (kTK / 2) + kk / 2);
-        const float a = sAbs[2 * row + kk / 64];
+        const float a = kFP4 ? sAbs[8 * row + kk / 16] : sAbs[2 * row + kk / 64];
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t byte = (cw >> (8 * (e >> 1))) & 0xFFu;
           const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);
-          const float dq = sLv[code] * a;
+          const float dq = kFP4 ? (sLv[code] * a) * tsc : sLv[code] * a;   // E2M1: inner product exact
           v[e] = r > 0 ? dq + s * acc[kt][nt][e] : dq;
         }
         o[0] = pack_bf16x2(v[0], v[1]);
@@ -171,14 +189,18 @@ hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, in
   if (r < 0 || r > kMaxR || w.k % 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((w.k + kTK - 1) / kTK), (unsigned)((w.n + kTN - 1) / kTN));
   const int rp = (r + 31) / 32 * 32;
-  const size_t lds = (size_t)kTN * kTK * 2 + kTN * kTK / 2 + 4 * (kTN * kTK / 64 + 16) +
+  const size_t lds = (size_t)kTN * kTK * 2 + kTN * kTK / 2 + 4 * (kTN * kTK / 16 + 16) +
                      2 * ((size_t)rp * kTK + (size_t)kTN * (rp + 8));
+  const void *fn = w.fp4 ? reinterpret_cast<const void *>(merge_kernel<true>)
+                         : reinterpret_cast<const void *>(merge_kernel<false>);
   if (lds > 65536) {   // above the default dynamic-LDS limit: opt in (gfx950 has 160 KB per CU)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(merge_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  merge_kernel<<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
+  if (w.fp4)
+    merge_kernel<true><<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
+  else
+    merge_kernel<false><<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
   return hipGetLastError();
 }
 

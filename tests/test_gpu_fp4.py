@@ -9,14 +9,16 @@
 * identity probes: X = I gives Y = bf16(deq(W))^T and dY = I gives dX = bf16(deq(W)), bit for
   bit (the decoded operand e2m1 * s is exact in bf16 and the tensor scale is applied once, in
   float32, so both equal one rounding of the exact dequantised value);
-* the grouped (MoE) layer and the gate/up SwiGLU pair with E2M1 weights.
+* the grouped (MoE) layer and the gate/up SwiGLU pair with E2M1 weights;
+* the LoRA merge of an E2M1 base: within one bf16 ulp of the oracle, r = 0 equal to the bf16
+  dequantisation, and its re-quantisation to E2M1 (a compressed FP4 export) bit-exact.
 """
 import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from oracle import fp4, moe, nf4, qlora, swiglu
+from oracle import fp4, merge, moe, nf4, qlora, swiglu
 from tests.gpu_helpers import assert_fp4_equal, check_close, f32, say, u16
 
 pytestmark = pytest.mark.gpu
@@ -151,3 +153,27 @@ def test_swiglu_pair_with_fp4_weight(lib):
     check_close("dAgu", f32(dAgu), np.concatenate([dAg, dAu]), warn_above=8e-3)
     check_close("dBg", f32(dBg), dBgr, warn_above=8e-3)
     check_close("dBu", f32(dBu), dBur, warn_above=8e-3)
+
+
+@pytest.mark.parametrize("n,k,r,s", [(64, 256, 16, 2.0), (200, 320, 5, -0.5), (40, 1024, 128, 0.25)])
+def test_merge_and_fp4_export(lib, n, k, r, s):
+    say(f"fp4 merge n={n} k={k} r={r} s={s}")
+    W = wl.normal_bf16(700 + n, (n, k), 0.02)
+    A = wl.normal_bf16(701 + n, (r, k), k ** -0.5)
+    B = wl.normal_bf16(702 + n, (n, r), 0.05)
+    qg = lib.fp4_quantize(W.to(DEV))
+    Wm = lib.qlora_merge(qg, A.to(DEV), B.to(DEV), s)
+    q2 = lib.fp4_quantize(Wm)
+    W0 = lib.qlora_merge(qg, None, None, s)
+    D0 = lib.nf4_dequantize(qg, torch.bfloat16)
+    torch.cuda.synchronize()
+    qo = fp4.quantize(W.float().numpy())
+    assert_fp4_equal(qg, qo)
+    ref = merge.merge(fp4.dequantize_f32(qo), f32(A), f32(B), s)
+    got = f32(Wm).astype(np.float64)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), np.finfo(np.float32).tiny))) - 7)
+    err = (np.abs(got - ref) / ulp).max()
+    say(f"  max error {err:.3f} bf16 ulp")
+    assert err <= 1.0
+    assert torch.equal(W0, D0)
+    assert_fp4_equal(q2, fp4.quantize(f32(Wm)))

@@ -193,7 +193,6 @@ def test_merge_rejects_bad_arguments():
     assert mg(r=-1) == m.NF4_EINVAL
     assert mg(q=wdesc(n=64, k=100)) == m.NF4_EUNSUPPORTED
     assert mg(q=wdesc(n=1 << 20, k=1 << 12)) == m.NF4_EUNSUPPORTED      # n*k = 2^32
-    assert mg(q=wdesc(block=16, scale=FAKE)) == m.NF4_EUNSUPPORTED     # E2M1 weights: NF4 only
 
 
 def test_moe_calls_reject_bad_arguments():
