@@ -135,3 +135,44 @@ def test_moe_recomputes_missing_t(lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_moe_full_size(lib):
+    """The moe_mlp_up layer at full size, as bench.py launches it (8 experts of K 4096, N 11008,
+    16384 routed rows, r 16): the stacked weight bit for bit; Y, T and dX on sampled rows of
+    every expert, dA on sampled columns and dB on sampled rows of every expert's block, against
+    the float64 oracle on the same seeded inputs."""
+    from tests.test_gpu_workloads import sample
+    mw = wl.MOES["moe_mlp_up"]
+    counts, E, K, N, r, s = mw.counts(), mw.E, mw.K, mw.N, mw.r, mw.s
+    say(f"moe {mw.name}: E={E} counts={counts} K={K} N={N} r={r} s={s}")
+    W = wl.moe_tensor(mw, "W")
+    X, A, B, dY = (wl.moe_tensor(mw, t) for t in ("X", "A", "B", "dY"))
+    qg = lib.nf4_quantize(W.to(DEV), mw.dq_block)
+    Xd, Ad, Bd = X.to(DEV), A.to(DEV), B.to(DEV)
+    Y, T = lib.qlora_moe_fwd(Xd, counts, qg, Ad, Bd, s)
+    dX, dA, dB = lib.qlora_moe_bwd(dY.to(DEV), Xd, counts, qg, Ad, Bd, s, T)
+    torch.cuda.synchronize()
+    say("  fwd + bwd done")
+    qo = nf4.quantize(W.float().numpy(), mw.dq_block)
+    assert_quant_equal(qg, qo)
+    del W
+    Wd = nf4.dequantize_f32(qo)
+    Xf, Af, Bf, dYf = (f32(t).astype(np.float64) for t in (X, A, B, dY))
+    off = moe.offsets(counts)
+    Yg, Tg, dXg = f32(Y), f32(T), f32(dX)
+    dAg, dBg = f32(dA), f32(dB)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        We = Wd[e * N:(e + 1) * N].astype(np.float64)
+        Ae, Be = Af[e * r:(e + 1) * r], Bf[e * N:(e + 1) * N]
+        rows = lo + sample(hi - lo, 16, 100 + e)
+        Te = Xf[lo:hi] @ Ae.T                                   # [me, r]
+        Ue = dYf[lo:hi] @ Be                                    # [me, r]
+        check_close(f"Y[expert {e}]", Yg[rows], Xf[rows] @ We.T + s * (Te[rows - lo] @ Be.T))
+        check_close(f"T[expert {e}]", Tg[rows], Te[rows - lo])
+        check_close(f"dX[expert {e}]", dXg[rows], dYf[rows] @ We + s * (Ue[rows - lo] @ Ae))
+        cols = sample(K, 32, 200 + e)
+        check_close(f"dA[expert {e}]", dAg[e * r:(e + 1) * r][:, cols], s * (Ue.T @ Xf[lo:hi, cols]))
+        nrows = sample(N, 32, 300 + e)
+        check_close(f"dB[expert {e}]", dBg[e * N:(e + 1) * N][nrows], s * (dYf[lo:hi, nrows].T @ Te))
