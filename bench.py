@@ -30,7 +30,8 @@ matrix-core-bound shapes, a device copy for the HBM-bound one.
 --workload mlp_swiglu measures the gate/up SwiGLU pair instead (a step: qlora_swiglu_fwd +
 qlora_swiglu_bwd on the mlp_up shape, two projections); --workload moe_mlp_up the grouped
 mixture-of-experts layer (a step: qlora_moe_fwd + qlora_moe_bwd, 8 experts of the mlp_up shape,
-16384 routed rows).
+16384 routed rows); --workload mlp_up_e2m1 the single layer of the mlp_up shape with an E2M1 base
+weight (4-bit floats, E4M3 scale per 16, float32 tensor scale) instead of NF4.
 """
 from __future__ import annotations
 
