@@ -582,11 +582,40 @@ int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void
     hipError_t e = nf4q::launch_blockdiag((const uint16_t *)Bg, (const uint16_t *)Bu, n, r, B2, sm);
     if (e != hipSuccess) return hip_status(e, "qlora_swiglu_fwd launch");
   }
-  st = qlora_fwd(X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, Ygu, T,
-                 lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd, stream);
-  if (st) return st;
-  return hip_status(nf4q::launch_swiglu_fwd((const uint16_t *)Ygu, m, n, (uint16_t *)H, sm),
-                    "qlora_swiglu_fwd launch");
+  const int64_t k = Wgu->k;
+  // shapes the stacked layer sends to the decode kernels (M <= 48): the stacked forward, then the
+  // activation kernel
+  if (m <= nf4q::kDecodeMaxM && k % 256 == 0 && Wgu->block == 64) {
+    st = qlora_fwd(X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, Ygu, T,
+                   lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd, stream);
+    if (st) return st;
+    return hip_status(nf4q::launch_swiglu_fwd((const uint16_t *)Ygu, m, n, (uint16_t *)H, sm),
+                      "qlora_swiglu_fwd launch");
+  }
+  // otherwise T = X Agu^T, then ONE launch of the fused kernel in its pair form: Yg, Yu and, in
+  // the epilogue, H
+  if (r > 0) {
+    st = qlora_lora_down(X, m, k, Agu, 2 * r, T, lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd,
+                         stream);
+    if (st) return st;
+  }
+  nf4q::GemmArgs g;
+  g.a_side = (const uint16_t *)X;
+  g.lda = k;
+  g.lora_a = r > 0 ? (const uint16_t *)T : nullptr;
+  g.lora_b = B2;
+  g.w = desc(Wgu);
+  g.M = m;
+  g.C = n;
+  g.R = k;
+  g.r = 2 * r;
+  g.s = s;
+  g.out = (uint16_t *)Ygu;
+  g.ldo = 2 * n;
+  g.t = tables();
+  g.hout = (uint16_t *)H;
+  g.ldh = n;
+  return hip_status(nf4q::launch_gemm_fwd_pair(g, sm), "qlora_swiglu_fwd launch");
 }
 
 int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor *Wgu,

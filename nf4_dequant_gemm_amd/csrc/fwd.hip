@@ -64,10 +64,12 @@ struct CStage {
 // chunk t % 8 of rows t / 8 + 64 i. When r is a multiple of 8 and T and B are 16-byte aligned,
 // each chunk is one 16-byte buffer load (rows past the tile edge and chunks past r read as zero);
 // otherwise values are read one at a time.
-__device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, int64_t rows_m,
-                           int64_t rows_n, int jb, int nch, uint4 *sA, uint4 *sB) {
-  // m0: first row of T; n0: first row of B (rows past rows_m / rows_n are zero); B is staged
-  // times sb
+__device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, int64_t rows_n,
+                           int64_t n1, int64_t rows_n1, int64_t rows_m, int jb, int nch, uint4 *sA,
+                           uint4 *sB) {
+  // m0: first row of T; tile rows 0..127 take B rows n0.. (rows_n of them valid), tile rows
+  // 128..255 B rows n1.. (rows_n1 valid; the plain tile has n1 = n0 + 128, rows_n1 = rows_n - 128);
+  // rows past the valid ones are zero; B is staged times sb
   const int tid = threadIdx.x;
   const int c = tid & 7, row0 = tid >> 3;
   if (c >= nch) return;
@@ -76,14 +78,18 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
                    ((reinterpret_cast<uintptr_t>(g.lora_a) | reinterpret_cast<uintptr_t>(g.lora_b)) & 15) == 0;
   if (vec) {
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.lora_a + m0 * g.r, rows_m * g.r * 2);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.lora_b + n0 * g.r, rows_n * g.r * 2);
+    const int64_t v0 = rows_n < 128 ? (rows_n > 0 ? rows_n : 0) : 128;
+    const int64_t v1 = rows_n1 < 128 ? (rows_n1 > 0 ? rows_n1 : 0) : 128;
+    const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(g.lora_b + n0 * g.r, v0 * g.r * 2);
+    const __amdgpu_buffer_rsrc_t rB1 = make_rsrc(g.lora_b + n1 * g.r, v1 * g.r * 2);
     u32x4 ta[kChunks / kThreads], tb[kChunks / kThreads];
 #pragma unroll
     for (int i = 0; i < kChunks / kThreads; ++i) {
       const int row = row0 + 64 * i;
       const uint32_t off = j0 < g.r ? (uint32_t)(row * g.r + j0) * 2 : 0x80000000u;
+      const uint32_t offb = j0 < g.r ? (uint32_t)((row & 127) * g.r + j0) * 2 : 0x80000000u;
       ta[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
-      tb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+      tb[i] = __builtin_amdgcn_raw_buffer_load_b128(i < 2 ? rB0 : rB1, offb, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kChunks / kThreads; ++i) {
@@ -100,7 +106,8 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
   for (int i = 0; i < kChunks / kThreads; ++i) {
     const int row = row0 + 64 * i;
     uint32_t wa[4], wb[4];
-    const int64_t m = m0 + row, n = n0 + row;
+    const int64_t m = m0 + row, n = row < 128 ? n0 + row : n1 + (row - 128);
+    const bool nvalid = row < 128 ? row < rows_n : row - 128 < rows_n1;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int ja = j0 + e, jc = ja + 1;
@@ -111,7 +118,7 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
       }
       wa[e >> 1] = lo | (hi << 16);
       float b0 = 0.f, b1 = 0.f;
-      if (row < rows_n) {
+      if (nvalid) {
         if (ja < g.r) b0 = bf16_to_f32(g.lora_b[n * g.r + ja]);
         if (jc < g.r) b1 = bf16_to_f32(g.lora_b[n * g.r + jc]);
       }
@@ -131,9 +138,15 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
 // a float32 tensor scale S. E2M1 values times group scales are exact in bf16, so the weight
 // operand is decoded without rounding and S multiplies the accumulators in the epilogue; the
 // LoRA steps stage B times s / S to share the accumulators.
-template <int kFmt, bool kGrp>
+// kPair: the gate/up pair with its SwiGLU epilogue. The weight is the stacked [Wg; Wu] [2N, K]
+// (N = g.C), B the stacked block-diagonal [2N, 2r]; a tile's 256 columns are gate columns
+// n0 .. n0 + 127 (weight and B rows n0 ..) and the up columns of the same indices (rows N + n0 ..),
+// so the epilogue holds Yg and Yu of the same columns: it writes both to g.out ([M, 2N], gate then
+// up) and H = silu(Yg) * Yu, from their bf16 values, to g.hout ([M, N], row stride g.ldh).
+template <int kFmt, bool kGrp, bool kPair = false>
 __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr) {
   constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
+  constexpr int kTN = kPair ? kT / 2 : kT;   // columns of each output a tile advances by
   // X and W tiles as separate arrays: the compiler then knows that LDS accesses to one do not
   // alias the DMA in flight into another (one array of two would make it wait for the DMA)
   __shared__ uint4 sX0[kChunks], sX1[kChunks];
@@ -145,7 +158,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const int tiles_n = (int)((g.C + kT - 1) / kT);
+  const int tiles_n = (int)((g.C + kTN - 1) / kTN);
   int local = tile_remap(blockIdx.x, gridDim.x);
   int64_t m_lo = 0, m_hi = g.M, wbase = 0;
   if (kGrp) {
@@ -157,20 +170,24 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     wbase = (int64_t)e * g.C;
   }
   const int64_t m0 = m_lo + (int64_t)(local / tiles_n) * kT;
-  const int64_t n0 = (int64_t)(local % tiles_n) * kT;    // columns of Y
+  const int64_t n0 = (int64_t)(local % tiles_n) * kTN;   // columns of Y
   const int64_t wn0 = wbase + n0;                         // rows of the (stacked) weight and B
   const int64_t K = g.w.k;
   const int64_t rows_m = (m_hi - m0 < kT) ? m_hi - m0 : kT;
-  const int64_t rows_n = (g.C - n0 < kT) ? g.C - n0 : kT;
+  const int64_t rows_n = (g.C - n0 < kTN) ? g.C - n0 : kTN;   // valid columns (of each half)
   const int kblk = (int)(K / kS);
   const int last = kblk - 1;
 
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.a_side + m0 * K, rows_m * K * 2);
-  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wn0 * (K / 2), rows_n * (K / 2));
+  // pair: the buffers span the whole stacked weight, rows addressed per thread (rows past N read
+  // as zero through out-of-range offsets)
+  const int64_t wrows = kPair ? 2 * g.C : rows_n;
+  const int64_t wfirst = kPair ? 0 : wn0;
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + wfirst * (K / 2), wrows * (K / 2));
   const __amdgpu_buffer_rsrc_t rQ =
-      kFP4  ? make_rsrc(reinterpret_cast<const uint8_t *>(g.w.absmax) + wn0 * (K / 16), rows_n * (K / 16))
-      : kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + wn0 * kblk, rows_n * kblk)
-            : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + wn0 * kblk, rows_n * kblk * 4);
+      kFP4  ? make_rsrc(reinterpret_cast<const uint8_t *>(g.w.absmax) + wfirst * (K / 16), wrows * (K / 16))
+      : kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + wfirst * kblk, wrows * kblk)
+            : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + wfirst * kblk, wrows * kblk * 4);
   const int64_t nruns = (g.w.n * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
   // E2M1: the tensor scale (1 for an all-zero weight, whose group scales are all 0), read where
@@ -199,10 +216,17 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
 #pragma unroll
   for (int i = 0; i < 8; ++i) lvh[i] = wh ? g.t.level[8 + i] : g.t.level[i];
   const uint32_t mhi = (wh && !kFP4) ? 0u : 0xFFFFFFFFu, mlo = (wh && !kFP4) ? 0xFFFFFFFFu : 0u;
-  const uint32_t coff = (uint32_t)(wr * (K / 2) + wh * 16);
+  // weight row of tile row wr (pair: gate rows n0 + wr, up rows N + n0 + wr - 128), and whether
+  // it holds data (a pair tile past N reads zeros)
+  const int64_t wrow = kPair ? (wr < 128 ? n0 + wr : g.C + n0 + (wr - 128)) : wr;
+  const bool wvalid = !kPair || n0 + (wr & 127) < g.C;
+  const uint32_t coff = wvalid ? (uint32_t)(wrow * (K / 2) + wh * 16) : 0x80000000u;
   // E2M1: the two group scales of the thread's 32 elements (bytes 4 s + 2 wh, + 1 of its row)
-  const uint32_t qoff = kFP4 ? (uint32_t)(wr * (K / 16) + 2 * wh) : (uint32_t)(wr * kblk);
-  const int64_t sbase = (wn0 + wr) * kblk;
+  // (out of range: 0x80000000 bytes, or that many after the float32 constants' scaling by 4)
+  const uint32_t qoff = !wvalid ? ((kFP4 || kDQ) ? 0x80000000u : 0x20000000u)
+                        : kFP4  ? (uint32_t)(wrow * (K / 16) + 2 * wh)
+                                : (uint32_t)(wrow * kblk);
+  const int64_t sbase = (kPair ? wrow : wn0 + wr) * kblk;
 
   const int g16 = lane >> 4, l16 = lane & 15;
   f32x4 acc[4][8];   // [n-tile][m-tile]
@@ -378,7 +402,12 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
-    stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, wn0, rows_m, rows_n, j * kS, 4 * nks, xbuf(buf), wbuf(buf));
+    if (kPair)
+      stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, n0, rows_n, g.C + n0, rows_n, rows_m, j * kS,
+                 4 * nks, xbuf(buf), wbuf(buf));
+    else
+      stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, wn0, rows_n, wn0 + 128, rows_n - 128, rows_m,
+                 j * kS, 4 * nks, xbuf(buf), wbuf(buf));
     __syncthreads();
     mma(xbuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(xbuf(buf), wbuf(buf), 1);
@@ -407,15 +436,45 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
                               pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
     __syncthreads();
     const int c = lane & 7;
-    const int64_t n = n0 + wn * 64 + c * 8;
+    // output column of this wave's piece c (pair: gate or up half of [M, 2N])
+    const int64_t ncol = kPair ? n0 + (wn & 1) * 64 + c * 8 : n0 + wn * 64 + c * 8;
+    const int64_t n = kPair ? (wn < 2 ? ncol : g.C + ncol) : ncol;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 8 * i + (lane >> 3);
       const int64_t m = m0 + wm * 128 + row;
       const uint4 v = blk[swzf(row, c)];
-      if (wm * 128 + row < rows_m && n < g.C)
+      if (wm * 128 + row < rows_m && ncol < g.C)
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
+    }
+    if (kPair) {
+      // H for 64 rows x 64 columns per wave: rows 64 (wn >> 1) .. of the wm block, columns
+      // (wn & 1) 64 .. of the tile's gate half; Yg from the block of wave (wm, wn & 1), Yu from
+      // that of wave (wm, (wn & 1) + 2), both already staged (the barrier above)
+      auto blk_of = [&](int wv) {
+        uint4 *b = (wv >> 1) == 0 ? sX0 : (wv >> 1) == 1 ? sX1 : (wv >> 1) == 2 ? sW0 : sW1;
+        return b + (wv & 1) * (kChunks / 2);
+      };
+      const uint4 *bg = blk_of(wm * 4 + (wn & 1));
+      const uint4 *bu = blk_of(wm * 4 + (wn & 1) + 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 64 * (wn >> 1) + 8 * i + (lane >> 3);
+        const int64_t m = m0 + wm * 128 + row;
+        const uint4 gv = bg[swzf(row, c)], uv = bu[swzf(row, c)];
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g0 = bf16_lo(gw[e]), g1 = bf16_hi(gw[e]);
+          // the activation kernel's expression, operation for operation (same rounding)
+          o[e] = pack_bf16x2(g0 * (1.f / (1.f + __expf(-g0))) * bf16_lo(uw[e]),
+                             g1 * (1.f / (1.f + __expf(-g1))) * bf16_hi(uw[e]));
+        }
+        if (wm * 128 + row < rows_m && ncol < g.C)
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(g.hout + m * g.ldh + ncol));
+      }
     }
   }
 }
@@ -428,6 +487,11 @@ __global__ __launch_bounds__(kThreads) void fwd_fused_kernel(GemmArgs g) {
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(GemmArgs g, GroupArgs gr) {
   fwd_body<kFmt, true>(g, gr);
+}
+
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void fwd_pair_kernel(GemmArgs g) {
+  fwd_body<kFmt, false, true>(g, GroupArgs{});
 }
 
 }  // namespace
@@ -457,6 +521,20 @@ hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipSt
     fwd_grouped_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
   else
     fwd_grouped_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fwd_pair(const GemmArgs &g, hipStream_t st) {
+  if (((g.C | g.ldo | g.ldh) & 7) != 0 || g.ldo < 2 * g.C || g.ldh < g.C || g.w.n != 2 * g.C ||
+      ((reinterpret_cast<uintptr_t>(g.out) | reinterpret_cast<uintptr_t>(g.hout)) & 15) != 0)
+    return hipErrorInvalidValue;
+  const int64_t tiles = ((g.C + kT / 2 - 1) / (kT / 2)) * ((g.M + kT - 1) / kT);
+  if (g.w.fp4)
+    fwd_pair_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else if (g.w.dq)
+    fwd_pair_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
+  else
+    fwd_pair_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
 }
 

@@ -35,9 +35,15 @@ struct GemmArgs {
   uint16_t *out;
   int64_t ldo;
   Tables t;
+  uint16_t *hout = nullptr;   // gate/up pair only: H [M, C], row stride ldh
+  int64_t ldh = 0;
 };
 
 hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
+// The gate/up pair with the SwiGLU epilogue: g.w the stacked [Wg; Wu] [2C, K], g.lora_b the
+// block-diagonal [2C, r] (r = 2 r'), g.out Ygu [M, 2C] (row stride ldo), g.hout H = silu(Yg) * Yu
+// [M, C] (row stride ldh), both from the bf16 values of Yg and Yu.
+hipError_t launch_gemm_fwd_pair(const GemmArgs &g, hipStream_t st);
 
 // Grouped (mixture-of-experts) forward: E experts, rows m_off[e] .. m_off[e+1] of X, T and Y
 // belong to expert e, whose weight rows are e N .. e N + N - 1 of the stacked weight g.w and whose

@@ -160,3 +160,26 @@ def test_swiglu_pair_full_size(lib):
     nrows = sample(N, 64, p.index + 2)
     check_close("dBg", f32(dBgg)[nrows], s * (dYg[:, nrows].T @ Tg))
     check_close("dBu", f32(dBug)[nrows], s * (dYu[:, nrows].T @ Tu))
+
+
+@pytest.mark.parametrize("M,K,N,r", [(300, 1024, 520, 16), (64, 256, 128, 8), (200, 320, 72, 0)])
+def test_pair_kernel_equals_stacked_layer(lib, M, K, N, r):
+    """Above the decode shapes the pair runs as ONE launch of the fused kernel with the activation
+    in its epilogue; its Ygu equals the plain stacked layer (qlora_fwd with [Wg; Wu] and the
+    block-diagonal B) bit for bit, ragged last tiles (N % 128 != 0) included."""
+    X, Wgu, Agu, Bg, Bu, _ = rand_pair(M, K, N, r, 300 + M)
+    qg = lib.nf4_quantize(Wgu.to(DEV), 256)
+    d = lambda t: t.to(DEV) if r else None
+    H, Ygu, Tgu = lib.qlora_swiglu_fwd(X.to(DEV), qg, d(Agu), d(Bg), d(Bu), 0.5)
+    B2 = None
+    if r:
+        B2 = torch.zeros(2 * N, 2 * r, dtype=torch.bfloat16)
+        B2[:N, :r], B2[N:, r:] = Bg, Bu
+        B2 = B2.to(DEV)
+    Y2, T2 = lib.qlora_fwd(X.to(DEV), qg, d(Agu), B2, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(Ygu, Y2)
+    if r:
+        assert torch.equal(Tgu, T2)
+    Yg, Yu = f32(Ygu)[:, :N].astype(np.float64), f32(Ygu)[:, N:].astype(np.float64)
+    check_close("H from Ygu", f32(H), Yg * swiglu.sigmoid(Yg) * Yu)
