@@ -241,9 +241,9 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
  * Bytes of device workspace qlora_moe_fwd and qlora_moe_bwd need for these counts. */
 size_t qlora_moe_workspace_bytes(const int64_t *counts, int32_t E, int64_t n, int64_t k, int32_t r);
 
-/* Forward: T (per expert rows, one row projection per expert with rows) and Y [sum(counts), n]
- * in ONE launch of the fused kernel for all experts (each workgroup finds its expert's rows and
- * weight). T must be non-NULL when r > 0. Errors: as qlora_fwd; NF4_EINVAL also for E out of
+/* Forward: T = X_e A_e^T for every expert's rows (ONE grouped row-projection launch) and Y
+ * [sum(counts), n] in ONE launch of the fused kernel for all experts (each workgroup finds its
+ * expert's rows and weight). T must be non-NULL when r > 0. Errors: as qlora_fwd; NF4_EINVAL also for E out of
  * range, a negative count, W->n not a multiple of E. */
 int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
                   const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
@@ -257,7 +257,8 @@ int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const n
 /* Backward for dY [sum(counts), n]: dX [sum(counts), k] (skipped when NULL), dA [E r, k] and
  * dB [E n, r], each expert's adapter gradients summed over its own rows (zero for an expert with
  * no rows); T from the forward or NULL (recomputed). dX of every expert comes from ONE launch of
- * the fused dX kernel; U = dY_e B_e, dA and dB are per-expert launches of the layer's kernels.
+ * the fused dX kernel; U = dY_e B_e is one grouped row projection, dA and dB one grouped
+ * M-reduction each (every expert summing over its own rows only).
  * Errors: as qlora_bwd and qlora_moe_fwd. */
 int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
                   const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
