@@ -243,8 +243,8 @@ size_t qlora_moe_workspace_bytes(const int64_t *counts, int32_t E, int64_t n, in
 
 /* Forward: T = X_e A_e^T for every expert's rows (ONE grouped row-projection launch) and Y
  * [sum(counts), n] in ONE launch of the fused kernel for all experts (each workgroup finds its
- * expert's rows and weight). T must be non-NULL when r > 0. Errors: as qlora_fwd; NF4_EINVAL also for E out of
- * range, a negative count, W->n not a multiple of E. */
+ * expert's rows and weight). T must be non-NULL when r > 0. Errors: as qlora_fwd; NF4_EINVAL
+ * also for E out of range, a negative count, W->n not a multiple of E. */
 int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
                   const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
                   size_t ws_bytes, void *stream);
