@@ -9,7 +9,9 @@
 // block-diagonal [[Bg, 0], [0, Bu]] [2n, 2r], so one forward yields Ygu = [Yg | Yu] per row and
 // one backward with dY = [dYg | dYu] yields dX, [dAg; dAu] and, on its diagonal blocks, dBg, dBu.
 // The kernels here are what that composition adds: the activation, its backward, and the
-// block-diagonal B and its gradient's diagonal blocks. All are HBM-bound streams; rows are read
+// block-diagonal B and its gradient's diagonal blocks. Above the decode shapes the forward runs
+// the fused kernel's pair form instead, with the activation in its epilogue (fwd.hip);
+// swiglu_fwd_kernel serves the decode shapes (M <= 48). All are HBM-bound streams; rows are read
 // and written in 16-byte pieces of 8 columns (n % 8 == 0), consecutive lanes on consecutive
 // pieces.
 #include "common.h"
