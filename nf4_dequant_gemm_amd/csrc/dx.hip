@@ -30,6 +30,11 @@
 // 2-unit term (which only permutes units inside a 32-byte group, so reads keep their banks) and
 // the decode ownership (the 8 lanes of a write pass take 8 different rows) put every decode write
 // on distinct banks. (Eight lanes of one row, the plain mapping, conflicted 4 ways.)
+//
+// The same body serves the grouped launch of a mixture-of-experts layer [NVFP4 update article,
+// "Comprehensive Improvements in Training Performance and Stability"] and the E2M1 weight format
+// with FP8 group scales [NVFP4 update article, "NVFP4: A Quantization Format for the Next
+// Generation of Hardware"] (template parameters of dx_body).
 #include "common.h"
 #include "launch.h"
 

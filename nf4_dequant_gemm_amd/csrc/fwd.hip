@@ -32,6 +32,13 @@
 // of a fragment read on distinct slots of the 256-byte window, and the 4 rows x 2 chunks of a
 // decode write on distinct slots of the 128-byte window (the plain (r >> 1) & 7 left those writes
 // 2-way conflicted).
+//
+// The same body serves three more forms (template parameters of fwd_body): the grouped launch of a
+// mixture-of-experts layer [NVFP4 update article, "Comprehensive Improvements in Training
+// Performance and Stability": grouped MoE with LoRA on the experts], the gate/up pair with its
+// SwiGLU activation in the epilogue [pyshine Unsloth code tour, "Why You Need This": the fused
+// gated-MLP activation], and the E2M1 weight format with FP8 group scales [NVFP4 update article,
+// "NVFP4: A Quantization Format for the Next Generation of Hardware"].
 #include "common.h"
 #include "launch.h"
 
