@@ -191,9 +191,10 @@ size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
  * also returned in Ygu bf16 [m, 2n] (each row: Yg then Yu), kept for the backward; Tgu bf16
  * [m, 2r] = [X Ag^T | X Au^T] (may be NULL: the backward then recomputes it). Agu, Bg, Bu, Tgu
  * NULL when r == 0. ws: at least qlora_swiglu_workspace_bytes(m, n, k, r) bytes, 16-byte aligned.
- * Above the decode shapes (m > 48, or k % 256 != 0, or an E2M1 weight) the GEMM and the activation
- * are ONE launch of the fused kernel, H computed in its epilogue; the decode shapes run the
- * stacked forward, then the activation kernel (H from Ygu by the same float32 expression).
+ * Above the decode shapes (m > 48, or k % 256 != 0, or m > 16 with an E2M1 weight) the GEMM and
+ * the activation are ONE launch of the fused kernel, H computed in its epilogue; the decode shapes
+ * run the stacked forward, then the activation kernel (H from Ygu by the same float32
+ * expression).
  * Errors: as qlora_fwd; NF4_EINVAL also when Wgu->n is odd, r > 64 or H / Ygu is NULL. */
 int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
                      const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,

@@ -447,7 +447,7 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
   g.t = tables();
   if (m <= 16 && W->dq_block > 0 && W->k % 256 == 0)
     return hip_status(nf4q::launch_decode16_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
-  if (m <= nf4q::kDecodeMaxM && W->k % 256 == 0 && W->block == 64)
+  if (m <= (W->block == 64 ? nf4q::kDecodeMaxM : 16) && W->k % 256 == 0)
     return hip_status(nf4q::launch_decode_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
   return hip_status(nf4q::launch_gemm_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
 }
@@ -585,7 +585,7 @@ int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void
   const int64_t k = Wgu->k;
   // shapes the stacked layer sends to the decode kernels (M <= 48): the stacked forward, then the
   // activation kernel
-  if (m <= nf4q::kDecodeMaxM && k % 256 == 0 && Wgu->block == 64) {
+  if (m <= (Wgu->block == 64 ? nf4q::kDecodeMaxM : 16) && k % 256 == 0) {
     st = qlora_fwd(X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, Ygu, T,
                    lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd, stream);
     if (st) return st;

@@ -33,6 +33,16 @@
 // Requires K % 256 == 0 (a whole number of 4-block groups per row keeps the block-constant DMA
 // dword-aligned and each group inside one scale run); the host sends other shapes to the
 // large-M kernel.
+// E2M1 weights (4-bit floats with an E4M3 scale per 16 elements and a float32 tensor scale S)
+// take the same kernel: the table holds pairs of E2M1 values (exact in bf16), the stage's
+// constants are the group scales (32 bytes per row), and since a 16x16x32 product sums two groups,
+// each X operand is split by lane half into two operands that keep one group each (lanes 0..31
+// hold k 0..15 of a 32-column slice, lanes 32..63 k 16..31): four products per row group and
+// block, each scaled by its group's scale (from a 128-entry E4M3 table in LDS). The sums are in
+// units of S, which multiplies Y at the end; the LoRA term is added times s / S. E2M1 takes this
+// kernel for M <= 16 only (the split operands and four partial sums per block need about twice
+// the registers: with 32 or 48 rows the kernel would spill), at one workgroup per CU (228
+// registers; held to 128 for two, it spills 154 of them).
 #include <type_traits>
 
 #include "common.h"
@@ -65,8 +75,9 @@ struct DecArgs {
   Tables t;
 };
 
-template <int MT, bool kDQ>
-__global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
+template <int MT, int kFmt>
+__device__ __forceinline__ void decode_body(const DecArgs &g) {
+  constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
   // [0, 16 KB) level-pair table, then the ring of kStages slots (16 KB of codes + the stage's
   // block constants). After the main loop the area from 0 holds the cross-wave reduction.
   constexpr int kSlot = kStageBytes + kConstBytes;
@@ -74,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
   constexpr int kArea = kTabBytes + kStages * kSlot;
   static_assert(kRedBytes <= kArea, "reduction area");
   __shared__ __align__(16) uint8_t smem[kArea];
+  __shared__ float se4m3[kFP4 ? 128 : 1];   // E2M1: E4M3 byte (sign ignored) -> float
   uint8_t *stab = smem;
   uint8_t *sring = smem + kTabBytes;
 
@@ -94,16 +106,24 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
   // earlier element); threads e and e + 256 write copies 0..7 and 8..15 of byte e
   {
     const int e = tid & 255;
-    const uint32_t v = pack_bf16x2(g.t.level[e >> 4], g.t.level[e & 15]);
+    auto e2m1 = [](int c) {
+      const int mi = c & 7;
+      const float mag = mi < 4 ? 0.5f * float(mi) : (mi == 4 ? 2.f : mi == 5 ? 3.f : mi == 6 ? 4.f : 6.f);
+      return (c & 8) ? -mag : mag;
+    };
+    const uint32_t v = kFP4 ? pack_bf16x2(e2m1(e >> 4), e2m1(e & 15))
+                            : pack_bf16x2(g.t.level[e >> 4], g.t.level[e & 15]);
     uint4 *dst = reinterpret_cast<uint4 *>(stab + e * kCopies * 4 + (tid >> 8) * (kCopies * 2));
 #pragma unroll
     for (int c = 0; c < kCopies / 8; ++c) dst[c] = make_uint4(v, v, v, v);
   }
 
   const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.w.codes + n0 * (K / 2), rows * (K / 2));
+  if (kFP4 && tid < 128) se4m3[tid] = e4m3_to_f32((uint32_t)tid);
   const __amdgpu_buffer_rsrc_t rQ =
-      kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows * kblk)
-          : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + n0 * kblk, rows * kblk * 4);
+      kFP4  ? make_rsrc(reinterpret_cast<const uint8_t *>(g.w.absmax) + n0 * (K / 16), rows * (K / 16))
+      : kDQ ? make_rsrc(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows * kblk)
+            : make_rsrc(reinterpret_cast<const float *>(g.w.absmax) + n0 * kblk, rows * kblk * 4);
   const int64_t nruns = (N * kblk + 255) / 256;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(g.w.scale, kDQ ? nruns * 4 : 0);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.X, g.M * K * 2);
@@ -127,9 +147,14 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
   //     wave's 256-byte piece (a branch around them would make the count of loads in flight
   //     unknown to the compiler).
   //   fp32: wave w, lane l -> value (64 w + l) % 8 of row (64 w + l) / 8.
+  //   E2M1: wave w, lane l -> dword (64 w + l) % 8 of the 32 group-scale bytes of row
+  //     (64 w + l) / 8 (LDS byte (64 w + l) * 4 = row * 32 + 4 * dword).
   const __amdgpu_buffer_rsrc_t rCst = kDQ ? (wave < 4 ? rQ : rS) : rQ;
   uint32_t coff;
-  if (kDQ) {
+  if (kFP4) {
+    const int idx = 64 * wave + lane;
+    coff = (uint32_t)((idx >> 3) * (K / 16) + (idx & 7) * 4);           // + 32 st
+  } else if (kDQ) {
     const int row = (wave & 3) * 16 + ((lane & 31) >> 1), h = lane & 1;
     coff = wave < 4 ? (uint32_t)(row * kblk + 4 * h)                     // + 8 st
                     : (uint32_t)((n0 + row) * kblk + 4 * h);             // block, not yet >> 8
@@ -152,6 +177,8 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rCst, (__attribute__((address_space(3))) void *)(cdst + wave * 256), 4, o, 0, 0, 0);
     } else {
+      // fp32 constants: 8 blocks x 4 bytes per row and stage; E2M1 group scales: 32 groups x 1
+      // byte -- the same 32 bytes per row and stage
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rQ, (__attribute__((address_space(3))) void *)(cdst + wave * 256), 4,
           coff + st * (kBlkPerStage * 4), 0, 0, 0);
@@ -236,14 +263,20 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
         cw[rg][t] = *reinterpret_cast<const uint32_t *>(
             S + row * 256 + ((chunk ^ (row & 15)) << 4) + gl * 4);
       }
-    // block constants a(row 16 rg + nl, the wave's block); blocks past K get zero
-    float ca[4];
+    // block constants a(row 16 rg + nl, the wave's block); blocks past K get zero. E2M1: the
+    // four group scales of that row and block (ca4)
+    float ca[4], ca4[kFP4 ? 4 : 1][4];
     const bool live = ph(st) * kBlkPerStage + wave < kblk;
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int row = rg * 16 + nl;
       float a;
-      if (kDQ) {
+      if (kFP4) {
+        const uint32_t sw = *reinterpret_cast<const uint32_t *>(C + row * 32 + wave * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ca4[kFP4 ? rg : 0][q] = live ? se4m3[(sw >> (8 * q)) & 0x7Fu] : 0.f;
+        a = 0.f;
+      } else if (kDQ) {
         // int8 code times the scale of the row's 4-block half
         const int q = reinterpret_cast<const int8_t *>(C)[(row >> 4) * 256 + (row & 15) * 8 + wave];
         const float sc = *reinterpret_cast<const float *>(
@@ -272,16 +305,38 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
       const uint32_t *o = lk[rg & 1];
       const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
       const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(o[4], o[5], o[6], o[7]));
-      f32x4 part[MT];
+      if constexpr (kFP4) {
+        // one product per group: the X operand with the other group's lanes zeroed
+        const uint32_t lm = gl < 2 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        part[mt] = mfma16x16x32(cur.x[mt][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-        part[mt] = mfma16x16x32(cur.x[mt][1], b1, part[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 pg[4];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 xw = __builtin_bit_cast(u32x4, cur.x[mt][t]);
+            const u32x4 xa = {xw[0] & lm, xw[1] & lm, xw[2] & lm, xw[3] & lm};
+            const u32x4 xb = {xw[0] & ~lm, xw[1] & ~lm, xw[2] & ~lm, xw[3] & ~lm};
+            const bf16x8 bt = t ? b1 : b0;
+            pg[2 * t] = mfma16x16x32(__builtin_bit_cast(bf16x8, xa), bt, f32x4{0.f, 0.f, 0.f, 0.f});
+            pg[2 * t + 1] = mfma16x16x32(__builtin_bit_cast(bf16x8, xb), bt, f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mt][rg][v] += ca4[kFP4 ? rg : 0][q] * pg[q][v];
+        }
+      } else {
+        f32x4 part[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          part[mt] = mfma16x16x32(cur.x[mt][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+          part[mt] = mfma16x16x32(cur.x[mt][1], b1, part[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mt][rg][v] += ca[rg] * part[mt][v];
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mt][rg][v] += ca[rg] * part[mt][v];
     }
     // every wave is done with this ring slot
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -310,8 +365,15 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
   // LoRA term on the matrix cores: wave w < 4 adds s * T[m][:] . B[n][:] for the 16 output
   // columns n = 16 w + (lane % 16) to its partial sums, in steps of 32 ranks (A operand: T row
   // m, B operand: B row n, both k-contiguous; ranks at or past r, rows past M or N read as zero).
+  // E2M1: the sums are in units of the tensor scale S (1 for an all-zero weight)
+  float tsc = 1.f;
+  if (kFP4) {
+    const float S = *g.w.scale;
+    tsc = S > 0.f ? S : 1.f;
+  }
   if (g.r > 0 && wave < 4) {
     const int r = g.r;
+    const float sl = kFP4 ? g.s / tsc : g.s;
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, g.M * r * 2);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + n0 * r, rows * r * 2);
     const int nrow = wave * 16 + nl;
@@ -343,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
         for (int rg = 0; rg < 4; ++rg)   // acc[mt][wave], without a dynamic register index
           if (rg == wave)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[mt][rg][v] += g.s * lp[v];
+            for (int v = 0; v < 4; ++v) acc[mt][rg][v] += sl * lp[v];
       }
     }
   }
@@ -377,11 +439,17 @@ __global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
   __syncthreads();
   for (int i = tid; i < MT * 16 * 64; i += kThreads) {
     const int m = i / 64, n = i % 64;
-    const float y = red[m * 64 + n] + red[(MT * 16 + m) * 64 + n] +
-                    red[(2 * MT * 16 + m) * 64 + n] + red[(3 * MT * 16 + m) * 64 + n];
+    float y = red[m * 64 + n] + red[(MT * 16 + m) * 64 + n] +
+              red[(2 * MT * 16 + m) * 64 + n] + red[(3 * MT * 16 + m) * 64 + n];
+    if (kFP4) y *= tsc;
     const int64_t gm = m, gn = n0 + n;
     if (gm < g.M && gn < N) g.Y[gm * N + gn] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
   }
+}
+
+template <int MT, int kFmt>
+__global__ __launch_bounds__(kThreads) void decode_fwd_kernel(DecArgs g) {
+  decode_body<MT, kFmt>(g);
 }
 
 }  // namespace
@@ -399,12 +467,15 @@ hipError_t launch_decode_fwd(const GemmArgs &ga, hipStream_t st) {
   g.t = ga.t;
   const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
   const int mt = (int)((ga.M + 15) / 16);
+  if (ga.w.fp4 && mt > 1) return hipErrorInvalidValue;   // E2M1: M <= 16 (registers)
 #define DEC_CASE(T)                                                              \
   case T:                                                                        \
-    if (ga.w.dq)                                                                 \
-      decode_fwd_kernel<T, true><<<dim3(grid), dim3(kThreads), 0, st>>>(g);      \
+    if (ga.w.fp4 && T == 1)                                                      \
+      decode_fwd_kernel<1, 2><<<dim3(grid), dim3(kThreads), 0, st>>>(g);         \
+    else if (ga.w.dq)                                                            \
+      decode_fwd_kernel<T, 1><<<dim3(grid), dim3(kThreads), 0, st>>>(g);         \
     else                                                                         \
-      decode_fwd_kernel<T, false><<<dim3(grid), dim3(kThreads), 0, st>>>(g);     \
+      decode_fwd_kernel<T, 0><<<dim3(grid), dim3(kThreads), 0, st>>>(g);         \
     break;
   switch (mt) {
     DEC_CASE(1) DEC_CASE(2) DEC_CASE(3)

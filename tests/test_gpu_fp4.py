@@ -63,7 +63,10 @@ LAYER_CASES = [
     # M, K, N, r, s
     (64, 256, 128, 8, 2.0),
     (300, 320, 72, 16, -0.5),
-    (7, 512, 264, 8, 1.0),           # M <= 16 (the large-M kernel serves every M for E2M1)
+    (7, 512, 264, 8, 1.0),           # M <= 16: the decode kernel's E2M1 form
+    (1, 1024, 264, 8, 1.0),
+    (16, 8192, 512, 16, 2.0),
+    (40, 512, 136, 8, 0.5),          # 16 < M <= 48: the large-M kernel (E2M1 decode form: M <= 16)
     (257, 1024, 64, 0, 1.0),         # no adapters
     (130, 512, 136, 128, 0.25),      # the largest rank
 ]
@@ -108,9 +111,12 @@ def test_identity_probes_are_exact(lib):
     I_N = torch.eye(N, dtype=torch.bfloat16, device=DEV)
     dX, _, _ = lib.qlora_bwd(I_N, torch.zeros(N, K, dtype=torch.bfloat16, device=DEV), qg, None, None,
                              1.0, None)
+    # the decode kernel (M <= 16): the first 16 rows of the identity give the first 16 columns
+    Y16, _ = lib.qlora_fwd(I_K[:16].contiguous(), qg, None, None, 1.0)
     torch.cuda.synchronize()
     assert torch.equal(Y, deq16.t().contiguous())
     assert torch.equal(dX, deq16)
+    assert torch.equal(Y16, deq16[:, :16].t().contiguous())
 
 
 def test_moe_with_fp4_experts(lib):
@@ -132,8 +138,9 @@ def test_moe_with_fp4_experts(lib):
         check_close(name, f32(got), ref)
 
 
-def test_swiglu_pair_with_fp4_weight(lib):
-    M, K, N, r, s = 96, 256, 64, 8, 0.5
+@pytest.mark.parametrize("M", [96, 8])   # the pair kernel; the decode kernel's E2M1 form
+def test_swiglu_pair_with_fp4_weight(lib, M):
+    K, N, r, s = 256, 64, 8, 0.5
     X = wl.normal_bf16(21, (M, K), 1.0)
     Wgu = wl.normal_bf16(22, (2 * N, K), 0.02)
     Agu = wl.normal_bf16(23, (2 * r, K), K ** -0.5)

@@ -14,6 +14,7 @@ the Unsloth pages' "About the Unsloth Project" section):
   decode  M=16    K=8192   N=28672  r=16  s=2   absmax int8/256     fwd (weight-stream bound)
   down    M=16384 K=14336  N=4096   r=32  s=1   absmax int8/256     fwd+bwd
   mlp_up_e2m1  the mlp_up shape with an E2M1 base (E4M3 scale per 16)  fwd+bwd
+  decode_e2m1  the decode shape with an E2M1 base                      fwd
 
 and one gate/up pair (two projections on the same X joined by SwiGLU, PAIRS below):
 
@@ -102,6 +103,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("down", 5, 16384, 14336, 4096, 32, 1.0, 256, 1.0, 0.02, 0.01, 1e-2, True),
     # the mlp_up shape with the E2M1 base weight (the 4-bit float variant of the format)
     Workload("mlp_up_e2m1", 8, 8192, 4096, 11008, 64, 0.5, 0, 1.0, 0.02, 0.01, 1.0, True, "e2m1"),
+    # and the decode shape with an E2M1 base
+    Workload("decode_e2m1", 9, 16, 8192, 28672, 16, 2.0, 0, 1.0, 0.015, 0.01, 1.0, False, "e2m1"),
 ]}
 
 
