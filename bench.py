@@ -1,42 +1,56 @@
 #!/usr/bin/env python3
 """Benchmark of the fused NF4 QLoRA linear layer on one MI355X.
 
-One step = one forward + backward of the layer on the "down" workload (a Llama down_proj training
-step: X bf16 [16384, 14336], W NF4 [4096, 14336] with double-quantised absmax, LoRA r = 32, s = 1,
-dY ~ N(0, 1e-2)):
+The default run measures the five layer workloads one after the other and prints ONE JSON line.
+Its top level is the "down" workload (a Llama down_proj training step: X bf16 [16384, 14336],
+W NF4 [4096, 14336] with double-quantised absmax, LoRA r = 32, s = 1, dY ~ N(0, 1e-2)), the
+largest forward + backward shape, where one step is
 
     qlora_lora_down   T = X A^T
     qlora_fwd_fused   Y = X deq(W)^T + s T B^T             (one launch)
     qlora_bwd (dX=0)  U = dY B, dA = s U^T X, dB = s dY^T T
     qlora_bwd_dx      dX = dY deq(W) + s U A                (one launch)
 
-Inputs are seeded synthetic tensors of that shape, resident in HBM before timing starts. W is
-quantised once (untimed), as a frozen base weight is, and then copied so that the steps rotate
-over enough distinct copies (>= 512 MB together) that no step finds its weight in the 256 MB
-last-level cache or the L2 left there by the step before (the weight is the only input read by
-every step; X and dY of the large workloads are far larger than the caches).
+and its "configs" object holds one entry per workload, each with its own step time, roofline
+and CPU baseline:
 
-Output: one JSON line with the whole-step throughput (algorithmic matmul flops / step time on the
-host clock), the roofline of the dominant kernel (the larger of the two fused dequant-GEMM
-launches, timed with HIP events on the stream it runs on), the weight-stream rate of the
-decode-shaped forward (M = 16, K = 8192, N = 28672: weight-stream bytes / whole qlora_fwd time)
-the CPU oracle timed on a bounded row sample of the same workload, and (context) measured-achievable
-references on this machine: the vendor bf16 GEMM and the unfused forward on the same data for the
-matrix-core-bound shapes, a device copy for the HBM-bound one.
+    small   M=64    K=256   N=256    r=8   fp32 absmax      fwd+bwd  (launch latency only)
+    q_proj  M=4096  K=4096  N=4096   r=16  int8/256 absmax  fwd      (matrix-core bound)
+    mlp_up  M=8192  K=4096  N=11008  r=64  int8/256 absmax  fwd+bwd  (matrix-core bound)
+    decode  M=16    K=8192  N=28672  r=16  int8/256 absmax  fwd      (weight-stream bound: GB/s)
+    down    M=16384 K=14336 N=4096   r=32  int8/256 absmax  fwd+bwd  (matrix-core bound)
 
-    python bench.py [--steps K] [--warmup W] [--workload down] [--no-cpu-baseline]
-                    [--no-weight-stream] [--copy-calibration]
+Inputs are seeded synthetic tensors of those shapes, resident in HBM before timing starts. W is
+quantised once per workload (untimed), as a frozen base weight is, then copied so that the steps
+rotate over enough distinct copies (>= 512 MB together) that no step finds its weight in the
+256 MB last-level cache or the L2 left there by the step before.
 
---workload mlp_swiglu measures the gate/up SwiGLU pair instead (a step: qlora_swiglu_fwd +
-qlora_swiglu_bwd on the mlp_up shape, two projections); --workload moe_mlp_up the grouped
-mixture-of-experts layer (a step: qlora_moe_fwd + qlora_moe_bwd, 8 experts of the mlp_up shape,
-16384 routed rows); --workload mlp_up_e2m1 the single layer of the mlp_up shape with an E2M1 base
-weight (4-bit floats, E4M3 scale per 16, float32 tensor scale) instead of NF4.
+Timing, per workload: W warm-up steps, then K steps between two synchronisations (host clock:
+ms_per_step and value), with a HIP event pair on the launch stream around every call of the
+step (phase_ms). The roofline of each workload is that of its dominant fused launch (forward
+and, with a backward, dX; decode: the forward's stream kernel), from its mean duration over
+the timed steps: algorithmic flops (or weight-stream bytes) per launch / mean duration.
+For the decode workload the value is the weight-stream rate of the whole qlora_fwd call
+(weight-stream bytes / call time, the T pre-pass included). cpu_baseline times the CPU oracle
+(float64) on a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-context] [--copy-calibration] [--summarize-trace DIR]
+
+--workload runs one workload alone (its entry becomes the top level). mlp_swiglu measures the
+gate/up SwiGLU pair instead (a step: qlora_swiglu_fwd + qlora_swiglu_bwd on the mlp_up shape, two
+projections); moe_mlp_up the grouped mixture-of-experts layer (a step: qlora_moe_fwd +
+qlora_moe_bwd, 8 experts of the mlp_up shape, 16384 routed rows); mlp_up_e2m1 / decode_e2m1 the
+single layer with an E2M1 base weight (4-bit floats, E4M3 scale per 16, float32 tensor scale).
+--summarize-trace DIR reads a rocprofv3 kernel trace of this command and prints the per-workload
+kernel durations (split by grid size) that the profiles record.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -55,6 +69,8 @@ COLD_BYTES = 512 << 20        # rotate weight copies until they add up to this
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"qlora_fwd_fused": "fwd.hip", "qlora_bwd_dx": "dx.hip",
                   "qlora_fwd_fused (decode)": "decode16.hip"}
+DEFAULT_CONFIGS = ("small", "q_proj", "mlp_up", "decode", "down")
+HEADLINE = "down"
 
 
 def parse():
@@ -62,18 +78,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="down")
+    ap.add_argument("--workload", default=None,
+                    help="run one workload alone (default: the five layer workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the vendor-GEMM / device-copy reference measurements")
-    ap.add_argument("--no-weight-stream", action="store_true",
-                    help="skip the decode-shaped weight-stream measurement")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target wall time of the CPU oracle sample")
+                    help="skip the vendor-GEMM / MFMA-loop / device-copy reference measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target wall time of each CPU oracle sample")
     ap.add_argument("--wcopies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for 512 MB)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-trace", default=None, metavar="DIR",
+                    help="summarise a rocprofv3 kernel trace of this command (no GPU needed)")
     return ap.parse_args()
 
 
@@ -85,6 +102,31 @@ def pct(vals, q):
     v = sorted(vals)
     i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
     return v[i]
+
+
+def stats(v):
+    return {"mean": sum(v) / len(v), "median": pct(v, 0.5), "p10": pct(v, 0.1), "p90": pct(v, 0.9)}
+
+
+def host_cores():
+    """Cores this process may run on (the CPU baseline's thread pool is sized to them)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
 
 
 class Layer:
@@ -131,44 +173,61 @@ class Layer:
         if st != 0:
             raise RuntimeError(self.c.nf4_last_error().decode())
 
+    def q(self, i):
+        return ctypes.byref(self.qs[i % len(self.qs)])
+
     def lora_down(self, i):
         w, p = self.w, self.p
         self.check(self.c.qlora_lora_down(p["X"], w.M, w.K, p["A"], w.r, p["T"], p["ws_f"], self.fws, self.sp))
 
     def fwd_fused(self, i):
         w, p = self.w, self.p
-        self.check(self.c.qlora_fwd_fused(p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["T"],
-                                          p["B"], w.r, w.s, p["Y"], self.sp))
+        self.check(self.c.qlora_fwd_fused(p["X"], w.M, self.q(i), p["T"], p["B"], w.r, w.s, p["Y"], self.sp))
 
     def fwd_whole(self, i):
         """The whole forward call (T pre-pass and fused kernel), as a caller makes it."""
         w, p = self.w, self.p
-        self.check(self.c.qlora_fwd(p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["A"], p["B"],
-                                    w.r, w.s, p["Y"], p["T"], p["ws_f"], self.fws, self.sp))
+        self.check(self.c.qlora_fwd(p["X"], w.M, self.q(i), p["A"], p["B"], w.r, w.s, p["Y"], p["T"],
+                                    p["ws_f"], self.fws, self.sp))
+
+    def bwd_whole(self, i):
+        """The whole backward call (U, dX, dA, dB)."""
+        w, p = self.w, self.p
+        self.check(self.c.qlora_bwd(p["dY"], p["X"], w.M, self.q(i), p["A"], p["B"], w.r, w.s, p["T"],
+                                    p["dX"], p["dA"], p["dB"], p["ws_b"], self.bws, self.sp))
 
     def bwd_lora(self, i):
         """U (left at the start of the workspace), dA and dB: qlora_bwd without dX."""
         w, p = self.w, self.p
-        self.check(self.c.qlora_bwd(p["dY"], p["X"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["A"],
-                                    p["B"], w.r, w.s, p["T"], None, p["dA"], p["dB"], p["ws_b"], self.bws,
-                                    self.sp))
+        self.check(self.c.qlora_bwd(p["dY"], p["X"], w.M, self.q(i), p["A"], p["B"], w.r, w.s, p["T"],
+                                    None, p["dA"], p["dB"], p["ws_b"], self.bws, self.sp))
 
     def bwd_dx(self, i):
         w, p = self.w, self.p
-        self.check(self.c.qlora_bwd_dx(p["dY"], w.M, ctypes.byref(self.qs[i % len(self.qs)]), p["ws_b"],
-                                       p["A"], w.r, w.s, p["dX"], self.sp))
+        self.check(self.c.qlora_bwd_dx(p["dY"], w.M, self.q(i), p["ws_b"], p["A"], w.r, w.s, p["dX"],
+                                       self.sp))
 
 
-PHASES = ("lora_down", "fwd_fused", "bwd_lora", "bwd_dx")
-
-
-def time_layer(L, steps, warmup):
-    """Run warmup + steps steps; per-phase HIP-event times (ms) and the host-clock step time."""
-    import torch
+def step_calls(L):
+    """The calls of one step, by phase name. Forward-only workloads call qlora_fwd whole (the
+    decode shapes take the T pre-pass into the stream kernel's prologue only there); forward +
+    backward workloads call the launches separately so that the two fused launches can be timed
+    on their own (the same kernels as qlora_fwd + qlora_bwd). The small workload calls qlora_fwd
+    and qlora_bwd whole: it is timed for latency."""
     w = L.w
-    calls = [L.lora_down, L.fwd_fused] + ([L.bwd_lora, L.bwd_dx] if w.backward else [])
+    if w.name == "small" or (w.backward and w.M <= 64):
+        return [("qlora_fwd", L.fwd_whole), ("qlora_bwd", L.bwd_whole)]
+    if not w.backward:
+        return [("qlora_fwd", L.fwd_whole)]
+    return [("lora_down", L.lora_down), ("fwd_fused", L.fwd_fused), ("bwd_lora", L.bwd_lora),
+            ("bwd_dx", L.bwd_dx)]
+
+
+def time_steps(L, calls, steps, warmup):
+    """warmup + steps steps; the host-clock step time (ms) and per-call HIP-event times (ms)."""
+    import torch
     for i in range(warmup):
-        for c in calls:
+        for _, c in calls:
             c(i)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
@@ -177,21 +236,19 @@ def time_layer(L, steps, warmup):
     for s in range(steps):
         e = ev[s]
         e[0].record(L.stream)
-        for j, c in enumerate(calls):
+        for j, (_, c) in enumerate(calls):
             c(warmup + s)
             e[j + 1].record(L.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     per = {}
-    for j in range(len(calls)):
-        v = [ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)]
-        per[PHASES[j]] = {"mean": sum(v) / len(v), "median": pct(v, 0.5), "p10": pct(v, 0.1),
-                          "p90": pct(v, 0.9)}
+    for j, (name, _) in enumerate(calls):
+        per[name] = stats([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)])
     return (t1 - t0) * 1e3 / steps, per
 
 
 def time_call(L, fn, steps, warmup):
-    """HIP-event times (ms) of one call over rotating weight copies: median, p10, p90."""
+    """HIP-event times (ms) of one call over rotating weight copies."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -202,8 +259,7 @@ def time_call(L, fn, steps, warmup):
         fn(warmup + s)
         b.record(L.stream)
     torch.cuda.synchronize()
-    v = [a.elapsed_time(b) for a, b in ev]
-    return {"median": pct(v, 0.5), "p10": pct(v, 0.1), "p90": pct(v, 0.9)}
+    return stats([a.elapsed_time(b) for a, b in ev])
 
 
 def source_sha(name):
@@ -224,24 +280,76 @@ def traffic_for(name, workload):
     return t.get("bytes_per_launch")
 
 
-def run_weight_stream(dev, steps, warmup):
-    """Decode-shaped forward (M = 16): weight-stream bytes / whole qlora_fwd time, cold weights."""
-    import workloads as wl
-    w = wl.WORKLOADS["decode"]
-    L = Layer(w, dev)
-    _, per = time_layer(L, steps, warmup)
-    fwd_ms = time_call(L, L.fwd_whole, steps, warmup)["median"]
-    wb = w.weight_stream_bytes()
-    gbs = wb / (fwd_ms * 1e-3) / 1e9
-    kern = wb / (per["fwd_fused"]["median"] * 1e-3) / 1e9
-    out = {"workload": f"decode: X [16,8192] bf16, W NF4 [28672,8192] double-quant int8/256, LoRA r=16, fwd",
-           "weight_stream_bytes": wb, "qlora_fwd_us": round(fwd_ms * 1e3, 2),
-           "value": round(gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
-           "fused_kernel_us": round(per["fwd_fused"]["median"] * 1e3, 2),
-           "fused_kernel_GBps": round(kern, 1),
-           "cold": f"{len(L.copies)} rotating weight copies"}
-    del L
-    return out
+def roofline_mfma(kernel, t_ms, flops, workload):
+    achieved = flops / (t_ms["mean"] * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops,
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in t_ms.items()},
+            "traffic": traffic_for(kernel, workload)}
+
+
+def roofline_hbm(kernel, t_ms, nbytes, workload):
+    achieved = nbytes / (t_ms["mean"] * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes,
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in t_ms.items()},
+            "traffic": traffic_for(kernel, workload)}
+
+
+def describe(w):
+    return (f"{w.name}: X [{w.M},{w.K}] bf16, "
+            + (f"W E2M1 [{w.N},{w.K}] E4M3 scale per 16 + fp32 tensor scale, " if w.fmt == "e2m1"
+               else f"W NF4 [{w.N},{w.K}] block 64"
+               f"{' double-quant int8/256' if w.dq_block else ' fp32 absmax'}, ")
+            + f"LoRA r={w.r} s={w.s}, {'fwd+bwd' if w.backward else 'fwd'}")
+
+
+def run_config(w, dev, args, cpu=True):
+    """One workload: step time, per-call times, the roofline of its dominant fused launch and
+    (cpu) the CPU oracle on a sample. Returns the JSON object and the Layer (for the context)."""
+    L = Layer(w, dev, args.wcopies)
+    calls = step_calls(L)
+    step_ms, per = time_steps(L, calls, args.steps, args.warmup)
+    M, N, K, r = w.M, w.N, w.K, w.r
+    out = {"workload": describe(w), "M": M, "K": K, "N": N, "r": r, "weight_copies": len(L.copies),
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+           "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}}
+    kernels = {}
+    if w.name == "small" or (w.backward and M <= 64):
+        out.update(bound="latency", value=round(step_ms * 1e3, 2), unit="us per fwd+bwd step",
+                   higher_is_better=False)
+    elif not w.backward:
+        # forward only: the whole qlora_fwd call is the step; its fused launch is timed alone too
+        fwd_only = time_call(L, L.fwd_fused, args.steps, args.warmup)
+        if M <= 64:
+            wb = w.weight_stream_bytes()
+            gbs = wb / (step_ms * 1e-3) / 1e9
+            out.update(bound="hbm", value=round(gbs, 1), unit="GB/s", higher_is_better=True,
+                       weight_stream_bytes=wb, frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+            kernels["qlora_fwd_fused (decode)"] = roofline_hbm("qlora_fwd_fused (decode)", fwd_only, wb, w.name)
+        else:
+            fl = w.fwd_flops()
+            out.update(bound="mfma", value=round(fl / (step_ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                       higher_is_better=True)
+            kernels["qlora_fwd_fused"] = roofline_mfma("qlora_fwd_fused", fwd_only,
+                                                       2 * M * N * K + 2 * M * N * r, w.name)
+        out["qlora_fwd_fused_ms"] = {q: round(x, 4) for q, x in fwd_only.items()}
+    else:
+        fl = w.fwd_flops() + w.bwd_flops()
+        out.update(bound="mfma", value=round(fl / (step_ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                   higher_is_better=True)
+        kernels["qlora_fwd_fused"] = roofline_mfma("qlora_fwd_fused", per["fwd_fused"],
+                                                   2 * M * N * K + 2 * M * N * r, w.name)
+        kernels["qlora_bwd_dx"] = roofline_mfma("qlora_bwd_dx", per["bwd_dx"],
+                                                2 * M * N * K + 2 * M * r * K, w.name)
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["kernel_us"]["mean"])
+        out["roofline"] = kernels[dom]
+        if len(kernels) > 1:
+            out["kernels"] = kernels
+    if cpu and not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds)
+    return out, L
 
 
 def run_merge(L, steps, warmup):
@@ -253,7 +361,7 @@ def run_merge(L, steps, warmup):
     P = lambda t: ctypes.c_void_p(t.data_ptr())
 
     def fn(i):
-        L.check(c.qlora_merge(ctypes.byref(L.qs[i % len(L.qs)]), P(L.A), P(L.B), w.r, w.s, P(out), L.sp))
+        L.check(c.qlora_merge(L.q(i), P(L.A), P(L.B), w.r, w.s, P(out), L.sp))
     t = time_call(L, fn, steps, warmup)
     nbytes = w.weight_stream_bytes() + 2 * w.r * w.K + 2 * w.N * w.r + 2 * w.N * w.K
     gbs = nbytes / (t["median"] * 1e-3) / 1e9
@@ -264,9 +372,8 @@ def run_merge(L, steps, warmup):
 
 
 def run_cpu_baseline(w, target_s):
-    """The oracle (float64 numpy/BLAS) on a row sample of the same step."""
-    from threadpoolctl import threadpool_info
-
+    """The oracle (float64 numpy/BLAS) on a bounded row sample of the same step, in the workload's
+    unit: TFLOP/s of algorithmic flops, or (decode) GB/s of weight-stream bytes."""
     import workloads as wl
     from oracle import nf4, qlora
     W = wl.tensor(w, "W").float().numpy()
@@ -276,37 +383,41 @@ def run_cpu_baseline(w, target_s):
     else:
         Wd = nf4.dequantize_f32(nf4.quantize(W, w.dq_block))
     A, B = wl.tensor(w, "A").float().numpy(), wl.tensor(w, "B").float().numpy()
-
     Xall = wl.tensor(w, "X").float().numpy()
     dYall = wl.tensor(w, "dY").float().numpy() if w.backward else None
 
-    def step(rows):
+    def step(rows, reps=1):
         X = Xall[:rows]
         dY = dYall[:rows] if w.backward else None
         t = time.perf_counter()
-        qlora.forward(X, Wd, A, B, w.s)
-        if w.backward:
-            qlora.backward(dY, X, Wd, A, B, w.s)
+        for _ in range(reps):
+            qlora.forward(X, Wd, A, B, w.s)
+            if w.backward:
+                qlora.backward(dY, X, Wd, A, B, w.s)
         return time.perf_counter() - t
 
-    rows = min(64, w.M)
+    rows, reps = min(64, w.M), 1
     dt = step(rows)
     while dt < 0.4 * target_s and rows < w.M:       # grow the sample until it takes ~target_s
         rows = int(min(w.M, max(2 * rows, rows * target_s / max(dt, 1e-3))))
         rows = max(64, rows // 64 * 64) if w.M >= 64 else w.M
         dt = step(rows)
-    flops = (w.fwd_flops() + (w.bwd_flops() if w.backward else 0)) * rows / w.M
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "cpu": model, "wall_s": round(dt, 2),
-            "sample": f"{rows} of {w.M} rows of the {w.name} workload, forward+backward in float64 "
-                      f"(numpy/BLAS), {dt:.1f}s wall; W dequantised once outside the timing"}
+    while dt < 0.4 * target_s:                      # whole workload is quick: repeat it
+        reps = int(max(2 * reps, reps * target_s / max(dt, 1e-3)))
+        dt = step(rows, reps)
+    frac = rows * reps / w.M
+    out = {"kind": "oracle", "cores": host_cores(), "threads": blas_threads(), "cpu": cpu_model(),
+           "wall_s": round(dt, 2)}
+    if not w.backward and w.M <= 64:
+        out.update(value=round(w.weight_stream_bytes() * frac / dt / 1e9, 4), unit="GB/s")
+    else:
+        flops = (w.fwd_flops() + (w.bwd_flops() if w.backward else 0)) * frac
+        out.update(value=round(flops / dt / 1e12, 5), unit="TFLOP/s")
+    out["sample"] = (f"{rows} of {w.M} rows of the {w.name} workload"
+                     + (f", {reps} times" if reps > 1 else "")
+                     + f", {'forward+backward' if w.backward else 'forward'} in float64 (numpy/BLAS),"
+                     f" {dt:.1f}s wall; W dequantised once outside the timing")
+    return out
 
 
 def run_pair(args, pw, dev):
@@ -512,8 +623,6 @@ def run_moe(args, mw, dev):
 def run_moe_cpu_baseline(mw, target_s):
     """The oracle's grouped layer (float64) on a sample: the first rows of every expert's group,
     in proportion to its count."""
-    from threadpoolctl import threadpool_info
-
     import numpy as np
     import workloads as wl
     from oracle import moe, nf4
@@ -538,8 +647,8 @@ def run_moe_cpu_baseline(mw, target_s):
         frac = min(1.0, max(2 * frac, frac * target_s / max(dt, 1e-3)))
         dt, rows = step(frac)
     flops = (mw.fwd_flops() + mw.bwd_flops()) * rows / mw.M
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": host_cores(),
+            "threads": blas_threads(), "kind": "oracle",
             "wall_s": round(dt, 2),
             "sample": f"{rows} of {mw.M} rows of the {mw.name} layer (the first rows of each expert's group, "
                       f"in proportion), forward+backward in float64 (numpy/BLAS), {dt:.1f}s wall; the weights "
@@ -548,8 +657,6 @@ def run_moe_cpu_baseline(mw, target_s):
 
 def run_pair_cpu_baseline(pw, target_s):
     """The oracle's gate/up pair (float64) on a row sample of the same step."""
-    from threadpoolctl import threadpool_info
-
     import workloads as wl
     from oracle import nf4, swiglu
     Wd = nf4.dequantize_f32(nf4.quantize(wl.pair_tensor(pw, "Wgu").float().numpy(), pw.dq_block))
@@ -572,8 +679,8 @@ def run_pair_cpu_baseline(pw, target_s):
         rows = max(64, rows // 64 * 64)
         dt = step(rows)
     flops = (pw.fwd_flops() + pw.bwd_flops()) * rows / pw.M
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": host_cores(),
+            "threads": blas_threads(), "kind": "oracle",
             "wall_s": round(dt, 2),
             "sample": f"{rows} of {pw.M} rows of the {pw.name} pair, forward+backward in float64 "
                       f"(numpy/BLAS), {dt:.1f}s wall; the weights dequantised once outside the timing"}
@@ -681,8 +788,60 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 5}), flush=True)
 
 
+def trace_groups():
+    """(kernel name prefix, workgroups) -> (workload, launch) for the fused launches of the
+    default run: the tile counts of the 256 x 256 forward and dX kernels and of the 112-row
+    stream kernel, from the workload shapes."""
+    import workloads as wl
+    out = {}
+    for name in DEFAULT_CONFIGS:
+        w = wl.WORKLOADS[name]
+        cd = lambda a, b: -(-a // b)
+        if w.M <= 16 and w.dq_block and w.K % 256 == 0:
+            out[("nf4q::decode16_fwd_kernel", cd(w.N, 112))] = (name, "qlora_fwd_fused (decode)")
+        elif w.M > 48 or w.K % 256:
+            out[("nf4q::fwd_fused_kernel", cd(w.N, 256) * cd(w.M, 256))] = (name, "qlora_fwd_fused")
+        if w.backward:
+            out[("nf4q::dx_fused_kernel", cd(w.K, 256) * cd(w.M, 256))] = (name, "qlora_bwd_dx")
+    return out
+
+
+def summarize_trace(path):
+    """Per-(kernel, grid) durations from a rocprofv3 kernel trace (CSV) of this command: the fused
+    kernels of different workloads share names, so they are told apart by their workgroup count."""
+    files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {path}")
+    groups = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                grid = int(row.get("Grid_Size_X", row.get("Grid_Size", 0)) or 0)
+                wg = int(row.get("Workgroup_Size_X", row.get("Workgroup_Size", 1)) or 1)
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                groups.setdefault((name, grid // max(wg, 1)), []).append(dur)
+    known = trace_groups()
+    print(f"# source: {', '.join(os.path.relpath(f, path) for f in files)}")
+    print("# durations in microseconds (End_Timestamp - Start_Timestamp of each dispatch)")
+    print(f"{'calls':>5} {'mean_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10}  {'wgs':>6}  "
+          f"{'workload/launch':<36} kernel")
+    rows = []
+    for (name, wgs), v in groups.items():
+        tag = next((f"{wl_}/{launch}" for (pre, n), (wl_, launch) in known.items()
+                    if n == wgs and name.startswith(pre)), "")
+        rows.append((sum(v), name, wgs, v, tag))
+    for _, name, wgs, v, tag in sorted(rows, reverse=True):
+        s = stats(v)
+        print(f"{len(v):5d} {s['mean']:10.2f} {s['median']:10.2f} {min(v):10.2f} {max(v):10.2f}  {wgs:6d}  "
+              f"{tag:<36} {name[:110]}")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -699,67 +858,54 @@ def main():
     if args.workload in wl.MOES:
         run_moe(args, wl.MOES[args.workload], dev)
         return
-    w = wl.WORKLOADS[args.workload]
-    L = Layer(w, dev, args.wcopies)
-    step_ms, per = time_layer(L, args.steps, args.warmup)
-    whole_fwd = time_call(L, L.fwd_whole, args.steps, args.warmup) if not w.backward else None
-    ncopies = len(L.copies)
-    merge = run_merge(L, args.steps, args.warmup) if w.M > 64 and w.fmt == "nf4" else None
-    context = None if args.no_context else run_context(L)
-    del L
-    torch.cuda.empty_cache()
-    flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0)
-    value = flops / (step_ms * 1e-3) / 1e12
-    M, N, K, r = w.M, w.N, w.K, w.r
-    kern = {"qlora_fwd_fused": (per["fwd_fused"], 2 * M * N * K + 2 * M * N * r)}
-    if w.backward:
-        kern["qlora_bwd_dx"] = (per["bwd_dx"], 2 * M * N * K + 2 * M * r * K)
-    name = max(kern, key=lambda k: kern[k][0]["mean"])
-    t, work = kern[name]
-    if M <= 64:     # the decode-shaped forward: bound by the weight stream
-        name = "qlora_fwd_fused (decode)"
-        achieved = w.weight_stream_bytes() / (t["mean"] * 1e-3) / 1e9
-        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = work / (t["mean"] * 1e-3) / 1e12
-        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["kernel_us"] = {k: round(v * 1e3, 2) for k, v in t.items()}
-    roof["traffic"] = traffic_for(name, w.name)
+    if args.workload is not None and args.workload not in wl.WORKLOADS:
+        raise SystemExit(f"unknown workload {args.workload}; one of "
+                         f"{sorted(wl.WORKLOADS) + sorted(wl.PAIRS) + sorted(wl.MOES)}")
+    names = [args.workload] if args.workload else list(DEFAULT_CONFIGS)
+    head = args.workload or HEADLINE
+    configs, extra = {}, {}
+    for name in names:
+        w = wl.WORKLOADS[name]
+        log(f"== {name}")
+        res, L = run_config(w, dev, args)
+        if res["bound"] == "mfma" and not args.no_context:
+            ctx = run_context(L)
+            loop = ctx.get("mfma_loop", {}).get("TFLOP/s")
+            vendor = ctx.get("vendor_bf16_gemm", {}).get("TFLOP/s")
+            for k in res.get("kernels", {"_": res["roofline"]}).values():
+                if loop:
+                    k["frac_of_mfma_loop"] = round(k["achieved"] / loop, 4)
+                if vendor:
+                    k["frac_of_vendor_gemm"] = round(k["achieved"] / vendor, 4)
+            res["context"] = ctx
+        elif res["bound"] == "hbm" and not args.no_context and name == head:
+            res["context"] = run_context(L)
+        if name == head and w.M > 64 and w.fmt == "nf4":
+            extra["merge"] = run_merge(L, args.steps, args.warmup)
+        del L
+        torch.cuda.empty_cache()
+        configs[name] = res
+        log(f"   {name}: {res['value']} {res['unit']}"
+            + (f", roofline {res['roofline']['kernel']} frac {res['roofline']['frac']}" if "roofline" in res else ""))
+    h = configs[head]
+    cfg = {k: h[k] for k in ("workload", "M", "K", "N", "r", "weight_copies", "phase_ms")}
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{w.name}: X [{M},{K}] bf16, "
-                               + (f"W E2M1 [{N},{K}] E4M3 scale per 16 + fp32 tensor scale, " if w.fmt == "e2m1"
-                                  else f"W NF4 [{N},{K}] block 64"
-                                  f"{' double-quant int8/256' if w.dq_block else ' fp32 absmax'}, ") +
-                               f"LoRA r={r} s={w.s}, {'fwd+bwd' if w.backward else 'fwd'}",
-                   "M": M, "K": K, "N": N, "r": r, "weight_copies": ncopies,
-                   "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}},
-        "roofline": roof,
+        "metric": METRIC, "value": h["value"], "unit": h["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+        "higher_is_better": h["higher_is_better"], "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "config": cfg,
     }
-    if merge:
-        out["merge"] = merge
-    if whole_fwd:
-        out["config"]["qlora_fwd_ms"] = {q: round(x, 4) for q, x in whole_fwd.items()}
-        if M <= 64:
-            gbs = w.weight_stream_bytes() / (whole_fwd["median"] * 1e-3) / 1e9
-            out["config"]["weight_stream_GBps"] = round(gbs, 1)
-    if context:
-        ref = context.get("vendor_bf16_gemm", {}).get("TFLOP/s") or context.get("device_copy", {}).get("GB/s")
-        if ref:
-            roof["frac_of_measured_achievable"] = round(roof["achieved"] / ref, 4)
-        loop = context.get("mfma_loop", {}).get("TFLOP/s")
-        if loop:
-            roof["frac_of_mfma_loop"] = round(roof["achieved"] / loop, 4)
-        out["context"] = context
-    if not args.no_weight_stream and w.name != "decode":
-        out["weight_stream"] = run_weight_stream(dev, 20, 5)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds)
+    if "roofline" in h:
+        out["roofline"] = h["roofline"]
+    if "cpu_baseline" in h:
+        out["cpu_baseline"] = h["cpu_baseline"]
+    if len(names) > 1:
+        out["configs"] = configs
+    else:
+        for k in ("kernels", "context", "qlora_fwd_fused_ms"):
+            if k in h:
+                out[k] = h[k]
+    out.update(extra)
     print(json.dumps(out), flush=True)
 
 

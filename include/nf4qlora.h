@@ -90,8 +90,13 @@ typedef struct {
 } nf4_tensor;
 
 /* Quantise W (bf16 or float32, [q->n, q->k]) into the buffers of *q, as described above (NF4
- * for block 64, E2M1 for block 16). NF4: one kernel launch; E2M1: four (the tensor maximum, then
- * the groups). No workspace. Bit-exact: the codes, block constants and scales equal those of the
+ * for block 64, E2M1 for block 16) [the frozen base stored as 4-bit NormalFloat with double
+ * quantisation of its constants: Unsloth v0.1.463-beta release article, "About the Unsloth
+ * Project"; E2M1: NVFP4 update article, "NVFP4: A Quantization Format for the Next Generation
+ * of Hardware"]. NF4: one kernel launch (the double quantisation of a run of 256 constants is
+ * finished by the workgroup that computes them, so no staging workspace is needed); E2M1: four
+ * (the tensor maximum, then the groups). No workspace. w_dtype is an nf4_dtype value.
+ * Bit-exact: the codes, block constants and scales equal those of the
  * definition for every finite input.
  * Errors: NF4_EINVAL for a NULL pointer, a misaligned pointer or n < 1;
  *         NF4_EUNSUPPORTED for k % 64 != 0, block not in {64, 16}, dq_block not in {0, 256}
@@ -112,14 +117,19 @@ int nf4_codebook(float *levels, float *thresholds);
 /* Bytes of device workspace qlora_fwd needs for these sizes (0 when r == 0). */
 size_t qlora_fwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 
-/* Forward of the QLoRA layer:  T = bf16(X A^T),  Y = bf16(X deq(W)^T + s T B^T).
+/* Forward of the QLoRA layer:  T = bf16(X A^T),  Y = bf16(X deq(W)^T + s T B^T)  [the
+ * layer with the low-rank correction Delta W = B A: Unsloth v0.1.463-beta release article,
+ * "About the Unsloth Project"; dequantisation, matmul and LoRA correction computed together:
+ * "Inside Unsloth" listing, "What You'll Learn", "LoRA and QLoRA"; pyshine Unsloth code tour,
+ * "Why You Need This"].
  *   X  bf16 [m, k]   input activations                     (k == W->k)
  *   W  NF4 [n, k]    frozen base weight
  *   A  bf16 [r, k]   LoRA down-projection; B bf16 [n, r] LoRA up-projection (NULL when r == 0)
  *   s  LoRA scaling (lora_alpha / r by the usual convention)
  *   Y  bf16 [m, n]   output
  *   T  bf16 [m, r]   output: X A^T, kept for qlora_bwd (NULL when r == 0)
- *   ws workspace of at least qlora_fwd_workspace_bytes(m, n, k, r) bytes (NULL when that is 0)
+ *   ws workspace of at least qlora_fwd_workspace_bytes(m, n, k, r) bytes (NULL when that is 0):
+ *      the float32 split-K partial sums of T = X A^T, owned by the caller, free after the call
  * The LoRA term uses T as rounded to bf16 and s*B rounded to bf16 (exact when s is a power of
  * two). Requires m >= 1, n % 8 == 0, 0 <= r <= 128.
  * Errors: NF4_EINVAL for NULL/misaligned pointers, m < 1, r out of range, a short workspace;
@@ -146,7 +156,10 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
 /* Bytes of device workspace qlora_bwd needs for these sizes. */
 size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 
-/* Backward of the QLoRA layer, given the upstream gradient dY bf16 [m, n] and T from qlora_fwd
+/* Backward of the QLoRA layer [only the adapters train, the 4-bit base is frozen: Unsloth
+ * v0.1.463-beta release article, "About the Unsloth Project"; the rewritten backward pass:
+ * same article and pyshine Unsloth code tour, "Why You Need This"], given the upstream gradient
+ * dY bf16 [m, n] and T from qlora_fwd
  * (T may be NULL: it is then recomputed as X A^T into the workspace, exactly as qlora_fwd and
  * qlora_lora_down compute it):
  *   U  = bf16(dY B)                               (left in the workspace: see below)
@@ -187,14 +200,14 @@ int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, 
  * Bytes of device workspace qlora_swiglu_fwd and qlora_swiglu_bwd need (the same for both). */
 size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 
-/* Forward: H bf16 [m, n] = bf16(silu(Yg) * Yu), computed in float32 from the bf16 Yg, Yu that are
- * also returned in Ygu bf16 [m, 2n] (each row: Yg then Yu), kept for the backward; Tgu bf16
+/* Forward: H bf16 [m, n] = bf16(silu(Yg) * Yu), computed in float32, and Ygu bf16 [m, 2n] (each
+ * row: Yg then Yu), kept for the backward; Tgu bf16
  * [m, 2r] = [X Ag^T | X Au^T] (may be NULL: the backward then recomputes it). Agu, Bg, Bu, Tgu
  * NULL when r == 0. ws: at least qlora_swiglu_workspace_bytes(m, n, k, r) bytes, 16-byte aligned.
  * Above the decode shapes (m > 48, or k % 256 != 0, or m > 16 with an E2M1 weight) the GEMM and
- * the activation are ONE launch of the fused kernel, H computed in its epilogue; the decode shapes
- * run the stacked forward, then the activation kernel (H from Ygu by the same float32
- * expression).
+ * the activation are ONE launch of the fused kernel, H computed in its epilogue from the float32
+ * sums of Yg and Yu (one rounding); the decode shapes run the stacked forward, then the
+ * activation kernel (H from the bf16 Ygu by the same float32 expression).
  * Errors: as qlora_fwd; NF4_EINVAL also when Wgu->n is odd, r > 64 or H / Ygu is NULL. */
 int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
                      const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,

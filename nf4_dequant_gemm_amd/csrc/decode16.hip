@@ -47,6 +47,13 @@ constexpr int kSOff = kXOff + 16 * 512;      // run scale of each row's group: 1
 constexpr int kSlotBytes = kSOff + 512;
 constexpr int kQWinBytes = 128 * 16;         // int8 block codes of 4 stages: 128 rows x 16
 constexpr int kTabBytes = 256 * 64 * 4;      // 64 KB
+// Copies (buffer_load ... lds) one wave issues per stage, and the extra one waves 0 and 1 issue in
+// the stages that also fetch a window of block codes. dma() below issues exactly these, and the
+// stage waits are derived from them: a stage waits until only the copies of the two stages after
+// it are in flight.
+constexpr int kStageCopies = 3;
+constexpr int kWindowCopies = 1;
+constexpr int kPending = 2 * kStageCopies;
 
 struct Dec16Args {
   const uint16_t *X;
@@ -170,18 +177,25 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     st = st < nst ? st : nst - 1;
     st += rot;
     st = st < nst ? st : st - nst;
-    dma16(rC, dst + cdst0, cvoff0, (uint32_t)(st * 128));
-    dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
-    if (wave < 6) {
-      dma16(rC, dst + cdst1, cvoff1, (uint32_t)(st * 128));
-      if (window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
-    } else {
-      const uint32_t run = (uint32_t)((boff + krow * kblk + 4 * st) >> 8);
-      dma4(rS, dst + sdst, run * 4);
+    // kStageCopies copies: codes, X, then codes (waves 0..5) or the run scales (waves 6, 7)
+#pragma unroll
+    for (int c = 0; c < kStageCopies; ++c) {
+      if (c == 0) {
+        dma16(rC, dst + cdst0, cvoff0, (uint32_t)(st * 128));
+      } else if (c == 1) {
+        dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
+      } else if (wave < 6) {
+        dma16(rC, dst + cdst1, cvoff1, (uint32_t)(st * 128));
+      } else {
+        const uint32_t run = (uint32_t)((boff + krow * kblk + 4 * st) >> 8);
+        dma4(rS, dst + sdst, run * 4);
+      }
     }
+    // kWindowCopies more: the block codes of stages st .. st + 3 (waves 0, 1)
+#pragma unroll
+    for (int c = 0; c < kWindowCopies; ++c)
+      if (window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
   };
-  // Copies this wave issues in one stage's DMA (the count the stage waits below rely on).
-  auto ndma = [&](bool window) { return 3 + (int)(window && wave < 2); };
 
   // LoRA operands of the tile this wave finishes (tile 4 g + j below, g = wave / 4,
   // j = wave % 4), loaded now so that their latency hides under the main loop: rank steps of 32,
@@ -330,11 +344,10 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     // copies issued in the two stages before st (phases (i + 2) % 4 and (i + 3) % 4 issue the
     // copies of phases i + 1 and i + 2 = (i + 1) % 4, (i + 2) % 4; the window goes with phase 0)
     const bool w1 = ((i + 1) & 3) == 0, w2 = ((i + 2) & 3) == 0;
-    const int pending = ndma(w1) + ndma(w2);
-    if (pending == 7)
-      asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if ((w1 || w2) && wave < 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending + kWindowCopies) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
     const int in = (i + 3) & 3;                      // phase of stage st + 3
     dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
     consume(opaque(lds_addr(slot(i))), opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i));  // 4 codes of each row

@@ -149,7 +149,7 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
 // (N = g.C), B the stacked block-diagonal [2N, 2r]; a tile's 256 columns are gate columns
 // n0 .. n0 + 127 (weight and B rows n0 ..) and the up columns of the same indices (rows N + n0 ..),
 // so the epilogue holds Yg and Yu of the same columns: it writes both to g.out ([M, 2N], gate then
-// up) and H = silu(Yg) * Yu, from their bf16 values, to g.hout ([M, N], row stride g.ldh).
+// up) and H = silu(Yg) * Yu, from their float32 sums, to g.hout ([M, N], row stride g.ldh).
 template <int kFmt, bool kGrp, bool kPair = false>
 __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr) {
   constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
@@ -427,24 +427,29 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   // this kernel, and streaming it out measured faster than write-back cached stores). Rows of Y
   // are 16-byte aligned and the column count is a multiple of 8 (checked at launch), so a 16-byte
   // piece lies wholly inside or wholly past the last column.
-  {
-    uint4 *blk = (wave >> 1) == 0 ? sX0 : (wave >> 1) == 1 ? sX1 : (wave >> 1) == 2 ? sW0 : sW1;
-    blk += (wave & 1) * (kChunks / 2);
-    uint2 *b2 = reinterpret_cast<uint2 *>(blk);
-    const float tsc = kFP4 ? tscale() : 1.f;
+  // E2M1: the sums are in units of the tensor scale S
+  if (kFP4) {
+    const float tsc = tscale();
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        b2[swzf(mt * 16 + l16, 2 * nt + (g16 >> 1)) * 2 + (g16 & 1)] =
-            kFP4 ? make_uint2(pack_bf16x2(tsc * acc[nt][mt][0], tsc * acc[nt][mt][1]),
-                              pack_bf16x2(tsc * acc[nt][mt][2], tsc * acc[nt][mt][3]))
-                 : make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
-                              pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
-    __syncthreads();
-    const int c = lane & 7;
-    // output column of this wave's piece c (pair: gate or up half of [M, 2N])
-    const int64_t ncol = kPair ? n0 + (wn & 1) * 64 + c * 8 : n0 + wn * 64 + c * 8;
+      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] *= tsc;
+  }
+  uint4 *blk = (wave >> 1) == 0 ? sX0 : (wave >> 1) == 1 ? sX1 : (wave >> 1) == 2 ? sW0 : sW1;
+  blk += (wave & 1) * (kChunks / 2);
+  uint2 *b2 = reinterpret_cast<uint2 *>(blk);
+  const int c = lane & 7;
+  // output column of this wave's piece c (pair: gate or up half of [M, 2N])
+  const int64_t ncol = kPair ? n0 + (wn & 1) * 64 + c * 8 : n0 + wn * 64 + c * 8;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      b2[swzf(mt * 16 + l16, 2 * nt + (g16 >> 1)) * 2 + (g16 & 1)] =
+          make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                     pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+  __syncthreads();
+  {
     const int64_t n = kPair ? (wn < 2 ? ncol : g.C + ncol) : ncol;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -455,32 +460,56 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<u32x4 *>(g.out + m * g.ldo + n));
     }
-    if (kPair) {
-      // H for 64 rows x 64 columns per wave: rows 64 (wn >> 1) .. of the wm block, columns
-      // (wn & 1) 64 .. of the tile's gate half; Yg from the block of wave (wm, wn & 1), Yu from
-      // that of wave (wm, (wn & 1) + 2), both already staged (the barrier above)
-      auto blk_of = [&](int wv) {
-        uint4 *b = (wv >> 1) == 0 ? sX0 : (wv >> 1) == 1 ? sX1 : (wv >> 1) == 2 ? sW0 : sW1;
-        return b + (wv & 1) * (kChunks / 2);
-      };
-      const uint4 *bg = blk_of(wm * 4 + (wn & 1));
-      const uint4 *bu = blk_of(wm * 4 + (wn & 1) + 2);
+  }
+  if (kPair) {
+    // H = silu(Yg) * Yu from the float32 sums. Wave (wm, wn) with wn < 2 holds Yg of tile
+    // columns 64 wn ..; wave (wm, wn + 2) holds Yu of the same columns in the same register
+    // positions. The up waves park their float32 accumulators in LDS (32 KB each: the four fill
+    // the 128 KB), the gate waves read them at their own positions and turn their accumulators
+    // into H, which they then stage and write like Y.
+    __syncthreads();
+    f32x4 *park = reinterpret_cast<f32x4 *>(wm == 0 ? (wn & 1 ? sX1 : sX0) : (wn & 1 ? sW1 : sW0));
+    if (wn >= 2) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 64 * (wn >> 1) + 8 * i + (lane >> 3);
-        const int64_t m = m0 + wm * 128 + row;
-        const uint4 gv = bg[swzf(row, c)], uv = bu[swzf(row, c)];
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-        u32x4 o;
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float g0 = bf16_lo(gw[e]), g1 = bf16_hi(gw[e]);
-          // the activation kernel's expression, operation for operation (same rounding)
-          o[e] = pack_bf16x2(g0 * (1.f / (1.f + __expf(-g0))) * bf16_lo(uw[e]),
-                             g1 * (1.f / (1.f + __expf(-g1))) * bf16_hi(uw[e]));
+        for (int mt = 0; mt < 8; ++mt) park[(nt * 8 + mt) * 64 + lane] = acc[nt][mt];
+    }
+    __syncthreads();
+    if (wn < 2) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const f32x4 u = park[(nt * 8 + mt) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[nt][mt][e], uv = u[e];
+            // the activation kernel's expression, in float32 on the unrounded sums
+            acc[nt][mt][e] = gv * (1.f / (1.f + __expf(-gv))) * uv;
+          }
         }
+    }
+    __syncthreads();
+    if (wn < 2) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+          b2[swzf(mt * 16 + l16, 2 * nt + (g16 >> 1)) * 2 + (g16 & 1)] =
+              make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                         pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+    }
+    __syncthreads();
+    if (wn < 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * i + (lane >> 3);
+        const int64_t m = m0 + wm * 128 + row;
+        const uint4 v = blk[swzf(row, c)];
         if (wm * 128 + row < rows_m && ncol < g.C)
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(g.hout + m * g.ldh + ncol));
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<u32x4 *>(g.hout + m * g.ldh + ncol));
       }
     }
   }

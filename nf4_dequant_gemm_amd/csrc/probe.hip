@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
-#include "nf4probe.h"
+#include "probe.h"
 
 namespace {
 

@@ -49,6 +49,32 @@ def backward(dY, X, Wd, A, B, s: float):
     return dX, dA, dB
 
 
+def forward_rows(X, Wd, A, B, s: float, rows):
+    """(Y[rows], T[rows]): the forward on a subset of rows (each row of Y and T depends on its
+    own row of X only)."""
+    return forward(np.asarray(X)[rows], Wd, A, B, s)
+
+
+def backward_sampled(dY, X, Wd, A, B, s: float, rows, cols, nrows, chunk: int = 2048):
+    """(dX[rows], dA[:, cols], dB[nrows]) of the backward, for full-size workloads where the
+    whole of dX is too costly: U = dY B and T = X A^T over every row (the adapter gradients sum
+    over all of them), taken in row chunks to bound host memory, then the same products as
+    backward() on the selected rows and columns."""
+    dY, X = np.asarray(dY), np.asarray(X)
+    Wd, A, B = _f64(Wd), _f64(A), _f64(B)
+    s = float(s)
+    M = dY.shape[0]
+    U = np.empty((M, B.shape[1]))
+    T = np.empty((M, A.shape[0]))
+    for lo in range(0, M, chunk):
+        U[lo:lo + chunk] = _f64(dY[lo:lo + chunk]) @ B
+        T[lo:lo + chunk] = _f64(X[lo:lo + chunk]) @ A.T
+    dX = _f64(dY[rows]) @ Wd + s * (U[rows] @ A)
+    dA = s * (U.T @ _f64(X[:, cols]))
+    dB = s * (_f64(dY[:, nrows]).T @ T)
+    return dX, dA, dB
+
+
 def rel_err(got, ref) -> float:
     """Normwise error max|got - ref| / max|ref| (0 when both are all zero)."""
     got, ref = _f64(got), _f64(ref)

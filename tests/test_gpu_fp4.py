@@ -155,7 +155,9 @@ def test_swiglu_pair_with_fp4_weight(lib, M):
     Hr = swiglu.forward(f32(X), Wd[:N], Wd[N:], f32(Agu)[:r], f32(Agu)[r:], f32(Bg), f32(Bu), s)[0]
     dXr, dAg, dAu, dBgr, dBur = swiglu.backward(f32(dH), f32(X), Wd[:N], Wd[N:], f32(Agu)[:r],
                                                 f32(Agu)[r:], f32(Bg), f32(Bu), s)
-    check_close("H", f32(H), Hr, warn_above=8e-3)
+    # H: one rounding from the pair kernel's float32 sums (M = 96), two through the bf16 Ygu on
+    # the decode shape (M = 8); the backward takes dYg, dYu rounded to bf16 (two roundings)
+    check_close("H", f32(H), Hr, warn_above=4e-3 if M > 16 else 8e-3)
     check_close("dX", f32(dX), dXr, warn_above=8e-3)
     check_close("dAgu", f32(dAgu), np.concatenate([dAg, dAu]), warn_above=8e-3)
     check_close("dBg", f32(dBg), dBgr, warn_above=8e-3)

@@ -6,9 +6,11 @@ saved Ygu and Tgu, and dX, dAgu, dBg, dBu are within max|got - ref| / max|ref| <
 float64 oracle (oracle/swiglu.py). Shapes span several 256-wide tiles with ragged tails, the
 M <= 16 kernels, r = 0 and the largest rank (2r = 128).
 
-The pair rounds twice where one layer rounds once (Yg, Yu are bf16 before the activation; dYg,
-dYu are bf16 before the backward GEMMs), so its errors sit near twice the one-rounding floor:
-the warning level for a bug hiding under the bar is 8e-3 here (4e-3 for one layer).
+Where the pair rounds twice and one layer rounds once, its errors sit near twice the
+one-rounding floor, so the warning level for a bug hiding under the bar is 8e-3 there (4e-3 for
+one layer): the backward (dYg, dYu are rounded to bf16 before the backward GEMMs take them as
+their dY) and H on the decode shapes (the activation kernel reads the bf16 Ygu). Above the decode
+shapes the fused kernel computes H from the float32 sums of Yg and Yu: one rounding, 4e-3.
 """
 import numpy as np
 import pytest
@@ -24,8 +26,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def check_close(name, got, ref):
-    return _check_close(name, got, ref, warn_above=8e-3)
+def check_close(name, got, ref, warn_above=8e-3):
+    return _check_close(name, got, ref, warn_above=warn_above)
+
+
+def decode_shaped(M, K):
+    """Shapes whose stacked forward takes the decode kernels (H then from the bf16 Ygu)."""
+    return M <= 48 and K % 256 == 0
 
 CASES = [
     # M, K, N, r, dq, s
@@ -72,11 +79,11 @@ def test_swiglu_pair_parity(lib, M, K, N, r, dq, s):
     say(f"swiglu pair M={M} K={K} N={N} r={r} dq={dq} s={s}")
     (H, Ygu, Tgu, dX, dAgu, dBg, dBu), (Hr, Yg, Yu, Tg, Tu), (dXr, dAg, dAu, dBgr, dBur) = \
         run_pair(lib, M, K, N, r, dq, s, seed=M * 11 + N)
-    check_close("H", f32(H), Hr)
-    check_close("Ygu", f32(Ygu), np.concatenate([Yg, Yu], axis=1))
+    check_close("H", f32(H), Hr, warn_above=8e-3 if decode_shaped(M, K) else 4e-3)
+    check_close("Ygu", f32(Ygu), np.concatenate([Yg, Yu], axis=1), warn_above=4e-3)
     check_close("dX", f32(dX), dXr)
     if r:
-        check_close("Tgu", f32(Tgu), np.concatenate([Tg, Tu], axis=1))
+        check_close("Tgu", f32(Tgu), np.concatenate([Tg, Tu], axis=1), warn_above=4e-3)
         check_close("dAgu", f32(dAgu), np.concatenate([dAg, dAu]))
         check_close("dBg", f32(dBg), dBgr)
         check_close("dBu", f32(dBu), dBur)
@@ -148,9 +155,9 @@ def test_swiglu_pair_full_size(lib):
     dYu = dHf * Yg * sg
     rows = sample(M, 48, p.index)
     rt = torch.from_numpy(rows).to(DEV)
-    check_close("H", f32(H[rt]), (Yg * sg * Yu)[rows])
-    check_close("Ygu", f32(Ygu[rt]), np.concatenate([Yg[rows], Yu[rows]], axis=1))
-    check_close("Tgu", f32(Tgu[rt]), np.concatenate([Tg[rows], Tu[rows]], axis=1))
+    check_close("H", f32(H[rt]), (Yg * sg * Yu)[rows], warn_above=4e-3)
+    check_close("Ygu", f32(Ygu[rt]), np.concatenate([Yg[rows], Yu[rows]], axis=1), warn_above=4e-3)
+    check_close("Tgu", f32(Tgu[rt]), np.concatenate([Tg[rows], Tu[rows]], axis=1), warn_above=4e-3)
     Ug, Uu = dYg @ Bgf, dYu @ Buf
     dXs = dYg[rows] @ Wd[:N] + dYu[rows] @ Wd[N:] + s * (Ug[rows] @ Ag + Uu[rows] @ Au)
     check_close("dX", f32(dX[rt]), dXs)

@@ -3,8 +3,9 @@ E2M1 base weight).
 
 The HIP path runs at full size, exactly as bench.py launches it. The quantised weight is compared
 bit for bit in full. Y, T and dX are compared on sampled rows (first, last and random rows), dA
-on sampled columns and dB on sampled rows, each computed by the float64 oracle from the same
-seeded inputs; the small workload is compared in full.
+on sampled columns and dB on sampled rows, each computed by the float64 oracle's sampled entries
+(oracle.qlora.forward_rows / backward_sampled, pinned to the full forward and backward) from the
+same seeded inputs; the small workload is compared in full.
 """
 import numpy as np
 import pytest
@@ -62,7 +63,7 @@ def test_workload(lib, name):
     del W
     Xf, Af, Bf = f32(X), f32(A), f32(B)
     rows = sample(w.M, 48, w.index)
-    Ys, Ts = qlora.forward(Xf[rows], Wd, Af, Bf, w.s)
+    Ys, Ts = qlora.forward_rows(Xf, Wd, Af, Bf, w.s, rows)
     check_close("Y", f32(Yg[torch.from_numpy(rows).to(DEV)]), Ys)
     check_close("T", f32(Tg[torch.from_numpy(rows).to(DEV)]), Ts)
     del Yg
@@ -72,14 +73,9 @@ def test_workload(lib, name):
     dXg, dAg, dBg = lib.qlora_bwd(dY.to(DEV), Xd, qg, Ad, Bd, w.s, Tg)
     torch.cuda.synchronize()
     say("  bwd done")
-    dYf = f32(dY)
-    U = dYf.astype(np.float64) @ Bf.astype(np.float64)                       # [M, r]
-    dXs = dYf[rows].astype(np.float64) @ Wd.astype(np.float64) + w.s * (U[rows] @ Af.astype(np.float64))
-    check_close("dX", f32(dXg[torch.from_numpy(rows).to(DEV)]), dXs)
     cols = sample(w.K, 64, w.index + 1)
-    dAs = w.s * (U.T @ Xf[:, cols].astype(np.float64))
-    check_close("dA", f32(dAg)[:, cols], dAs)
-    T = t_full(Xf, Af)
     nrows = sample(w.N, 64, w.index + 2)
-    dBs = w.s * (dYf[:, nrows].astype(np.float64).T @ T)
+    dXs, dAs, dBs = qlora.backward_sampled(f32(dY), Xf, Wd, Af, Bf, w.s, rows, cols, nrows)
+    check_close("dX", f32(dXg[torch.from_numpy(rows).to(DEV)]), dXs)
+    check_close("dA", f32(dAg)[:, cols], dAs)
     check_close("dB", f32(dBg)[nrows], dBs)

@@ -252,10 +252,10 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 
 
 def test_probe_library_exports_its_header():
-    """libnf4probe.so (the matrix-core loop bench.py times) exports what include/nf4probe.h
-    declares; its argument checks run on the host and its flop count is closed-form."""
+    """libnf4probe.so (the matrix-core loop bench.py times) exports what its header
+    (nf4_dequant_gemm_amd/csrc/probe.h) declares; its argument checks run on the host and its flop count is closed-form."""
     from nf4_dequant_gemm_amd.build import PROBE_LIB
-    hdr = os.path.join(os.path.dirname(HEADER), "nf4probe.h")
+    hdr = os.path.join(os.path.dirname(m.__file__), "csrc", "probe.h")
     src = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
     assert names == {"nf4probe_mfma_loop", "nf4probe_mfma_loop_flops"}

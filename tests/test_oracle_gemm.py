@@ -157,3 +157,24 @@ def test_rel_err_definition():
     got = ref + np.array([[0.0, 0.04], [0.0, -0.02]])
     assert abs(qlora.rel_err(got, ref) - 0.01) < 1e-15
     assert qlora.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+@pytest.mark.parametrize("M,K,N,r", [(37, 128, 24, 4), (70, 192, 40, 0), (5, 64, 8, 3)])
+def test_sampled_backward_equals_backward(M, K, N, r):
+    """backward_sampled (the full-size parity references) selects exactly the rows and columns of
+    backward(); forward_rows the rows of forward()."""
+    X, q, A, B, dY = make(M, K, N, r, 800 + M)
+    Wd = nf4.dequantize_f32(q)
+    rng = np.random.default_rng(M)
+    rows = np.sort(rng.choice(M, min(M, 9), replace=False))
+    cols = np.sort(rng.choice(K, 11, replace=False))
+    nrows = np.sort(rng.choice(N, min(N, 7), replace=False))
+    dX, dA, dB = qlora.backward(dY, X, Wd, A, B, 1.5)
+    sX, sA, sB = qlora.backward_sampled(dY, X, Wd, A, B, 1.5, rows, cols, nrows, chunk=16)
+    assert np.allclose(sX, dX[rows], rtol=1e-13, atol=1e-13)
+    assert np.allclose(sA, dA[:, cols], rtol=1e-13, atol=1e-13)
+    assert np.allclose(sB, dB[nrows], rtol=1e-13, atol=1e-13)
+    Y, T = qlora.forward(X, Wd, A, B, 1.5)
+    fY, fT = qlora.forward_rows(X, Wd, A, B, 1.5, rows)
+    assert np.allclose(fY, Y[rows], rtol=1e-13, atol=1e-13)
+    assert np.allclose(fT, T[rows], rtol=1e-13, atol=1e-13)
