@@ -279,6 +279,24 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
                   const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
                   void *stream);
 
+/* ---- No-allocation forward -------------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. qlora_fwd_noalloc is qlora_fwd (same arguments, same
+ * kernels, same results bit for bit) without the workspace argument: its scratch (the float32
+ * split-K partial sums of T = X A^T) is a static device array of NF4_NOALLOC_SCRATCH_BYTES on
+ * each GPU, which that GPU holds until the process ends. The call allocates nothing; its first
+ * call on a device looks the array's device address up (hipGetSymbolAddress) with that device
+ * current. The stream must belong to the current device.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's partial sums (none
+ * needs it cleared): calls that overlap on one GPU (on different streams or host threads) race
+ * on it and give undefined results; serialise them.
+ * Errors: as qlora_fwd; NF4_EUNSUPPORTED when the sizes need more scratch than the array holds
+ * (qlora_fwd_workspace_bytes(m, n, k, r) > NF4_NOALLOC_SCRATCH_BYTES), checked before any HIP
+ * call. */
+#define NF4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int qlora_fwd_noalloc(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
+                      int32_t r, float s, void *Y, void *T, void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);
 

@@ -33,7 +33,7 @@ EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspa
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
             "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
             "qlora_swiglu_bwd", "qlora_merge", "qlora_moe_workspace_bytes", "qlora_moe_fwd",
-            "qlora_moe_fwd_fused", "qlora_moe_bwd", "nf4_last_error")
+            "qlora_moe_fwd_fused", "qlora_moe_bwd", "qlora_fwd_noalloc", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -64,6 +64,7 @@ def library() -> ctypes.CDLL:
         "nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
         "qlora_fwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_fwd_noalloc": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp, vp]),
         "qlora_lora_down": (ctypes.c_int, [vp, i64, i64, vp, i32, vp, vp, sz, vp]),
         "qlora_fwd_fused": (ctypes.c_int, [vp, i64, P, vp, vp, i32, f32, vp, vp]),
         "qlora_bwd_workspace_bytes": (sz, [i64, i64, i64, i32]),
@@ -232,6 +233,26 @@ def qlora_fwd(X: torch.Tensor, q: NF4Tensor, A: Optional[torch.Tensor], B: Optio
     _check(lib.qlora_fwd(_ptr(X), m, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
                          _ptr(T), _ptr(ws), wsb, _stream(X.device)))
     return Y, T
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # NF4_NOALLOC_SCRATCH_BYTES of the header
+
+
+def qlora_fwd_noalloc(X: torch.Tensor, q: NF4Tensor, A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+                      s: float, Y: torch.Tensor, T: Optional[torch.Tensor] = None) -> None:
+    """qlora_fwd into caller-provided Y [m, n] and T [m, r] with no workspace: the library's
+    static per-GPU scratch array holds the partial sums (calls on one GPU must not overlap)."""
+    m = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    _need(Y, "Y", torch.bfloat16, (m, q.n))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, q.k))
+        _need(B, "B", torch.bfloat16, (q.n, r))
+        _need(T, "T", torch.bfloat16, (m, r))
+    st = q.c_struct()
+    _check(library().qlora_fwd_noalloc(_ptr(X), m, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s),
+                                       _ptr(Y), _ptr(T), _stream(X.device)))
 
 
 def qlora_lora_down(X: torch.Tensor, A: torch.Tensor) -> torch.Tensor:

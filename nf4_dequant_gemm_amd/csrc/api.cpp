@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -350,6 +351,37 @@ int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr, i
   return NF4_OK;
 }
 
+// ------------------------------------------------------------------ no-allocation forward
+// The workspace of qlora_fwd_noalloc: a static device array, one per GPU the library runs on
+// (each holds its own copy until the process ends). Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and is what the kernels receive.
+constexpr size_t kNoAllocScratchBytes = NF4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "qlora_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NF4_EUNSUPPORTED, "qlora_fwd_noalloc: device %d beyond the %d it serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "qlora_fwd_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(NF4_EHIP, "qlora_fwd_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NF4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -497,6 +529,27 @@ int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, cons
     if (st) return st;
   }
   return qlora_fwd_fused(X, m, W, T, B, r, s, Y, stream);
+}
+
+int qlora_fwd_noalloc(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
+                      int32_t r, float s, void *Y, void *T, void *stream) {
+  // every check before any HIP call (the scratch lookup included)
+  int st = check_layer(X, m, W, A, B, r);
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  if (r > 0 && (!T || !aligned16(T))) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
+  const size_t need = fwd_ws(m, W->k, r).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(NF4_EUNSUPPORTED,
+                "qlora_fwd_noalloc: these sizes need %zu bytes of scratch, its static array holds %zu "
+                "(call qlora_fwd with a workspace instead)",
+                need, kNoAllocScratchBytes);
+  void *ws = nullptr;
+  if (need) {
+    st = scratch_of_current_device(&ws);
+    if (st) return st;
+  }
+  return qlora_fwd(X, m, W, A, B, r, s, Y, T, ws, need ? kNoAllocScratchBytes : 0, stream);
 }
 
 size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {

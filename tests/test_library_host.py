@@ -271,3 +271,23 @@ def test_probe_library_exports_its_header():
     assert lib.nf4probe_mfma_loop(ctypes.c_void_p(64), ctypes.c_void_p(64), 64, 8, 0, ctypes.c_void_p(64), None) == -1
     # 4 waves x iters x 8 MFMAs x 16*16*32 multiply-adds per workgroup
     assert lib.nf4probe_mfma_loop_flops(3, 5) == 3 * 4 * 5 * 8 * 16 * 16 * 32 * 2
+
+
+def test_noalloc_forward_rejects_on_the_host():
+    """qlora_fwd_noalloc checks its arguments and its scratch limit before any HIP call: sizes
+    whose partial sums exceed the static array are refused with a message naming the limit."""
+    lib = m.library()
+    cap = m.NOALLOC_SCRATCH_BYTES
+    big_m, big_k, big_r = 8192, 4096, 128
+    assert lib.qlora_fwd_workspace_bytes(big_m, 64, big_k, big_r) > cap
+    q = wdesc(n=64, k=big_k)
+    call = lambda **kw: lib.qlora_fwd_noalloc(kw.get("X", FAKE), kw.get("m", big_m), ctypes.byref(kw.get("q", q)),
+                                              kw.get("A", FAKE), kw.get("B", FAKE), kw.get("r", big_r), 1.0,
+                                              kw.get("Y", FAKE), kw.get("T", FAKE), None)
+    assert call() == m.NF4_EUNSUPPORTED
+    msg = lib.nf4_last_error().decode()
+    assert "scratch" in msg and str(cap) in msg
+    assert call(Y=None) == m.NF4_EINVAL
+    assert call(T=None) == m.NF4_EINVAL
+    assert call(r=129) == m.NF4_EINVAL
+    assert call(q=wdesc(n=60, k=big_k)) == m.NF4_EUNSUPPORTED
