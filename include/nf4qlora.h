@@ -242,7 +242,7 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
                 void *stream);
 
 /* ---- Grouped (mixture-of-experts) layer -------------------------------------------------------
- * E experts (1 <= E <= 64), each a QLoRA layer with its own frozen NF4 base and adapters
+ * E experts (1 <= E <= 256), each a QLoRA layer with its own frozen NF4 base and adapters
  * [NVFP4 update article, "Comprehensive Improvements in Training Performance and Stability":
  * grouped MoE, LoRA on the experts' MLP layers; pyshine Unsloth code tour, "Why You Need This":
  * the grouped-GEMM interface for MoE experts]. The routing is given: the rows of X (and of Y, T,
@@ -296,6 +296,35 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
 #define NF4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 int qlora_fwd_noalloc(const void *X, int64_t m, const nf4_tensor *W, const void *A, const void *B,
                       int32_t r, float s, void *Y, void *T, void *stream);
+
+/* ---- Grouped layer with the routing in device memory ------------------------------------------
+ * The same layer when the router runs on the GPU: counts is a DEVICE pointer to E int64 values
+ * (8-byte aligned) and m, the number of routed rows (the rows of X, Y, T, dY, dX), is given on the
+ * host, so nothing waits for the device and the calls can be captured in a HIP graph whose
+ * replays route differently [NVFP4 update article, "Comprehensive Improvements in Training
+ * Performance and Stability": grouped MoE training]. Each call first builds the group tables
+ * (row offsets and first tiles) from the counts into its workspace with one small kernel; the
+ * grouped launches are then sized by bounds from m and E, and workgroups past the last tile exit
+ * at once. Results equal those of qlora_moe_fwd / qlora_moe_bwd for the same counts bit for bit
+ * (the same split counts, which depend on m only). The counts should sum to m; the experts' row
+ * ranges are clipped at m (no row past m is read or written), negative counts count as 0, and
+ * rows past the counts' sum are left unwritten.
+ *
+ * Bytes of device workspace qlora_moe_fwd_dev and qlora_moe_bwd_dev need (any counts summing to
+ * at most m). */
+size_t qlora_moe_workspace_bytes_dev(int64_t m, int32_t E, int64_t n, int64_t k, int32_t r);
+
+/* Forward (T and Y), as qlora_moe_fwd. Errors: as qlora_moe_fwd (checked on the host; the
+ * device counts are not read there), NF4_EINVAL also for a NULL or misaligned counts pointer. */
+int qlora_moe_fwd_dev(const void *X, int64_t m, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                      const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Backward (dX, dA, dB), as qlora_moe_bwd. Errors: as qlora_moe_fwd_dev. */
+int qlora_moe_bwd_dev(const void *dY, const void *X, int64_t m, const int64_t *counts, int32_t E,
+                      const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
+                      const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char *nf4_last_error(void);

@@ -33,7 +33,8 @@ EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspa
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
             "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
             "qlora_swiglu_bwd", "qlora_merge", "qlora_moe_workspace_bytes", "qlora_moe_fwd",
-            "qlora_moe_fwd_fused", "qlora_moe_bwd", "qlora_fwd_noalloc", "nf4_last_error")
+            "qlora_moe_fwd_fused", "qlora_moe_bwd", "qlora_moe_workspace_bytes_dev", "qlora_moe_fwd_dev",
+            "qlora_moe_bwd_dev", "qlora_fwd_noalloc", "nf4_last_error")
 
 
 class NF4Error(RuntimeError):
@@ -75,6 +76,10 @@ def library() -> ctypes.CDLL:
         "qlora_moe_fwd": (ctypes.c_int, [vp, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "qlora_moe_fwd_fused": (ctypes.c_int, [vp, vp, i32, P, vp, vp, i32, f32, vp, vp]),
         "qlora_moe_bwd": (ctypes.c_int, [vp, vp, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
+        "qlora_moe_workspace_bytes_dev": (sz, [i64, i32, i64, i64, i32]),
+        "qlora_moe_fwd_dev": (ctypes.c_int, [vp, i64, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_moe_bwd_dev": (ctypes.c_int, [vp, vp, i64, vp, i32, P, vp, vp, i32, f32, vp, vp, vp, vp, vp,
+                                             sz, vp]),
         "qlora_swiglu_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_swiglu_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_swiglu_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
@@ -415,6 +420,52 @@ def qlora_moe_bwd(dY: torch.Tensor, X: torch.Tensor, counts, q: NF4Tensor, A: Op
     _check(lib.qlora_moe_bwd(_ptr(dY), _ptr(X), c, E, ctypes.byref(st), _ptr(A), _ptr(B), r, float(s),
                              _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(dev)))
     return dX, dA, dB
+
+
+def moe_workspace_bytes_dev(m: int, E: int, n: int, k: int, r: int) -> int:
+    """Workspace bytes of the device-routed grouped calls for m routed rows."""
+    return int(library().qlora_moe_workspace_bytes_dev(m, E, n, k, r))
+
+
+def qlora_moe_fwd_dev(X: torch.Tensor, counts: torch.Tensor, q: NF4Tensor, A: Optional[torch.Tensor],
+                      B: Optional[torch.Tensor], s: float, Y: torch.Tensor, T: Optional[torch.Tensor],
+                      ws: torch.Tensor) -> None:
+    """The grouped forward with the routing on the device: counts int64 [E] device tensor; Y, T
+    and the workspace ws (moe_workspace_bytes_dev bytes) are the caller's, so the call allocates
+    nothing and can be captured in a graph."""
+    E = counts.numel()
+    if counts.dtype != torch.int64 or not counts.is_cuda or not counts.is_contiguous():
+        raise ValueError("counts must be a contiguous int64 device tensor")
+    if E < 1 or q.n % E:
+        raise ValueError("the stacked weight must hold E*n rows for E = counts.numel() experts")
+    M, n = X.shape[0], q.n // E
+    r = 0 if A is None else A.shape[0] // E
+    _need(X, "X", torch.bfloat16, (M, q.k))
+    _need(Y, "Y", torch.bfloat16, (M, n))
+    if r:
+        _need(A, "A", torch.bfloat16, (E * r, q.k))
+        _need(B, "B", torch.bfloat16, (E * n, r))
+        _need(T, "T", torch.bfloat16, (M, r))
+    st = q.c_struct()
+    _check(library().qlora_moe_fwd_dev(_ptr(X), M, _ptr(counts), E, ctypes.byref(st), _ptr(A), _ptr(B), r,
+                                       float(s), _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream(X.device)))
+
+
+def qlora_moe_bwd_dev(dY: torch.Tensor, X: torch.Tensor, counts: torch.Tensor, q: NF4Tensor,
+                      A: Optional[torch.Tensor], B: Optional[torch.Tensor], s: float,
+                      T: Optional[torch.Tensor], dX: Optional[torch.Tensor], dA: Optional[torch.Tensor],
+                      dB: Optional[torch.Tensor], ws: torch.Tensor) -> None:
+    """The grouped backward with the routing on the device, into the caller's dX, dA, dB."""
+    E = counts.numel()
+    if counts.dtype != torch.int64 or not counts.is_cuda or not counts.is_contiguous():
+        raise ValueError("counts must be a contiguous int64 device tensor")
+    M, n = X.shape[0], q.n // E
+    r = 0 if A is None else A.shape[0] // E
+    _need(dY, "dY", torch.bfloat16, (M, n))
+    st = q.c_struct()
+    _check(library().qlora_moe_bwd_dev(_ptr(dY), _ptr(X), M, _ptr(counts), E, ctypes.byref(st), _ptr(A),
+                                       _ptr(B), r, float(s), _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB),
+                                       _ptr(ws), ws.numel(), _stream(X.device)))
 
 
 def _swiglu_args(X, q: NF4Tensor, Agu, Bg, Bu):

@@ -251,95 +251,119 @@ int check_swiglu(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Ag
   return NF4_OK;
 }
 
-// Mixture of experts: E experts, counts[e] rows each (grouped in expert order), stacked tensors
-// W [E n, k], A [E r, k], B [E n, r].
+// Mixture of experts: E experts, rows grouped in expert order, stacked tensors W [E n, k],
+// A [E r, k], B [E n, r]. The routing (rows per expert) is either given on the host (counts[e],
+// summed into off) or held in device memory (the row total m given on the host; the group table
+// is then built on the device, in the workspace).
 struct Moe {
-  int64_t off[nf4q::kMaxExperts + 1];
+  int64_t off[nf4q::kMaxExperts + 1];   // host routing
   int64_t n = 0, mtotal = 0;
+  const int64_t *dcounts = nullptr;     // device routing: counts [E] in device memory
 };
+
+int check_moe_shape(const void *X, int32_t E, const nf4_tensor *W, const void *A, const void *B,
+                    int32_t r, Moe *mo) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (W->n % E) return fail(NF4_EINVAL, "W must hold E*n rows (got %lld for E = %d)", (long long)W->n, E);
+  mo->n = W->n / E;
+  if (mo->n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)mo->n);
+  return check_layer(X, mo->mtotal, W, A, B, r);   // m >= 1, the GEMM limits, X, A, B
+}
 
 int check_moe(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W, const void *A,
               const void *B, int32_t r, Moe *mo) {
   if (E < 1 || E > nf4q::kMaxExperts)
     return fail(NF4_EINVAL, "E must lie in [1, %d] (got %d)", nf4q::kMaxExperts, E);
   if (!counts) return fail(NF4_EINVAL, "counts is NULL");
-  int st = check_weight(W);
-  if (st) return st;
-  if (W->n % E) return fail(NF4_EINVAL, "W must hold E*n rows (got %lld for E = %d)", (long long)W->n, E);
-  mo->n = W->n / E;
-  if (mo->n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)mo->n);
   mo->off[0] = 0;
   for (int e = 0; e < E; ++e) {
     if (counts[e] < 0) return fail(NF4_EINVAL, "counts[%d] is negative", e);
     mo->off[e + 1] = mo->off[e] + counts[e];
   }
   mo->mtotal = mo->off[E];
-  st = check_layer(X, mo->mtotal, W, A, B, r);   // m >= 1, the GEMM limits, X, A, B
-  if (st) return st;
-  return NF4_OK;
+  return check_moe_shape(X, E, W, A, B, r, mo);
+}
+
+int check_moe_dev(const void *X, int64_t m, const int64_t *dcounts, int32_t E, const nf4_tensor *W,
+                  const void *A, const void *B, int32_t r, Moe *mo) {
+  if (E < 1 || E > nf4q::kMaxExperts)
+    return fail(NF4_EINVAL, "E must lie in [1, %d] (got %d)", nf4q::kMaxExperts, E);
+  if (!dcounts || (reinterpret_cast<uintptr_t>(dcounts) & 7))
+    return fail(NF4_EINVAL, "counts must be a non-NULL, 8-byte aligned device pointer");
+  mo->mtotal = m;
+  mo->dcounts = dcounts;
+  return check_moe_shape(X, E, W, A, B, r, mo);
 }
 
 // Launch plan of the grouped layer's rank-r products: the row projections (T = X_e A_e^T,
 // U = dY_e B_e) run over every expert's 64-row blocks in one launch, split over the reduction
 // like the single layer's; the M-reductions (dA_e, dB_e) run over (expert, column tile, split)
-// in one launch, with the same split count for every expert, aiming at about 1024 workgroups.
+// in one launch, aiming at about 1024 workgroups, each expert's rows cut into that many splits.
+// The split counts depend on the row total only, so the same routing gives the same sums in the
+// same order whether it is given on the host or on the device.
 struct MoePlan {
-  int64_t blocks64 = 0, maxrows = 0;
   int sp_k = 1, sp_n = 1, sa = 1, sb = 1;
 };
 
-MoePlan moe_plan(const Moe &mo, int32_t E, int64_t k) {
+MoePlan moe_plan(int64_t mtotal, int32_t E, int64_t n, int64_t k) {
   MoePlan pl;
-  for (int e = 0; e < E; ++e) {
-    const int64_t me = mo.off[e + 1] - mo.off[e];
-    pl.blocks64 += (me + 63) / 64;
-    pl.maxrows = std::max(pl.maxrows, me);
-  }
-  pl.sp_k = nf4q::rowproj_splits(pl.blocks64 * 64, k);
-  pl.sp_n = nf4q::rowproj_splits(pl.blocks64 * 64, mo.n);
+  pl.sp_k = nf4q::rowproj_splits(mtotal, k);
+  pl.sp_n = nf4q::rowproj_splits(mtotal, n);
   auto mr = [&](int64_t C) {
     const int64_t ct = (C + 127) / 128;
     int64_t sp = (1024 + ct * E - 1) / (ct * E);
-    sp = std::min<int64_t>(sp, std::max<int64_t>(1, (pl.maxrows + 63) / 64));
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, (mtotal + 63) / 64));
     return (int)std::max<int64_t>(sp, 1);
   };
   pl.sa = mr(k);
-  pl.sb = mr(mo.n);
+  pl.sb = mr(n);
   return pl;
 }
 
-// Workspace of the grouped layer: U [sum(counts), r] at 0, the transposed stacked B [r, E n] at
-// u, T (recomputed when the caller passes none) at u + bt, then float partials of the row
-// projections or of the M-reductions (never both at once).
+// Workspace of the grouped layer: with device routing the group table first (table bytes),
+// then U [m, r], the transposed stacked B [r, E n], T (recomputed when the caller passes none),
+// then float partials of the row projections or of the M-reductions (never both at once).
 struct MoeWs {
-  size_t u = 0, bt = 0, t = 0, part = 0, total = 0;
+  size_t table = 0, u = 0, bt = 0, t = 0, part = 0, total = 0;
 };
 
-MoeWs moe_ws_layout(const Moe &mo, int32_t E, int64_t k, int32_t r) {
+MoeWs moe_ws_layout(int64_t mtotal, int32_t E, int64_t n, int64_t k, int32_t r, bool dev) {
   MoeWs w;
-  if (r <= 0) return w;
-  const MoePlan pl = moe_plan(mo, E, k);
-  w.u = align256((size_t)mo.mtotal * r * 2);
-  w.bt = align256((size_t)r * E * mo.n * 2);
-  w.t = w.u;
-  size_t p = 0;
-  if (pl.sp_k > 1) p = std::max(p, (size_t)pl.sp_k * mo.mtotal * r * 4);
-  if (pl.sp_n > 1) p = std::max(p, (size_t)pl.sp_n * mo.mtotal * r * 4);
-  p = std::max(p, (size_t)E * pl.sa * r * k * 4);
-  p = std::max(p, (size_t)E * pl.sb * r * mo.n * 4);
-  w.part = align256(p);
-  w.total = w.u + w.bt + w.t + w.part;
+  if (dev) w.table = align256(nf4q::moe_table_bytes(E));
+  if (r > 0) {
+    const MoePlan pl = moe_plan(mtotal, E, n, k);
+    w.u = align256((size_t)mtotal * r * 2);
+    w.bt = align256((size_t)r * E * n * 2);
+    w.t = w.u;
+    size_t p = 0;
+    if (pl.sp_k > 1) p = std::max(p, (size_t)pl.sp_k * mtotal * r * 4);
+    if (pl.sp_n > 1) p = std::max(p, (size_t)pl.sp_n * mtotal * r * 4);
+    p = std::max(p, (size_t)E * pl.sa * r * k * 4);
+    p = std::max(p, (size_t)E * pl.sb * r * n * 4);
+    w.part = align256(p);
+  }
+  w.total = w.table + w.u + w.bt + w.t + w.part;
   return w;
 }
 
-size_t moe_ws(const Moe &mo, int32_t E, int64_t k, int32_t r) {
-  return moe_ws_layout(mo, E, k, r).total;
-}
-
-// Groups of the grouped launches: experts' row offsets and the first tile of each expert (its
-// rows in blocks of `rows` times `tiles_c` column tiles).
-int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr, int64_t rows = 256) {
+// Groups of a grouped launch whose tiles are `rows` rows of an expert times tiles_c column tiles.
+// Host routing: the experts' row offsets and first tiles by value, the grid exact. Device
+// routing: the device table (`which`: 0 forward tiles, 1 dX tiles, 2 64-row blocks) and a grid
+// bounded by the row total (sum of ceil(rows_e / rows) <= (m + (rows - 1) E) / rows, and <= m).
+int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr, int64_t rows,
+               void *table, int which) {
   gr->E = E;
+  if (mo.dcounts) {
+    gr->dm_off = nf4q::moe_table_m_off(table);
+    gr->dtile_off = nf4q::moe_table_tiles(table, E, which);
+    const int64_t blocks = std::min<int64_t>((mo.mtotal + (rows - 1) * E) / rows, mo.mtotal);
+    gr->grid = blocks * tiles_c;
+    if (gr->grid >= (int64_t(1) << 31)) return fail(NF4_EUNSUPPORTED, "too many tiles");
+    return NF4_OK;
+  }
+  gr->dm_off = nullptr;
+  gr->dtile_off = nullptr;
   gr->tile_off[0] = 0;
   for (int e = 0; e <= E; ++e) gr->m_off[e] = mo.off[e];
   for (int e = 0; e < E; ++e) {
@@ -348,7 +372,14 @@ int moe_groups(const Moe &mo, int32_t E, int64_t tiles_c, nf4q::GroupArgs *gr, i
     if (t >= (int64_t(1) << 31)) return fail(NF4_EUNSUPPORTED, "too many tiles");
     gr->tile_off[e + 1] = (int32_t)t;
   }
+  gr->grid = gr->tile_off[E];
   return NF4_OK;
+}
+
+// Device routing: the group tables, built from the device counts into the workspace.
+hipError_t moe_build_table(const Moe &mo, int32_t E, int64_t k, void *table, hipStream_t sm) {
+  if (!mo.dcounts) return hipSuccess;
+  return nf4q::launch_moe_plan(mo.dcounts, E, mo.mtotal, (mo.n + 255) / 256, (k + 255) / 256, table, sm);
 }
 
 // ------------------------------------------------------------------ no-allocation forward
@@ -458,6 +489,11 @@ int qlora_lora_down(const void *X, int64_t m, int64_t k, const void *A, int32_t 
                     "qlora_lora_down launch");
 }
 
+// Shapes of the M <= 16 stream kernel: double-quantised NF4 codes, K a multiple of 256.
+static bool stream16_shape(int64_t m, const nf4_tensor *W) {
+  return m <= 16 && W->dq_block > 0 && W->k % 256 == 0;
+}
+
 int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T, const void *B,
                     int32_t r, float s, void *Y, void *stream) {
   int st = check_layer(X, m, W, T, B, r);
@@ -477,7 +513,7 @@ int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T
   g.out = (uint16_t *)Y;
   g.ldo = W->n;
   g.t = tables();
-  if (m <= 16 && W->dq_block > 0 && W->k % 256 == 0)
+  if (stream16_shape(m, W))
     return hip_status(nf4q::launch_decode16_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
   if (m <= (W->block == 64 ? nf4q::kDecodeMaxM : 16) && W->k % 256 == 0)
     return hip_status(nf4q::launch_decode_fwd(g, (hipStream_t)stream), "qlora_fwd_fused launch");
@@ -493,7 +529,7 @@ int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, cons
   // fused kernel (its prologue hides them under the first weight copies), saving the separate
   // reduction launch; workgroup 0 of the fused kernel writes T.
   const int64_t k = W->k;
-  if (r > 0 && m <= 16 && W->dq_block > 0 && k % 256 == 0 && r % 8 == 0) {
+  if (r > 0 && stream16_shape(m, W) && r % 8 == 0) {
     const FwdWs lay = fwd_ws(m, k, r);
     if (lay.splits > 1 && (int64_t)r * lay.splits <= 1024) {
       if (!T || !aligned16(T)) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
@@ -728,78 +764,82 @@ int qlora_merge(const nf4_tensor *W, const void *A, const void *B, int32_t r, fl
 
 size_t qlora_moe_workspace_bytes(const int64_t *counts, int32_t E, int64_t n, int64_t k, int32_t r) {
   if (!counts || E < 1 || E > nf4q::kMaxExperts || n < 1 || k < 1 || r < 0) return 0;
-  Moe mo;
-  mo.n = n;
-  mo.off[0] = 0;
-  for (int e = 0; e < E; ++e) mo.off[e + 1] = mo.off[e] + std::max<int64_t>(counts[e], 0);
-  mo.mtotal = mo.off[E];
-  return moe_ws(mo, E, k, r);
+  int64_t m = 0;
+  for (int e = 0; e < E; ++e) m += std::max<int64_t>(counts[e], 0);
+  return moe_ws_layout(m, E, n, k, r, false).total;
 }
 
-int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
-                        const void *T, const void *B, int32_t r, float s, void *Y, void *stream) {
-  Moe mo;
-  int st = check_moe(X, counts, E, W, T, B, r, &mo);   // T [sum(counts), r] in A's place
-  if (st) return st;
-  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
-  const int64_t k = W->k, n = mo.n;
-  // every expert's tiles in one launch of the fused kernel
+size_t qlora_moe_workspace_bytes_dev(int64_t m, int32_t E, int64_t n, int64_t k, int32_t r) {
+  if (m < 1 || E < 1 || E > nf4q::kMaxExperts || n < 1 || k < 1 || r < 0) return 0;
+  return moe_ws_layout(m, E, n, k, r, true).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Every expert's tiles in one launch of the fused forward kernel.
+int moe_fused_impl(const void *X, const Moe &mo, int32_t E, const nf4_tensor *W, const void *T,
+                   const void *B, int32_t r, float s, void *Y, void *table, hipStream_t sm) {
   nf4q::GroupArgs gr;
-  st = moe_groups(mo, E, (n + 255) / 256, &gr);
+  int st = moe_groups(mo, E, (mo.n + 255) / 256, &gr, 256, table, 0);
   if (st) return st;
   nf4q::GemmArgs g;
   g.a_side = (const uint16_t *)X;
-  g.lda = k;
+  g.lda = W->k;
   g.lora_a = r > 0 ? (const uint16_t *)T : nullptr;
   g.lora_b = (const uint16_t *)B;
   g.w = desc(W);
   g.M = mo.mtotal;
-  g.C = n;
-  g.R = k;
+  g.C = mo.n;
+  g.R = W->k;
   g.r = r;
   g.s = s;
   g.out = (uint16_t *)Y;
-  g.ldo = n;
+  g.ldo = mo.n;
   g.t = tables();
-  return hip_status(nf4q::launch_gemm_fwd_grouped(g, gr, (hipStream_t)stream),
-                    "qlora_moe_fwd_fused launch");
+  return hip_status(nf4q::launch_gemm_fwd_grouped(g, gr, sm), "grouped forward launch");
 }
 
-int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
-                  const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
-                  size_t ws_bytes, void *stream) {
-  Moe mo;
-  int st = check_moe(X, counts, E, W, A, B, r, &mo);
-  if (st) return st;
+int check_moe_ws(const MoeWs &lay, void *ws, size_t ws_bytes) {
+  if (ws_bytes < lay.total || (lay.total && !ws))
+    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, lay.total);
+  if (lay.total && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  return NF4_OK;
+}
+
+// T = X_e A_e^T for every expert's rows (one grouped row projection), then the fused launch.
+int moe_fwd_impl(const void *X, const Moe &mo, int32_t E, const nf4_tensor *W, const void *A,
+                 const void *B, int32_t r, float s, void *Y, void *T, void *ws, size_t ws_bytes,
+                 hipStream_t sm) {
   if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
   if (r > 0 && (!T || !aligned16(T))) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
   const int64_t k = W->k;
-  const size_t need = moe_ws(mo, E, k, r);
-  if (ws_bytes < need || (need && !ws))
-    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
-  if (need && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
-  // T = X_e A_e^T for every expert's rows in one grouped row projection
+  const bool dev = mo.dcounts != nullptr;
+  const MoeWs lay = moe_ws_layout(mo.mtotal, E, mo.n, k, r, dev);
+  int st = check_moe_ws(lay, ws, ws_bytes);
+  if (st) return st;
+  char *base = (char *)ws;
+  void *table = dev ? base : nullptr;
+  hipError_t he = moe_build_table(mo, E, k, table, sm);
+  if (he != hipSuccess) return hip_status(he, "grouped forward plan launch");
   if (r > 0) {
     nf4q::GroupArgs g64;
-    st = moe_groups(mo, E, 1, &g64, 64);
+    st = moe_groups(mo, E, 1, &g64, 64, table, 2);
     if (st) return st;
-    const MoePlan pl = moe_plan(mo, E, k);
-    const MoeWs lay = moe_ws_layout(mo, E, k, r);
-    hipError_t he = nf4q::launch_rowproj_grouped(
-        (const uint16_t *)X, k, (const uint16_t *)A, (int64_t)r * k, k, mo.mtotal, k, r, pl.sp_k,
-        (float *)((char *)ws + lay.u + lay.bt + lay.t), (uint16_t *)T, g64, (hipStream_t)stream);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_fwd T launch");
+    const MoePlan pl = moe_plan(mo.mtotal, E, mo.n, k);
+    he = nf4q::launch_rowproj_grouped((const uint16_t *)X, k, (const uint16_t *)A, (int64_t)r * k, k,
+                                      mo.mtotal, k, r, pl.sp_k,
+                                      (float *)(base + lay.table + lay.u + lay.bt + lay.t), (uint16_t *)T,
+                                      g64, sm);
+    if (he != hipSuccess) return hip_status(he, "grouped forward T launch");
   }
-  return qlora_moe_fwd_fused(X, counts, E, W, T, B, r, s, Y, stream);
+  return moe_fused_impl(X, mo, E, W, T, B, r, s, Y, table, sm);
 }
 
-int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
-                  const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
-                  const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
-                  void *stream) {
-  Moe mo;
-  int st = check_moe(X, counts, E, W, A, B, r, &mo);
-  if (st) return st;
+int moe_bwd_impl(const void *dY, const void *X, const Moe &mo, int32_t E, const nf4_tensor *W,
+                 const void *A, const void *B, int32_t r, float s, const void *T, void *dX, void *dA,
+                 void *dB, void *ws, size_t ws_bytes, hipStream_t sm) {
   if (!dY || !aligned16(dY)) return fail(NF4_EINVAL, "dY must be non-NULL and 16-byte aligned");
   if (dX && !aligned16(dX)) return fail(NF4_EINVAL, "dX must be 16-byte aligned");
   if (r > 0) {
@@ -808,44 +848,44 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
       return fail(NF4_EINVAL, "T, dA and dB must be 16-byte aligned");
   }
   const int64_t k = W->k, n = mo.n;
-  const MoeWs lay = moe_ws_layout(mo, E, k, r);
-  if (ws_bytes < lay.total || (lay.total && !ws))
-    return fail(NF4_EINVAL, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
-                lay.total);
-  if (lay.total && !aligned16(ws)) return fail(NF4_EINVAL, "ws must be 16-byte aligned");
+  const bool dev = mo.dcounts != nullptr;
+  const MoeWs lay = moe_ws_layout(mo.mtotal, E, n, k, r, dev);
+  int st = check_moe_ws(lay, ws, ws_bytes);
+  if (st) return st;
   if (!dX && r == 0) return ok();
-  hipStream_t sm = (hipStream_t)stream;
   char *base = (char *)ws;
-  uint16_t *U = (uint16_t *)base;
-  uint16_t *Bt = (uint16_t *)(base + lay.u);
-  float *part = (float *)(base + lay.u + lay.bt + lay.t);
+  void *table = dev ? base : nullptr;
+  uint16_t *U = (uint16_t *)(base + lay.table);
+  uint16_t *Bt = (uint16_t *)(base + lay.table + lay.u);
+  float *part = (float *)(base + lay.table + lay.u + lay.bt + lay.t);
   const uint16_t *dy = (const uint16_t *)dY, *x = (const uint16_t *)X;
   const uint16_t *a = (const uint16_t *)A;
-  hipError_t he;
+  hipError_t he = moe_build_table(mo, E, k, table, sm);
+  if (he != hipSuccess) return hip_status(he, "grouped backward plan launch");
   // U = dY_e B_e for every expert's rows in one grouped row projection (and T = X_e A_e^T the
   // same way when the caller keeps none), B_e from one transpose of the stacked B: Bt [r, E n],
   // expert e's columns e n .. e n + n - 1
-  const MoePlan pl = moe_plan(mo, E, k);
+  const MoePlan pl = moe_plan(mo.mtotal, E, n, k);
   nf4q::GroupArgs g64;
-  st = moe_groups(mo, E, 1, &g64, 64);
+  st = moe_groups(mo, E, 1, &g64, 64, table, 2);
   if (st) return st;
   if (r > 0) {
     he = nf4q::launch_transpose((const uint16_t *)B, E * n, r, Bt, sm);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd transpose launch");
+    if (he != hipSuccess) return hip_status(he, "grouped backward transpose launch");
     if (!T) {
-      uint16_t *Tw = (uint16_t *)(base + lay.u + lay.bt);
+      uint16_t *Tw = (uint16_t *)(base + lay.table + lay.u + lay.bt);
       he = nf4q::launch_rowproj_grouped(x, k, a, (int64_t)r * k, k, mo.mtotal, k, r, pl.sp_k, part, Tw,
                                         g64, sm);
-      if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd T launch");
+      if (he != hipSuccess) return hip_status(he, "grouped backward T launch");
       T = Tw;
     }
     he = nf4q::launch_rowproj_grouped(dy, n, Bt, n, E * n, mo.mtotal, n, r, pl.sp_n, part, U, g64, sm);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd U launch");
+    if (he != hipSuccess) return hip_status(he, "grouped backward U launch");
   }
   // dX of every expert in one launch
   if (dX) {
     nf4q::GroupArgs gr;
-    st = moe_groups(mo, E, (k + 255) / 256, &gr);
+    st = moe_groups(mo, E, (k + 255) / 256, &gr, 256, table, 1);
     if (st) return st;
     nf4q::GemmArgs g;
     g.a_side = dy;
@@ -862,18 +902,69 @@ int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t 
     g.ldo = k;
     g.t = tables();
     he = nf4q::launch_gemm_dx_grouped(g, gr, sm);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dX launch");
+    if (he != hipSuccess) return hip_status(he, "grouped backward dX launch");
   }
   // dA_e = s U_e^T X_e, dB_e = s dY_e^T T_e over each expert's own rows, every expert in one
   // launch each (an expert with no rows sums nothing: zero gradients)
   if (r > 0) {
     he = nf4q::launch_mreduce_grouped(U, x, k, k, r, s, pl.sa, part, (uint16_t *)dA, false, g64, sm);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dA launch");
+    if (he != hipSuccess) return hip_status(he, "grouped backward dA launch");
     he = nf4q::launch_mreduce_grouped((const uint16_t *)T, dy, n, n, r, s, pl.sb, part, (uint16_t *)dB,
                                       true, g64, sm);
-    if (he != hipSuccess) return hip_status(he, "qlora_moe_bwd dB launch");
+    if (he != hipSuccess) return hip_status(he, "grouped backward dB launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                        const void *T, const void *B, int32_t r, float s, void *Y, void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, T, B, r, &mo);   // T [sum(counts), r] in A's place
+  if (st) return st;
+  if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
+  return moe_fused_impl(X, mo, E, W, T, B, r, s, Y, nullptr, (hipStream_t)stream);
+}
+
+int qlora_moe_fwd(const void *X, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                  const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
+                  size_t ws_bytes, void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  return moe_fwd_impl(X, mo, E, W, A, B, r, s, Y, T, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int qlora_moe_fwd_dev(const void *X, int64_t m, const int64_t *counts, int32_t E, const nf4_tensor *W,
+                      const void *A, const void *B, int32_t r, float s, void *Y, void *T, void *ws,
+                      size_t ws_bytes, void *stream) {
+  Moe mo;
+  int st = check_moe_dev(X, m, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  return moe_fwd_impl(X, mo, E, W, A, B, r, s, Y, T, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
+                  const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
+                  const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
+                  void *stream) {
+  Moe mo;
+  int st = check_moe(X, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  return moe_bwd_impl(dY, X, mo, E, W, A, B, r, s, T, dX, dA, dB, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int qlora_moe_bwd_dev(const void *dY, const void *X, int64_t m, const int64_t *counts, int32_t E,
+                      const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
+                      const void *T, void *dX, void *dA, void *dB, void *ws, size_t ws_bytes,
+                      void *stream) {
+  Moe mo;
+  int st = check_moe_dev(X, m, counts, E, W, A, B, r, &mo);
+  if (st) return st;
+  return moe_bwd_impl(dY, X, mo, E, W, A, B, r, s, T, dX, dA, dB, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, const void *A,

@@ -168,15 +168,20 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   // first, so the 32 workgroups an XCD runs at once cover 4 row blocks x 8 column tiles and
   // share 4 dY row blocks and 8 weight column tiles in its L2 (one row block x 32 column tiles
   // re-fetched the whole weight from beyond L2 once per row block).
-  int logical = tile_remap(blockIdx.x, gridDim.x);
+  int logical;
   int64_t m_lo = 0, m_hi = g.M, wbase = 0;
   if (kGrp) {
-    int e = 0;
-    while (e + 1 < gr.E && logical >= gr.tile_off[e + 1]) ++e;
-    logical -= gr.tile_off[e];
-    m_lo = gr.m_off[e];
-    m_hi = gr.m_off[e + 1];
+    // a grid sized by an upper bound (routing on the device) has workgroups past the last tile
+    const int total = grp_tile_off(gr, gr.E);
+    if ((int)blockIdx.x >= total) return;
+    logical = tile_remap(blockIdx.x, total);
+    const int e = find_group(gr, logical);
+    logical -= grp_tile_off(gr, e);
+    m_lo = grp_m_off(gr, e);
+    m_hi = grp_m_off(gr, e + 1);
     wbase = (int64_t)e * g.R;
+  } else {
+    logical = tile_remap(blockIdx.x, gridDim.x);
   }
   const int tiles_m = (int)((m_hi - m_lo + kT - 1) / kT);
   const int gsz = kGroupM * tiles_k, grp0 = logical / gsz, gin = logical % gsz;
@@ -188,6 +193,12 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   const int kblk = (int)(K / kS);
   const int nsteps = (int)((N + kS - 1) / kS);
   const int last = nsteps - 1;
+  // The tiles of one row block start their walk over n at step rot (and wrap around), tiles of
+  // different row blocks at different steps, so that the workgroups of a launch do not all
+  // request the same offsets at once; rot depends on the row block only (the grouped form with
+  // one expert sums in the plain kernel's order).
+  const int rot = (int)(((m0 - m_lo) / kT) * 5 % nsteps);
+  auto phys = [&](int s) { return s + rot < nsteps ? s + rot : s + rot - nsteps; };
 
   // dY rows m0.. (reduction index n contiguous). Chunks past n = N read the next row's values
   // (finite) and meet weight rows past N, which decode to exact zeros (codes and constants read
@@ -325,9 +336,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    dma_y(s1, ybuf(P ^ 1));
+    dma_y(phys(s1), ybuf(P ^ 1));
     __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
-    load_c(s2, cm);
+    load_c(phys(s2), cm);
     const uint4 *Y = ybuf(P);
     const uint16_t *W = wbuf(P);
     uint16_t *Wn = wbuf(P ^ 1);
@@ -396,9 +407,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   };
 
   CStage c0, c1;
-  dma_y(0, ybuf(0));
-  load_c(0, c0);
-  load_c(nsteps > 1 ? 1 : 0, c1);
+  dma_y(phys(0), ybuf(0));
+  load_c(phys(0), c0);
+  load_c(phys(nsteps > 1 ? 1 : 0), c1);
   decode_all(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -475,7 +486,7 @@ hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStr
   if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || gr.E < 1 ||
       gr.E > kMaxExperts || g.w.n != (int64_t)gr.E * g.R)
     return hipErrorInvalidValue;
-  const int tiles = gr.tile_off[gr.E];
+  const int64_t tiles = gr.grid;
   if (tiles < 1) return hipSuccess;
   if (g.w.fp4)
     dx_grouped_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);

@@ -64,6 +64,8 @@ __device__ __forceinline__ int tile_remap(int hw, int tiles) {
 struct CStage {
   u32x4 c;           // 16 bytes of codes (32 elements) of the thread's half-row
   uint32_t q, sc;    // block constant (int8 or float bits) and run scale bits
+  uint16_t q16;      // E2M1: the two group scales (kept 16-bit: a widening of the just-loaded
+                     // value would make the compiler wait for every load in flight)
 };
 
 // LoRA step staging: A side T columns jb..jb+63, B side s * B (rows n), zero-padded; only the
@@ -166,15 +168,20 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int tiles_n = (int)((g.C + kTN - 1) / kTN);
-  int local = tile_remap(blockIdx.x, gridDim.x);
+  int local;
   int64_t m_lo = 0, m_hi = g.M, wbase = 0;
   if (kGrp) {
-    int e = 0;
-    while (e + 1 < gr.E && local >= gr.tile_off[e + 1]) ++e;
-    local -= gr.tile_off[e];
-    m_lo = gr.m_off[e];
-    m_hi = gr.m_off[e + 1];
+    // a grid sized by an upper bound (routing on the device) has workgroups past the last tile
+    const int total = grp_tile_off(gr, gr.E);
+    if ((int)blockIdx.x >= total) return;
+    local = tile_remap(blockIdx.x, total);
+    const int e = find_group(gr, local);
+    local -= grp_tile_off(gr, e);
+    m_lo = grp_m_off(gr, e);
+    m_hi = grp_m_off(gr, e + 1);
     wbase = (int64_t)e * g.C;
+  } else {
+    local = tile_remap(blockIdx.x, gridDim.x);
   }
   const int64_t m0 = m_lo + (int64_t)(local / tiles_n) * kT;
   const int64_t n0 = (int64_t)(local % tiles_n) * kTN;   // columns of Y
@@ -184,6 +191,12 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   const int64_t rows_n = (g.C - n0 < kTN) ? g.C - n0 : kTN;   // valid columns (of each half)
   const int kblk = (int)(K / kS);
   const int last = kblk - 1;
+  // The tiles of one row block start their walk over K at step rot (and wrap around), tiles of
+  // different row blocks at different steps, so that the workgroups of a launch do not all
+  // request the same K offsets at once. rot depends on the row block only: every output element
+  // still sums its K steps in an order fixed by its row (the pair and grouped forms agree).
+  const int rot = (int)(((m0 - m_lo) / kT) * 5 % kblk);
+  auto phys = [&](int s) { return s + rot < kblk ? s + rot : s + rot - kblk; };
 
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.a_side + m0 * K, rows_m * K * 2);
   // pair: the buffers span the whole stacked weight, rows addressed per thread (rows past N read
@@ -253,7 +266,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   auto load_c = [&](int s, CStage &c) {
     c.c = __builtin_amdgcn_raw_buffer_load_b128(rC, coff + s * 32, 0, 0);
     if (kFP4) {
-      c.q = __builtin_amdgcn_raw_buffer_load_b16(rQ, qoff + 4 * s, 0, 0);
+      c.q16 = __builtin_amdgcn_raw_buffer_load_b16(rQ, qoff + 4 * s, 0, 0);
     } else if (kDQ) {
       c.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, qoff + s, 0, 0);
       c.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (uint32_t)(((sbase + s) >> 8) * 4), 0, 0);
@@ -268,11 +281,11 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     return j == 0 ? c.c.x : j == 1 ? c.c.y : j == 2 ? c.c.z : c.c.w;
   };
   auto decode_half = [&](const CStage &c, uint4 *sB) {
-    RowTable t = kFP4 ? make_e2m1_table(e4m3_to_f32(c.q & 0xFFu)) : make_row_table(absmax_of(c), g.t);
+    RowTable t = kFP4 ? make_e2m1_table(e4m3_to_f32(c.q16 & 0xFFu)) : make_row_table(absmax_of(c), g.t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t o[4];
-      if (kFP4 && j == 2) t = make_e2m1_table(e4m3_to_f32((c.q >> 8) & 0xFFu));
+      if (kFP4 && j == 2) t = make_e2m1_table(e4m3_to_f32((c.q16 >> 8) & 0xFFu));
       if (kFP4) decode8_e2m1(t, word(c, j), o); else decode8(t, word(c, j), o);
       sB[swzf(wr, 4 * wh + j)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -304,9 +317,9 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    dma_x(s1, xbuf(P ^ 1));
+    dma_x(phys(s1), xbuf(P ^ 1));
     __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
-    load_c(s2, cm);
+    load_c(phys(s2), cm);
     const uint4 *A = xbuf(P);
     const uint4 *B = wbuf(P);
     uint4 *Bn = wbuf(P ^ 1);
@@ -324,7 +337,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     // (E2M1: the whole table of the thread's first group)
     RowTable t;
     if (kFP4) {
-      t = make_e2m1_table(e4m3_to_f32(cn.q & 0xFFu));
+      t = make_e2m1_table(e4m3_to_f32(cn.q16 & 0xFFu));
     } else {
       const float a = absmax_of(cn);
 #pragma unroll
@@ -371,7 +384,7 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
           // E2M1: words 2 and 3 belong to the thread's second group. The empty asm keeps this
           // table from being hoisted above the groups before (two live tables spill registers).
           if (kFP4 && j == 1) {
-            uint32_t q2 = cn.q;
+            uint16_t q2 = cn.q16;
             asm volatile("" : "+v"(q2));
             t = make_e2m1_table(e4m3_to_f32((q2 >> 8) & 0xFFu));
           }
@@ -387,9 +400,9 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   };
 
   CStage c0, c1;
-  dma_x(0, xbuf(0));
-  load_c(0, c0);
-  load_c(kblk > 1 ? 1 : 0, c1);
+  dma_x(phys(0), xbuf(0));
+  load_c(phys(0), c0);
+  load_c(phys(kblk > 1 ? 1 : 0), c1);
   decode_half(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -549,7 +562,7 @@ hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipSt
   if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || gr.E < 1 ||
       gr.E > kMaxExperts)
     return hipErrorInvalidValue;
-  const int64_t tiles = gr.tile_off[gr.E];
+  const int64_t tiles = gr.grid;
   if (tiles < 1) return hipSuccess;
   if (g.w.fp4)
     fwd_grouped_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);

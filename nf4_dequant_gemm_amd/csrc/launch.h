@@ -49,12 +49,56 @@ hipError_t launch_gemm_fwd_pair(const GemmArgs &g, hipStream_t st);
 // belong to expert e, whose weight rows are e N .. e N + N - 1 of the stacked weight g.w and whose
 // B rows are the same rows of g.lora_b (N = g.C). tile_off[e] = sum over e' < e of
 // ceil(rows_e' / 256) * ceil(N / 256): one launch runs every expert's tiles.
-constexpr int kMaxExperts = 64;
+// The table is either held in the arguments (routing known on the host) or, with dm_off set, in
+// device memory (routing computed on the device: launch_moe_plan writes it, and the launch's
+// grid is an upper bound; workgroups past tile_off[E] exit at once).
+constexpr int kMaxExperts = 256;
 struct GroupArgs {
   int E;
+  int64_t grid;                 // workgroups of the launch (x): tile_off[E] or an upper bound
+  const int64_t *dm_off;        // device table [E + 1], or NULL: m_off below
+  const int32_t *dtile_off;     // device table [E + 1], or NULL: tile_off below
   int64_t m_off[kMaxExperts + 1];
   int32_t tile_off[kMaxExperts + 1];
 };
+// Table entries, for a group index the same in every lane (kept in scalar registers: values
+// derived from it address every tile load).
+__device__ __forceinline__ int64_t grp_m_off(const GroupArgs &g, int e) {
+  const int64_t v = g.dm_off ? g.dm_off[e] : g.m_off[e];
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int grp_tile_off(const GroupArgs &g, int e) {
+  return __builtin_amdgcn_readfirstlane(g.dtile_off ? g.dtile_off[e] : g.tile_off[e]);
+}
+// The group holding logical tile `local` (tile_off[e] <= local < tile_off[e + 1]; empty groups
+// hold none): every thread tests some groups, the match goes through LDS. Call with the whole
+// workgroup; `local` is the same in every lane, and so is the result.
+__device__ __forceinline__ int find_group(const GroupArgs &g, int local) {
+  __shared__ int s_group;
+  for (int t = threadIdx.x; t < g.E; t += blockDim.x) {
+    const int lo = g.dtile_off ? g.dtile_off[t] : g.tile_off[t];
+    const int hi = g.dtile_off ? g.dtile_off[t + 1] : g.tile_off[t + 1];
+    if (local >= lo && local < hi) s_group = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_group);
+}
+
+// Device group tables of a grouped layer from expert row counts held in device memory (int64
+// [E]): m_off int64 [E + 1], then int32 [E + 1] first-tile tables for 256-row tiles times tiles_n
+// (forward) and times tiles_k (dX) column tiles, and for 64-row blocks. Negative counts count as
+// 0 and the row offsets are clipped at m, so no row past m is ever read or written. One
+// workgroup; the table takes moe_table_bytes(E) bytes.
+size_t moe_table_bytes(int E);
+hipError_t launch_moe_plan(const int64_t *dcounts, int E, int64_t m, int64_t tiles_n,
+                           int64_t tiles_k, void *table, hipStream_t st);
+__host__ __device__ inline int64_t *moe_table_m_off(void *t) { return reinterpret_cast<int64_t *>(t); }
+__host__ __device__ inline int32_t *moe_table_tiles(void *t, int E, int which) {   // 0 forward, 1 dX, 2 64-row blocks
+  return reinterpret_cast<int32_t *>(reinterpret_cast<char *>(t) + 8 * (E + 1)) + which * (E + 1);
+}
 hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st);
 // Forward for M <= 48 and K % 256 == 0 (weight-stream bound): codes streamed by LDS DMA, table
 // decode of unscaled levels, block constant applied to the per-block partial sums.

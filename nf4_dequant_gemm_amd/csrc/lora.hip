@@ -39,10 +39,11 @@ __device__ __forceinline__ void rowproj_body(const uint16_t *__restrict__ in, in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t mbase = (int64_t)blockIdx.x * 64, mhi = M;
   if (kGrp) {
-    int e = 0;
-    while (e + 1 < gr.E && (int)blockIdx.x >= gr.tile_off[e + 1]) ++e;
-    mbase = gr.m_off[e] + (int64_t)((int)blockIdx.x - gr.tile_off[e]) * 64;
-    mhi = gr.m_off[e + 1];
+    // a grid sized by an upper bound (routing on the device) has blocks past the last one
+    if ((int)blockIdx.x >= grp_tile_off(gr, gr.E)) return;
+    const int e = find_group(gr, (int)blockIdx.x);
+    mbase = grp_m_off(gr, e) + (int64_t)((int)blockIdx.x - grp_tile_off(gr, e)) * 64;
+    mhi = grp_m_off(gr, e + 1);
     p += e * pstride;
   }
   const int split = blockIdx.y;
@@ -293,7 +294,7 @@ hipError_t launch_rowproj(const uint16_t *in, int64_t ldin, const uint16_t *p, i
 hipError_t launch_rowproj_grouped(const uint16_t *in, int64_t ldin, const uint16_t *p, int64_t pstride,
                                   int64_t ldp, int64_t M, int64_t L, int r, int splits, float *part,
                                   uint16_t *out, const GroupArgs &gr, hipStream_t st) {
-  const int blocks = gr.tile_off[gr.E];
+  const int64_t blocks = gr.grid;
   if (blocks < 1) return hipSuccess;
   int64_t lsplit = (L + splits - 1) / splits;
   lsplit = (lsplit + 63) / 64 * 64;
@@ -313,6 +314,47 @@ hipError_t launch_rowproj_grouped(const uint16_t *in, int64_t ldin, const uint16
   int64_t nb = (n + 255) / 256;
   if (nb > 4096) nb = 4096;
   rowproj_reduce_kernel<<<dim3((unsigned)nb), dim3(256), 0, st>>>(part, n, splits, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- group tables (routing on the device)
+size_t moe_table_bytes(int E) { return 8 * (size_t)(E + 1) + 3 * 4 * (size_t)(E + 1); }
+
+__global__ __launch_bounds__(256) void moe_plan_kernel(const int64_t *__restrict__ dcounts, int E,
+                                                       int64_t m, int64_t tiles_n, int64_t tiles_k,
+                                                       void *table) {
+  __shared__ int64_t cnt[kMaxExperts];
+  const int t = threadIdx.x;
+  if (t < E) {
+    const int64_t c = dcounts[t];
+    cnt[t] = c > 0 ? c : 0;
+  }
+  __syncthreads();
+  if (t != 0) return;
+  int64_t *mo = moe_table_m_off(table);
+  int32_t *tf = moe_table_tiles(table, E, 0), *td = moe_table_tiles(table, E, 1);
+  int32_t *tb = moe_table_tiles(table, E, 2);
+  int64_t off = 0, a = 0, b = 0, c = 0;
+  mo[0] = 0;
+  tf[0] = td[0] = tb[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t hi = off + cnt[e] < m ? off + cnt[e] : m;
+    const int64_t blocks = (hi - off + 255) / 256;
+    a += blocks * tiles_n;
+    b += blocks * tiles_k;
+    c += (hi - off + 63) / 64;
+    off = hi;
+    mo[e + 1] = off;
+    tf[e + 1] = (int32_t)a;
+    td[e + 1] = (int32_t)b;
+    tb[e + 1] = (int32_t)c;
+  }
+}
+
+hipError_t launch_moe_plan(const int64_t *dcounts, int E, int64_t m, int64_t tiles_n,
+                           int64_t tiles_k, void *table, hipStream_t st) {
+  if (E < 1 || E > kMaxExperts || !dcounts || !table) return hipErrorInvalidValue;
+  moe_plan_kernel<<<dim3(1), dim3(256), 0, st>>>(dcounts, E, m, tiles_n, tiles_k, table);
   return hipGetLastError();
 }
 
@@ -351,8 +393,8 @@ __device__ __forceinline__ void mreduce_body(const uint16_t *__restrict__ P,
   const int split = blockIdx.y;
   int64_t lo = 0, hi = M;
   if (kGrp) {
-    lo = gr.m_off[blockIdx.z];
-    hi = gr.m_off[blockIdx.z + 1];
+    lo = grp_m_off(gr, blockIdx.z);
+    hi = grp_m_off(gr, blockIdx.z + 1);
     msplit = (hi - lo + gridDim.y - 1) / gridDim.y;
     msplit = (msplit + kMR_BM - 1) / kMR_BM * kMR_BM;
   }
@@ -492,7 +534,7 @@ __global__ __launch_bounds__(256) void mreduce_grouped_kernel(const uint16_t *__
                                                               const uint16_t *__restrict__ Q,
                                                               int64_t ldq, int64_t C, int r,
                                                               float *__restrict__ part, GroupArgs gr) {
-  mreduce_body<TJ, true>(P, Q, ldq, gr.m_off[gr.E], C, r, 0, part, gr);
+  mreduce_body<TJ, true>(P, Q, ldq, 0, C, r, 0, part, gr);
 }
 
 // out = s * (sum over splits of part), for E blocks of [r][C] (E = 1 unless grouped); block e of

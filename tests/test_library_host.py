@@ -214,7 +214,8 @@ def test_moe_calls_reject_bad_arguments():
     assert fwd(wsb=wsb - 1) == m.NF4_EINVAL
     assert fwd(ws=None) == m.NF4_EINVAL
     assert fwd(E=0) == m.NF4_EINVAL
-    assert fwd(E=65, c=cnt(*([1] * 65)), q=wdesc(n=65 * 8, k=128)) == m.NF4_EINVAL   # at most 64 experts
+    assert fwd(E=257, c=cnt(*([1] * 257)), q=wdesc(n=257 * 8, k=128), r=0) == m.NF4_EINVAL   # at most 256
+    assert lib.qlora_moe_workspace_bytes(cnt(*([1] * 256)), 256, 8, 128, 8) > 0   # 256 experts
     assert fwd(E=3, c=cnt(1, 2, 3)) == m.NF4_EINVAL          # 256 rows are not 3 experts
     assert fwd(c=cnt(10, -1, 300, 7)) == m.NF4_EINVAL        # negative count
     assert fwd(c=cnt(0, 0, 0, 0)) == m.NF4_EINVAL            # no rows at all
@@ -291,3 +292,31 @@ def test_noalloc_forward_rejects_on_the_host():
     assert call(T=None) == m.NF4_EINVAL
     assert call(r=129) == m.NF4_EINVAL
     assert call(q=wdesc(n=60, k=big_k)) == m.NF4_EUNSUPPORTED
+
+
+def test_device_routed_moe_calls_reject_on_the_host():
+    """qlora_moe_fwd_dev / qlora_moe_bwd_dev take a device pointer to the counts and the row total:
+    the host checks the pointer, E, the stacked shapes and the workspace (sized from m and E)."""
+    lib = m.library()
+    q = wdesc(n=4 * 64, k=128)
+    wsb = lib.qlora_moe_workspace_bytes_dev(317, 4, 64, 128, 8)
+    assert wsb > 0 and lib.qlora_moe_workspace_bytes_dev(0, 4, 64, 128, 8) == 0
+    assert lib.qlora_moe_workspace_bytes_dev(317, 257, 64, 128, 8) == 0
+    # the same counts through the host: the device form adds only the group tables
+    c4 = (ctypes.c_int64 * 4)(10, 0, 300, 7)
+    assert 0 < wsb - lib.qlora_moe_workspace_bytes(c4, 4, 64, 128, 8) <= 4096
+    fwd = lambda **kw: lib.qlora_moe_fwd_dev(FAKE, kw.get("m", 317), kw.get("c", FAKE), kw.get("E", 4),
+                                             ctypes.byref(kw.get("q", q)), FAKE, FAKE, kw.get("r", 8), 1.0,
+                                             FAKE, FAKE, kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert fwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert fwd(c=None) == m.NF4_EINVAL
+    assert fwd(c=ctypes.c_void_p(4100)) == m.NF4_EINVAL      # counts not 8-byte aligned
+    assert fwd(E=257) == m.NF4_EINVAL
+    assert fwd(m=0) == m.NF4_EINVAL
+    assert fwd(E=3) == m.NF4_EINVAL                            # 256 rows are not 3 experts
+    bwd = lambda **kw: lib.qlora_moe_bwd_dev(kw.get("dY", FAKE), FAKE, 317, kw.get("c", FAKE), 4,
+                                             ctypes.byref(q), FAKE, FAKE, 8, 1.0, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, kw.get("wsb", wsb), None)
+    assert bwd(wsb=wsb - 1) == m.NF4_EINVAL
+    assert bwd(dY=None) == m.NF4_EINVAL
+    assert bwd(c=None) == m.NF4_EINVAL
