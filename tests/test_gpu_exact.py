@@ -115,7 +115,7 @@ def test_identity_probe_dx_steps(lib, N, dq):
 # ---------------------------------------------------------------- decode-shaped kernels
 # M <= 16 with double quantisation: the stream kernel (stages of 4 blocks, an 8-stage unrolled
 # loop, code windows of 4 stages, staggered start stages when the stage count is a multiple of 4
-# and at least 8). N = 336 is three workgroups of 112 rows; 300 leaves a ragged last workgroup.
+# and at least 8). N = 336 is three workgroups of 112 rows; 296 leaves a ragged last workgroup.
 STREAM_STAGES = [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17, 33]
 
 
@@ -136,7 +136,7 @@ def run_unit_probe(lib, qg, qo, K, rows, ncalls=None):
 
 
 @pytest.mark.parametrize("nst", STREAM_STAGES)
-@pytest.mark.parametrize("N", [336, 300])
+@pytest.mark.parametrize("N", [336, 296])
 def test_decode16_unit_probe(lib, nst, N):
     K = 256 * nst
     say(f"stream-kernel unit probe stages={nst} K={K} N={N}")
@@ -161,7 +161,7 @@ def test_decode_unit_probe(lib, M, dq, K):
 @pytest.mark.parametrize("K", [256, 1280])
 def test_decode_e2m1_unit_probe(lib, K):
     """E2M1 weights on the decode shape: e2m1 * s is exact in bf16 and S multiplies the float32
-    sum once, so Y = bf16(deq(W)) bit for bit at any group scale."""
+    sum once, so Y = bf16(deq(W)) at any group scale (bit for bit up to the sign of zero)."""
     N, M = 200, 16
     W = wl.normal_bf16(950 + K, (N, K), 0.02)
     qg = lib.fp4_quantize(W.to(DEV))
@@ -171,4 +171,7 @@ def test_decode_e2m1_unit_probe(lib, K):
         cols = probe_columns(kblk, c, M)
         Yg, _ = lib.qlora_fwd(unit_rows(K, cols).to(DEV), qg, None, None, 1.0)
         torch.cuda.synchronize()
-        assert np.array_equal(u16(Yg), want_full[:, cols].T)
+        # equal values bit for bit; the E2M1 code for -0 dequantises to -0, which a sum of zero
+        # products returns as +0
+        got, want = nf4.bf16_value(u16(Yg)), nf4.bf16_value(want_full[:, cols].T)
+        assert np.array_equal(got, want)
