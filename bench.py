@@ -224,27 +224,37 @@ def step_calls(L):
 
 
 def time_steps(L, calls, steps, warmup):
-    """warmup + steps steps; the host-clock step time (ms) and per-call HIP-event times (ms)."""
+    """warmup + steps steps, twice. First the plain steps between two synchronisations: the
+    host-clock time per step and the GPU time per step (one HIP event pair around the whole
+    timed region on the launch stream). Then the same steps with a HIP event pair around every
+    call: the per-call times (ms). Returns (host ms/step, GPU ms/step, per-call stats)."""
     import torch
     for i in range(warmup):
         for _, c in calls:
             c(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record(L.stream)
+    for s in range(steps):
+        for _, c in calls:
+            c(warmup + s)
+    b.record(L.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    host_ms, gpu_ms = (t1 - t0) * 1e3 / steps, a.elapsed_time(b) / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     for s in range(steps):
         e = ev[s]
         e[0].record(L.stream)
         for j, (_, c) in enumerate(calls):
-            c(warmup + s)
+            c(warmup + steps + s)
             e[j + 1].record(L.stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     per = {}
     for j, (name, _) in enumerate(calls):
         per[name] = stats([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)])
-    return (t1 - t0) * 1e3 / steps, per
+    return host_ms, gpu_ms, per
 
 
 def time_call(L, fn, steps, warmup):
@@ -309,10 +319,14 @@ def run_config(w, dev, args, cpu=True):
     (cpu) the CPU oracle on a sample. Returns the JSON object and the Layer (for the context)."""
     L = Layer(w, dev, args.wcopies)
     calls = step_calls(L)
-    step_ms, per = time_steps(L, calls, args.steps, args.warmup)
+    host_ms, gpu_ms, per = time_steps(L, calls, args.steps, args.warmup)
+    # the GPU time per step (the host may be slower than the GPU at issuing the short steps of
+    # the small and decode workloads); the host-clock time is reported beside it
+    step_ms = gpu_ms
     M, N, K, r = w.M, w.N, w.K, w.r
     out = {"workload": describe(w), "M": M, "K": K, "N": N, "r": r, "weight_copies": len(L.copies),
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+           "host_ms_per_step": round(host_ms, 4),
            "phase_ms": {k: {q: round(x, 4) for q, x in v.items()} for k, v in per.items()}}
     kernels = {}
     if w.name == "small" or (w.backward and M <= 64):
@@ -741,6 +755,21 @@ def run_context(L):
         out["device_copy"] = {"what": "1 GiB device-to-device copy", "ms": round(ms, 4),
                               "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
         del src, dst
+        # the same forward without fusion: the weight dequantised to bf16 in HBM, then read back
+        # by the vendor GEMM, and the two LoRA products (its HBM bytes beside the fused launch's
+        # are in the counter profiles)
+        q = L.copies[0]
+        At = L.A.t().contiguous()
+        Bt = (w.s * L.B.float()).to(torch.bfloat16).t().contiguous()
+
+        def unfused():
+            Wd = L.lib.nf4_dequantize(q, torch.bfloat16)
+            return torch.matmul(L.X, Wd.t()) + torch.matmul(torch.matmul(L.X, At), Bt)
+        ms_u = _median_ms(unfused, 5)
+        out["unfused_fwd"] = {"what": "nf4_dequantize (bf16 W written) + vendor GEMM + LoRA GEMMs (forward)",
+                              "ms": round(ms_u, 4),
+                              "GB/s": round(w.weight_stream_bytes() / (ms_u * 1e-3) / 1e9, 1)}
+        del At, Bt
     torch.cuda.empty_cache()
     return out
 
@@ -789,26 +818,28 @@ def copy_calibration():
 
 
 def trace_groups():
-    """(kernel name prefix, workgroups) -> (workload, launch) for the fused launches of the
-    default run: the tile counts of the 256 x 256 forward and dX kernels and of the 112-row
-    stream kernel, from the workload shapes."""
+    """(kernel name part, workgroups) -> (workload, launch) for the fused launches of the default
+    run: the tile counts of the 256 x 256 forward and dX kernels and of the 112-row stream
+    kernel, from the workload shapes."""
     import workloads as wl
     out = {}
     for name in DEFAULT_CONFIGS:
         w = wl.WORKLOADS[name]
         cd = lambda a, b: -(-a // b)
         if w.M <= 16 and w.dq_block and w.K % 256 == 0:
-            out[("nf4q::decode16_fwd_kernel", cd(w.N, 112))] = (name, "qlora_fwd_fused (decode)")
+            out[("decode16_fwd_kernel", cd(w.N, 112))] = (name, "qlora_fwd_fused (decode)")
         elif w.M > 48 or w.K % 256:
-            out[("nf4q::fwd_fused_kernel", cd(w.N, 256) * cd(w.M, 256))] = (name, "qlora_fwd_fused")
+            out[("fwd_fused_kernel", cd(w.N, 256) * cd(w.M, 256))] = (name, "qlora_fwd_fused")
         if w.backward:
-            out[("nf4q::dx_fused_kernel", cd(w.K, 256) * cd(w.M, 256))] = (name, "qlora_bwd_dx")
+            out[("dx_fused_kernel", cd(w.K, 256) * cd(w.M, 256))] = (name, "qlora_bwd_dx")
     return out
 
 
-def summarize_trace(path):
+def summarize_trace(path, steps, warmup):
     """Per-(kernel, grid) durations from a rocprofv3 kernel trace (CSV) of this command: the fused
-    kernels of different workloads share names, so they are told apart by their workgroup count."""
+    kernels of different workloads share names, so they are told apart by their workgroup count.
+    mean_timed leaves out the warm-up launches (in every run of warmup + steps launches of a
+    fused kernel, the first warmup), as the bench's own means do."""
     files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no *kernel_trace.csv under {path}")
@@ -817,30 +848,35 @@ def summarize_trace(path):
         with open(fn, newline="") as f:
             for row in csv.DictReader(f):
                 name = row["Kernel_Name"]
-                grid = int(row.get("Grid_Size_X", row.get("Grid_Size", 0)) or 0)
-                wg = int(row.get("Workgroup_Size_X", row.get("Workgroup_Size", 1)) or 1)
+                wgs = 1
+                for ax in "XYZ":
+                    grid = int(row.get(f"Grid_Size_{ax}", 1) or 1)
+                    wg = int(row.get(f"Workgroup_Size_{ax}", 1) or 1)
+                    wgs *= -(-grid // max(wg, 1))
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-                groups.setdefault((name, grid // max(wg, 1)), []).append(dur)
+                groups.setdefault((name, wgs), []).append((int(row["Start_Timestamp"]), dur))
     known = trace_groups()
     print(f"# source: {', '.join(os.path.relpath(f, path) for f in files)}")
-    print("# durations in microseconds (End_Timestamp - Start_Timestamp of each dispatch)")
-    print(f"{'calls':>5} {'mean_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10}  {'wgs':>6}  "
-          f"{'workload/launch':<36} kernel")
+    print("# durations in microseconds (End_Timestamp - Start_Timestamp of each dispatch); wgs = workgroups")
+    print(f"{'calls':>5} {'mean_us':>10} {'mean_timed':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10}"
+          f"  {'wgs':>6}  {'workload/launch':<34} kernel")
     rows = []
-    for (name, wgs), v in groups.items():
-        tag = next((f"{wl_}/{launch}" for (pre, n), (wl_, launch) in known.items()
-                    if n == wgs and name.startswith(pre)), "")
-        rows.append((sum(v), name, wgs, v, tag))
-    for _, name, wgs, v, tag in sorted(rows, reverse=True):
+    for (name, wgs), tv in groups.items():
+        v = [d for _, d in sorted(tv)]
+        tag = next((f"{wl_}/{launch}" for (part, n), (wl_, launch) in known.items()
+                    if n == wgs and part in name), "")
+        timed = [d for i, d in enumerate(v) if i % (warmup + steps) >= warmup] if tag else v
+        rows.append((sum(v), name, wgs, v, timed or v, tag))
+    for _, name, wgs, v, timed, tag in sorted(rows, reverse=True):
         s = stats(v)
-        print(f"{len(v):5d} {s['mean']:10.2f} {s['median']:10.2f} {min(v):10.2f} {max(v):10.2f}  {wgs:6d}  "
-              f"{tag:<36} {name[:110]}")
+        print(f"{len(v):5d} {s['mean']:10.2f} {sum(timed) / len(timed):10.2f} {s['median']:10.2f} "
+              f"{min(v):10.2f} {max(v):10.2f}  {wgs:6d}  {tag:<34} {name[:100]}")
 
 
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -878,8 +914,12 @@ def main():
                 if vendor:
                     k["frac_of_vendor_gemm"] = round(k["achieved"] / vendor, 4)
             res["context"] = ctx
-        elif res["bound"] == "hbm" and not args.no_context and name == head:
-            res["context"] = run_context(L)
+        elif res["bound"] == "hbm" and not args.no_context:
+            ctx = run_context(L)
+            copy = ctx.get("device_copy", {}).get("GB/s")
+            if copy:
+                res["roofline"]["frac_of_device_copy"] = round(res["roofline"]["achieved"] / copy, 4)
+            res["context"] = ctx
         if name == head and w.M > 64 and w.fmt == "nf4":
             extra["merge"] = run_merge(L, args.steps, args.warmup)
         del L
