@@ -489,9 +489,9 @@ int qlora_lora_down(const void *X, int64_t m, int64_t k, const void *A, int32_t 
                     "qlora_lora_down launch");
 }
 
-// Shapes of the M <= 16 stream kernel: double-quantised NF4 codes, K a multiple of 256.
+// Shapes of the M <= 16 stream kernel: double-quantised NF4 or E2M1 codes, K a multiple of 256.
 static bool stream16_shape(int64_t m, const nf4_tensor *W) {
-  return m <= 16 && W->dq_block > 0 && W->k % 256 == 0;
+  return m <= 16 && (W->dq_block > 0 || W->block == 16) && W->k % 256 == 0;
 }
 
 int qlora_fwd_fused(const void *X, int64_t m, const nf4_tensor *W, const void *T, const void *B,

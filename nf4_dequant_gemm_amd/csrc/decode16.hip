@@ -111,16 +111,41 @@ __device__ __forceinline__ void dma4(const i32x4 &rs, uint32_t lds, uint32_t vof
                ::"s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
+template <int N>
+struct TileCount {
+  static constexpr int n = N;
+};
+
+// Two E2M1 values (byte kByte of w) as a bf16 pair, low nibble -> low half. The conversion's
+// scale operand contributes only its power of two (measured on gfx950: the mantissa of the
+// scale is ignored), so it is 1 here and the E4M3 group scales are applied to the sums.
+template <int kByte>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, kByte));
+}
+
+// kFP4: E2M1 codes with an E4M3 scale per group of 16 and a float32 tensor scale S (block 16 of
+// the weight descriptor). A stage then carries the 16 group-scale bytes of each row (4 blocks x 4
+// groups) in place of the run scales, and needs no windows of block codes and no level table
+// (the codes convert to bf16 in one instruction per byte). Each lane takes 8 consecutive
+// elements of a 32-element slice, so a slice holds two groups split by lane half; each group's
+// product is its own MFMA (the X operand masked to that half), times its scale, and the sums are
+// in units of S, which multiplies the tile at the end.
+template <bool kFP4>
 __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // Four stage slots, two windows of block codes and the level-pair table, which holds the
   // cross-wave sums at the end.
-  __shared__ __align__(16) uint8_t slot0[kSlotBytes];
-  __shared__ __align__(16) uint8_t slot1[kSlotBytes];
-  __shared__ __align__(16) uint8_t slot2[kSlotBytes];
-  __shared__ __align__(16) uint8_t slot3[kSlotBytes];
-  __shared__ __align__(16) uint8_t qwin0[kQWinBytes];
-  __shared__ __align__(16) uint8_t qwin1[kQWinBytes];
-  __shared__ __align__(16) uint32_t stab[kTabBytes / 4];
+  constexpr int kSlot = kFP4 ? kSOff + kRows * 16 : kSlotBytes;
+  constexpr int kQWin = kFP4 ? 16 : kQWinBytes;
+  __shared__ __align__(16) uint8_t slot0[kSlot];
+  __shared__ __align__(16) uint8_t slot1[kSlot];
+  __shared__ __align__(16) uint8_t slot2[kSlot];
+  __shared__ __align__(16) uint8_t slot3[kSlot];
+  __shared__ __align__(16) uint8_t qwin0[kQWin];
+  __shared__ __align__(16) uint8_t qwin1[kQWin];
+  // E2M1: no level table; the area holds only the cross-wave sums (7 tiles x 4 blocks x 1 KB)
+  constexpr int kTab = kFP4 ? kTiles * 4 * 64 * 16 : kTabBytes;
+  __shared__ __align__(16) uint32_t stab[kTab / 4];
   auto slot = [&](int i) -> uint8_t * {
     return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3;
   };
@@ -137,12 +162,14 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // zero. Run indices are taken relative to run0 = floor(n0 * kblk / 256), the run of the
   // workgroup's first block, with that block's offset in its run (boff) added back.
   const i32x4 rC = rsrc_words(g.w.codes + n0 * (K / 2), rows * (K / 2));
-  const i32x4 rQ = rsrc_words(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows * kblk);
+  // NF4: int8 block codes; E2M1: the E4M3 group scales (K / 16 bytes per row)
+  const i32x4 rQ = kFP4 ? rsrc_words(reinterpret_cast<const uint8_t *>(g.w.absmax) + n0 * (K / 16), rows * (K / 16))
+                        : rsrc_words(reinterpret_cast<const int8_t *>(g.w.absmax) + n0 * kblk, rows * kblk);
   const int64_t b0 = n0 * kblk;                    // flattened index of the first block
   const int64_t run0 = b0 >> 8;
   const int boff = (int)(b0 & 255);
   const int64_t nruns = (N * kblk + 255) / 256;
-  const i32x4 rS = rsrc_words(g.w.scale + run0, (nruns - run0) * 4);
+  const i32x4 rS = rsrc_words(g.w.scale + run0, kFP4 ? 0 : (nruns - run0) * 4);
   const i32x4 rX = rsrc_words(g.X, g.M * K * 2);
 
   // DMA roles, per stage (3 copies per wave): the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7;
@@ -161,6 +188,10 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const uint32_t xvoff = (uint32_t)(xrow * K * 2 + 16 * ((lane & 31) ^ (xrow & 15)));
   const int krow = 64 * (wave & 1) + lane;          // row of the block constants copied
   const uint32_t qvoff = (uint32_t)(krow * kblk);
+  // E2M1: waves 6, 7 copy the 16 scale bytes of the stage for rows 64 (w - 6) + L; the lanes of
+  // rows past the 112 (wave 7, lanes 48 ..) copy nothing (their LDS bytes would lie past the slot)
+  const uint32_t gvoff = (uint32_t)(krow * (K / 16));
+  const bool gcopy = !kFP4 || wave == 6 || lane < kRows - 64;
   const uint32_t cdst0 = 1024 * wave, cdst1 = 1024 * (wave + 8), xdst = kXOff + 1024 * wave;
   const uint32_t sdst = kSOff + 256 * (wave & 1), qdst = 1024 * (wave & 1);
 
@@ -186,15 +217,17 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
         dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
       } else if (wave < 6) {
         dma16(rC, dst + cdst1, cvoff1, (uint32_t)(st * 128));
+      } else if (kFP4) {
+        if (gcopy) dma16(rQ, dst + kSOff + 1024 * (wave - 6), gvoff, (uint32_t)(st * 16));
       } else {
         const uint32_t run = (uint32_t)((boff + krow * kblk + 4 * st) >> 8);
         dma4(rS, dst + sdst, run * 4);
       }
     }
-    // kWindowCopies more: the block codes of stages st .. st + 3 (waves 0, 1)
+    // kWindowCopies more: the block codes of stages st .. st + 3 (waves 0, 1; NF4 only)
 #pragma unroll
     for (int c = 0; c < kWindowCopies; ++c)
-      if (window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
+      if (!kFP4 && window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
   };
 
   // LoRA operands of the tile this wave finishes (tile 4 g + j below, g = wave / 4,
@@ -224,20 +257,22 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   dma(1, lds_addr(slot1), false, 0);
   dma(2, lds_addr(slot2), false, 0);
 
-  // Table: uint4 i holds four copies of entry e = i / 16: (level[e >> 4], level[e & 15]) as a
-  // bf16 pair (the high nibble is the earlier element). The 16 levels go through LDS (the start of
-  // slot 3, whose first copy is issued after the first stage barrier) so that the indexed reads
+  // Table (NF4): uint4 i holds four copies of entry e = i / 16: (level[e >> 4], level[e & 15]) as
+  // a bf16 pair (the high nibble is the earlier element). The 16 levels go through LDS (the start
+  // of slot 3, whose first copy is issued after the first stage barrier) so that the indexed reads
   // are LDS reads, not memory loads that would join the copies in flight.
-  float *lv = reinterpret_cast<float *>(slot3);
-  if (tid == 0) {
+  if constexpr (!kFP4) {
+    float *lv = reinterpret_cast<float *>(slot3);
+    if (tid == 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) lv[j] = g.t.level[j];
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int i = tid; i < kTabBytes / 16; i += kThreads) {
-    const int e = i >> 4;
-    const uint32_t v = pack_bf16x2(lv[e >> 4], lv[e & 15]);
-    reinterpret_cast<uint4 *>(stab)[i] = make_uint4(v, v, v, v);
+      for (int j = 0; j < 16; ++j) lv[j] = g.t.level[j];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int i = tid; i < kTabBytes / 16; i += kThreads) {
+      const int e = i >> 4;
+      const uint32_t v = pack_bf16x2(lv[e >> 4], lv[e & 15]);
+      reinterpret_cast<uint4 *>(stab)[i] = make_uint4(v, v, v, v);
+    }
   }
 
   // T from split partials: every workgroup adds them (in split order, as the separate reduction
@@ -292,17 +327,22 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const int grp = wave >> 2, jb = wave & 3;
   const int ntiles = grp == 0 ? 4 : kTiles - 4;
   const int nl = lane & 15, gl = lane >> 4;
+  // E2M1: the lane takes bytes 16 h + 4 gl .. + 3 of the block for slice h (elements
+  // 32 h + 8 gl .. + 7; lanes gl = 0, 1 hold the slice's first group, gl = 2, 3 its second), the
+  // same elements of X, and the block's 4 group scales (saddr).
   uint32_t caddr[4], qaddr[4], saddr[4], xaddr[2];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int row = 16 * (4 * grp + tt) + nl;
-    caddr[tt] = (uint32_t)(row * 128 + 16 * ((2 * jb + (gl >> 1)) ^ ((row >> 1) & 7)) + 8 * (gl & 1));
+    caddr[tt] = kFP4 ? (uint32_t)(row * 128 + 16 * ((2 * jb) ^ ((row >> 1) & 7)) + 4 * gl)
+                     : (uint32_t)(row * 128 + 16 * ((2 * jb + (gl >> 1)) ^ ((row >> 1) & 7)) + 8 * (gl & 1));
     qaddr[tt] = (uint32_t)(row * 16 + jb);          // in the window, + 4 * (stage % 4)
-    saddr[tt] = (uint32_t)(kSOff + row * 4);
+    saddr[tt] = kFP4 ? (uint32_t)(kSOff + row * 16 + 4 * jb) : (uint32_t)(kSOff + row * 4);
   }
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
-    xaddr[hh] = (uint32_t)(kXOff + nl * 512 + 16 * ((8 * jb + 2 * gl + hh) ^ nl));
+    xaddr[hh] = kFP4 ? (uint32_t)(kXOff + nl * 512 + 16 * ((8 * jb + 4 * hh + gl) ^ nl))
+                     : (uint32_t)(kXOff + nl * 512 + 16 * ((8 * jb + 2 * gl + hh) ^ nl));
   const uint32_t lane_off = (uint32_t)lane * 4;
   const char *ctab = reinterpret_cast<const char *>(stab);
 
@@ -310,9 +350,45 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // One stage from slot base sb and window base qb (LDS byte addresses).
-  auto consume = [&](uint32_t sb, uint32_t qb) {
+  // nt: TileCount<4> or TileCount<3> (E2M1: the wave's tile count as a constant, which keeps the
+  // stage one straight block; NF4 takes it from ntiles)
+  auto consume = [&](uint32_t sb, uint32_t qb, auto nt) {
     const bf16x8 x0 = lds_ld<bf16x8>(sb + xaddr[0]);
     const bf16x8 x1 = lds_ld<bf16x8>(sb + xaddr[1]);
+    if constexpr (kFP4) {
+      // X with the halves of each dword swapped (element 2 i + 1 low, 2 i high, as the codes
+      // convert), masked to one group each: xs[q] keeps the lanes holding group q of the block
+      // (slice q / 2, lanes gl < 2 for even q, gl >= 2 for odd q) and zeroes the rest
+      const uint32_t lm = gl < 2 ? 0xFFFFFFFFu : 0u;
+      u32x4 u0 = __builtin_bit_cast(u32x4, x0), u1 = __builtin_bit_cast(u32x4, x1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u0[e] = __builtin_amdgcn_alignbit(u0[e], u0[e], 16);
+        u1[e] = __builtin_amdgcn_alignbit(u1[e], u1[e], 16);
+      }
+      const bf16x8 xs[4] = {__builtin_bit_cast(bf16x8, u0 & lm), __builtin_bit_cast(bf16x8, u0 & ~lm),
+                            __builtin_bit_cast(bf16x8, u1 & lm), __builtin_bit_cast(bf16x8, u1 & ~lm)};
+#pragma unroll
+      for (int tt = 0; tt < decltype(nt)::n; ++tt) {
+        const uint32_t cw0 = lds_ld<uint32_t>(sb + caddr[tt]);
+        const uint32_t cw1 = lds_ld<uint32_t>(sb + (caddr[tt] ^ 16u));
+        const uint32_t sc = lds_ld<uint32_t>(sb + saddr[tt]);
+        const bf16x8 w0 = __builtin_bit_cast(
+            bf16x8, u32x4{cvt_fp4x2<0>(cw0), cvt_fp4x2<1>(cw0), cvt_fp4x2<2>(cw0), cvt_fp4x2<3>(cw0)});
+        const bf16x8 w1 = __builtin_bit_cast(
+            bf16x8, u32x4{cvt_fp4x2<0>(cw1), cvt_fp4x2<1>(cw1), cvt_fp4x2<2>(cw1), cvt_fp4x2<3>(cw1)});
+        // group q's partial sum times its scale (byte q of sc, E4M3)
+        const float sg[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sc, 0), __builtin_amdgcn_cvt_f32_fp8((int)sc, 1),
+                             __builtin_amdgcn_cvt_f32_fp8((int)sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)sc, 3)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 pg = mfma16x16x32(xs[q], q < 2 ? w0 : w1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[tt][v] += sg[q] * pg[v];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       if (tt == 3 && ntiles == 3) break;
@@ -340,27 +416,41 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // landed and everyone is done with stage st - 1, whose slot the next copies overwrite), copies
   // of st + 3, then the stage's MFMAs. The window of stages 4 j .. 4 j + 3 is copied with stage
   // 4 j (issued in stage 4 j - 3, after window j - 2 was last read in stage 4 j - 5).
-  auto stage = [&](int st, int i, int win) {
+  auto stage = [&](int st, int i, int win, auto nt) {
     // copies issued in the two stages before st (phases (i + 2) % 4 and (i + 3) % 4 issue the
     // copies of phases i + 1 and i + 2 = (i + 1) % 4, (i + 2) % 4; the window goes with phase 0)
     const bool w1 = ((i + 1) & 3) == 0, w2 = ((i + 2) & 3) == 0;
-    if ((w1 || w2) && wave < 2)
+    if (!kFP4 && (w1 || w2) && wave < 2)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending + kWindowCopies) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
     const int in = (i + 3) & 3;                      // phase of stage st + 3
     dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
-    consume(opaque(lds_addr(slot(i))), opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i));  // 4 codes of each row
+    consume(opaque(lds_addr(slot(i))), opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i), nt);  // 4 codes of each row
   };
   int st = 0;
+  if constexpr (kFP4) {   // no code windows: a loop over the four slots, one copy per tile count
+    auto walk = [&](auto nt) {
 #pragma unroll 1
-  for (; st + 8 <= nst; st += 8) {
+      for (; st + 4 <= nst; st += 4) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) stage(st + j, j & 3, j >> 2);
+        for (int j = 0; j < 4; ++j) stage(st + j, j, 0, nt);
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (st + j < nst) stage(st + j, j, 0, nt);
+    };
+    if (ntiles == 4) walk(TileCount<4>{}); else walk(TileCount<3>{});
+  } else {
+#pragma unroll 1
+    for (; st + 8 <= nst; st += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) stage(st + j, j & 3, j >> 2, TileCount<4>{});
+    }
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (st + j < nst) stage(st + j, j & 3, j >> 2, TileCount<4>{});
   }
-#pragma unroll
-  for (int j = 0; j < 7; ++j)
-    if (st + j < nst) stage(st + j, j & 3, j >> 2);
 
   // Every wave past its last stage (and every DMA landed: the look-ahead loads wrote into slots
   // nobody reads any more) before the table area is reused for the cross-wave sums.
@@ -377,6 +467,10 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   f32x4 y = red[(t * 4) * 64 + lane];
 #pragma unroll
   for (int jj = 1; jj < 4; ++jj) y += red[(t * 4 + jj) * 64 + lane];
+  if (kFP4) {   // the sums are in units of the tensor scale (1 for an all-zero weight)
+    const float S = *g.w.scale;
+    y *= S > 0.f ? S : 1.f;
+  }
 
   // LoRA term on the matrix cores: s * T[m][:] . B[n][:] for the tile's 16 columns, in steps of
   // 32 ranks (A operand: T row m, B operand: B row n, both rank-contiguous). With r % 8 == 0 the
@@ -442,9 +536,12 @@ hipError_t launch_decode16_fwd(const GemmArgs &ga, hipStream_t st) {
   g.tpart = nullptr;
   g.tsplits = 0;
   g.tout = nullptr;
-  if (ga.M > 16 || !ga.w.dq || ga.w.k % 256 != 0) return hipErrorInvalidValue;
+  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
-  decode16_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  if (ga.w.fp4)
+    decode16_fwd_kernel<true><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  else
+    decode16_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
 }
 
@@ -463,10 +560,13 @@ hipError_t launch_decode16_fwd_tpart(const GemmArgs &ga, const float *tpart, int
   g.tpart = tpart;
   g.tsplits = tsplits;
   g.tout = tout;
-  if (ga.M > 16 || !ga.w.dq || ga.w.k % 256 != 0 || ga.r % 8 != 0 || !tpart || tsplits < 1)
+  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0 || ga.r % 8 != 0 || !tpart || tsplits < 1)
     return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
-  decode16_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  if (ga.w.fp4)
+    decode16_fwd_kernel<true><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  else
+    decode16_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
 }
 

@@ -193,12 +193,6 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   const int kblk = (int)(K / kS);
   const int nsteps = (int)((N + kS - 1) / kS);
   const int last = nsteps - 1;
-  // The tiles of one row block start their walk over n at step rot (and wrap around), tiles of
-  // different row blocks at different steps, so that the workgroups of a launch do not all
-  // request the same offsets at once; rot depends on the row block only (the grouped form with
-  // one expert sums in the plain kernel's order).
-  const int rot = (int)(((m0 - m_lo) / kT) * 5 % nsteps);
-  auto phys = [&](int s) { return s + rot < nsteps ? s + rot : s + rot - nsteps; };
 
   // dY rows m0.. (reduction index n contiguous). Chunks past n = N read the next row's values
   // (finite) and meet weight rows past N, which decode to exact zeros (codes and constants read
@@ -336,9 +330,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   auto body = [&](int s, int P, CStage &cm, CStage &cn) {
     const int s1 = s + 1 < last ? s + 1 : last;
     const int s2 = s + 2 < last ? s + 2 : last;
-    dma_y(phys(s1), ybuf(P ^ 1));
+    dma_y(s1, ybuf(P ^ 1));
     __builtin_amdgcn_sched_barrier(0);   // the DMA stays ahead of the code loads (see the wait)
-    load_c(phys(s2), cm);
+    load_c(s2, cm);
     const uint4 *Y = ybuf(P);
     const uint16_t *W = wbuf(P);
     uint16_t *Wn = wbuf(P ^ 1);
@@ -407,9 +401,9 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   };
 
   CStage c0, c1;
-  dma_y(phys(0), ybuf(0));
-  load_c(phys(0), c0);
-  load_c(phys(nsteps > 1 ? 1 : 0), c1);
+  dma_y(0, ybuf(0));
+  load_c(0, c0);
+  load_c(nsteps > 1 ? 1 : 0, c1);
   decode_all(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

@@ -158,12 +158,16 @@ def test_decode_unit_probe(lib, M, dq, K):
     run_unit_probe(lib, qg, qo, K, M)
 
 
-@pytest.mark.parametrize("K", [256, 1280])
-def test_decode_e2m1_unit_probe(lib, K):
-    """E2M1 weights on the decode shape: e2m1 * s is exact in bf16 and S multiplies the float32
-    sum once, so Y = bf16(deq(W)) at any group scale (bit for bit up to the sign of zero)."""
-    N, M = 200, 16
-    W = wl.normal_bf16(950 + K, (N, K), 0.02)
+@pytest.mark.parametrize("nst", [1, 2, 3, 4, 5, 7, 8, 9, 12, 17])
+@pytest.mark.parametrize("N", [336, 200])
+def test_decode_e2m1_unit_probe(lib, nst, N):
+    """E2M1 weights on the stream kernel (M <= 16, K % 256 == 0; stages of 256 elements, a
+    4-stage loop): a group's product e2m1 * s is exact in float32 and S multiplies the sum once,
+    so Y = bf16(deq(W)) at any group scale (bit for bit up to the sign of zero), for every stage
+    count around the loop and a ragged last workgroup (N = 200)."""
+    K, M = 256 * nst, 16
+    say(f"E2M1 stream-kernel unit probe stages={nst} K={K} N={N}")
+    W = wl.normal_bf16(950 + K + N, (N, K), 0.02)
     qg = lib.fp4_quantize(W.to(DEV))
     want_full = nf4.bf16_bits(fp4.dequantize_f32(fp4.quantize(W.float().numpy())))
     kblk = K // 64

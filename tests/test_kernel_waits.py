@@ -54,33 +54,41 @@ def kernels(lines):
 
 
 def loops(body):
-    """Innermost loop bodies laid out from their header down to their backward branch, as lists
-    of (kind, text, in_asm). (A loop whose latch block sits above its header, such as a short
-    search loop, is left out: its body is not one straight run of lines.)"""
-    res = []
+    """Innermost loops, each as the list of (kind, text, in_asm) of one iteration in execution
+    order. Blocks carry the compiler's loop annotation ('Inner Loop Header' on the header, 'in
+    Loop: Header=...' on the other blocks of the innermost loop holding them); an iteration runs
+    from the header down through the loop's blocks below it, then through those laid out above it
+    (a latch block placed above the header falls through into it)."""
+    blocks = []                       # (first line, innermost loop header name or None, is header)
     for i, ln in enumerate(body):
-        if ln.startswith(".LBB") and "Inner Loop Header" in ln:
-            lab = ln.split(":")[0]
-            seq, inasm, closed = [], False, False
-            for t in body[i + 1:]:
+        m = re.match(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)", ln)
+        if not m:
+            continue
+        if "Inner Loop Header" in ln:
+            blocks.append((i, ln.split(":")[0][len(".L"):], True))
+        else:
+            h = re.search(r"in Loop: Header=(\S+)", ln)
+            blocks.append((i, h.group(1) if h else None, False))
+    ends = [b[0] for b in blocks[1:]] + [len(body)]
+    res = []
+    for hb, (start, name, is_hdr) in enumerate(blocks):
+        if not is_hdr:
+            continue
+        members = [k for k, b in enumerate(blocks) if b[1] == name]
+        order = [k for k in members if k >= hb] + [k for k in members if k < hb]
+        seq, inasm = [], False
+        for k in order:
+            for t in body[blocks[k][0]:ends[k]]:
                 t = t.strip()
-                if "Loop Header" in t or t.startswith("s_endpgm"):
-                    break
                 if t == ";;#ASMSTART":
                     inasm = True
-                    continue
-                if t == ";;#ASMEND":
+                elif t == ";;#ASMEND":
                     inasm = False
-                    continue
-                if (t.startswith("s_cbranch") or t.startswith("s_branch")) and t.endswith(lab):
-                    closed = True
-                    break
-                if VMEM.match(t):
+                elif VMEM.match(t):
                     seq.append(("mem", t, inasm))
                 elif re.match(r"s_waitcnt.*vmcnt\(\d+\)", t):
                     seq.append(("wait", t, inasm))
-            if closed:
-                res.append(seq)
+        res.append(seq)
     return res
 
 
@@ -135,15 +143,19 @@ def test_stream_kernel_stage_waits(tmp_path):
     src = open(os.path.join(CSRC, "decode16.hip")).read()
     const = {k: int(v) for k, v in re.findall(r"constexpr int (kStageCopies|kWindowCopies) = (\d+);", src)}
     pending = 2 * const["kStageCopies"]
-    allowed = {pending, pending + const["kWindowCopies"], 0}
-    ks = kernels(device_asm("decode16.hip", str(tmp_path)))
-    (name, body), = [(k, b) for k, b in ks.items() if "decode16" in k]
-    mls = main_loops(body)
-    assert len(mls) == 1
-    seq = mls[0]
-    waits = [t for k, t, a in seq if k == "wait"]
-    assert waits and all(a for k, t, a in seq if k == "wait"), "compiler waits in the stage loop"
-    assert {vmcnt(t) for t in waits} <= allowed, waits
-    mem = [t for k, t, a in seq if k == "mem"]
-    assert mem and all(t.endswith(" lds") and a for (k, t, a) in seq if k == "mem"), \
-        "the stage loop must hold only the hand-issued copies"
+    ks = {k: b for k, b in kernels(device_asm("decode16.hip", str(tmp_path))).items() if "decode16" in k}
+    assert len(ks) == 2, sorted(ks)      # the NF4 (Lb0) and E2M1 (Lb1) instances
+    for name, body in ks.items():
+        fp4 = "ILb1E" in name
+        # the E2M1 form copies no windows of block codes: only the stage count
+        allowed = {pending, 0} if fp4 else {pending, pending + const["kWindowCopies"], 0}
+        mls = main_loops(body)
+        # the E2M1 form has one stage loop per tile count of the wave (4 or 3)
+        assert len(mls) == (2 if fp4 else 1), (name, len(mls))
+        for seq in mls:
+            waits = [t for k, t, a in seq if k == "wait"]
+            assert waits and all(a for k, t, a in seq if k == "wait"), f"{name}: compiler waits in the stage loop"
+            assert {vmcnt(t) for t in waits} <= allowed, (name, waits)
+            mem = [t for k, t, a in seq if k == "mem"]
+            assert mem and all(t.endswith(" lds") and a for (k, t, a) in seq if k == "mem"), \
+                f"{name}: the stage loop must hold only the hand-issued copies"
