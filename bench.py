@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None,
                     help="run one workload alone (default: the five layer workloads)")
+    ap.add_argument("--order", default=None,
+                    help="comma-separated layer workloads to run, in this order (default: the five, "
+                         "headline first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the vendor-GEMM / MFMA-loop / device-copy reference measurements")
@@ -897,7 +900,9 @@ def main():
     if args.workload is not None and args.workload not in wl.WORKLOADS:
         raise SystemExit(f"unknown workload {args.workload}; one of "
                          f"{sorted(wl.WORKLOADS) + sorted(wl.PAIRS) + sorted(wl.MOES)}")
-    names = [args.workload] if args.workload else list(DEFAULT_CONFIGS)
+    names = [args.workload] if args.workload else (args.order.split(",") if args.order else list(DEFAULT_CONFIGS))
+    if not args.workload and HEADLINE not in names:
+        raise SystemExit(f"--order must include the headline workload {HEADLINE}")
     head = args.workload or HEADLINE
     configs, extra = {}, {}
     for name in names:

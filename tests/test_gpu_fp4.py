@@ -69,8 +69,8 @@ LAYER_CASES = [
     (5, 768, 232, 12, 0.5),          # r % 8 != 0: T by the separate projection, the LoRA term
                                      # element by element; ragged last workgroup
     (12, 2304, 448, 0, 1.0),         # no adapters, four full workgroups
-    (9, 320, 136, 8, 1.0),           # K % 256 != 0: the other decode kernel's E2M1 form
-    (40, 512, 136, 8, 0.5),          # 16 < M <= 48: the large-M kernel (E2M1 decode form: M <= 16)
+    (9, 320, 136, 8, 1.0),           # K % 256 != 0: the large-M kernel's E2M1 form
+    (40, 512, 136, 8, 0.5),          # 16 < M <= 48: the large-M kernel (E2M1 stream form: M <= 16)
     (257, 1024, 64, 0, 1.0),         # no adapters
     (130, 512, 136, 128, 0.25),      # the largest rank
 ]
