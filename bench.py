@@ -94,6 +94,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", default=None, metavar="DIR",
                     help="summarise a rocprofv3 kernel trace of this command (no GPU needed)")
+    ap.add_argument("--summarize-counters", default=None, nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs of this command (no GPU needed)")
     return ap.parse_args()
 
 
@@ -226,11 +228,23 @@ def step_calls(L):
             ("bwd_dx", L.bwd_dx)]
 
 
+HOLD_CYCLES = 10_000_000   # ~4 ms of GPU spin ahead of each timed region
+
+
+def hold_stream():
+    """Keep the launch stream busy (a spin kernel) while the host enqueues the timed launches and
+    their events, so that no timed interval contains host issue time: the short launches of the
+    decode and small workloads are issued more slowly than they run."""
+    import torch
+    torch.cuda._sleep(HOLD_CYCLES)
+
+
 def time_steps(L, calls, steps, warmup):
-    """warmup + steps steps, twice. First the plain steps between two synchronisations: the
-    host-clock time per step and the GPU time per step (one HIP event pair around the whole
-    timed region on the launch stream). Then the same steps with a HIP event pair around every
-    call: the per-call times (ms). Returns (host ms/step, GPU ms/step, per-call stats)."""
+    """warmup + steps steps, three times. First the plain steps between two synchronisations: the
+    host-clock time per step. Then the GPU time per step (one HIP event pair around the whole
+    timed region on the launch stream, the launches queued behind a spin kernel). Then the same
+    steps with a HIP event pair around every call: the per-call times (ms). Returns (host
+    ms/step, GPU ms/step, per-call stats)."""
     import torch
     for i in range(warmup):
         for _, c in calls:
@@ -245,8 +259,19 @@ def time_steps(L, calls, steps, warmup):
     b.record(L.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    host_ms, gpu_ms = (t1 - t0) * 1e3 / steps, a.elapsed_time(b) / steps
+    host_ms = (t1 - t0) * 1e3 / steps
+    # the GPU time per step: the same steps again, enqueued behind a spin kernel so that the GPU
+    # runs them back to back whatever the host's issue rate
+    hold_stream()
+    a.record(L.stream)
+    for s in range(steps):
+        for _, c in calls:
+            c(warmup + s)
+    b.record(L.stream)
+    torch.cuda.synchronize()
+    gpu_ms = a.elapsed_time(b) / steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    hold_stream()
     for s in range(steps):
         e = ev[s]
         e[0].record(L.stream)
@@ -261,18 +286,34 @@ def time_steps(L, calls, steps, warmup):
 
 
 def time_call(L, fn, steps, warmup):
-    """HIP-event times (ms) of one call over rotating weight copies."""
+    """HIP-event times (ms) of one call over rotating weight copies. The mean is the average
+    launch duration: one event pair around `steps` back-to-back launches, queued behind a spin
+    kernel (no host gaps, no per-launch event overhead, which is about 1.5 us and would inflate a
+    30 us launch by 5%). The spread (median, p10, p90) comes from an event pair around each
+    launch of a second pass; its own mean is kept as mean_per_launch_events."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_stream()
+    a.record(L.stream)
+    for s in range(steps):
+        fn(warmup + s)
+    b.record(L.stream)
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    hold_stream()
     for s, (a, b) in enumerate(ev):
         a.record(L.stream)
-        fn(warmup + s)
+        fn(warmup + steps + s)
         b.record(L.stream)
     torch.cuda.synchronize()
-    return stats([a.elapsed_time(b) for a, b in ev])
+    st = stats([a.elapsed_time(b) for a, b in ev])
+    st["mean_per_launch_events"] = st["mean"]
+    st["mean"] = mean
+    return st
 
 
 def source_sha(name):
@@ -838,11 +879,20 @@ def trace_groups():
     return out
 
 
+def timed_launches(v, steps, warmup):
+    """The launches of a fused kernel that bench.py's roofline times, in launch order. time_steps
+    issues warmup + 3 steps launches of each call of the step (host pass, GPU pass, per-call
+    pass); a forward-only workload then times its fused launch alone (time_call: warmup +
+    2 steps launches), and that block is the roofline's. Warm-up launches are left out."""
+    if len(v) >= 2 * warmup + 5 * steps:             # forward only: the time_call block
+        return v[warmup + 3 * steps + warmup:]
+    return v[warmup:warmup + 3 * steps] or v
+
+
 def summarize_trace(path, steps, warmup):
     """Per-(kernel, grid) durations from a rocprofv3 kernel trace (CSV) of this command: the fused
     kernels of different workloads share names, so they are told apart by their workgroup count.
-    mean_timed leaves out the warm-up launches (in every run of warmup + steps launches of a
-    fused kernel, the first warmup), as the bench's own means do."""
+    mean_timed leaves out the warm-up launches (see timed_launches), as the bench's own means do."""
     files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no *kernel_trace.csv under {path}")
@@ -868,7 +918,7 @@ def summarize_trace(path, steps, warmup):
         v = [d for _, d in sorted(tv)]
         tag = next((f"{wl_}/{launch}" for (part, n), (wl_, launch) in known.items()
                     if n == wgs and part in name), "")
-        timed = [d for i, d in enumerate(v) if i % (warmup + steps) >= warmup] if tag else v
+        timed = timed_launches(v, steps, warmup) if tag else v
         rows.append((sum(v), name, wgs, v, timed or v, tag))
     for _, name, wgs, v, timed, tag in sorted(rows, reverse=True):
         s = stats(v)
@@ -876,10 +926,63 @@ def summarize_trace(path, steps, warmup):
               f"{min(v):10.2f} {max(v):10.2f}  {wgs:6d}  {tag:<34} {name[:100]}")
 
 
+def summarize_counters(paths):
+    """Per-(kernel, grid) means of rocprofv3 --pmc counters (run_counter_collection.csv under each
+    path), with derived figures where their inputs were collected: matrix-core busy share and
+    clock (SQ counters summed over the 1024 SIMDs, GRBM_GUI_ACTIVE over the 8 XCDs), vector
+    instructions per MFMA, LDS busy share, and HBM-side KiB per dispatch."""
+    import collections
+    rows = collections.defaultdict(lambda: collections.defaultdict(list))
+    known = trace_groups()
+    for path in paths:
+        for fn in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+            per = collections.defaultdict(lambda: collections.defaultdict(float))
+            meta = {}
+            with open(fn, newline="") as f:
+                for r in csv.DictReader(f):
+                    wgs = max(1, int(float(r["Grid_Size"])) // max(1, int(float(r["Workgroup_Size"]))))
+                    key = (r["Kernel_Name"], wgs)
+                    per[(key, r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+                    meta[(key, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for (key, d), cs in per.items():
+                for c, v in cs.items():
+                    rows[key][c].append(v)
+                rows[key]["_us"].append(meta[(key, d)])
+    print("# means per dispatch; durations are the profiler's (counter collection replays kernels)")
+    for (name, wgs), cs in sorted(rows.items(), key=lambda kv: -sum(kv[1]["_us"])):
+        tag = next((f"{w}/{launch}" for (part, n), (w, launch) in known.items() if n == wgs and part in name), "")
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        out = [f"dispatches {len(cs['_us'])}", f"us {m['_us']:.1f}"]
+        gui = m.get("GRBM_GUI_ACTIVE")
+        if gui:
+            out.append(f"clk_GHz {gui / 8 / (m['_us'] * 1e3):.3f}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                out.append(f"mfma_busy {m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (gui / 8):.3f}")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+                out.append(f"coexec {m['SQ_VALU_MFMA_COEXEC_CYCLES'] / 1024 / (gui / 8):.3f}")
+            if "SQ_LDS_IDX_ACTIVE" in m:
+                out.append(f"lds_busy {m['SQ_LDS_IDX_ACTIVE'] / 256 / (gui / 8):.3f}")
+            if "SQ_ACTIVE_INST_VALU" in m:
+                out.append(f"valu_busy {4 * m['SQ_ACTIVE_INST_VALU'] / 1024 / (gui / 8):.3f}")
+        if "SQ_INSTS_MFMA" in m and "SQ_INSTS_VALU" in m and m["SQ_INSTS_MFMA"]:
+            out.append(f"valu_per_mfma {(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_INSTS_MFMA']:.2f}")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in m:
+                out.append(f"{c}_KiB {m[c]:.0f}")
+        for c in sorted(m):
+            if c.startswith("SQ_") or c.startswith("TCC_") or c.startswith("TCP_"):
+                out.append(f"{c} {m[c]:.4g}")
+        print(f"{tag or '-'}  wgs {wgs}  {name[:90]}")
+        print("    " + "  ".join(out))
+
+
 def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
