@@ -861,16 +861,16 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 5}), flush=True)
 
 
-def trace_groups():
-    """(kernel name part, workgroups) -> (workload, launch) for the fused launches of the default
-    run: the tile counts of the 256 x 256 forward and dX kernels and of the 112-row stream
-    kernel, from the workload shapes."""
+def trace_groups(names=DEFAULT_CONFIGS):
+    """(kernel name part, workgroups) -> (workload, launch) for the fused launches of a run of the
+    named layer workloads (default: the default run): the tile counts of the 256 x 256 forward
+    and dX kernels and of the 112-row stream kernel, from the workload shapes."""
     import workloads as wl
     out = {}
-    for name in DEFAULT_CONFIGS:
+    for name in names:
         w = wl.WORKLOADS[name]
         cd = lambda a, b: -(-a // b)
-        if w.M <= 16 and w.dq_block and w.K % 256 == 0:
+        if w.M <= 16 and (w.dq_block or w.fmt == "e2m1") and w.K % 256 == 0:
             out[("decode16_fwd_kernel", cd(w.N, 112))] = (name, "qlora_fwd_fused (decode)")
         elif w.M > 48 or w.K % 256:
             out[("fwd_fused_kernel", cd(w.N, 256) * cd(w.M, 256))] = (name, "qlora_fwd_fused")
@@ -889,7 +889,7 @@ def timed_launches(v, steps, warmup):
     return v[warmup:warmup + 3 * steps] or v
 
 
-def summarize_trace(path, steps, warmup):
+def summarize_trace(path, steps, warmup, names=DEFAULT_CONFIGS):
     """Per-(kernel, grid) durations from a rocprofv3 kernel trace (CSV) of this command: the fused
     kernels of different workloads share names, so they are told apart by their workgroup count.
     mean_timed leaves out the warm-up launches (see timed_launches), as the bench's own means do."""
@@ -908,7 +908,7 @@ def summarize_trace(path, steps, warmup):
                     wgs *= -(-grid // max(wg, 1))
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
                 groups.setdefault((name, wgs), []).append((int(row["Start_Timestamp"]), dur))
-    known = trace_groups()
+    known = trace_groups(names)
     print(f"# source: {', '.join(os.path.relpath(f, path) for f in files)}")
     print("# durations in microseconds (End_Timestamp - Start_Timestamp of each dispatch); wgs = workgroups")
     print(f"{'calls':>5} {'mean_us':>10} {'mean_timed':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10}"
@@ -979,7 +979,9 @@ def summarize_counters(paths):
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        import workloads as wl
+        names = [args.workload] if args.workload in wl.WORKLOADS else DEFAULT_CONFIGS
+        summarize_trace(args.summarize_trace, args.steps, args.warmup, names)
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
