@@ -171,6 +171,10 @@ size_t qlora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
  * When r > 0 the call leaves U (bf16 [m, r], row-major) in the first m*r*2 bytes of ws, where
  * qlora_bwd_dx can take it: qlora_bwd with dX == NULL followed by qlora_bwd_dx is the same work
  * as one qlora_bwd call.
+ * Non-finite inputs: when n % 64 != 0, dX row i may also multiply zeros by the first
+ * 64 - n % 64 values of dY row i + 1 (the last 64-column step of the reduction reads whole
+ * 128-byte lines); an Inf or NaN among those values turns dX row i into NaN. With finite dY the
+ * result is as stated.
  * Errors: as qlora_fwd, plus NF4_EINVAL when ws is smaller than qlora_bwd_workspace_bytes. */
 int qlora_bwd(const void *dY, const void *X, int64_t m, const nf4_tensor *W, const void *A,
               const void *B, int32_t r, float s, const void *T, void *dX, void *dA, void *dB,
