@@ -325,9 +325,9 @@ __global__ __launch_bounds__(256) void moe_plan_kernel(const int64_t *__restrict
                                                        void *table) {
   __shared__ int64_t cnt[kMaxExperts];
   const int t = threadIdx.x;
-  if (t < E) {
+  if (t < E) {   // each count clamped to [0, m] first, so the running sums below cannot overflow
     const int64_t c = dcounts[t];
-    cnt[t] = c > 0 ? c : 0;
+    cnt[t] = c > 0 ? (c < m ? c : m) : 0;
   }
   __syncthreads();
   if (t != 0) return;

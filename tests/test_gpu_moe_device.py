@@ -144,3 +144,24 @@ def test_graph_replays_follow_device_routing(lib):
         for name, want in (("Y", Yh), ("T", Th), ("dX", dXh), ("dA", dAh), ("dB", dBh)):
             assert torch.equal(out[name].view(torch.int16), want.view(torch.int16)), \
                 f"replay {rep}: {name} differs from the host-routed calls"
+
+
+def test_device_counts_are_clipped(lib):
+    """Counts that do not sum to m: negative counts count as 0 and the experts' row ranges are
+    clipped at m, so the result equals the host-routed call with the clipped counts; a count
+    near the int64 limit does not overflow the running offsets."""
+    E, M, K, N, r, s = 6, 300, 256, 64, 8, 1.0
+    raw = [5, -3, 1000, 2 ** 62, 7, 0]
+    clipped = [5, 0, 295, 0, 0, 0]
+    say(f"moe device routing with clipped counts {raw} -> {clipped}")
+    X, W, A, B, dY = layer(clipped, K, N, r, 4242)
+    q = lib.nf4_quantize(W.to(DEV), 256)
+    Xd, dYd, Ad, Bd = X.to(DEV), dY.to(DEV), A.to(DEV), B.to(DEV)
+    Yh, Th = lib.qlora_moe_fwd(Xd, clipped, q, Ad, Bd, s)
+    dXh, dAh, dBh = lib.qlora_moe_bwd(dYd, Xd, clipped, q, Ad, Bd, s, Th)
+    cd = torch.tensor(raw, dtype=torch.int64, device=DEV)
+    o = device_calls(lib, Xd, dYd, cd, q, Ad, Bd, s, M, E, N, K, r)
+    torch.cuda.synchronize()
+    for name, got, want in (("Y", o["Y"], Yh), ("T", o["T"], Th), ("dX", o["dX"], dXh),
+                            ("dA", o["dA"], dAh), ("dB", o["dB"], dBh)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{name}: clipped routing differs"
