@@ -198,7 +198,8 @@ int qlora_bwd_dx(const void *dY, int64_t m, const nf4_tensor *W, const void *U, 
  * Layout: Wgu is ONE NF4 tensor [2n, k] quantised from the stacked weight [Wg; Wu] (rows 0 .. n-1
  * gate, n .. 2n-1 up: the usual fused gate_up layout); Agu bf16 [2r, k] is [Ag; Au]; Bg and Bu
  * are bf16 [n, r] each. The pair runs as one stacked QLoRA layer with the block-diagonal up
- * projection [[Bg, 0], [0, Bu]] (built in the workspace), so its GEMMs are qlora_fwd's and
+ * projection [[Bg, 0], [0, Bu]] (applied by the pair's fused launch as it stages B; built in the
+ * workspace for the decode shapes and the backward), so its GEMMs are qlora_fwd's and
  * qlora_bwd's kernels on [2n, k]. Requires n % 8 == 0 and 0 <= r <= 64 (2r <= 128).
  *
  * Bytes of device workspace qlora_swiglu_fwd and qlora_swiglu_bwd need (the same for both). */
@@ -216,6 +217,17 @@ size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
 int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
                      const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
                      void *Tgu, void *ws, size_t ws_bytes, void *stream);
+
+/* qlora_swiglu_fwd_fused: the pair's forward in ONE kernel launch given Tgu bf16 [m, 2r]
+ * (= [X Ag^T | X Au^T], as qlora_swiglu_fwd returns it; NULL when r == 0): Yg and Yu with the
+ * NF4 decode inside the GEMM and the rank-r terms as extra reduction steps of the same tile, and
+ * H = silu(Yg) * Yu from their float32 sums in the epilogue [same passages as qlora_swiglu_fwd].
+ * Any m >= 1 (this is the launch qlora_swiglu_fwd makes above the decode shapes, whose H and Ygu
+ * it reproduces bit for bit for the same Tgu). No workspace.
+ * Errors: as qlora_swiglu_fwd (no workspace checks). */
+int qlora_swiglu_fwd_fused(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Tgu,
+                           const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
+                           void *stream);
 
 /* Backward for the upstream gradient dH bf16 [m, n], given Ygu and Tgu from the forward (Tgu may
  * be NULL: recomputed):

@@ -32,6 +32,7 @@ NF4_BF16, NF4_F32 = 0, 1
 EXPORTED = ("nf4_quantize", "nf4_dequantize", "nf4_codebook", "qlora_fwd_workspace_bytes",
             "qlora_fwd", "qlora_lora_down", "qlora_fwd_fused", "qlora_bwd_workspace_bytes",
             "qlora_bwd", "qlora_bwd_dx", "qlora_swiglu_workspace_bytes", "qlora_swiglu_fwd",
+            "qlora_swiglu_fwd_fused",
             "qlora_swiglu_bwd", "qlora_merge", "qlora_moe_workspace_bytes", "qlora_moe_fwd",
             "qlora_moe_fwd_fused", "qlora_moe_bwd", "qlora_moe_workspace_bytes_dev", "qlora_moe_fwd_dev",
             "qlora_moe_bwd_dev", "qlora_fwd_noalloc", "nf4_last_error")
@@ -82,6 +83,7 @@ def library() -> ctypes.CDLL:
                                              sz, vp]),
         "qlora_swiglu_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_swiglu_fwd": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "qlora_swiglu_fwd_fused": (ctypes.c_int, [vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp]),
         "qlora_swiglu_bwd": (ctypes.c_int, [vp, vp, i64, P, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]),
         "nf4_last_error": (ctypes.c_char_p, []),
@@ -498,6 +500,29 @@ def qlora_swiglu_fwd(X: torch.Tensor, q: NF4Tensor, Agu: Optional[torch.Tensor],
                                 float(s), _ptr(H), _ptr(Ygu), _ptr(Tgu), _ptr(ws), wsb,
                                 _stream(dev)))
     return H, Ygu, Tgu
+
+
+def qlora_swiglu_fwd_fused(X: torch.Tensor, q: NF4Tensor, Tgu: Optional[torch.Tensor],
+                           Bg: Optional[torch.Tensor], Bu: Optional[torch.Tensor], s: float):
+    """(H, Ygu) of the gate/up pair in one kernel launch, given Tgu = [X Ag^T | X Au^T] [m, 2r]."""
+    m = X.shape[0]
+    if q.n % 2:
+        raise ValueError(f"the stacked weight must have an even number of rows (got {q.n})")
+    n = q.n // 2
+    r = 0 if Tgu is None else Tgu.shape[1] // 2
+    _need(X, "X", torch.bfloat16, (m, q.k))
+    if r:
+        _need(Tgu, "Tgu", torch.bfloat16, (m, 2 * r))
+        _need(Bg, "Bg", torch.bfloat16, (n, r))
+        _need(Bu, "Bu", torch.bfloat16, (n, r))
+    dev = X.device
+    H = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    Ygu = torch.empty(m, 2 * n, dtype=torch.bfloat16, device=dev)
+    st = q.c_struct()
+    _check(library().qlora_swiglu_fwd_fused(_ptr(X), m, ctypes.byref(st), _ptr(Tgu if r else None),
+                                            _ptr(Bg if r else None), _ptr(Bu if r else None), r,
+                                            float(s), _ptr(H), _ptr(Ygu), _stream(dev)))
+    return H, Ygu
 
 
 def qlora_swiglu_bwd(dH: torch.Tensor, X: torch.Tensor, q: NF4Tensor, Agu: Optional[torch.Tensor],

@@ -652,6 +652,32 @@ size_t qlora_swiglu_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) 
   return swi_ws(m, n, k, r).total;
 }
 
+// One launch of the fused kernel in its pair form: Yg, Yu and, in the epilogue, H; the up
+// projection is the block-diagonal [[Bg, 0], [0, Bu]] applied by the kernel.
+static int swiglu_pair_launch(const void *X, int64_t m, const nf4_tensor *Wgu, const void *T,
+                              const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
+                              hipStream_t sm, const char *what) {
+  const int64_t n = Wgu->n / 2, k = Wgu->k;
+  nf4q::GemmArgs g;
+  g.a_side = (const uint16_t *)X;
+  g.lda = k;
+  g.lora_a = r > 0 ? (const uint16_t *)T : nullptr;
+  g.lora_b = r > 0 ? (const uint16_t *)Bg : nullptr;
+  g.lora_b2 = r > 0 ? (const uint16_t *)Bu : nullptr;
+  g.w = desc(Wgu);
+  g.M = m;
+  g.C = n;
+  g.R = k;
+  g.r = 2 * r;
+  g.s = s;
+  g.out = (uint16_t *)Ygu;
+  g.ldo = 2 * n;
+  g.t = tables();
+  g.hout = (uint16_t *)H;
+  g.ldh = n;
+  return hip_status(nf4q::launch_gemm_fwd_pair(g, sm), what);
+}
+
 int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Agu,
                      const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
                      void *Tgu, void *ws, size_t ws_bytes, void *stream) {
@@ -665,46 +691,50 @@ int qlora_swiglu_fwd(const void *X, int64_t m, const nf4_tensor *Wgu, const void
   const SwiWs lay = swi_ws(m, n, Wgu->k, r);
   hipStream_t sm = (hipStream_t)stream;
   char *base = (char *)ws;
-  uint16_t *B2 = r > 0 ? (uint16_t *)base : nullptr;
   void *T = r > 0 ? (Tgu ? Tgu : (void *)(base + lay.b2)) : nullptr;
-  if (r > 0) {
-    hipError_t e = nf4q::launch_blockdiag((const uint16_t *)Bg, (const uint16_t *)Bu, n, r, B2, sm);
-    if (e != hipSuccess) return hip_status(e, "qlora_swiglu_fwd launch");
-  }
   const int64_t k = Wgu->k;
-  // shapes the stacked layer sends to the decode kernels (M <= 48): the stacked forward, then the
-  // activation kernel
+  // shapes the stacked layer sends to the decode kernels (M <= 48): the stacked forward with the
+  // block-diagonal up projection built in the workspace, then the activation kernel
   if (m <= (Wgu->block == 64 ? nf4q::kDecodeMaxM : 16) && k % 256 == 0) {
+    uint16_t *B2 = r > 0 ? (uint16_t *)base : nullptr;
+    if (r > 0) {
+      hipError_t e = nf4q::launch_blockdiag((const uint16_t *)Bg, (const uint16_t *)Bu, n, r, B2, sm);
+      if (e != hipSuccess) return hip_status(e, "qlora_swiglu_fwd launch");
+    }
     st = qlora_fwd(X, m, Wgu, r > 0 ? Agu : nullptr, B2, 2 * r, s, Ygu, T,
                    lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd, stream);
     if (st) return st;
     return hip_status(nf4q::launch_swiglu_fwd((const uint16_t *)Ygu, m, n, (uint16_t *)H, sm),
                       "qlora_swiglu_fwd launch");
   }
-  // otherwise T = X Agu^T, then ONE launch of the fused kernel in its pair form: Yg, Yu and, in
-  // the epilogue, H
+  // otherwise T = X Agu^T, then the pair's one fused launch
   if (r > 0) {
     st = qlora_lora_down(X, m, k, Agu, 2 * r, T, lay.fwd ? base + lay.b2 + lay.t : nullptr, lay.fwd,
                          stream);
     if (st) return st;
   }
-  nf4q::GemmArgs g;
-  g.a_side = (const uint16_t *)X;
-  g.lda = k;
-  g.lora_a = r > 0 ? (const uint16_t *)T : nullptr;
-  g.lora_b = B2;
-  g.w = desc(Wgu);
-  g.M = m;
-  g.C = n;
-  g.R = k;
-  g.r = 2 * r;
-  g.s = s;
-  g.out = (uint16_t *)Ygu;
-  g.ldo = 2 * n;
-  g.t = tables();
-  g.hout = (uint16_t *)H;
-  g.ldh = n;
-  return hip_status(nf4q::launch_gemm_fwd_pair(g, sm), "qlora_swiglu_fwd launch");
+  return swiglu_pair_launch(X, m, Wgu, T, Bg, Bu, r, s, H, Ygu, sm, "qlora_swiglu_fwd launch");
+}
+
+int qlora_swiglu_fwd_fused(const void *X, int64_t m, const nf4_tensor *Wgu, const void *Tgu,
+                           const void *Bg, const void *Bu, int32_t r, float s, void *H, void *Ygu,
+                           void *stream) {
+  int st = check_weight(Wgu);
+  if (st) return st;
+  if (Wgu->n % 2) return fail(NF4_EINVAL, "Wgu must hold 2n rows (got %lld)", (long long)Wgu->n);
+  const int64_t n = Wgu->n / 2;
+  if (n % 8) return fail(NF4_EUNSUPPORTED, "n must be a multiple of 8 (got %lld)", (long long)n);
+  if (r < 0 || r > 64) return fail(NF4_EINVAL, "r must lie in [0, 64] (got %d)", r);
+  st = check_layer(X, m, Wgu, Tgu, Tgu, 2 * r);   // X, the stacked weight, Tgu
+  if (st) return st;
+  if (r > 0) {
+    if (!Bg || !Bu) return fail(NF4_EINVAL, "Bg and Bu must be non-NULL when r > 0");
+    if (!aligned16(Bg) || !aligned16(Bu)) return fail(NF4_EINVAL, "Bg and Bu must be 16-byte aligned");
+  }
+  if (!H || !aligned16(H) || !Ygu || !aligned16(Ygu))
+    return fail(NF4_EINVAL, "H and Ygu must be non-NULL and 16-byte aligned");
+  return swiglu_pair_launch(X, m, Wgu, Tgu, Bg, Bu, r, s, H, Ygu, (hipStream_t)stream,
+                            "qlora_swiglu_fwd_fused launch");
 }
 
 int qlora_swiglu_bwd(const void *dH, const void *X, int64_t m, const nf4_tensor *Wgu,

@@ -138,6 +138,76 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
   }
 }
 
+// LoRA step staging of the gate/up pair. The A side is T as in stage_lora (columns jb .. of the
+// 2 r' ranks [X Ag^T | X Au^T]); on the B side tile rows 0..127 take Bg row n0 + row at ranks
+// 0 .. r' - 1 and rows 128..255 Bu row n0 + row - 128 at ranks r' .. 2 r' - 1, zero at the other
+// half's ranks: the block-diagonal [[Bg, 0], [0, Bu]] without storing it (r' = g.r / 2).
+__device__ void stage_lora_pair(const GemmArgs &g, float sb, int64_t m0, int64_t n0, int64_t rows_n,
+                                int64_t rows_m, int jb, int nch, uint4 *sA, uint4 *sB) {
+  const int tid = threadIdx.x;
+  const int c = tid & 7, row0 = tid >> 3;
+  if (c >= nch) return;
+  const int j0 = jb + c * 8;
+  const int rh = g.r / 2;
+  const bool vec = (rh & 7) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(g.lora_a) | reinterpret_cast<uintptr_t>(g.lora_b) |
+                     reinterpret_cast<uintptr_t>(g.lora_b2)) & 15) == 0;
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.lora_a + m0 * g.r, rows_m * g.r * 2);
+    const int64_t v = rows_n < 128 ? (rows_n > 0 ? rows_n : 0) : 128;
+    const __amdgpu_buffer_rsrc_t rBg = make_rsrc(g.lora_b + n0 * rh, v * rh * 2);
+    const __amdgpu_buffer_rsrc_t rBu = make_rsrc(g.lora_b2 + n0 * rh, v * rh * 2);
+    u32x4 ta[kChunks / kThreads], tb[kChunks / kThreads];
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+      const int row = row0 + 64 * i;
+      const int jj = i < 2 ? j0 : j0 - rh;   // rank within the row's own half (rows 128.. are up)
+      const uint32_t off = j0 < g.r ? (uint32_t)(row * g.r + j0) * 2 : 0x80000000u;
+      const uint32_t offb = jj >= 0 && jj < rh ? (uint32_t)((row & 127) * rh + jj) * 2 : 0x80000000u;
+      ta[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+      tb[i] = __builtin_amdgcn_raw_buffer_load_b128(i < 2 ? rBg : rBu, offb, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+      const int row = row0 + 64 * i;
+      uint32_t wb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wb[e] = pack_bf16x2(sb * bf16_lo(tb[i][e]), sb * bf16_hi(tb[i][e]));
+      sA[swzf(row, c)] = make_uint4(ta[i][0], ta[i][1], ta[i][2], ta[i][3]);
+      sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int i = 0; i < kChunks / kThreads; ++i) {
+    const int row = row0 + 64 * i;
+    const bool up = row >= 128;
+    const uint16_t *Bh = up ? g.lora_b2 : g.lora_b;
+    const int64_t m = m0 + row, n = n0 + (row & 127);
+    const bool nvalid = (row & 127) < rows_n;
+    uint32_t wa[4], wb[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int ja = j0 + e, jc = ja + 1;
+      uint32_t lo = 0, hi = 0;
+      if (row < rows_m) {
+        if (ja < g.r) lo = g.lora_a[m * g.r + ja];
+        if (jc < g.r) hi = g.lora_a[m * g.r + jc];
+      }
+      wa[e >> 1] = lo | (hi << 16);
+      const int ka = up ? ja - rh : ja, kc = ka + 1;
+      float b0 = 0.f, b1 = 0.f;
+      if (nvalid) {
+        if (ka >= 0 && ka < rh) b0 = bf16_to_f32(Bh[n * rh + ka]);
+        if (kc >= 0 && kc < rh) b1 = bf16_to_f32(Bh[n * rh + kc]);
+      }
+      wb[e >> 1] = pack_bf16x2(sb * b0, sb * b1);
+    }
+    sA[swzf(row, c)] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    sB[swzf(row, c)] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  }
+}
+
 // The kernel body, shared by the plain launch and the grouped (mixture-of-experts) launch. With
 // kGrp, the tiles of every expert follow one another: the workgroup finds its expert e from the
 // first-tile table, takes rows m_off[e] .. m_off[e+1] of X, T and Y, and rows e N .. of the stacked
@@ -148,8 +218,9 @@ __device__ void stage_lora(const GemmArgs &g, float sb, int64_t m0, int64_t n0, 
 // operand is decoded without rounding and S multiplies the accumulators in the epilogue; the
 // LoRA steps stage B times s / S to share the accumulators.
 // kPair: the gate/up pair with its SwiGLU epilogue. The weight is the stacked [Wg; Wu] [2N, K]
-// (N = g.C), B the stacked block-diagonal [2N, 2r]; a tile's 256 columns are gate columns
-// n0 .. n0 + 127 (weight and B rows n0 ..) and the up columns of the same indices (rows N + n0 ..),
+// (N = g.C), the up projection the block-diagonal [[Bg, 0], [0, Bu]] (stage_lora_pair); a tile's
+// 256 columns are gate columns n0 .. n0 + 127 (weight rows n0 .., Bg rows n0 ..) and the up
+// columns of the same indices (weight rows N + n0 .., Bu rows n0 ..),
 // so the epilogue holds Yg and Yu of the same columns: it writes both to g.out ([M, 2N], gate then
 // up) and H = silu(Yg) * Yu, from their float32 sums, to g.hout ([M, N], row stride g.ldh).
 template <int kFmt, bool kGrp, bool kPair = false>
@@ -423,8 +494,8 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
     const int buf = j & 1;
     const int nks = g.r - j * kS > kS / 2 ? 2 : 1;
     if (kPair)
-      stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, n0, rows_n, g.C + n0, rows_n, rows_m, j * kS,
-                 4 * nks, xbuf(buf), wbuf(buf));
+      stage_lora_pair(g, kFP4 ? g.s / tscale() : g.s, m0, n0, rows_n, rows_m, j * kS, 4 * nks,
+                      xbuf(buf), wbuf(buf));
     else
       stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, wn0, rows_n, wn0 + 128, rows_n - 128, rows_m,
                  j * kS, 4 * nks, xbuf(buf), wbuf(buf));
@@ -575,7 +646,8 @@ hipError_t launch_gemm_fwd_grouped(const GemmArgs &g, const GroupArgs &gr, hipSt
 
 hipError_t launch_gemm_fwd_pair(const GemmArgs &g, hipStream_t st) {
   if (((g.C | g.ldo | g.ldh) & 7) != 0 || g.ldo < 2 * g.C || g.ldh < g.C || g.w.n != 2 * g.C ||
-      ((reinterpret_cast<uintptr_t>(g.out) | reinterpret_cast<uintptr_t>(g.hout)) & 15) != 0)
+      ((reinterpret_cast<uintptr_t>(g.out) | reinterpret_cast<uintptr_t>(g.hout)) & 15) != 0 ||
+      (g.r > 0 && ((g.r & 1) != 0 || !g.lora_a || !g.lora_b || !g.lora_b2)))
     return hipErrorInvalidValue;
   const int64_t tiles = ((g.C + kT / 2 - 1) / (kT / 2)) * ((g.M + kT - 1) / kT);
   if (g.w.fp4)

@@ -37,12 +37,15 @@ struct GemmArgs {
   Tables t;
   uint16_t *hout = nullptr;   // gate/up pair only: H [M, C], row stride ldh
   int64_t ldh = 0;
+  const uint16_t *lora_b2 = nullptr;   // gate/up pair only: Bu [C, r / 2] (lora_b is Bg [C, r / 2])
 };
 
 hipError_t launch_gemm_fwd(const GemmArgs &g, hipStream_t st);
-// The gate/up pair with the SwiGLU epilogue: g.w the stacked [Wg; Wu] [2C, K], g.lora_b the
-// block-diagonal [2C, r] (r = 2 r'), g.out Ygu [M, 2C] (row stride ldo), g.hout H = silu(Yg) * Yu
-// [M, C] (row stride ldh), both from the bf16 values of Yg and Yu.
+// The gate/up pair with the SwiGLU epilogue: g.w the stacked [Wg; Wu] [2C, K], g.lora_a T
+// [M, r] (r = 2 r': [X Ag^T | X Au^T]), g.lora_b Bg and g.lora_b2 Bu [C, r'] each (the up
+// projection is the block-diagonal [[Bg, 0], [0, Bu]], applied without storing it), g.out Ygu
+// [M, 2C] (row stride ldo), g.hout H = silu(Yg) * Yu [M, C] (row stride ldh) from the float32
+// sums of Yg and Yu.
 hipError_t launch_gemm_fwd_pair(const GemmArgs &g, hipStream_t st);
 
 // Grouped (mixture-of-experts) forward: E experts, rows m_off[e] .. m_off[e+1] of X, T and Y

@@ -169,11 +169,14 @@ def test_swiglu_pair_full_size(lib):
     check_close("dBu", f32(dBug)[nrows], s * (dYu[:, nrows].T @ Tu))
 
 
-@pytest.mark.parametrize("M,K,N,r", [(300, 1024, 520, 16), (64, 256, 128, 8), (200, 320, 72, 0)])
+@pytest.mark.parametrize("M,K,N,r", [(300, 1024, 520, 16), (64, 256, 128, 8), (200, 320, 72, 0),
+                                     (264, 320, 136, 5)])
 def test_pair_kernel_equals_stacked_layer(lib, M, K, N, r):
     """Above the decode shapes the pair runs as ONE launch of the fused kernel with the activation
-    in its epilogue; its Ygu equals the plain stacked layer (qlora_fwd with [Wg; Wu] and the
-    block-diagonal B) bit for bit, ragged last tiles (N % 128 != 0) included."""
+    in its epilogue, the block-diagonal up projection applied as B is staged; its Ygu equals the
+    plain stacked layer (qlora_fwd with [Wg; Wu] and the block-diagonal B stored) bit for bit,
+    ragged last tiles (N % 128 != 0) and a rank that is not a multiple of 8 (element-wise B
+    staging) included."""
     X, Wgu, Agu, Bg, Bu, _ = rand_pair(M, K, N, r, 300 + M)
     qg = lib.nf4_quantize(Wgu.to(DEV), 256)
     d = lambda t: t.to(DEV) if r else None
@@ -190,3 +193,30 @@ def test_pair_kernel_equals_stacked_layer(lib, M, K, N, r):
         assert torch.equal(Tgu, T2)
     Yg, Yu = f32(Ygu)[:, :N].astype(np.float64), f32(Ygu)[:, N:].astype(np.float64)
     check_close("H from Ygu", f32(H), Yg * swiglu.sigmoid(Yg) * Yu)
+
+
+@pytest.mark.parametrize("M,K,N,r,s", [(300, 1024, 520, 16, 0.5), (200, 320, 72, 5, -1.5),
+                                       (64, 256, 128, 0, 1.0), (9, 512, 264, 8, 2.0)])
+def test_swiglu_fwd_fused_entry(lib, M, K, N, r, s):
+    """qlora_swiglu_fwd_fused (Tgu given, one launch, no workspace) is the launch qlora_swiglu_fwd
+    makes above the decode shapes: the same H and Ygu bit for bit there. On a decode shape (M = 9),
+    where qlora_swiglu_fwd runs the decode kernels, it still runs the pair kernel: H and Ygu
+    against the oracle."""
+    say(f"swiglu fused entry M={M} K={K} N={N} r={r} s={s}")
+    X, Wgu, Agu, Bg, Bu, _ = rand_pair(M, K, N, r, 700 + M)
+    qg = lib.nf4_quantize(Wgu.to(DEV), 256)
+    d = lambda t: t.to(DEV) if r else None
+    H, Ygu, Tgu = lib.qlora_swiglu_fwd(X.to(DEV), qg, d(Agu), d(Bg), d(Bu), s)
+    H2, Y2 = lib.qlora_swiglu_fwd_fused(X.to(DEV), qg, Tgu, d(Bg), d(Bu), s)
+    torch.cuda.synchronize()
+    if not decode_shaped(M, K):
+        assert torch.equal(Y2, Ygu)
+        assert torch.equal(H2, H)
+    qo = nf4.quantize(Wgu.float().numpy(), 256)
+    Wd = nf4.dequantize_f32(qo)
+    f = lambda t: t.float().numpy()
+    Ag, Au = (f(Agu[:r]), f(Agu[r:])) if r else (np.zeros((0, K)), np.zeros((0, K)))
+    Bgo, Buo = (f(Bg), f(Bu)) if r else (np.zeros((N, 0)), np.zeros((N, 0)))
+    Hr, Yg, Yu, _, _ = swiglu.forward(f(X), Wd[:N], Wd[N:], Ag, Au, Bgo, Buo, s)
+    check_close("H", f32(H2), Hr, warn_above=4e-3)
+    check_close("Ygu", f32(Y2), np.concatenate([Yg, Yu], axis=1), warn_above=4e-3)

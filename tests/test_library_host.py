@@ -167,6 +167,18 @@ def test_swiglu_calls_reject_bad_arguments():
     assert fwd(T=ctypes.c_void_p(4100)) == m.NF4_EINVAL
     assert fwd(q=wdesc(n=129, k=128)) == m.NF4_EINVAL         # odd row count: not a stacked pair
     assert fwd(q=wdesc(n=120, k=128)) == m.NF4_EUNSUPPORTED   # n = 60 per projection
+    fused = lambda **kw: lib.qlora_swiglu_fwd_fused(kw.get("X", FAKE), kw.get("m", 100), ctypes.byref(kw.get("q", q)),
+                                                     kw.get("T", FAKE), kw.get("Bg", FAKE), kw.get("Bu", FAKE),
+                                                     kw.get("r", 8), 1.0, kw.get("H", FAKE), kw.get("Y", FAKE), None)
+    assert fused(m=0) == m.NF4_EINVAL
+    assert fused(r=65) == m.NF4_EINVAL
+    assert fused(T=None) == m.NF4_EINVAL        # Tgu is required when r > 0
+    assert fused(Bg=None) == m.NF4_EINVAL
+    assert fused(Bu=ctypes.c_void_p(4100)) == m.NF4_EINVAL
+    assert fused(H=None) == m.NF4_EINVAL
+    assert fused(Y=ctypes.c_void_p(4104)) == m.NF4_EINVAL
+    assert fused(q=wdesc(n=129, k=128)) == m.NF4_EINVAL
+    assert fused(q=wdesc(n=120, k=128)) == m.NF4_EUNSUPPORTED
     bwd = lambda **kw: lib.qlora_swiglu_bwd(kw.get("dH", FAKE), FAKE, 100, ctypes.byref(q), FAKE, FAKE, FAKE,
                                              kw.get("r", 8), 1.0, kw.get("Y", FAKE), kw.get("T", FAKE), FAKE,
                                              kw.get("dA", FAKE), kw.get("dBg", FAKE), FAKE,
