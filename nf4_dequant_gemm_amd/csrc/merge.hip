@@ -3,27 +3,34 @@
 // [pyshine Unsloth code tour, the save.py walkthrough: merged saves, LoRA weights merged layer by
 // layer; NVFP4 update article, "A More Flexible Quantization Export Pipeline"].
 //
-// One workgroup (4 waves) owns a 32 (n) x 128 (k) tile of W'. The rank-r product B A runs on the
-// matrix cores with MFMA 16x16x32 over r (zero-padded to a multiple of 32): A [r, k] is staged in
-// LDS row-major and read with the transposing LDS load ds_read_b64_tr_b16 (each lane receives 4
-// consecutive rows r of one column k, the operand layout with r as the reduction index), B [n, r]
-// is staged row-major and read 16 bytes per lane. The tile's codes (one 16-byte load per thread)
-// and its block constants are staged in LDS as well: loaded per lane, 2 bytes at a time, they
-// made the kernel request-bound (1.35 TB/s). For an E2M1 weight the constants are the tile's E4M3
-// group scales (8 per row), the levels the E2M1 values, and the dequantised element is
-// fl32(fl32(e2m1 * s_g) * S) with S the tensor scale. With A as the first operand, a lane holds 4
-// consecutive columns k of one row n; it adds fl32(level * a') of those 4 elements (codes, block
-// constant and a 16-entry level table from LDS) to s times the fp32 sum, rounds to bf16 and
-// stages the tile in LDS, from which rows leave in 16-byte pieces. The work is the weight stream:
-// 0.52 bytes read and 2 bytes written per element.
+// The work is the weight stream: 0.52 bytes read and 2 bytes written per element, so the kernel
+// is built like a plain streaming pass. A workgroup (4 waves) owns a strip of 128 columns k and
+// stages A [r, those columns] in LDS once; after that each wave works alone, with no barrier, on
+// units of 16 rows x 128 columns: lane (g, l) takes row l of the unit and the 32 consecutive
+// columns 32 g .. 32 g + 31, loads their 16 bytes of codes, their block constant and its 16-byte
+// pieces of B row l directly into registers (the next two units' loads are in flight while a
+// unit is computed and written) and puts its 64 bytes of W' in the wave's own 4 KB of LDS, from
+// which the unit leaves as 4 rows x 256 contiguous bytes per store instruction (straight from the
+// registers, each instruction would write 64 pieces of 16 bytes 64 bytes apart: half the rate).
+// The rank-r product runs on the matrix cores: 8 MFMA 16x16x32 per 32 ranks, B as the second
+// operand (lane: 8 ranks of row l) and A as the first, read from LDS with the transposing load
+// ds_read_b64_tr_b16 (each lane receives 4 consecutive ranks of one column). MFMA m's output rows
+// are mapped to the columns 32 q + 4 m + (0..3), q = 0..3, so that a lane, which receives output
+// rows 4 g .. 4 g + 3 of every MFMA, ends up with the 32 consecutive columns above: A is staged
+// with its 4-column groups permuted accordingly. Per element the lane adds fl32(level * a') (codes
+// and block constant from its registers, the 16 levels from LDS) to s times the float32 sum and
+// rounds once to bf16. For an E2M1 weight the constants are the E4M3 group scales (two per lane),
+// the levels the E2M1 values, and the dequantised element is fl32(fl32(e2m1 * s_g) * S) with S
+// the tensor scale.
 #include "common.h"
 #include "launch.h"
 
 namespace nf4q {
 namespace {
 
-constexpr int kTN = 32, kTK = 128, kThreads = 256;
-constexpr int kNT = kTN / 16;     // 16-row MFMA tiles per workgroup tile
+constexpr int kTK = 128;          // columns of a strip
+constexpr int kUnit = 16;         // rows of a unit
+constexpr int kThreads = 256;
 constexpr int kMaxR = 128;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -35,29 +42,55 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint16_t *p) {
 __device__ __forceinline__ int aunit(int j, int u) {
   return j * kTK + ((u ^ (4 * ((j + 4 * (j >> 3)) & 7))) << 2);
 }
+// LDS place of the strip's 4-column group c (0..31): MFMA m reads places 4 m .. 4 m + 3 as its
+// output rows, which are to be the groups m, m + 8, m + 16, m + 24
+__device__ __forceinline__ int aplace(int c) { return 4 * (c & 7) + (c >> 3); }
 
-template <bool kFP4>
-__global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t *__restrict__ A,
-                                                         const uint16_t *__restrict__ B, int r,
-                                                         float s, Tables t, uint16_t *__restrict__ out) {
-  // LDS sized to the rank (dynamic): the output tile, codes, block constants and levels, then A
-  // (rp rows of 128 columns) and B (32 rows of rp + 8 ranks); 21 KB at r <= 32, seven workgroups
-  // per CU. The kernel is latency-bound (each workgroup loads, computes and stores in turn), so
-  // occupancy sets its rate: on a 4096 x 14336 weight, r = 32, a fixed 128-rank layout with 64-row
-  // tiles (2 workgroups per CU) ran 93 us, rank-sized 64-row tiles 64 us, 32-row tiles 61 us.
+// LDS bytes of the kernel for padded rank rp: the 16 levels, each wave's output unit (16 rows of
+// 256 bytes) and A (rp rows of 128 columns)
+__host__ __device__ constexpr size_t merge_lds_bytes(int rp) {
+  return 64 + 4 * kUnit * kTK * 2 + 2 * (size_t)rp * kTK;
+}
+
+// One unit's inputs as loaded into registers: the lane's 16 bytes of codes, its block constant
+// words (NF4: the int8 code or the float bits, and the run scale; E2M1: the two group-scale
+// bytes) and its kBQ 16-byte pieces of B (ranks 32 q + 8 g .. + 7 of row l); kBQ = rp / 32
+// rounded up to 1, 2 or 4, a template parameter so that the registers in flight are those the
+// rank needs.
+template <int kBQ>
+struct UnitIn {
+  u32x4 c;
+  uint32_t q, sc;
+  u32x4 b[kBQ];
+};
+
+// Waves per SIMD the kernel is built for (its register budget: 128, 168 or 256 VGPRs), by kBQ.
+__host__ __device__ constexpr int merge_occupancy(int bq) { return bq == 1 ? 4 : bq == 2 ? 3 : 2; }
+
+template <bool kFP4, int kBQ>
+__global__ __launch_bounds__(kThreads, merge_occupancy(kBQ)) void merge_kernel(WDesc w, const uint16_t *__restrict__ A,
+                                                            const uint16_t *__restrict__ B, int r, float s,
+                                                            Tables t, uint16_t *__restrict__ out, int per) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int rp = (r + 31) / 32 * 32;
-  const int bstride = rp + 8;
-  uint16_t *sO = reinterpret_cast<uint16_t *>(smem);                    // kTN * kTK bf16
-  uint8_t *sC = smem + kTN * kTK * 2;                                    // kTN * kTK / 2 bytes
-  float *sAbs = reinterpret_cast<float *>(sC + kTN * kTK / 2);          // 2 (NF4) or 8 per row
-  float *sLv = sAbs + kTN * kTK / 16;                                    // 16 levels
-  uint16_t *sA = reinterpret_cast<uint16_t *>(sLv + 16);                 // rp * kTK bf16
-  uint16_t *sB = sA + rp * kTK;                                          // kTN * bstride bf16
+  float *sLv = reinterpret_cast<float *>(smem);                          // 16 levels
+  uint4 *sO = reinterpret_cast<uint4 *>(smem + 64);                      // 4 x 16 rows x 16 pieces
+  uint16_t *sA = reinterpret_cast<uint16_t *>(smem + 64 + 4 * kUnit * kTK * 2);   // rp * kTK bf16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int64_t N = w.n, K = w.k;
-  const int64_t n0 = (int64_t)blockIdx.y * kTN, k0 = (int64_t)blockIdx.x * kTK;
+  const int strips = (int)((K + kTK - 1) / kTK);
+  const int nun = (int)((N + kUnit - 1) / kUnit);
+  // Workgroups are dealt round-robin to the 8 XCDs; each XCD gets a contiguous range of work
+  // items (item = strip + strips * run), so that neighbouring strips, which read the two halves
+  // of the same 128-byte lines of codes, and the strips of one run, which read the same rows of
+  // B, share an L2.
+  const int items = (int)gridDim.x, xcd = (int)blockIdx.x & 7;
+  const int item = xcd * (items >> 3) + (xcd < (items & 7) ? xcd : (items & 7)) + ((int)blockIdx.x >> 3);
+  const int64_t k0 = (int64_t)(item % strips) * kTK;
+  const int ubeg = (item / strips) * per;
+  const int uend = ubeg + per < nun ? ubeg + per : nun;
+
   if (tid < 16) {
     if (kFP4) {   // E2M1 value of code tid: sign bit 3, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
       const int mi = tid & 7;
@@ -68,118 +101,138 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
     }
   }
   const float tsc = kFP4 ? *w.scale : 1.f;
-  // the tile's codes (one 16-byte load per thread of the first 128; rows past N read as zero) and
-  // block constants
-  {
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(w.codes, N * K / 2);
-    const int row = tid >> 2, piece = tid & 3;
-    const int64_t n = n0 + row;
-    const uint32_t off = row < kTN && n < N ? (uint32_t)((n * K + k0) / 2 + 16 * piece) : 0x80000000u;
-    if (row < kTN)
-      *reinterpret_cast<u32x4 *>(sC + row * (kTK / 2) + 16 * piece) =
-          __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
-    if (kFP4) {
-      // 8 group scales per row: thread t takes row t / 8, group t % 8
-      const int64_t bn = n0 + (tid >> 3), bk = k0 + 16 * (tid & 7);
-      sAbs[tid] = (tid < kTN * kTK / 16 && bn < N && bk < K)
-                      ? e4m3_to_f32(reinterpret_cast<const uint8_t *>(w.absmax)[(bn * K + bk) / 16])
-                      : 0.f;
-    } else if (tid < kTN * kTK / 64) {
-      const int64_t bn = n0 + (tid >> 1), bk = k0 + 64 * (tid & 1);
-      sAbs[tid] = (bn < N && bk < K) ? block_absmax(w, (bn * K + bk) / 64) : 0.f;
-    }
-  }
-  // stage A rows 0 .. rp-1, columns k0 .. k0+127 (zero past r and past K) and B rows n0 .. n0+31,
-  // ranks 0 .. rp-1 (zero past r and past N), 16 bytes at a time
+  // A rows 0 .. rp-1 of the strip's columns (zero past r and past K), 16 bytes (two 4-column
+  // groups) at a time, each group at its LDS place
   for (int i = tid; i < rp * (kTK / 8); i += kThreads) {
     const int j = i / (kTK / 8), c = i % (kTK / 8);
     const int64_t k = k0 + 8 * c;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (j < r && k < K) v = *reinterpret_cast<const uint4 *>(A + (int64_t)j * K + k);
-    *reinterpret_cast<uint2 *>(sA + aunit(j, 2 * c)) = make_uint2(v.x, v.y);
-    *reinterpret_cast<uint2 *>(sA + aunit(j, 2 * c + 1)) = make_uint2(v.z, v.w);
+    *reinterpret_cast<uint2 *>(sA + aunit(j, aplace(2 * c))) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2 *>(sA + aunit(j, aplace(2 * c + 1))) = make_uint2(v.z, v.w);
   }
-  for (int i = tid; i < kTN * (rp / 8); i += kThreads) {
-    const int row = i / (rp / 8), c = i % (rp / 8);
-    const int64_t n = n0 + row;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (n < N && 8 * c < r) {
-      // ranks 8c .. 8c+7; r % 8 != 0 leaves a partial last piece, read element by element
-      if (8 * c + 8 <= r && (r & 7) == 0) {
-        v = *reinterpret_cast<const uint4 *>(B + n * r + 8 * c);
+  __syncthreads();
+
+  // Buffer resources: loads past the end of a buffer return zero (rows past N and columns past K
+  // read through out-of-range offsets)
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(w.codes, N * K / 2);
+  const __amdgpu_buffer_rsrc_t rQ =
+      kFP4 ? make_rsrc(w.absmax, N * K / 16) : make_rsrc(w.absmax, w.dq ? N * K / 64 : N * K / 16);
+  const int64_t nruns = (N * (K / 64) + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(w.scale, (!kFP4 && w.dq) ? nruns * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, r > 0 ? N * r * 2 : 0);
+  constexpr uint32_t kOut = 0x80000000u;
+  const int nks = rp / 32;   // 32-rank slices (0 .. kBQ)
+  const bool bvec = (r & 7) == 0;
+  const int64_t kl = k0 + 32 * g16;   // the lane's first column
+  const bool kin = kl < K;            // K % 64 == 0: the lane's 32 columns are all inside or all past K
+
+  auto load = [&](int u, UnitIn<kBQ> &in) {
+    const int64_t n = (int64_t)u * kUnit + l16;
+    const bool ok = n < N && kin;
+    in.c = __builtin_amdgcn_raw_buffer_load_b128(rC, ok ? (uint32_t)((n * K + kl) / 2) : kOut, 0, 0);
+    if (kFP4) {
+      in.q = __builtin_amdgcn_raw_buffer_load_b16(rQ, ok ? (uint32_t)((n * K + kl) / 16) : kOut, 0, 0);
+    } else {
+      const int64_t b = n * (K / 64) + kl / 64;
+      if (w.dq) {
+        in.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, ok ? (uint32_t)b : kOut, 0, 0);
+        in.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, ok ? (uint32_t)((b >> 8) * 4) : kOut, 0, 0);
       } else {
-        uint32_t e[4] = {0, 0, 0, 0};
-        for (int q = 0; q < 8 && 8 * c + q < r; ++q)
-          e[q >> 1] |= (uint32_t)B[n * r + 8 * c + q] << (16 * (q & 1));
-        v = make_uint4(e[0], e[1], e[2], e[3]);
+        in.q = __builtin_amdgcn_raw_buffer_load_b32(rQ, ok ? (uint32_t)(b * 4) : kOut, 0, 0);
       }
     }
-    *reinterpret_cast<uint4 *>(sB + row * bstride + 8 * c) = v;
-  }
-  __syncthreads();
-
-  // wave w: columns 32 w .. 32 w + 31 (2 tiles of 16) x the tile's rows (kNT tiles of 16)
-  f32x4 acc[2][kNT];
+    const uint32_t boff = n < N ? (uint32_t)(n * r * 2) : kOut;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < kNT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int ks = 0; ks < rp / 32; ++ks) {
-    bf16x8 af[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int j = 32 * ks + 8 * g16 + (l16 >> 2);
-      const int u = (32 * wave + 16 * kt) / 4 + (l16 & 3);
-      const s16x4 lo = lds_tr16(sA + aunit(j, u));
-      const s16x4 hi = lds_tr16(sA + aunit(j + 4, u));
-      const short v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      af[kt] = __builtin_bit_cast(bf16x8, v8);
-    }
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const bf16x8 bf = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4 *>(sB + (16 * nt + l16) * bstride + 32 * ks + 8 * g16));
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) acc[kt][nt] = mfma16x16x32(af[kt], bf, acc[kt][nt]);
-    }
-  }
-
-  // lane: row n = n0 + 16 nt + l16, columns k .. k+3 with k = k0 + 32 w + 16 kt + 4 g16
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int row = 16 * nt + l16;
-    const int64_t n = n0 + row;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int kk = 32 * wave + 16 * kt + 4 * g16;
-      const int64_t k = k0 + kk;
-      uint32_t o[2] = {0, 0};
-      if (n < N && k < K) {
-        // codes of k .. k+3 (two bytes, high nibble first) and the constant of their block
-        const uint32_t cw = *reinterpret_cast<const uint16_t *>(sC + row * (kTK / 2) + kk / 2);
-        const float a = kFP4 ? sAbs[8 * row + kk / 16] : sAbs[2 * row + kk / 64];
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t byte = (cw >> (8 * (e >> 1))) & 0xFFu;
-          const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);
-          const float dq = kFP4 ? (sLv[code] * a) * tsc : sLv[code] * a;   // E2M1: inner product exact
-          v[e] = r > 0 ? dq + s * acc[kt][nt][e] : dq;
+    for (int q = 0; q < kBQ; ++q) {
+      if (q < nks) {
+        const int j0 = 32 * q + 8 * g16;   // the piece's first rank
+        if (bvec) {
+          in.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rB, j0 < r ? boff + 2 * j0 : kOut, 0, 0);
+        } else {   // a rank that is not a multiple of 8: element by element
+          uint32_t e[4] = {0, 0, 0, 0};
+          if (n < N)
+            for (int x = 0; x < 8 && j0 + x < r; ++x)
+              e[x >> 1] |= (uint32_t)B[n * r + j0 + x] << (16 * (x & 1));
+          in.b[q] = u32x4{e[0], e[1], e[2], e[3]};
         }
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
       }
-      *reinterpret_cast<uint2 *>(sO + (16 * nt + l16) * kTK + kk) = make_uint2(o[0], o[1]);
     }
+  };
+
+  auto unit = [&](int u, const UnitIn<kBQ> &in) {
+    // the lane's block constant (E2M1: the scales of its two groups of 16)
+    float a0, a1;
+    if (kFP4) {
+      a0 = e4m3_to_f32(in.q & 0xFFu);
+      a1 = e4m3_to_f32((in.q >> 8) & 0xFFu);
+    } else {
+      a0 = a1 = w.dq ? int8_code(in.q) * __uint_as_float(in.sc) : __uint_as_float(in.q);
+    }
+    // Piece p (columns kl + 8 p .. + 7) takes MFMAs 2 p and 2 p + 1 (acc[h][v]: column
+    // kl + 8 p + 4 h + v of row l), then goes through the wave's LDS: 16-byte piece c of row i at
+    // place c ^ i (the 16 rows of a write and the 16 pieces of a row read hit distinct banks).
+    uint4 *ob = sO + wave * (kUnit * 16);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < kBQ; ++ks) {
+        if (ks < nks) {
+          const bf16x8 bf = __builtin_bit_cast(bf16x8, in.b[ks]);
+          const int j = 32 * ks + 8 * g16 + (l16 >> 2);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int pu = 4 * (2 * p + h) + (l16 & 3);
+            const s16x4 lo = lds_tr16(sA + aunit(j, pu));
+            const s16x4 hi = lds_tr16(sA + aunit(j + 4, pu));
+            const short v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[h] = mfma16x16x32(__builtin_bit_cast(bf16x8, v8), bf, acc[h]);
+          }
+        }
+      }
+      uint32_t o[4];
+#pragma unroll
+      for (int x = 0; x < 8; x += 2) {
+        // columns kl + 8 p + x, + 1: code byte 4 p + x / 2, high nibble first
+        const uint32_t byte = (in.c[p] >> (8 * (x >> 1))) & 0xFFu;
+        const float a = p < 2 ? a0 : a1;
+        float v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t code = h ? (byte & 15u) : (byte >> 4);
+          const float dq = kFP4 ? (sLv[code] * a) * tsc : sLv[code] * a;   // E2M1: inner product exact
+          v[h] = r > 0 ? dq + s * acc[(x + h) >> 2][(x + h) & 3] : dq;
+        }
+        o[x >> 1] = pack_bf16x2(v[0], v[1]);
+      }
+      ob[l16 * 16 + ((4 * g16 + p) ^ l16)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    const int c = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (lane >> 4) + 4 * q;
+      const int64_t nr = (int64_t)u * kUnit + row, k = k0 + 8 * c;
+      const uint4 v = ob[row * 16 + (c ^ row)];
+      if (nr < N && k < K)
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(out + nr * K + k));
+    }
+  };
+
+  // wave w takes the units ubeg + w, ubeg + w + 4, ...; two units' loads in flight ahead of the
+  // unit being computed
+  UnitIn<kBQ> in0, in1;
+  int u = ubeg + wave;
+  if (u < uend) load(u, in0);
+  if (u + 4 < uend) load(u + 4, in1);
+#pragma unroll 1
+  for (; u + 4 < uend; u += 8) {
+    unit(u, in0);
+    if (u + 8 < uend) load(u + 8, in0);
+    unit(u + 4, in1);
+    if (u + 12 < uend) load(u + 12, in1);
   }
-  __syncthreads();
-  // rows of the tile leave in 16-byte pieces (K % 64 == 0: a piece is wholly inside or past K)
-  for (int i = tid; i < kTN * (kTK / 8); i += kThreads) {
-    const int row = i / (kTK / 8), c = i % (kTK / 8);
-    const int64_t n = n0 + row, k = k0 + 8 * c;
-    if (n < N && k < K)
-      *reinterpret_cast<uint4 *>(out + n * K + k) = *reinterpret_cast<const uint4 *>(sO + row * kTK + 8 * c);
-  }
+  if (u < uend) unit(u, in0);
 }
 
 }  // namespace
@@ -187,20 +240,30 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(WDesc w, const uint16_t
 hipError_t launch_merge(const WDesc &w, const uint16_t *A, const uint16_t *B, int r, float s,
                         const Tables &t, uint16_t *out, hipStream_t st) {
   if (r < 0 || r > kMaxR || w.k % 64) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((w.k + kTK - 1) / kTK), (unsigned)((w.n + kTN - 1) / kTN));
   const int rp = (r + 31) / 32 * 32;
-  const size_t lds = (size_t)kTN * kTK * 2 + kTN * kTK / 2 + 4 * (kTN * kTK / 16 + 16) +
-                     2 * ((size_t)rp * kTK + (size_t)kTN * (rp + 8));
-  const void *fn = w.fp4 ? reinterpret_cast<const void *>(merge_kernel<true>)
-                         : reinterpret_cast<const void *>(merge_kernel<false>);
-  if (lds > 65536) {   // above the default dynamic-LDS limit: opt in (gfx950 has 160 KB per CU)
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  const size_t lds = merge_lds_bytes(rp);
+  const int bq = rp <= 32 ? 1 : rp <= 64 ? 2 : 4;
+  // Workgroups of a launch: about as many per CU as the kernel's register budget lets run at
+  // once, each column strip's units split into runs of `per`.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int64_t strips = (w.k + kTK - 1) / kTK, nun = (w.n + kUnit - 1) / kUnit;
+  const int64_t runs = std::max<int64_t>(1, std::min<int64_t>((nun + 3) / 4, (int64_t)cus * merge_occupancy(bq) / strips));
+  const int64_t per = (nun + runs - 1) / runs;
+  const int64_t grid = strips * ((nun + per - 1) / per);
+  const dim3 gd((unsigned)grid), bd(kThreads);
+  const int p = (int)per;
+  if (w.fp4) {
+    if (bq == 1) merge_kernel<true, 1><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
+    else if (bq == 2) merge_kernel<true, 2><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
+    else merge_kernel<true, 4><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
+  } else {
+    if (bq == 1) merge_kernel<false, 1><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
+    else if (bq == 2) merge_kernel<false, 2><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
+    else merge_kernel<false, 4><<<gd, bd, lds, st>>>(w, A, B, r, s, t, out, p);
   }
-  if (w.fp4)
-    merge_kernel<true><<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
-  else
-    merge_kernel<false><<<grid, dim3(kThreads), lds, st>>>(w, A, B, r, s, t, out);
   return hipGetLastError();
 }
 
