@@ -331,18 +331,22 @@ struct MoeWs {
 MoeWs moe_ws_layout(int64_t mtotal, int32_t E, int64_t n, int64_t k, int32_t r, bool dev) {
   MoeWs w;
   if (dev) w.table = align256(nf4q::moe_table_bytes(E));
+  // the grouped dX's split tail tiles: at most kDxMaxWidth pieces, and at most kDxMaxPieces per
+  // tile of the launch (row blocks bounded as in moe_groups)
+  const int64_t blocks = std::min<int64_t>((mtotal + 255 * (int64_t)E) / 256, mtotal);
+  const int64_t pieces = std::min<int64_t>(nf4q::kDxMaxWidth, nf4q::kDxMaxPieces * blocks * ((k + 255) / 256));
+  size_t p = (size_t)pieces * nf4q::kDxPieceFloats * 4;
   if (r > 0) {
     const MoePlan pl = moe_plan(mtotal, E, n, k);
     w.u = align256((size_t)mtotal * r * 2);
     w.bt = align256((size_t)r * E * n * 2);
     w.t = w.u;
-    size_t p = 0;
     if (pl.sp_k > 1) p = std::max(p, (size_t)pl.sp_k * mtotal * r * 4);
     if (pl.sp_n > 1) p = std::max(p, (size_t)pl.sp_n * mtotal * r * 4);
     p = std::max(p, (size_t)E * pl.sa * r * k * 4);
     p = std::max(p, (size_t)E * pl.sb * r * n * 4);
-    w.part = align256(p);
   }
+  w.part = align256(p);
   w.total = w.table + w.u + w.bt + w.t + w.part;
   return w;
 }
@@ -931,6 +935,14 @@ int moe_bwd_impl(const void *dY, const void *X, const Moe &mo, int32_t E, const 
     g.out = (uint16_t *)dX;
     g.ldo = k;
     g.t = tables();
+    // split the tiles of a last, partly filled round (one workgroup per CU at a time)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+      gr.width = std::min(cus, nf4q::kDxMaxWidth);
+      gr.smax = nf4q::kDxMaxPieces;
+      gr.part = part;
+    }
     he = nf4q::launch_gemm_dx_grouped(g, gr, sm);
     if (he != hipSuccess) return hip_status(he, "grouped backward dX launch");
   }

@@ -147,6 +147,17 @@ __device__ void stage_lora_dx(const GemmArgs &g, float sa, const uint16_t *A, in
 // scales of 16 (a thread's 32 columns are two groups, each with its own whole table; the operand
 // is exact in bf16) and a float32 tensor scale applied in the epilogue (the LoRA steps stage
 // s / S times A).
+// Origin (m0, k0) of tile `logical` of a group of rows m_lo .. m_hi: tiles in groups of kGroupM
+// row blocks, consecutive logical tiles walking the row blocks of a group first.
+__device__ __forceinline__ void dx_origin(int64_t m_lo, int64_t m_hi, int tiles_k, int logical, int64_t &m0,
+                                          int64_t &k0) {
+  const int tiles_m = (int)((m_hi - m_lo + kT - 1) / kT);
+  const int gsz = kGroupM * tiles_k, grp0 = logical / gsz, gin = logical % gsz;
+  const int gm = tiles_m - grp0 * kGroupM < kGroupM ? tiles_m - grp0 * kGroupM : kGroupM;
+  m0 = m_lo + (int64_t)(grp0 * kGroupM + gin % gm) * kT;
+  k0 = (int64_t)(gin / gm) * kT;
+}
+
 template <int kFmt, bool kGrp>
 __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) {
   constexpr bool kDQ = kFmt == 1, kFP4 = kFmt == 2;
@@ -170,11 +181,25 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   // re-fetched the whole weight from beyond L2 once per row block).
   int logical;
   int64_t m_lo = 0, m_hi = g.M, wbase = 0;
+  const int nsteps = (int)((g.R + kS - 1) / kS);
+  // Grouped launches may split the tiles of a last, partly filled round (dx_split): workgroup
+  // full + tail_i * S + piece runs steps [sbeg, send) of tail tile tail_i and writes its float32
+  // sums to gr.part; a second launch (dx_tail_kernel) adds the pieces.
+  int piece = -1, tail_i = 0;
+  DxSplit sp{0, 0, 1};
   if (kGrp) {
     // a grid sized by an upper bound (routing on the device) has workgroups past the last tile
     const int total = grp_tile_off(gr, gr.E);
-    if ((int)blockIdx.x >= total) return;
-    logical = tile_remap(blockIdx.x, total);
+    sp = dx_split(gr.width, gr.smax, gr.part != nullptr, total, nsteps);
+    const int b = (int)blockIdx.x;
+    if (b >= sp.full + sp.tail * sp.S) return;
+    if (b < sp.full) {
+      logical = tile_remap(b, sp.full);
+    } else {
+      tail_i = (b - sp.full) / sp.S;
+      piece = (b - sp.full) - tail_i * sp.S;
+      logical = sp.full + tail_i;
+    }
     const int e = find_group(gr, logical);
     logical -= grp_tile_off(gr, e);
     m_lo = grp_m_off(gr, e);
@@ -183,16 +208,14 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   } else {
     logical = tile_remap(blockIdx.x, gridDim.x);
   }
-  const int tiles_m = (int)((m_hi - m_lo + kT - 1) / kT);
-  const int gsz = kGroupM * tiles_k, grp0 = logical / gsz, gin = logical % gsz;
-  const int gm = tiles_m - grp0 * kGroupM < kGroupM ? tiles_m - grp0 * kGroupM : kGroupM;
-  const int64_t m0 = m_lo + (int64_t)(grp0 * kGroupM + gin % gm) * kT;
-  const int64_t k0 = (int64_t)(gin / gm) * kT;
+  const int sbeg = piece < 0 ? 0 : piece * nsteps / sp.S;
+  const int send = piece < 0 ? nsteps : (piece + 1) * nsteps / sp.S;
+  int64_t m0, k0;
+  dx_origin(m_lo, m_hi, tiles_k, logical, m0, k0);
   const int64_t K = g.w.k, N = g.R;   // N: the reduction length (one expert's rows of the weight)
   const int64_t rows_m = (m_hi - m0 < kT) ? m_hi - m0 : kT;
   const int kblk = (int)(K / kS);
-  const int nsteps = (int)((N + kS - 1) / kS);
-  const int last = nsteps - 1;
+  const int last = send - 1;
 
   // dY rows m0.. (reduction index n contiguous). Chunks past n = N read the next row's values
   // (finite) and meet weight rows past N, which decode to exact zeros (codes and constants read
@@ -401,23 +424,24 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
   };
 
   CStage c0, c1;
-  dma_y(0, ybuf(0));
-  load_c(0, c0);
-  load_c(nsteps > 1 ? 1 : 0, c1);
+  dma_y(sbeg, ybuf(0));
+  load_c(sbeg, c0);
+  load_c(send - sbeg > 1 ? sbeg + 1 : sbeg, c1);
   decode_all(c0, wbuf(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int s = 0;
+  int s = sbeg;
 #pragma unroll 1
-  for (; s + 2 <= nsteps; s += 2) {
+  for (; s + 2 <= send; s += 2) {
     body(s, 0, c0, c1);
     body(s + 1, 1, c1, c0);
   }
-  if (s < nsteps) body(s, 0, c0, c1);
+  if (s < send) body(s, 0, c0, c1);
   __syncthreads();
 
-  // LoRA steps; a k-slice of 32 rows j that lies wholly past r is skipped.
-  const int nlora = (g.r + kS - 1) / kS;
+  // LoRA steps (a split tile's last piece only); a k-slice of 32 rows j that lies wholly past r
+  // is skipped.
+  const int nlora = piece < sp.S - 1 && piece >= 0 ? 0 : (g.r + kS - 1) / kS;
   const uint16_t *Ae = g.lora_b + (kGrp ? (wbase / g.R) * g.r * K : 0);   // the expert's A
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
@@ -429,6 +453,18 @@ __device__ __forceinline__ void dx_body(const GemmArgs &g, const GroupArgs &gr) 
     mma(ybuf(buf), wbuf(buf), 0);
     if (nks > 1) mma(ybuf(buf), wbuf(buf), 1);
     __syncthreads();
+  }
+
+  // A piece of a split tile: its float32 sums, [wave][k-tile * 8 + m-tile][lane] as f32x4, for
+  // dx_tail_kernel to add.
+  if (kGrp && piece >= 0) {
+    f32x4 *pp = reinterpret_cast<f32x4 *>(gr.part + ((int64_t)tail_i * sp.S + piece) * kDxPieceFloats) +
+                wave * 32 * 64 + lane;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) pp[(kt * 8 + mt) * 64] = acc[kt][mt];
+    return;
   }
 
   // Epilogue. With the weight as the MFMA A operand, a lane holds columns k..k+3 of row m. Each
@@ -474,20 +510,84 @@ __global__ __launch_bounds__(kThreads) void dx_grouped_kernel(GemmArgs g, GroupA
   dx_body<kFmt, true>(g, gr);
 }
 
+// The split tiles of a grouped dX launch: workgroups 4 i .. 4 i + 3 add the S float32 pieces of
+// tail tile i in piece order (a fixed order: the result does not depend on which piece finished
+// first), each a quarter of the tile (8 of the 32 accumulator blocks of every wave), scale E2M1
+// sums by the tensor scale, round to bf16 and write the tile. Workgroups past the tail (a grid
+// sized by an upper bound) exit at once.
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void dx_tail_kernel(GemmArgs g, GroupArgs gr) {
+  const int nsteps = (int)((g.R + kS - 1) / kS);
+  const int total = grp_tile_off(gr, gr.E);
+  const DxSplit sp = dx_split(gr.width, gr.smax, gr.part != nullptr, total, nsteps);
+  const int i = (int)blockIdx.x >> 2, quarter = (int)blockIdx.x & 3;
+  if (i >= sp.tail) return;
+  int logical = sp.full + i;
+  const int e = find_group(gr, logical);
+  logical -= grp_tile_off(gr, e);
+  const int64_t m_lo = grp_m_off(gr, e), m_hi = grp_m_off(gr, e + 1);
+  const int tiles_k = (int)((g.C + kT - 1) / kT);
+  int64_t m0, k0;
+  dx_origin(m_lo, m_hi, tiles_k, logical, m0, k0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wk = wave & 3, g16 = lane >> 4, l16 = lane & 15;
+  float tsc = 1.f;
+  if (kFmt == 2) {
+    const float S = *g.w.scale;
+    tsc = S > 0.f ? S : 1.f;
+  }
+  const f32x4 *pp = reinterpret_cast<const f32x4 *>(gr.part + (int64_t)i * sp.S * kDxPieceFloats) +
+                    wave * 32 * 64 + lane;
+  constexpr int kPiece = kDxPieceFloats / 4;   // f32x4 per piece
+#pragma unroll 4
+  for (int q = 8 * quarter; q < 8 * quarter + 8; ++q) {   // q = k-tile * 8 + m-tile
+    f32x4 a = pp[q * 64];
+    for (int p = 1; p < sp.S; ++p) a += pp[p * kPiece + q * 64];
+    const int kt = q >> 3, mt = q & 7;
+    const int64_t m = m0 + wm * 128 + mt * 16 + l16;
+    const int64_t k = k0 + wk * 64 + kt * 16 + 4 * g16;
+    if (m < m_hi && k < g.C)
+      *reinterpret_cast<uint2 *>(g.out + m * g.ldo + k) =
+          make_uint2(pack_bf16x2(tsc * a[0], tsc * a[1]), pack_bf16x2(tsc * a[2], tsc * a[3]));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st) {
   if (((g.C | g.ldo) & 7) != 0 || (reinterpret_cast<uintptr_t>(g.out) & 15) != 0 || gr.E < 1 ||
-      gr.E > kMaxExperts || g.w.n != (int64_t)gr.E * g.R)
+      gr.E > kMaxExperts || g.w.n != (int64_t)gr.E * g.R || gr.width < 0 || gr.width > kDxMaxWidth ||
+      gr.smax < 1)
     return hipErrorInvalidValue;
-  const int64_t tiles = gr.grid;
-  if (tiles < 1) return hipSuccess;
+  const int nsteps = (int)((g.R + kS - 1) / kS);
+  const bool split = gr.width > 0 && gr.part != nullptr;
+  int64_t grid = gr.grid, tail_grid = 0;
+  if (split) {
+    if (gr.dtile_off) {   // device routing: upper bounds (the split adds fewer than width pieces)
+      grid += gr.width;
+      tail_grid = gr.width;
+    } else {
+      const DxSplit d = dx_split(gr.width, gr.smax, true, gr.tile_off[gr.E], nsteps);
+      grid = d.full + (int64_t)d.tail * d.S;
+      tail_grid = d.tail;
+    }
+  }
+  if (grid < 1) return hipSuccess;
   if (g.w.fp4)
-    dx_grouped_kernel<2><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+    dx_grouped_kernel<2><<<dim3((unsigned)grid), dim3(kThreads), 0, st>>>(g, gr);
   else if (g.w.dq)
-    dx_grouped_kernel<1><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+    dx_grouped_kernel<1><<<dim3((unsigned)grid), dim3(kThreads), 0, st>>>(g, gr);
   else
-    dx_grouped_kernel<0><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(g, gr);
+    dx_grouped_kernel<0><<<dim3((unsigned)grid), dim3(kThreads), 0, st>>>(g, gr);
+  if (tail_grid > 0) {
+    tail_grid *= 4;   // four workgroups per tile
+    if (g.w.fp4)
+      dx_tail_kernel<2><<<dim3((unsigned)tail_grid), dim3(kThreads), 0, st>>>(g, gr);
+    else if (g.w.dq)
+      dx_tail_kernel<1><<<dim3((unsigned)tail_grid), dim3(kThreads), 0, st>>>(g, gr);
+    else
+      dx_tail_kernel<0><<<dim3((unsigned)tail_grid), dim3(kThreads), 0, st>>>(g, gr);
+  }
   return hipGetLastError();
 }
 

@@ -63,7 +63,42 @@ struct GroupArgs {
   const int32_t *dtile_off;     // device table [E + 1], or NULL: tile_off below
   int64_t m_off[kMaxExperts + 1];
   int32_t tile_off[kMaxExperts + 1];
+  // Grouped dX only: the tiles of a last, partly filled round of `width` workgroups (one per CU)
+  // are split along the reduction into up to `smax` pieces that write float32 partial sums to
+  // `part`; a second launch adds them (dx_split below). width 0 or part NULL: no split.
+  int width = 0, smax = 1;
+  float *part = nullptr;
 };
+
+// The split of a grouped dX launch of `total` tiles with `nsteps` reduction steps per tile: the
+// first `full` tiles run whole (whole rounds of `width` workgroups); each of the `tail` others
+// becomes S pieces of consecutive steps (S >= 2, S <= smax, S * tail <= width, S <= nsteps), or
+// none is split (tail 0, S 1). The workgroups of a launch: full + tail * S. Only a tail behind
+// at least one full round is split: a launch of at most one round keeps whole tiles, as the
+// plain dX launch does (a grouped launch with one expert then equals it bit for bit).
+struct DxSplit {
+  int full, tail, S;
+};
+__host__ __device__ inline DxSplit dx_split(int width, int smax, bool enabled, int total, int nsteps) {
+  DxSplit d{total, 0, 1};
+  if (!enabled || width <= 0 || total <= width) return d;
+  const int tail = total % width;
+  if (tail == 0) return d;
+  int S = width / tail;
+  S = S < smax ? S : smax;
+  S = S < nsteps ? S : nsteps;
+  if (S >= 2) {
+    d.full = total - tail;
+    d.tail = tail;
+    d.S = S;
+  }
+  return d;
+}
+// Float32 values of one piece (a 256 x 256 tile); a split launch writes at most width pieces,
+// and width is at most kDxMaxWidth (the workspace is sized for that).
+constexpr int64_t kDxPieceFloats = 256 * 256;
+constexpr int kDxMaxWidth = 256;
+constexpr int kDxMaxPieces = 8;
 // Table entries, for a group index the same in every lane (kept in scalar registers: values
 // derived from it address every tile load).
 __device__ __forceinline__ int64_t grp_m_off(const GroupArgs &g, int e) {
@@ -119,6 +154,9 @@ hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 // dX of every expert in one launch: g.R = N (one expert's rows of the stacked weight, the
 // reduction), g.w.n = E N, g.lora_b = the stacked A [E r, K]; rows of dY, U, dX grouped by
 // expert as gr.m_off says; gr.tile_off[e] = sum over e' < e of ceil(rows_e' / 256) * ceil(K / 256).
+// With gr.width (the workgroups that run at once, <= kDxMaxWidth) and gr.part (kDxMaxWidth *
+// kDxPieceFloats float32) set, the tiles of a last, partly filled round are split along the
+// reduction (dx_split) and a second, small launch adds the pieces.
 hipError_t launch_gemm_dx_grouped(const GemmArgs &g, const GroupArgs &gr, hipStream_t st);
 
 // out[m][j] = sum_l in[m][l] * p[j][l] for j < r (p row-major [r][L], leading dim ldp).

@@ -67,6 +67,7 @@ CASES = [
     (256, 300, 512, 72, 16, 0, -0.5),      # most experts empty or one row
     (8, 700, 320, 264, 32, 256, 2.0),
     (64, 64, 256, 128, 0, 256, 1.0),        # no adapters
+    (8, 7000, 2304, 512, 16, 256, 0.5),     # dX: a round of 256 tiles and a tail split into pieces
 ]
 
 

@@ -129,9 +129,11 @@ def check_step_pipeline(name, seq):
                                                f"the step's DMA group")
 
 
-@pytest.mark.parametrize("src,prefix", [("fwd.hip", "fwd_"), ("dx.hip", "dx_")])
-def test_gemm_step_waits(tmp_path, src, prefix):
-    ks = {k: b for k, b in kernels(device_asm(src, str(tmp_path))).items() if prefix in k}
+@pytest.mark.parametrize("src,pattern", [("fwd.hip", r"fwd_(fused|grouped|pair)_kernel"),
+                                         ("dx.hip", r"dx_(fused|grouped)_kernel")])
+def test_gemm_step_waits(tmp_path, src, pattern):
+    """The pipelined GEMM kernels (not the small tail kernel beside the grouped dX)."""
+    ks = {k: b for k, b in kernels(device_asm(src, str(tmp_path))).items() if re.search(pattern, k)}
     assert len(ks) >= 6
     for name, body in ks.items():
         mls = main_loops(body)
