@@ -287,8 +287,11 @@ int qlora_moe_fwd_fused(const void *X, const int64_t *counts, int32_t E, const n
 /* Backward for dY [sum(counts), n]: dX [sum(counts), k] (skipped when NULL), dA [E r, k] and
  * dB [E n, r], each expert's adapter gradients summed over its own rows (zero for an expert with
  * no rows); T from the forward or NULL (recomputed). dX of every expert comes from ONE launch of
- * the fused dX kernel; U = dY_e B_e is one grouped row projection, dA and dB one grouped
- * M-reduction each (every expert summing over its own rows only).
+ * the fused dX kernel (when its tiles fill at least one round of the GPU's CUs and leave a partly
+ * filled last round, the tiles of that round are split along the reduction into float32 pieces
+ * kept in ws, and a second small launch adds them in a fixed order: results are deterministic
+ * and the same for host and device routing); U = dY_e B_e is one grouped row projection, dA and
+ * dB one grouped M-reduction each (every expert summing over its own rows only).
  * Errors: as qlora_bwd and qlora_moe_fwd. */
 int qlora_moe_bwd(const void *dY, const void *X, const int64_t *counts, int32_t E,
                   const nf4_tensor *W, const void *A, const void *B, int32_t r, float s,
