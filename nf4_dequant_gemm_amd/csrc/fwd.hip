@@ -487,8 +487,13 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
   __syncthreads();
 
   // LoRA steps: [T | s B] as extra reduction steps of the same tile; a k-slice of 32 columns
-  // that lies wholly past r is skipped.
+  // that lies wholly past r is skipped. The pair: when r' = r / 2 is a multiple of 32, every
+  // k-slice holds ranks of one half only (gate: below r'), and the waves of the other half
+  // (waves wn < 2 hold gate columns) skip it: their B there is zero.
   const int nlora = (g.r + kS - 1) / kS;
+  auto pair_skips = [&](int j, int ks) {
+    return kPair && (g.r / 2) % 32 == 0 && ((j * kS + 32 * ks < g.r / 2) != (wn < 2));
+  };
 #pragma unroll 1
   for (int j = 0; j < nlora; ++j) {
     const int buf = j & 1;
@@ -500,8 +505,8 @@ __device__ __forceinline__ void fwd_body(const GemmArgs &g, const GroupArgs &gr)
       stage_lora(g, kFP4 ? g.s / tscale() : g.s, m0, wn0, rows_n, wn0 + 128, rows_n - 128, rows_m,
                  j * kS, 4 * nks, xbuf(buf), wbuf(buf));
     __syncthreads();
-    mma(xbuf(buf), wbuf(buf), 0);
-    if (nks > 1) mma(xbuf(buf), wbuf(buf), 1);
+    if (!pair_skips(j, 0)) mma(xbuf(buf), wbuf(buf), 0);
+    if (nks > 1 && !pair_skips(j, 1)) mma(xbuf(buf), wbuf(buf), 1);
     __syncthreads();
   }
 

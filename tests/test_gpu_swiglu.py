@@ -170,13 +170,14 @@ def test_swiglu_pair_full_size(lib):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(300, 1024, 520, 16), (64, 256, 128, 8), (200, 320, 72, 0),
-                                     (264, 320, 136, 5)])
+                                     (264, 320, 136, 5), (300, 512, 264, 32), (72, 256, 200, 64)])
 def test_pair_kernel_equals_stacked_layer(lib, M, K, N, r):
     """Above the decode shapes the pair runs as ONE launch of the fused kernel with the activation
     in its epilogue, the block-diagonal up projection applied as B is staged; its Ygu equals the
     plain stacked layer (qlora_fwd with [Wg; Wu] and the block-diagonal B stored) bit for bit,
     ragged last tiles (N % 128 != 0) and a rank that is not a multiple of 8 (element-wise B
-    staging) included."""
+    staging) included; with r a multiple of 32 the waves of each half skip the other half's rank
+    slices (all-zero B there) and the result is still the same."""
     X, Wgu, Agu, Bg, Bu, _ = rand_pair(M, K, N, r, 300 + M)
     qg = lib.nf4_quantize(Wgu.to(DEV), 256)
     d = lambda t: t.to(DEV) if r else None
