@@ -68,9 +68,9 @@ struct UnitIn {
 __host__ __device__ constexpr int merge_occupancy(int bq) { return bq == 1 ? 4 : bq == 2 ? 3 : 2; }
 
 template <bool kFP4, int kBQ>
-__global__ __launch_bounds__(kThreads, merge_occupancy(kBQ)) void merge_kernel(WDesc w, const uint16_t *__restrict__ A,
-                                                            const uint16_t *__restrict__ B, int r, float s,
-                                                            Tables t, uint16_t *__restrict__ out, int per) {
+__global__ __launch_bounds__(kThreads, merge_occupancy(kBQ)) void merge_kernel(
+    WDesc w, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int r, float s, Tables t,
+    uint16_t *__restrict__ out, int per) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int rp = (r + 31) / 32 * 32;
   float *sLv = reinterpret_cast<float *>(smem);                          // 16 levels
