@@ -123,8 +123,13 @@ def test_identity_probes_are_exact(lib):
     assert torch.equal(Y16, deq16[:, :16].t().contiguous())
 
 
-def test_moe_with_fp4_experts(lib):
-    counts, K, N, r, s = [40, 0, 300, 7], 512, 72, 16, 1.5
+@pytest.mark.parametrize("counts,K,N,r,s", [
+    ([40, 0, 300, 7], 512, 72, 16, 1.5),
+    # the grouped dX launch has a full round of 256 tiles and a tail it splits into pieces, whose
+    # adding launch applies the tensor scale
+    ([1300, 0, 700, 2000, 900, 1100, 1000, 0], 2304, 264, 16, 0.5),
+])
+def test_moe_with_fp4_experts(lib, counts, K, N, r, s):
     E, M = len(counts), sum(counts)
     X = wl.normal_bf16(11, (M, K), 1.0)
     W = wl.normal_bf16(12, (E * N, K), 0.02)
