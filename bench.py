@@ -28,10 +28,10 @@ rotate over enough distinct copies (>= 512 MB together) that no step finds its w
 Timing, per workload: W warm-up steps, then K steps between two synchronisations (host clock:
 ms_per_step and value), with a HIP event pair on the launch stream around every call of the
 step (phase_ms). The roofline of each workload is that of its dominant fused launch (forward
-and, with a backward, dX; decode: the forward's stream kernel), from its mean duration over
-the timed steps: algorithmic flops (or weight-stream bytes) per launch / mean duration.
-For the decode workload the value is the weight-stream rate of the whole qlora_fwd call
-(weight-stream bytes / call time, the T pre-pass included). cpu_baseline times the CPU oracle
+and, with a backward, dX; decode: the forward's stream kernel, which on this shape is the whole
+qlora_fwd call, T = X A^T included), from its mean duration over the timed steps: algorithmic
+flops (or weight-stream bytes) per launch / mean duration. For the decode workload the value is
+the weight-stream rate of the whole qlora_fwd call (weight-stream bytes / call time). cpu_baseline times the CPU oracle
 (float64) on a bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -68,7 +68,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COLD_BYTES = 512 << 20        # rotate weight copies until they add up to this
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"qlora_fwd_fused": "fwd.hip", "qlora_bwd_dx": "dx.hip",
-                  "qlora_fwd_fused (decode)": "decode16.hip"}
+                  "qlora_fwd (decode)": "decode16.hip", "qlora_fwd_fused (decode)": "decode16.hip"}
 DEFAULT_CONFIGS = ("small", "q_proj", "mlp_up", "decode", "down")
 HEADLINE = "down"
 
@@ -350,6 +350,13 @@ def roofline_hbm(kernel, t_ms, nbytes, workload):
             "traffic": traffic_for(kernel, workload)}
 
 
+def single_launch_decode(w):
+    """qlora_fwd is one launch of the stream kernel (which forms T itself): an NF4 weight with
+    double quantisation, M <= 16, K % 256 == 0, r % 8 == 0 and 8 <= r <= 64."""
+    return (w.fmt == "nf4" and w.dq_block > 0 and w.M <= 16 and w.K % 256 == 0 and w.r % 8 == 0
+            and 8 <= w.r <= 64)
+
+
 def describe(w):
     return (f"{w.name}: X [{w.M},{w.K}] bf16, "
             + (f"W E2M1 [{w.N},{w.K}] E4M3 scale per 16 + fp32 tensor scale, " if w.fmt == "e2m1"
@@ -377,21 +384,27 @@ def run_config(w, dev, args, cpu=True):
         out.update(bound="latency", value=round(step_ms * 1e3, 2), unit="us per fwd+bwd step",
                    higher_is_better=False)
     elif not w.backward:
-        # forward only: the whole qlora_fwd call is the step; its fused launch is timed alone too
-        fwd_only = time_call(L, L.fwd_fused, args.steps, args.warmup)
+        # forward only: the whole qlora_fwd call is the step. Its fused launch is timed alone too;
+        # on the NF4 decode shape (M <= 16, r % 8 == 0, r <= 64) the call is that one launch (the
+        # stream kernel forms T itself), so the call is what is timed.
         if M <= 64:
+            one = single_launch_decode(w)
+            fwd_only = time_call(L, L.fwd_whole if one else L.fwd_fused, args.steps, args.warmup)
             wb = w.weight_stream_bytes()
             gbs = wb / (step_ms * 1e-3) / 1e9
             out.update(bound="hbm", value=round(gbs, 1), unit="GB/s", higher_is_better=True,
                        weight_stream_bytes=wb, frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
-            kernels["qlora_fwd_fused (decode)"] = roofline_hbm("qlora_fwd_fused (decode)", fwd_only, wb, w.name)
+            label = "qlora_fwd (decode)" if one else "qlora_fwd_fused (decode)"
+            kernels[label] = roofline_hbm(label, fwd_only, wb, w.name)
         else:
+            fwd_only = time_call(L, L.fwd_fused, args.steps, args.warmup)
             fl = w.fwd_flops()
             out.update(bound="mfma", value=round(fl / (step_ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
                        higher_is_better=True)
             kernels["qlora_fwd_fused"] = roofline_mfma("qlora_fwd_fused", fwd_only,
                                                        2 * M * N * K + 2 * M * N * r, w.name)
-        out["qlora_fwd_fused_ms"] = {q: round(x, 4) for q, x in fwd_only.items()}
+        out["qlora_fwd_ms" if M <= 64 and single_launch_decode(w) else "qlora_fwd_fused_ms"] = \
+            {q: round(x, 4) for q, x in fwd_only.items()}
     else:
         fl = w.fwd_flops() + w.bwd_flops()
         out.update(bound="mfma", value=round(fl / (step_ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
@@ -869,7 +882,8 @@ def trace_groups(names=DEFAULT_CONFIGS):
         w = wl.WORKLOADS[name]
         cd = lambda a, b: -(-a // b)
         if w.M <= 16 and (w.dq_block or w.fmt == "e2m1") and w.K % 256 == 0:
-            out[("decode16_fwd_kernel", cd(w.N, 112))] = (name, "qlora_fwd_fused (decode)")
+            out[("decode16_fwd_kernel", cd(w.N, 112))] = \
+                (name, "qlora_fwd (decode)" if single_launch_decode(w) else "qlora_fwd_fused (decode)")
         elif w.M > 48 or w.K % 256:
             out[("fwd_fused_kernel", cd(w.N, 256) * cd(w.M, 256))] = (name, "qlora_fwd_fused")
         if w.backward:
@@ -1050,7 +1064,7 @@ def main():
     if len(names) > 1:
         out["configs"] = configs
     else:
-        for k in ("kernels", "context", "qlora_fwd_fused_ms"):
+        for k in ("kernels", "context", "qlora_fwd_fused_ms", "qlora_fwd_ms"):
             if k in h:
                 out[k] = h[k]
     out.update(extra)

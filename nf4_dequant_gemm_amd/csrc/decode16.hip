@@ -25,7 +25,14 @@
 //         Y[m][n] += a(n, b) * sum_{k in block b} X[m][k] * level(code[n][k]);
 //   * wave (g, j) takes block j of every stage for tiles 4g .. 4g + 3 (3 tiles for g = 1), so each
 //     X fragment is read from LDS once per block and serves every tile of the wave; the four
-//     partial sums of a tile meet in LDS at the end.
+//     partial sums of a tile meet in LDS at the end;
+//   * the four 3-tile waves (g = 1) issue every copy; the 4-tile waves (g = 0) issue none, which
+//     leaves their vector-memory counter to loads the compiler tracks. With the adapter A given
+//     (NF4) they form T = X A^T themselves: wave (0, j) multiplies the X fragments of block j it
+//     already holds by A's matching 16-byte pieces, loaded straight into registers two stages
+//     ahead (2 MFMAs per rank tile of 16 and stage), and the four block sums of T meet in LDS at the
+//     end, so the decode forward needs no separate launch for T. (The E2M1 form does not: its
+//     4-tile waves are at the register limit, and the same work cost it 8 us of a 34 us launch.)
 // LDS layouts are XOR-swizzled so the matrix-core reads hit distinct banks; the swizzle is applied
 // on the DMA source side (the DMA writes 1 KB contiguously).
 // Numerics: the NF4 level (not level * a) is rounded to bf16 before the product, as in the other
@@ -47,11 +54,12 @@ constexpr int kSOff = kXOff + 16 * 512;      // run scale of each row's group: 1
 constexpr int kSlotBytes = kSOff + 512;
 constexpr int kQWinBytes = 128 * 16;         // int8 block codes of 4 stages: 128 rows x 16
 constexpr int kTabBytes = 256 * 64 * 4;      // 64 KB
-// Copies (buffer_load ... lds) one wave issues per stage, and the extra one waves 0 and 1 issue in
-// the stages that also fetch a window of block codes. dma() below issues exactly these, and the
-// stage waits are derived from them: a stage waits until only the copies of the two stages after
-// it are in flight.
-constexpr int kStageCopies = 3;
+// Copies (buffer_load ... lds) each of the kDmaWaves copying waves (4..7) issues per stage, and the
+// extra one waves 4 and 5 issue in the stages that also fetch a window of block codes. dma() below
+// issues exactly these, and the stage waits are derived from them: a stage waits until only the
+// copies of the two stages after it are in flight.
+constexpr int kDmaWaves = 4;
+constexpr int kStageCopies = 6;
 constexpr int kWindowCopies = 1;
 constexpr int kPending = 2 * kStageCopies;
 
@@ -67,7 +75,16 @@ struct Dec16Args {
   Tables t;
   const float *tpart;   // T = X A^T as split partials [M][r][tsplits] (NULL: T is given)
   int tsplits;
-  uint16_t *tout;       // with tpart: T (bf16 [M][r]) written by workgroup 0
+  uint16_t *tout;       // with tpart or A: T (bf16 [M][r]) written by workgroup 0
+  const uint16_t *A;    // adapter A [r][K] when the kernel forms T itself (kQ > 0)
+};
+
+// Roles of the two wave groups in the stage loop (see the header comment).
+struct CopyRole {
+  static constexpr bool copies = true;
+};
+struct TRole {
+  static constexpr bool copies = false;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -131,10 +148,13 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
 // elements of a 32-element slice, so a slice holds two groups split by lane half; each group's
 // product is its own MFMA (the X operand masked to that half), times its scale, and the sums are
 // in units of S, which multiplies the tile at the end.
-template <bool kFP4>
+// kQ: rank tiles of 16 of T = X A^T formed in the kernel (0: T given, or added from split
+// partials; NF4 only otherwise).
+template <bool kFP4, int kQ>
 __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
+  static_assert(!kFP4 || kQ == 0, "the E2M1 form takes T given or as split partials");
   // Four stage slots, two windows of block codes and the level-pair table, which holds the
-  // cross-wave sums at the end.
+  // cross-wave sums at the end (and after them the block sums of T).
   constexpr int kSlot = kFP4 ? kSOff + kRows * 16 : kSlotBytes;
   constexpr int kQWin = kFP4 ? 16 : kQWinBytes;
   __shared__ __align__(16) uint8_t slot0[kSlot];
@@ -143,8 +163,11 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   __shared__ __align__(16) uint8_t slot3[kSlot];
   __shared__ __align__(16) uint8_t qwin0[kQWin];
   __shared__ __align__(16) uint8_t qwin1[kQWin];
-  // E2M1: no level table; the area holds only the cross-wave sums (7 tiles x 4 blocks x 1 KB)
-  constexpr int kTab = kFP4 ? kTiles * 4 * 64 * 16 : kTabBytes;
+  // E2M1: no level table; the area holds only the cross-wave sums (7 tiles x 4 blocks x 1 KB).
+  // NF4 with kQ > 0: T's block sums (4 blocks x kQ tiles x 1 KB) follow the cross-wave sums.
+  constexpr int kRed = kTiles * 4 * 64 * 16;
+  constexpr int kTab = kFP4 ? kRed : kTabBytes;
+  static_assert(kRed + 4 * kQ * 64 * 16 <= kTab, "cross-wave sums exceed the table area");
   __shared__ __align__(16) uint32_t stab[kTab / 4];
   auto slot = [&](int i) -> uint8_t * {
     return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3;
@@ -172,27 +195,34 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const i32x4 rS = rsrc_words(g.w.scale + run0, kFP4 ? 0 : (nruns - run0) * 4);
   const i32x4 rX = rsrc_words(g.X, g.M * K * 2);
 
-  // DMA roles, per stage (3 copies per wave): the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7;
-  // lane L -> row 8 i + L / 8, LDS chunk L % 8, which holds the row's 16-byte chunk
-  // (L % 8) ^ ((row / 2) % 8). Wave w copies pieces w and, for w < 6, w + 8. X is 8 pieces,
-  // rows 2 w, 2 w + 1: lane L -> row 2 w + L / 32, LDS chunk L % 32 holding chunk
-  // (L % 32) ^ (row % 16) of the row's 512 bytes; wave w copies piece w. Waves 6, 7 copy the run
-  // scale of the stage's group for rows 64 (w - 6) + L. Once every 4 stages, waves 0, 1 also copy
-  // the int8 codes of the next 4 groups (16 bytes) for rows 64 w + L into a code window.
+  // Copy roles, per stage (6 copies for each of waves 4..7, none for waves 0..3), with w = wave % 4:
+  // the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7: lane L -> row 8 i + L / 8, LDS chunk
+  // L % 8, which holds the row's 16-byte chunk (L % 8) ^ ((row / 2) % 8); wave w copies pieces w,
+  // w + 4, w + 8 and, for w < 2, w + 12. X is 8 pieces, rows 2 i, 2 i + 1: lane L -> row
+  // 2 i + L / 32, LDS chunk L % 32 holding chunk (L % 32) ^ (row % 16) of the row's 512 bytes; wave
+  // w copies pieces w and w + 4. Waves w = 2, 3 copy the run scale of the stage's group for rows
+  // 64 (w - 2) + L. Once every 4 stages, waves w = 0, 1 also copy the int8 codes of the next 4
+  // groups (16 bytes) for rows 64 w + L into a code window. (Used by waves 4..7 only.)
+  const int cw = wave & 3;
   auto code_voff = [&](int i) {
     const int r = 8 * i + (lane >> 3);
     return (uint32_t)(r * (K / 2) + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
   };
-  const uint32_t cvoff0 = code_voff(wave), cvoff1 = code_voff(wave < 6 ? wave + 8 : wave);
-  const int xrow = 2 * wave + (lane >> 5);
-  const uint32_t xvoff = (uint32_t)(xrow * K * 2 + 16 * ((lane & 31) ^ (xrow & 15)));
+  // pieces w + 4 c lie 32 c rows below piece w with the same chunk placement: one lane offset,
+  // 16 K c bytes more in the scalar offset
+  const uint32_t cvoff = code_voff(cw);
+  uint32_t xvoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int xrow = 2 * (cw + 4 * h) + (lane >> 5);
+    xvoff[h] = (uint32_t)(xrow * K * 2 + 16 * ((lane & 31) ^ (xrow & 15)));
+  }
   const int krow = 64 * (wave & 1) + lane;          // row of the block constants copied
   const uint32_t qvoff = (uint32_t)(krow * kblk);
-  // E2M1: waves 6, 7 copy the 16 scale bytes of the stage for rows 64 (w - 6) + L; the lanes of
-  // rows past the 112 (wave 7, lanes 48 ..) copy nothing (their LDS bytes would lie past the slot)
+  // E2M1: waves 2, 3 copy the 16 scale bytes of the stage for rows 64 (w - 2) + L; the lanes of
+  // rows past the 112 (wave 3, lanes 48 ..) copy nothing (their LDS bytes would lie past the slot)
   const uint32_t gvoff = (uint32_t)(krow * (K / 16));
-  const bool gcopy = !kFP4 || wave == 6 || lane < kRows - 64;
-  const uint32_t cdst0 = 1024 * wave, cdst1 = 1024 * (wave + 8), xdst = kXOff + 1024 * wave;
+  const bool gcopy = !kFP4 || cw == 2 || lane < kRows - 64;
   const uint32_t sdst = kSOff + 256 * (wave & 1), qdst = 1024 * (wave & 1);
 
   // Workgroups start at different groups of K (in steps of 4, which keeps the code windows
@@ -201,33 +231,35 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // at 4.1 TB/s in step and 5.0 TB/s staggered).
   const int rot = (nst >= 8 && nst % 4 == 0) ? (int)(blockIdx.x % (unsigned)(nst / 4)) * 4 : 0;
   // Copies of stage st into slot dst (look-ahead past the end re-reads the last stage into a slot
-  // nobody reads any more); with the window flag, waves 8, 9 also copy the block codes of stages
-  // st .. st + 3 into window qw. Stage numbers here are the workgroup's own order; the group of
-  // K they read is rotated by rot.
-  auto dma = [&](int st, uint32_t dst, bool window, uint32_t qw) {
+  // nobody reads any more); with the window flag, waves w = 0, 1 also copy the block codes of
+  // stages st .. st + 3 into window qw. Stage numbers here are the workgroup's own order; the
+  // group of K they read is rotated by rot. Called by waves 4..7 only.
+  auto group_of = [&](int st) {
     st = st < nst ? st : nst - 1;
     st += rot;
-    st = st < nst ? st : st - nst;
-    // kStageCopies copies: codes, X, then codes (waves 0..5) or the run scales (waves 6, 7)
+    return st < nst ? st : st - nst;
+  };
+  auto dma = [&](int st, uint32_t dst, bool window, uint32_t qw) {
+    st = group_of(st);
+    // kStageCopies = 6 copies: codes (3, and a 4th for w = 0, 1), X (2), then the run scales or
+    // E2M1 group scales (w = 2, 3)
 #pragma unroll
-    for (int c = 0; c < kStageCopies; ++c) {
-      if (c == 0) {
-        dma16(rC, dst + cdst0, cvoff0, (uint32_t)(st * 128));
-      } else if (c == 1) {
-        dma16(rX, dst + xdst, xvoff, (uint32_t)(st * 512));
-      } else if (wave < 6) {
-        dma16(rC, dst + cdst1, cvoff1, (uint32_t)(st * 128));
-      } else if (kFP4) {
-        if (gcopy) dma16(rQ, dst + kSOff + 1024 * (wave - 6), gvoff, (uint32_t)(st * 16));
+    for (int c = 0; c < 3; ++c) dma16(rC, dst + 1024 * (cw + 4 * c), cvoff, (uint32_t)(st * 128 + c * 16 * K));
+    if (cw < 2) dma16(rC, dst + 1024 * (cw + 12), cvoff, (uint32_t)(st * 128 + 48 * K));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dma16(rX, dst + kXOff + 1024 * (cw + 4 * h), xvoff[h], (uint32_t)(st * 512));
+    if (cw >= 2) {
+      if constexpr (kFP4) {
+        if (gcopy) dma16(rQ, dst + kSOff + 1024 * (cw - 2), gvoff, (uint32_t)(st * 16));
       } else {
         const uint32_t run = (uint32_t)((boff + krow * kblk + 4 * st) >> 8);
         dma4(rS, dst + sdst, run * 4);
       }
     }
-    // kWindowCopies more: the block codes of stages st .. st + 3 (waves 0, 1; NF4 only)
+    // kWindowCopies more: the block codes of stages st .. st + 3 (w = 0, 1; NF4 only)
 #pragma unroll
     for (int c = 0; c < kWindowCopies; ++c)
-      if (!kFP4 && window && wave < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
+      if (!kFP4 && window && cw < 2) dma16(rQ, qw + qdst, qvoff + 4 * st, 0);
   };
 
   // LoRA operands of the tile this wave finishes (tile 4 g + j below, g = wave / 4,
@@ -241,21 +273,57 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   u32x4 tpre[4], bpre[4];
   {
     // every load is issued (no branch, no register copies that would wait for them); those not
-    // needed read outside the buffers and return zero
+    // needed read outside the buffers and return zero (T is read from LDS at the end when the
+    // kernel forms it)
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.T, lvec && !g.tpart ? g.M * g.r * 2 : 0);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (lvec ? n0 * g.r : 0), lvec ? rows * g.r * 2 : 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j0 = 32 * q + 8 * glf;
       const uint32_t off = j0 < g.r ? 0u : 0x80000000u;   // ranks past r: outside both buffers
-      tpre[q] = __builtin_amdgcn_raw_buffer_load_b128(rT, (uint32_t)((nlf * g.r + j0) * 2) | off, 0, 0);
+      if constexpr (kQ == 0)
+        tpre[q] = __builtin_amdgcn_raw_buffer_load_b128(rT, (uint32_t)((nlf * g.r + j0) * 2) | off, 0, 0);
+      else
+        tpre[q] = u32x4{0u, 0u, 0u, 0u};
       bpre[q] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(((16 * tfin + nlf) * g.r + j0) * 2) | off, 0, 0);
     }
   }
 
-  dma(0, lds_addr(slot0), true, lds_addr(qwin0));
-  dma(1, lds_addr(slot1), false, 0);
-  dma(2, lds_addr(slot2), false, 0);
+  // In-kernel T (kQ > 0, waves 0..3): wave (0, jb) holds, per rank tile q, the pieces of A rows
+  // 16 q + nl that match its X fragments of block jb (the same 8 elements per lane as the weight
+  // operand: 16 gl + 8 h), loaded two stages ahead into abuf[stage % 2] (one stage ahead, the
+  // wait for them measured 2.5 us of a 33 us launch); tacc[q] sums X A^T over the stages for
+  // block jb (lane (nl, gl): T[4 gl + v][16 q + nl]). Ranks past r and rows of X past M read as
+  // zero.
+  const int grp = wave >> 2, jb = wave & 3;
+  const int nl = lane & 15, gl = lane >> 4;
+  f32x4 tacc[kQ > 0 ? kQ : 1];
+  u32x4 abuf[2][kQ > 0 ? kQ : 1][2];
+  uint32_t avoff[kQ > 0 ? kQ : 1];
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A, kQ > 0 ? (int64_t)g.r * K * 2 : 0);
+  auto aload = [&](int st) {
+    const uint32_t soff = (uint32_t)(group_of(st) * 512);
+    const int b = st & 1;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        abuf[b][q][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, avoff[q] + 16u * h, soff, 0);
+  };
+  if constexpr (kQ > 0) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      tacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int64_t j = 16 * q + nl;
+      avoff[q] = (uint32_t)((j * K + 64 * jb + 16 * gl) * 2);
+    }
+  }
+
+  if (grp == 1) {
+    dma(0, lds_addr(slot0), true, lds_addr(qwin0));
+    dma(1, lds_addr(slot1), false, 0);
+    dma(2, lds_addr(slot2), false, 0);
+  }
 
   // Table (NF4): uint4 i holds four copies of entry e = i / 16: (level[e >> 4], level[e & 15]) as
   // a bf16 pair (the high nibble is the earlier element). The 16 levels go through LDS (the start
@@ -280,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // finishing waves take their LoRA operands from LDS. The partial loads wait for the copies
   // issued above too (the compiler does not see those), which costs little: the first stage waits
   // for them anyway.
-  if (g.tpart) {
+  if (kQ == 0 && g.tpart) {
     uint16_t *tl = reinterpret_cast<uint16_t *>(slot3 + 1024);
     const int r = g.r;
     for (int idx = tid; idx < 16 * r; idx += kThreads) {
@@ -324,9 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // (weight row 16 t + nl) and X row, gl = k-group: the lane takes bytes 8 gl .. 8 gl + 7 of the
   // row's block (elements 16 gl .. 16 gl + 15; the first 8 feed MFMA 0, the next 8 MFMA 1) and the
   // same elements of X.
-  const int grp = wave >> 2, jb = wave & 3;
   const int ntiles = grp == 0 ? 4 : kTiles - 4;
-  const int nl = lane & 15, gl = lane >> 4;
   // E2M1: the lane takes bytes 16 h + 4 gl .. + 3 of the block for slice h (elements
   // 32 h + 8 gl .. + 7; lanes gl = 0, 1 hold the slice's first group, gl = 2, 3 its second), the
   // same elements of X, and the block's 4 group scales (saddr).
@@ -349,10 +415,22 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   f32x4 acc[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // T's products for this stage's block jb (waves 0..3 with kQ > 0), after the wave's tiles, from
+  // abuf[tpar] (tpar = stage % 2): the A pieces were loaded two stages ago, and they are the only
+  // vector-memory loads these waves have in flight, so the compiler's wait for them is exact.
+  int tpar = 0;
+  auto tmma = [&](const bf16x8 &x0, const bf16x8 &x1, auto role) {
+    if constexpr (!decltype(role)::copies && kQ > 0) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        tacc[q] = mfma16x16x32(x0, __builtin_bit_cast(bf16x8, abuf[tpar][q][0]), tacc[q]);
+        tacc[q] = mfma16x16x32(x1, __builtin_bit_cast(bf16x8, abuf[tpar][q][1]), tacc[q]);
+      }
+    }
+  };
   // One stage from slot base sb and window base qb (LDS byte addresses).
-  // nt: TileCount<4> or TileCount<3> (E2M1: the wave's tile count as a constant, which keeps the
-  // stage one straight block; NF4 takes it from ntiles)
-  auto consume = [&](uint32_t sb, uint32_t qb, auto nt) {
+  // nt: the wave's tile count as a constant (TileCount<4> for waves 0..3, TileCount<3> for 4..7)
+  auto consume = [&](uint32_t sb, uint32_t qb, auto nt, auto role) {
     const bf16x8 x0 = lds_ld<bf16x8>(sb + xaddr[0]);
     const bf16x8 x1 = lds_ld<bf16x8>(sb + xaddr[1]);
     if constexpr (kFP4) {
@@ -387,11 +465,11 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
           for (int v = 0; v < 4; ++v) acc[tt][v] += sg[q] * pg[v];
         }
       }
+      tmma(x0, x1, role);
       return;
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt == 3 && ntiles == 3) break;
+    for (int tt = 0; tt < decltype(nt)::n; ++tt) {
       const u32x2 cw = lds_ld<u32x2>(sb + caddr[tt]);
       const float a = float(lds_ld<int8_t>(qb + qaddr[tt])) * lds_ld<float>(sb + saddr[tt]);
       uint32_t o[8];
@@ -409,47 +487,71 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[tt][v] += a * part[v];
     }
+    tmma(x0, x1, role);
   };
 
-  // Stage st (slot st % 4, code window st / 4 % 2): wait until this wave's copies of st have
-  // landed (those of st + 1 and st + 2 may stay in flight), barrier (everyone's copies of st have
-  // landed and everyone is done with stage st - 1, whose slot the next copies overwrite), copies
-  // of st + 3, then the stage's MFMAs. The window of stages 4 j .. 4 j + 3 is copied with stage
-  // 4 j (issued in stage 4 j - 3, after window j - 2 was last read in stage 4 j - 5).
-  auto stage = [&](int st, int i, int win, auto nt) {
-    // copies issued in the two stages before st (phases (i + 2) % 4 and (i + 3) % 4 issue the
-    // copies of phases i + 1 and i + 2 = (i + 1) % 4, (i + 2) % 4; the window goes with phase 0)
-    const bool w1 = ((i + 1) & 3) == 0, w2 = ((i + 2) & 3) == 0;
-    if (!kFP4 && (w1 || w2) && wave < 2)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending + kWindowCopies) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
-    const int in = (i + 3) & 3;                      // phase of stage st + 3
-    dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
-    consume(opaque(lds_addr(slot(i))), opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i), nt);  // 4 codes of each row
+  // Stage st (slot st % 4, code window st / 4 % 2). Waves 4..7: wait until this wave's copies of
+  // st have landed (those of st + 1 and st + 2 may stay in flight), barrier (everyone's copies of
+  // st have landed and everyone is done with stage st - 1, whose slot the next copies overwrite),
+  // copies of st + 3, then the stage's MFMAs. Waves 0..3: the barrier, the stage's MFMAs, then
+  // (kQ > 0) the A pieces of stage st + 2 into the buffer the stage has just used. The window of stages 4 j .. 4 j + 3 is copied with
+  // stage 4 j (issued in stage 4 j - 3, after window j - 2 was last read in stage 4 j - 5).
+  auto stage = [&](int st, int i, int win, auto nt, auto role) {
+    const uint32_t sb = opaque(lds_addr(slot(i)));
+    const uint32_t qb = opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i);   // 4 codes of each row
+    if constexpr (decltype(role)::copies) {
+      // copies issued in the two stages before st (phases (i + 2) % 4 and (i + 3) % 4 issue the
+      // copies of phases i + 1 and i + 2 = (i + 1) % 4, (i + 2) % 4; the window goes with phase 0)
+      const bool w1 = ((i + 1) & 3) == 0, w2 = ((i + 2) & 3) == 0;
+      if (!kFP4 && (w1 || w2) && cw < 2)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending + kWindowCopies) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPending) : "memory");
+      const int in = (i + 3) & 3;                      // phase of stage st + 3
+      dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
+      consume(sb, qb, nt, role);
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      tpar = st & 1;
+      consume(sb, qb, nt, role);
+      if constexpr (kQ > 0) aload(st + 2);
+    }
   };
-  int st = 0;
-  if constexpr (kFP4) {   // no code windows: a loop over the four slots, one copy per tile count
-    auto walk = [&](auto nt) {
+  // One stage loop per wave group (each runs nst stages with one barrier each).
+  auto walk = [&](auto role, auto nt) {
+    int st = 0;
+    if constexpr (kFP4) {   // no code windows: a loop over the four slots
 #pragma unroll 1
       for (; st + 4 <= nst; st += 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stage(st + j, j, 0, nt);
+        for (int j = 0; j < 4; ++j) stage(st + j, j, 0, nt, role);
       }
 #pragma unroll
       for (int j = 0; j < 3; ++j)
-        if (st + j < nst) stage(st + j, j, 0, nt);
-    };
-    if (ntiles == 4) walk(TileCount<4>{}); else walk(TileCount<3>{});
-  } else {
+        if (st + j < nst) stage(st + j, j, 0, nt, role);
+    } else {
 #pragma unroll 1
-    for (; st + 8 <= nst; st += 8) {
+      for (; st + 8 <= nst; st += 8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) stage(st + j, j & 3, j >> 2, TileCount<4>{});
+        for (int j = 0; j < 8; ++j) stage(st + j, j & 3, j >> 2, nt, role);
+      }
+#pragma unroll
+      for (int j = 0; j < 7; ++j)
+        if (st + j < nst) stage(st + j, j & 3, j >> 2, nt, role);
     }
-#pragma unroll
-    for (int j = 0; j < 7; ++j)
-      if (st + j < nst) stage(st + j, j & 3, j >> 2, TileCount<4>{});
+  };
+  if (grp == 1) {
+    walk(CopyRole{}, TileCount<3>{});
+  } else {
+    // the first A pieces (stages 0 and 1) here, on this branch only: issued before the branch, the
+    // compiler would count them as possibly in flight on the copying waves' path too and wait for
+    // them there
+    if constexpr (kQ > 0) { aload(0); aload(1); }
+    walk(TRole{}, TileCount<4>{});
+    // the look-ahead A pieces of the last two stages retired here, as the compiler sees it (an
+    // s_waitcnt it emits itself, vmcnt(0)), so that no path into the copying waves' loop carries
+    // loads it would wait for there
+    if constexpr (kQ > 0) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // Every wave past its last stage (and every DMA landed: the look-ahead loads wrote into slots
@@ -460,7 +562,40 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
     if (tt < ntiles) red[((4 * grp + tt) * 4 + jb) * 64 + lane] = acc[tt];
+  // and T's block sums tp[block][rank tile][lane] after them
+  f32x4 *tp = red + kTiles * 4 * 64;
+  if constexpr (kQ > 0) {
+    if (grp == 0) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) tp[(jb * kQ + q) * 64 + lane] = tacc[q];
+    }
+  }
   __syncthreads();
+  if constexpr (kQ > 0) {
+    // T[m][j]: the four block sums added in block order, rounded to bf16, into LDS (slot 0, free
+    // now) for the LoRA term below; workgroup 0 also stores T. Each workgroup sums T in its own
+    // walk order over K; workgroup 0's (rot = 0) is the plain order.
+    uint16_t *tl = reinterpret_cast<uint16_t *>(slot0);
+    const int r = g.r;
+    for (int idx = tid; idx < 16 * r; idx += kThreads) {
+      const int m = idx / r, j = idx - m * r;
+      const int li = (j & 15) + 16 * (m >> 2), q = j >> 4, v = m & 3;
+      float a = tp[q * 64 + li][v];
+#pragma unroll
+      for (int b = 1; b < 4; ++b) a += tp[(b * kQ + q) * 64 + li][v];
+      const uint16_t tb = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFFu);
+      tl[idx] = tb;
+      if (blockIdx.x == 0 && m < g.M) g.tout[idx] = tb;
+    }
+    __syncthreads();
+    if (lvec) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j0 = 32 * q + 8 * glf;
+        tpre[q] = j0 < r ? *reinterpret_cast<const u32x4 *>(tl + nlf * r + j0) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
   const int t = 4 * grp + jb;
   if (t >= kTiles) return;
   const int row = 16 * t + nl;
@@ -522,7 +657,8 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
 
 }  // namespace
 
-hipError_t launch_decode16_fwd(const GemmArgs &ga, hipStream_t st) {
+namespace {
+Dec16Args dec16_args(const GemmArgs &ga) {
   Dec16Args g;
   g.X = ga.a_side;
   g.T = ga.lora_a;
@@ -536,38 +672,51 @@ hipError_t launch_decode16_fwd(const GemmArgs &ga, hipStream_t st) {
   g.tpart = nullptr;
   g.tsplits = 0;
   g.tout = nullptr;
-  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
-  if (ga.w.fp4)
-    decode16_fwd_kernel<true><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
-  else
-    decode16_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+  g.A = nullptr;
+  return g;
+}
+
+template <int kQ>
+hipError_t launch_dec16(const Dec16Args &g, hipStream_t st) {
+  const unsigned grid = (unsigned)((g.w.n + kRows - 1) / kRows);
+  if constexpr (kQ == 0) {
+    if (g.w.fp4) {
+      decode16_fwd_kernel<true, 0><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+      return hipGetLastError();
+    }
+  }
+  decode16_fwd_kernel<false, kQ><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode16_fwd(const GemmArgs &ga, hipStream_t st) {
+  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0) return hipErrorInvalidValue;
+  return launch_dec16<0>(dec16_args(ga), st);
 }
 
 hipError_t launch_decode16_fwd_tpart(const GemmArgs &ga, const float *tpart, int tsplits,
                                      uint16_t *tout, hipStream_t st) {
-  Dec16Args g;
-  g.X = ga.a_side;
-  g.T = ga.lora_a;
-  g.B = ga.lora_b;
-  g.w = ga.w;
-  g.M = ga.M;
-  g.r = ga.r;
-  g.s = ga.s;
-  g.Y = ga.out;
-  g.t = ga.t;
+  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0 || ga.r % 8 != 0 || !tpart || tsplits < 1)
+    return hipErrorInvalidValue;
+  Dec16Args g = dec16_args(ga);
   g.tpart = tpart;
   g.tsplits = tsplits;
   g.tout = tout;
-  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0 || ga.r % 8 != 0 || !tpart || tsplits < 1)
+  return launch_dec16<0>(g, st);
+}
+
+hipError_t launch_decode16_fwd_tin(const GemmArgs &ga, const uint16_t *A, uint16_t *tout, hipStream_t st) {
+  if (ga.M > 16 || !ga.w.dq || ga.w.fp4 || ga.w.k % 256 != 0 || ga.r < 8 || ga.r > kDecode16MaxTinRank ||
+      ga.r % 8 != 0 || !A || !tout)
     return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((ga.w.n + kRows - 1) / kRows);
-  if (ga.w.fp4)
-    decode16_fwd_kernel<true><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
-  else
-    decode16_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
-  return hipGetLastError();
+  Dec16Args g = dec16_args(ga);
+  g.T = nullptr;
+  g.A = A;
+  g.tout = tout;
+  if (ga.r <= 16) return launch_dec16<1>(g, st);
+  if (ga.r <= 32) return launch_dec16<2>(g, st);
+  return launch_dec16<4>(g, st);
 }
 
 }  // namespace nf4q

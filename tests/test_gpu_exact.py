@@ -179,3 +179,53 @@ def test_decode_e2m1_unit_probe(lib, nst, N):
         # products returns as +0
         got, want = nf4.bf16_value(u16(Yg)), nf4.bf16_value(want_full[:, cols].T)
         assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- T and the LoRA term, exactly
+# With an NF4 weight and the adapter A (r % 8 == 0, 8 <= r <= 64) the stream kernel forms
+# T = X A^T from the X slices it streams; with E2M1 qlora_fwd takes T's split partials or the
+# separate row projection. With unit rows of X every entry of T is one product A[j, k_i], exact in
+# any summation order, so T must equal A's probed columns bit for bit; with B the rank selector
+# (B[n, j] = 1 for j = n mod r) and s = 2, output (i, n) is bf16(fl32(base + fl32(2 A[n mod r, k_i])))
+# with base the decode's float32 value (fl32(a' * bf16(level)) for NF4, the E2M1 dequantisation
+# for E2M1), so every workgroup's T shows in its own columns bit for bit, staggered start stages
+# included. Stage counts run around the 8-stage (NF4) and 4-stage (E2M1) loops; ranks cover one,
+# two and four rank tiles of 16.
+LORA_PROBES = [(nst, r, 336 if i % 2 == 0 else 296, fmt)
+               for fmt, stages in (("nf4", STREAM_STAGES), ("e2m1", [1, 2, 3, 4, 5, 7, 8, 9, 12, 17]))
+               for i, (nst, r) in enumerate(zip(stages, [8, 16, 24, 32, 40, 48, 56, 64, 16, 32, 64, 8, 24]))]
+
+
+@pytest.mark.parametrize("nst,r,N,fmt", LORA_PROBES)
+def test_stream_kernel_lora_unit_probe(lib, nst, r, N, fmt):
+    K, M, s = 256 * nst, 16, 2.0
+    say(f"stream-kernel T probe {fmt} stages={nst} K={K} N={N} r={r}")
+    kblk = K // 64
+    if fmt == "nf4":
+        W = probe_weight(N, K, 256, 960 + nst + N + r)
+        qg = lib.nf4_quantize(W.to(DEV), 256)
+        qo = nf4.quantize(W.float().numpy(), 256)
+        lv_bf = nf4.bf16_value(nf4.bf16_bits(nf4.codebook()))
+        codes = nf4.unpack(qo.codes).reshape(N, K)
+        a = nf4.decode_absmax(qo).reshape(N, kblk).astype(np.float32)
+    else:
+        W = wl.normal_bf16(970 + nst + N + r, (N, K), 0.02)
+        qg = lib.fp4_quantize(W.to(DEV))
+        deq = fp4.dequantize_f32(fp4.quantize(W.float().numpy()))
+    A = wl.normal_bf16(980 + nst + r, (r, K), 0.5)
+    B = torch.zeros(N, r, dtype=torch.bfloat16)
+    B[torch.arange(N), torch.arange(N) % r] = 1.0
+    cols = probe_columns(kblk, 1, M)
+    Yg, Tg = lib.qlora_fwd(unit_rows(K, cols).to(DEV), qg, A.to(DEV), B.to(DEV), s)
+    torch.cuda.synchronize()
+    Af = A.float().numpy()
+    assert np.array_equal(u16(Tg), nf4.bf16_bits(Af[:, cols].T.astype(np.float32)))
+    if fmt == "nf4":
+        base = np.stack([(a[:, kk // 64] * lv_bf[codes[:, kk]]).astype(np.float32) for kk in cols])
+    else:
+        base = deq[:, cols].T.astype(np.float32)
+    lora = (np.float32(s) * Af[np.arange(N) % r][:, cols].T).astype(np.float32)
+    want = nf4.bf16_value(nf4.bf16_bits((base + lora).astype(np.float32)))
+    got = nf4.bf16_value(u16(Yg))
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first (row, n) {bad[:4].tolist()}"

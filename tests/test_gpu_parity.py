@@ -309,11 +309,11 @@ def test_bwd_split_matches_bwd(lib):
     check_close("U", f32(U), f32(dY).astype(np.float64) @ f32(B).astype(np.float64))
 
 
-@pytest.mark.parametrize("M,K,N,r", [(16, 8192, 336, 16), (7, 2304, 120, 8), (1, 768, 232, 64)])
+@pytest.mark.parametrize("M,K,N,r", [(16, 2048, 448, 128), (5, 1024, 200, 96)])
 def test_decode_qlora_fwd_matches_two_calls(lib, M, K, N, r):
-    """On decode shapes qlora_fwd adds the split partials of T inside the fused kernel; Y and T
-    equal those of qlora_lora_down followed by qlora_fwd_fused bit for bit (same partials, same
-    summation order), and T matches X A^T from the oracle."""
+    """On decode shapes with r > 64 qlora_fwd adds the split partials of T inside the fused
+    kernel; Y and T equal those of qlora_lora_down followed by qlora_fwd_fused bit for bit (same
+    partials, same summation order), and T matches X A^T from the oracle."""
     s = 2.0
     X, W, A, _, _ = rand_layer(M, K, N, r, seed=M * 7 + K + N)
     B = wl.normal_bf16(M + K + N + 5, (N, r), 0.1)
@@ -328,15 +328,39 @@ def test_decode_qlora_fwd_matches_two_calls(lib, M, K, N, r):
     check_close("T", f32(T1), f32(X).astype(np.float64) @ f32(A).astype(np.float64).T)
 
 
+@pytest.mark.parametrize("M,K,N,r", [(16, 8192, 336, 16), (7, 2304, 120, 8), (1, 768, 232, 64),
+                                     (16, 4096, 1000, 32), (3, 512, 120, 48)])
+def test_decode_qlora_fwd_forms_T(lib, M, K, N, r):
+    """On decode shapes with r <= 64 the stream kernel forms T = X A^T itself (one launch). T and Y
+    match the oracle; where no workgroup's walk over K is rotated (fewer than 8 stages, or a
+    count not a multiple of 4), every workgroup sums T in the same order, so Y equals
+    qlora_fwd_fused given that T bit for bit."""
+    s = 2.0
+    X, W, A, _, _ = rand_layer(M, K, N, r, seed=M * 5 + K + N + r)
+    B = wl.normal_bf16(M + K + N + 6, (N, r), 0.1)
+    qg = lib.nf4_quantize(W.to(DEV), 256)
+    Xd, Ad, Bd = X.to(DEV), A.to(DEV), B.to(DEV)
+    Y1, T1 = lib.qlora_fwd(Xd, qg, Ad, Bd, s)
+    Y2 = lib.qlora_fwd_fused(Xd, qg, T1, Bd, s)
+    torch.cuda.synchronize()
+    nst = K // 256
+    if nst < 8 or nst % 4:
+        assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    qo = nf4.quantize(W.float().numpy(), 256)
+    Yo, To = qlora.forward(f32(X), nf4.dequantize_f32(qo), f32(A), f32(B), s)
+    check_close("T", f32(T1), To)
+    check_close("Y", f32(Y1), Yo)
+
+
 @pytest.mark.parametrize("M,K,N,r", [(200, 512, 264, 16), (16, 2304, 120, 8)])
 def test_bwd_recomputes_missing_T(lib, M, K, N, r):
-    """qlora_bwd with T = NULL recomputes T = X A^T in its workspace: dX, dA and dB equal those of
-    a call given the T of qlora_fwd, bit for bit."""
+    """qlora_bwd with T = NULL recomputes T = X A^T in its workspace by the row projection of
+    qlora_lora_down: dX, dA and dB equal those of a call given that T, bit for bit."""
     s = 0.5
     X, W, A, B, dY = rand_layer(M, K, N, r, seed=M + 3 * K + N)
     qg = lib.nf4_quantize(W.to(DEV), 256)
     Xd, Ad, Bd, dYd = X.to(DEV), A.to(DEV), B.to(DEV), dY.to(DEV)
-    _, T = lib.qlora_fwd(Xd, qg, Ad, Bd, s)
+    T = lib.qlora_lora_down(Xd, Ad)
     g1 = lib.qlora_bwd(dYd, Xd, qg, Ad, Bd, s, T)
     g2 = lib.qlora_bwd(dYd, Xd, qg, Ad, Bd, s, None)
     torch.cuda.synchronize()

@@ -142,22 +142,33 @@ def test_gemm_step_waits(tmp_path, src, pattern):
 
 
 def test_stream_kernel_stage_waits(tmp_path):
+    """The M <= 16 stream kernel (NF4 and E2M1 with T given, NF4 with T formed in the kernel from
+    1, 2 or 4 rank tiles): the copying waves' stage loop holds the hand-issued copies and the hand
+    waits only; the other waves' stage loop issues no copy, and with T formed in the kernel it
+    holds A's loads, which the compiler tracks and waits for itself."""
     src = open(os.path.join(CSRC, "decode16.hip")).read()
     const = {k: int(v) for k, v in re.findall(r"constexpr int (kStageCopies|kWindowCopies) = (\d+);", src)}
     pending = 2 * const["kStageCopies"]
     ks = {k: b for k, b in kernels(device_asm("decode16.hip", str(tmp_path))).items() if "decode16" in k}
-    assert len(ks) == 2, sorted(ks)      # the NF4 (Lb0) and E2M1 (Lb1) instances
+    # NF4 (Lb0) and E2M1 (Lb1) with T given (Li0); NF4 with 1, 2 or 4 rank tiles of T formed
+    assert sorted(re.search(r"ILb([01])ELi(\d)E", k).groups() for k in ks) == \
+        [("0", "0"), ("0", "1"), ("0", "2"), ("0", "4"), ("1", "0")], sorted(ks)
     for name, body in ks.items():
         fp4 = "ILb1E" in name
+        kq = int(re.search(r"ILb[01]ELi(\d)E", name).group(1))
         # the E2M1 form copies no windows of block codes: only the stage count
         allowed = {pending, 0} if fp4 else {pending, pending + const["kWindowCopies"], 0}
-        mls = main_loops(body)
-        # the E2M1 form has one stage loop per tile count of the wave (4 or 3)
-        assert len(mls) == (2 if fp4 else 1), (name, len(mls))
-        for seq in mls:
-            waits = [t for k, t, a in seq if k == "wait"]
-            assert waits and all(a for k, t, a in seq if k == "wait"), f"{name}: compiler waits in the stage loop"
-            assert {vmcnt(t) for t in waits} <= allowed, (name, waits)
-            mem = [t for k, t, a in seq if k == "mem"]
-            assert mem and all(t.endswith(" lds") and a for (k, t, a) in seq if k == "mem"), \
-                f"{name}: the stage loop must hold only the hand-issued copies"
+        ls = loops(body)
+        copying = [seq for seq in ls if any(k == "mem" and t.endswith(" lds") for k, t, a in seq)]
+        assert len(copying) == 1, (name, len(copying))
+        seq = copying[0]
+        waits = [t for k, t, a in seq if k == "wait"]
+        assert waits and all(a for k, t, a in seq if k == "wait"), f"{name}: compiler waits in the copying loop"
+        assert {vmcnt(t) for t in waits} <= allowed, (name, waits)
+        assert all(t.endswith(" lds") and a for (k, t, a) in seq if k == "mem"), \
+            f"{name}: the copying loop must hold only the hand-issued copies"
+        others = [q for q in ls if q is not seq]
+        assert not any(a for q in others for k, t, a in q if k == "mem"), f"{name}: hand-issued loads elsewhere"
+        if kq:
+            tl = [q for q in others if any(k == "mem" and t.startswith("buffer_load_dwordx4") for k, t, a in q)]
+            assert tl, f"{name}: no stage loop loading A"

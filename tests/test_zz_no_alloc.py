@@ -1,7 +1,8 @@
 """qlora_fwd_noalloc (the forward with its scratch in a static per-GPU array) against qlora_fwd
 with a caller workspace: the same kernels and the same split-K partial sums, so Y and T must be
 equal bit for bit. Two calls in a row, the second with a smaller input (the array keeps the first
-call's partial sums), both through the C ABI, then a third larger-row call.
+call's partial sums), both through the C ABI, then a decode shape whose stream kernel forms T
+itself (no scratch) and a larger-row call.
 """
 import ctypes
 
@@ -58,8 +59,11 @@ def run_both(lib, c, M, K, N, r, s, seed):
 
 def test_noalloc_forward_matches_qlora_fwd(lib):
     c = lib.library()
-    # decode shape (T's partial sums added inside the stream kernel), then a smaller one
-    run_both(lib, c, 16, 8192, 2240, 16, 2.0, 1100)
-    run_both(lib, c, 4, 2048, 448, 8, 0.5, 1200)
+    # decode shapes: T's partial sums (in the scratch array) added inside the stream kernel
+    # (r > 64), then a smaller one
+    run_both(lib, c, 16, 2048, 2240, 128, 2.0, 1100)
+    run_both(lib, c, 4, 1024, 448, 96, 0.5, 1200)
+    # a decode shape whose stream kernel forms T itself (no scratch)
+    run_both(lib, c, 16, 8192, 2240, 16, 2.0, 1150)
     # more rows: the separate row projection with its split partials in the scratch array
     run_both(lib, c, 300, 1024, 264, 24, 1.0, 1300)
