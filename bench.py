@@ -351,10 +351,11 @@ def roofline_hbm(kernel, t_ms, nbytes, workload):
 
 
 def single_launch_decode(w):
-    """qlora_fwd is one launch of the stream kernel (which forms T itself): an NF4 weight with
-    double quantisation, M <= 16, K % 256 == 0, r % 8 == 0 and 8 <= r <= 64."""
-    return (w.fmt == "nf4" and w.dq_block > 0 and w.M <= 16 and w.K % 256 == 0 and w.r % 8 == 0
-            and 8 <= w.r <= 64)
+    """qlora_fwd is one launch of the stream kernel (which forms T itself): M <= 16, K % 256 == 0,
+    r % 8 == 0 and 8 <= r <= 64 with a double-quantised NF4 weight, 8 <= r <= 16 with E2M1."""
+    if w.M > 16 or w.K % 256 or w.r % 8 or w.r < 8:
+        return False
+    return w.r <= 16 if w.fmt == "e2m1" else (w.dq_block > 0 and w.r <= 64)
 
 
 def describe(w):

@@ -132,8 +132,9 @@ size_t qlora_fwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
  *      the float32 split-K partial sums of T = X A^T, owned by the caller, free after the call
  * The LoRA term uses T as rounded to bf16 and s*B rounded to bf16 (exact when s is a power of
  * two). Requires m >= 1, n % 8 == 0, 0 <= r <= 128.
- * Decode shapes with a double-quantised NF4 weight (m <= 16, k % 256 == 0), r % 8 == 0 and
- * r <= 64 run as ONE launch that forms T from the X slices it streams, and leave ws untouched.
+ * Decode shapes (m <= 16, k % 256 == 0) with r % 8 == 0 and r <= 64 for a double-quantised NF4
+ * weight, r <= 16 for an E2M1 weight, run as ONE launch that forms T from the X slices it
+ * streams, and leave ws untouched.
  * Each of its workgroups adds T over k in its own order (start points staggered across the
  * workgroups); the T written is that of the workgroup starting at k = 0, and the T another
  * workgroup uses for its columns of Y may differ from it in the last bf16 bit of an entry.

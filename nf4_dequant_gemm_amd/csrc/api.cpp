@@ -529,13 +529,13 @@ int qlora_fwd(const void *X, int64_t m, const nf4_tensor *W, const void *A, cons
   int st = check_layer(X, m, W, A, B, r);
   if (st) return st;
   if (!Y || !aligned16(Y)) return fail(NF4_EINVAL, "Y must be non-NULL and 16-byte aligned");
-  // Decode shapes (the M <= 16 kernel): with an NF4 weight and up to rank 64 the fused kernel
-  // forms T = X A^T itself from the X slices it streams (one launch, no workspace); otherwise the
-  // split partials of T are added inside it (its prologue hides them under the first weight
-  // copies), saving the separate reduction launch. Either way workgroup 0 of the fused kernel
-  // writes T.
+  // Decode shapes (the M <= 16 kernel): up to rank 64 (NF4) or 16 (E2M1) the fused kernel forms
+  // T = X A^T itself from the X slices it streams (one launch, no workspace); otherwise the split
+  // partials of T are added inside it (its prologue hides them under the first weight copies),
+  // saving the separate reduction launch. Either way workgroup 0 of the fused kernel writes T.
   const int64_t k = W->k;
-  if (r > 0 && stream16_shape(m, W) && W->block == 64 && r % 8 == 0 && r <= nf4q::kDecode16MaxTinRank) {
+  const int tin_max = W->block == 16 ? nf4q::kDecode16MaxTinRankE2M1 : nf4q::kDecode16MaxTinRank;
+  if (r > 0 && stream16_shape(m, W) && r % 8 == 0 && r <= tin_max) {
     if (!T || !aligned16(T)) return fail(NF4_EINVAL, "T must be non-NULL and 16-byte aligned");
     nf4q::GemmArgs g;
     g.a_side = (const uint16_t *)X;

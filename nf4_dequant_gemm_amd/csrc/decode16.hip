@@ -31,8 +31,10 @@
 //     (NF4) they form T = X A^T themselves: wave (0, j) multiplies the X fragments of block j it
 //     already holds by A's matching 16-byte pieces, loaded straight into registers two stages
 //     ahead (2 MFMAs per rank tile of 16 and stage), and the four block sums of T meet in LDS at the
-//     end, so the decode forward needs no separate launch for T. (The E2M1 form does not: its
-//     4-tile waves are at the register limit, and the same work cost it 8 us of a 34 us launch.)
+//     end, so the decode forward needs no separate launch for T. The E2M1 form's 4-tile waves are
+//     at the register limit (the same work cost it 8 us of a 34 us launch); it has LDS to spare,
+//     so there (r <= 16) the copying waves also copy A's slice of each stage next to X's, in the
+//     same layout, and form T from LDS with the X fragments they hold.
 // LDS layouts are XOR-swizzled so the matrix-core reads hit distinct banks; the swizzle is applied
 // on the DMA source side (the DMA writes 1 KB contiguously).
 // Numerics: the NF4 level (not level * a) is rounded to bf16 before the product, as in the other
@@ -61,7 +63,8 @@ constexpr int kTabBytes = 256 * 64 * 4;      // 64 KB
 constexpr int kDmaWaves = 4;
 constexpr int kStageCopies = 6;
 constexpr int kWindowCopies = 1;
-constexpr int kPending = 2 * kStageCopies;
+// and, in the E2M1 form that forms T, the pieces of A's slice for the stage
+constexpr int kACopies = 2;
 
 struct Dec16Args {
   const uint16_t *X;
@@ -149,13 +152,19 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
 // product is its own MFMA (the X operand masked to that half), times its scale, and the sums are
 // in units of S, which multiplies the tile at the end.
 // kQ: rank tiles of 16 of T = X A^T formed in the kernel (0: T given, or added from split
-// partials; NF4 only otherwise).
+// partials; E2M1 at most 1).
 template <bool kFP4, int kQ>
 __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
-  static_assert(!kFP4 || kQ == 0, "the E2M1 form takes T given or as split partials");
+  static_assert(!kFP4 || kQ <= 1, "the E2M1 form forms T for r <= 16 only");
+  // E2M1 forming T: A's slice (16 ranks x 256 elements, laid out as X's) follows the group scales
+  // in each slot, copied by the copying waves, which form T
+  constexpr bool kTlds = kFP4 && kQ > 0;
+  constexpr int kAOff = kSOff + kRows * 16;
+  constexpr int kCopies = kStageCopies + (kTlds ? kACopies : 0);   // per copying wave and stage
+  constexpr int kPending = 2 * kCopies;
   // Four stage slots, two windows of block codes and the level-pair table, which holds the
   // cross-wave sums at the end (and after them the block sums of T).
-  constexpr int kSlot = kFP4 ? kSOff + kRows * 16 : kSlotBytes;
+  constexpr int kSlot = kFP4 ? kAOff + (kTlds ? 16 * 512 : 0) : kSlotBytes;
   constexpr int kQWin = kFP4 ? 16 : kQWinBytes;
   __shared__ __align__(16) uint8_t slot0[kSlot];
   __shared__ __align__(16) uint8_t slot1[kSlot];
@@ -164,9 +173,9 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   __shared__ __align__(16) uint8_t qwin0[kQWin];
   __shared__ __align__(16) uint8_t qwin1[kQWin];
   // E2M1: no level table; the area holds only the cross-wave sums (7 tiles x 4 blocks x 1 KB).
-  // NF4 with kQ > 0: T's block sums (4 blocks x kQ tiles x 1 KB) follow the cross-wave sums.
+  // With kQ > 0, T's block sums (4 blocks x kQ tiles x 1 KB) follow the cross-wave sums.
   constexpr int kRed = kTiles * 4 * 64 * 16;
-  constexpr int kTab = kFP4 ? kRed : kTabBytes;
+  constexpr int kTab = kFP4 ? kRed + 4 * kQ * 64 * 16 : kTabBytes;
   static_assert(kRed + 4 * kQ * 64 * 16 <= kTab, "cross-wave sums exceed the table area");
   __shared__ __align__(16) uint32_t stab[kTab / 4];
   auto slot = [&](int i) -> uint8_t * {
@@ -194,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const int64_t nruns = (N * kblk + 255) / 256;
   const i32x4 rS = rsrc_words(g.w.scale + run0, kFP4 ? 0 : (nruns - run0) * 4);
   const i32x4 rX = rsrc_words(g.X, g.M * K * 2);
+  const i32x4 rAw = rsrc_words(g.A, kTlds ? (int64_t)g.r * K * 2 : 0);   // ranks past r read as zero
 
   // Copy roles, per stage (6 copies for each of waves 4..7, none for waves 0..3), with w = wave % 4:
   // the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7: lane L -> row 8 i + L / 8, LDS chunk
@@ -241,13 +251,19 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   };
   auto dma = [&](int st, uint32_t dst, bool window, uint32_t qw) {
     st = group_of(st);
-    // kStageCopies = 6 copies: codes (3, and a 4th for w = 0, 1), X (2), then the run scales or
-    // E2M1 group scales (w = 2, 3)
+    // kStageCopies = 6 copies: codes (3, and a 4th for w = 0, 1), X (2) (and A, kACopies), then the
+    // run scales or E2M1 group scales (w = 2, 3)
 #pragma unroll
     for (int c = 0; c < 3; ++c) dma16(rC, dst + 1024 * (cw + 4 * c), cvoff, (uint32_t)(st * 128 + c * 16 * K));
     if (cw < 2) dma16(rC, dst + 1024 * (cw + 12), cvoff, (uint32_t)(st * 128 + 48 * K));
 #pragma unroll
     for (int h = 0; h < 2; ++h) dma16(rX, dst + kXOff + 1024 * (cw + 4 * h), xvoff[h], (uint32_t)(st * 512));
+    // kACopies more (E2M1 forming T): A's pieces in X's layout (rank rows at X's row offsets)
+    if constexpr (kTlds) {
+#pragma unroll
+      for (int h = 0; h < kACopies; ++h)
+        dma16(rAw, dst + kAOff + 1024 * (cw + 4 * h), xvoff[h], (uint32_t)(st * 512));
+    }
     if (cw >= 2) {
       if constexpr (kFP4) {
         if (gcopy) dma16(rQ, dst + kSOff + 1024 * (cw - 2), gvoff, (uint32_t)(st * 16));
@@ -415,17 +431,24 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   f32x4 acc[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // T's products for this stage's block jb (waves 0..3 with kQ > 0), after the wave's tiles, from
+  // T's products for this stage's block jb, after the wave's tiles. NF4 (waves 0..3): from
   // abuf[tpar] (tpar = stage % 2): the A pieces were loaded two stages ago, and they are the only
   // vector-memory loads these waves have in flight, so the compiler's wait for them is exact.
+  // E2M1 (waves 4..7): from the stage's A slice in LDS, at the X fragments' addresses.
   int tpar = 0;
-  auto tmma = [&](const bf16x8 &x0, const bf16x8 &x1, auto role) {
-    if constexpr (!decltype(role)::copies && kQ > 0) {
+  auto tmma = [&](const bf16x8 &x0, const bf16x8 &x1, uint32_t sb, auto role) {
+    if constexpr (!kFP4 && kQ > 0 && !decltype(role)::copies) {
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
         tacc[q] = mfma16x16x32(x0, __builtin_bit_cast(bf16x8, abuf[tpar][q][0]), tacc[q]);
         tacc[q] = mfma16x16x32(x1, __builtin_bit_cast(bf16x8, abuf[tpar][q][1]), tacc[q]);
       }
+    }
+    if constexpr (kTlds && decltype(role)::copies) {
+      const bf16x8 a0 = lds_ld<bf16x8>(sb + xaddr[0] + (kAOff - kXOff));
+      const bf16x8 a1 = lds_ld<bf16x8>(sb + xaddr[1] + (kAOff - kXOff));
+      tacc[0] = mfma16x16x32(x0, a0, tacc[0]);
+      tacc[0] = mfma16x16x32(x1, a1, tacc[0]);
     }
   };
   // One stage from slot base sb and window base qb (LDS byte addresses).
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
           for (int v = 0; v < 4; ++v) acc[tt][v] += sg[q] * pg[v];
         }
       }
-      tmma(x0, x1, role);
+      tmma(x0, x1, sb, role);
       return;
     }
 #pragma unroll
@@ -487,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[tt][v] += a * part[v];
     }
-    tmma(x0, x1, role);
+    tmma(x0, x1, sb, role);
   };
 
   // Stage st (slot st % 4, code window st / 4 % 2). Waves 4..7: wait until this wave's copies of
@@ -514,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       tpar = st & 1;
       consume(sb, qb, nt, role);
-      if constexpr (kQ > 0) aload(st + 2);
+      if constexpr (!kFP4 && kQ > 0) aload(st + 2);
     }
   };
   // One stage loop per wave group (each runs nst stages with one barrier each).
@@ -546,12 +569,12 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     // the first A pieces (stages 0 and 1) here, on this branch only: issued before the branch, the
     // compiler would count them as possibly in flight on the copying waves' path too and wait for
     // them there
-    if constexpr (kQ > 0) { aload(0); aload(1); }
+    if constexpr (!kFP4 && kQ > 0) { aload(0); aload(1); }
     walk(TRole{}, TileCount<4>{});
     // the look-ahead A pieces of the last two stages retired here, as the compiler sees it (an
     // s_waitcnt it emits itself, vmcnt(0)), so that no path into the copying waves' loop carries
     // loads it would wait for there
-    if constexpr (kQ > 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (!kFP4 && kQ > 0) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // Every wave past its last stage (and every DMA landed: the look-ahead loads wrote into slots
@@ -565,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // and T's block sums tp[block][rank tile][lane] after them
   f32x4 *tp = red + kTiles * 4 * 64;
   if constexpr (kQ > 0) {
-    if (grp == 0) {
+    if (grp == (kFP4 ? 1 : 0)) {   // the waves that formed T
 #pragma unroll
       for (int q = 0; q < kQ; ++q) tp[(jb * kQ + q) * 64 + lane] = tacc[q];
     }
@@ -679,9 +702,9 @@ Dec16Args dec16_args(const GemmArgs &ga) {
 template <int kQ>
 hipError_t launch_dec16(const Dec16Args &g, hipStream_t st) {
   const unsigned grid = (unsigned)((g.w.n + kRows - 1) / kRows);
-  if constexpr (kQ == 0) {
+  if constexpr (kQ <= 1) {
     if (g.w.fp4) {
-      decode16_fwd_kernel<true, 0><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
+      decode16_fwd_kernel<true, kQ><<<dim3(grid), dim3(kThreads), 0, st>>>(g);
       return hipGetLastError();
     }
   }
@@ -707,8 +730,9 @@ hipError_t launch_decode16_fwd_tpart(const GemmArgs &ga, const float *tpart, int
 }
 
 hipError_t launch_decode16_fwd_tin(const GemmArgs &ga, const uint16_t *A, uint16_t *tout, hipStream_t st) {
-  if (ga.M > 16 || !ga.w.dq || ga.w.fp4 || ga.w.k % 256 != 0 || ga.r < 8 || ga.r > kDecode16MaxTinRank ||
-      ga.r % 8 != 0 || !A || !tout)
+  const int maxr = ga.w.fp4 ? kDecode16MaxTinRankE2M1 : kDecode16MaxTinRank;
+  if (ga.M > 16 || !(ga.w.dq || ga.w.fp4) || ga.w.k % 256 != 0 || ga.r < 8 || ga.r > maxr || ga.r % 8 != 0 ||
+      !A || !tout)
     return hipErrorInvalidValue;
   Dec16Args g = dec16_args(ga);
   g.T = nullptr;

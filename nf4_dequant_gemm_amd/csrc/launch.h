@@ -152,9 +152,11 @@ hipError_t launch_decode16_fwd_tpart(const GemmArgs &g, const float *tpart, int 
                                      uint16_t *tout, hipStream_t st);
 // The same with T = X A^T formed inside the launch from A bf16 [r, K] (g.lora_a unused): every
 // workgroup sums T for its own LoRA term and workgroup 0 writes T (bf16 [M][r]) to tout.
-// Requires a double-quantised NF4 weight, r % 8 == 0 and 8 <= r <= kDecode16MaxTinRank.
+// Requires r % 8 == 0 and 8 <= r <= kDecode16MaxTinRank (double-quantised NF4) or
+// kDecode16MaxTinRankE2M1 (E2M1).
 hipError_t launch_decode16_fwd_tin(const GemmArgs &g, const uint16_t *A, uint16_t *tout, hipStream_t st);
 constexpr int kDecode16MaxTinRank = 64;
+constexpr int kDecode16MaxTinRankE2M1 = 16;
 hipError_t launch_gemm_dx(const GemmArgs &g, hipStream_t st);
 // dX of every expert in one launch: g.R = N (one expert's rows of the stacked weight, the
 // reduction), g.w.n = E N, g.lora_b = the stacked A [E r, K]; rows of dY, U, dX grouped by

@@ -182,18 +182,20 @@ def test_decode_e2m1_unit_probe(lib, nst, N):
 
 
 # ---------------------------------------------------------------- T and the LoRA term, exactly
-# With an NF4 weight and the adapter A (r % 8 == 0, 8 <= r <= 64) the stream kernel forms
-# T = X A^T from the X slices it streams; with E2M1 qlora_fwd takes T's split partials or the
-# separate row projection. With unit rows of X every entry of T is one product A[j, k_i], exact in
+# With the adapter A (r % 8 == 0, 8 <= r <= 64 for NF4, r <= 16 for E2M1) the stream kernel
+# forms T = X A^T from the X slices it streams (NF4: A from registers on the 4-tile waves; E2M1:
+# A's slice copied to LDS beside X's by the copying waves); above, qlora_fwd takes T's split
+# partials or the separate row projection. With unit rows of X every entry of T is one product A[j, k_i], exact in
 # any summation order, so T must equal A's probed columns bit for bit; with B the rank selector
 # (B[n, j] = 1 for j = n mod r) and s = 2, output (i, n) is bf16(fl32(base + fl32(2 A[n mod r, k_i])))
 # with base the decode's float32 value (fl32(a' * bf16(level)) for NF4, the E2M1 dequantisation
 # for E2M1), so every workgroup's T shows in its own columns bit for bit, staggered start stages
 # included. Stage counts run around the 8-stage (NF4) and 4-stage (E2M1) loops; ranks cover one,
 # two and four rank tiles of 16.
-LORA_PROBES = [(nst, r, 336 if i % 2 == 0 else 296, fmt)
-               for fmt, stages in (("nf4", STREAM_STAGES), ("e2m1", [1, 2, 3, 4, 5, 7, 8, 9, 12, 17]))
-               for i, (nst, r) in enumerate(zip(stages, [8, 16, 24, 32, 40, 48, 56, 64, 16, 32, 64, 8, 24]))]
+LORA_PROBES = ([(nst, r, 336 if i % 2 == 0 else 296, "nf4")
+                for i, (nst, r) in enumerate(zip(STREAM_STAGES, [8, 16, 24, 32, 40, 48, 56, 64, 16, 32, 64, 8, 24]))]
+               + [(nst, r, 336 if i % 2 == 0 else 296, "e2m1")
+                  for i, (nst, r) in enumerate(zip([1, 2, 3, 4, 5, 7, 8, 9, 12, 17], [8, 16, 24, 16, 8, 48, 16, 8, 16, 64]))])
 
 
 @pytest.mark.parametrize("nst,r,N,fmt", LORA_PROBES)

@@ -142,20 +142,22 @@ def test_gemm_step_waits(tmp_path, src, pattern):
 
 
 def test_stream_kernel_stage_waits(tmp_path):
-    """The M <= 16 stream kernel (NF4 and E2M1 with T given, NF4 with T formed in the kernel from
-    1, 2 or 4 rank tiles): the copying waves' stage loop holds the hand-issued copies and the hand
-    waits only; the other waves' stage loop issues no copy, and with T formed in the kernel it
-    holds A's loads, which the compiler tracks and waits for itself."""
+    """The M <= 16 stream kernel (NF4 and E2M1 with T given; T formed in the kernel, NF4 from 1, 2
+    or 4 rank tiles, E2M1 from 1): the copying waves' stage loop holds the hand-issued copies and
+    the hand waits only (E2M1 forming T: two more copies per stage, A's slice); the other waves'
+    stage loop issues no copy, and with NF4 forming T it holds A's loads, which the compiler
+    tracks and waits for itself."""
     src = open(os.path.join(CSRC, "decode16.hip")).read()
-    const = {k: int(v) for k, v in re.findall(r"constexpr int (kStageCopies|kWindowCopies) = (\d+);", src)}
-    pending = 2 * const["kStageCopies"]
+    const = {k: int(v) for k, v in re.findall(r"constexpr int (kStageCopies|kWindowCopies|kACopies) = (\d+);", src)}
     ks = {k: b for k, b in kernels(device_asm("decode16.hip", str(tmp_path))).items() if "decode16" in k}
-    # NF4 (Lb0) and E2M1 (Lb1) with T given (Li0); NF4 with 1, 2 or 4 rank tiles of T formed
+    # NF4 (Lb0) and E2M1 (Lb1) with T given (Li0); NF4 with 1, 2 or 4 rank tiles of T formed,
+    # E2M1 with 1
     assert sorted(re.search(r"ILb([01])ELi(\d)E", k).groups() for k in ks) == \
-        [("0", "0"), ("0", "1"), ("0", "2"), ("0", "4"), ("1", "0")], sorted(ks)
+        [("0", "0"), ("0", "1"), ("0", "2"), ("0", "4"), ("1", "0"), ("1", "1")], sorted(ks)
     for name, body in ks.items():
         fp4 = "ILb1E" in name
         kq = int(re.search(r"ILb[01]ELi(\d)E", name).group(1))
+        pending = 2 * (const["kStageCopies"] + (const["kACopies"] if fp4 and kq else 0))
         # the E2M1 form copies no windows of block codes: only the stage count
         allowed = {pending, 0} if fp4 else {pending, pending + const["kWindowCopies"], 0}
         ls = loops(body)
@@ -169,6 +171,6 @@ def test_stream_kernel_stage_waits(tmp_path):
             f"{name}: the copying loop must hold only the hand-issued copies"
         others = [q for q in ls if q is not seq]
         assert not any(a for q in others for k, t, a in q if k == "mem"), f"{name}: hand-issued loads elsewhere"
-        if kq:
+        if kq and not fp4:
             tl = [q for q in others if any(k == "mem" and t.startswith("buffer_load_dwordx4") for k, t, a in q)]
             assert tl, f"{name}: no stage loop loading A"
