@@ -305,10 +305,11 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     }
   }
 
-  // In-kernel T (kQ > 0, waves 0..3): wave (0, jb) holds, per rank tile q, the pieces of A rows
-  // 16 q + nl that match its X fragments of block jb (the same 8 elements per lane as the weight
-  // operand: 16 gl + 8 h), loaded two stages ahead into abuf[stage % 2] (one stage ahead, the
-  // wait for them measured 2.5 us of a 33 us launch); tacc[q] sums X A^T over the stages for
+  // In-kernel T (kQ > 0). NF4, waves 0..3: wave (0, jb) holds, per rank tile q, the pieces of A
+  // rows 16 q + nl that match its X fragments of block jb (the same 8 elements per lane as the
+  // weight operand: 16 gl + 8 h), loaded two stages ahead into abuf[stage % 2] (one stage ahead,
+  // the wait for them measured 2.5 us of a 33 us launch). E2M1, waves 4..7: the same pieces from
+  // the stage's A slice in LDS (tmma below). Either way tacc[q] sums X A^T over the stages for
   // block jb (lane (nl, gl): T[4 gl + v][16 q + nl]). Ranks past r and rows of X past M read as
   // zero.
   const int grp = wave >> 2, jb = wave & 3;
