@@ -196,8 +196,8 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int32_t r) {
   w.t = align256((size_t)m * r * 2);
   w.splits_u = nf4q::rowproj_splits(m, n);
   w.splits_t = nf4q::rowproj_splits(m, k);
-  w.splits_a = nf4q::mreduce_splits(m, k);
-  w.splits_b = nf4q::mreduce_splits(m, n);
+  w.splits_a = nf4q::mreduce_splits(m, k, r);
+  w.splits_b = nf4q::mreduce_splits(m, n, r);
   size_t p = 0;
   if (w.splits_u > 1) p = std::max(p, (size_t)w.splits_u * m * r * 4);
   if (w.splits_t > 1) p = std::max(p, (size_t)w.splits_t * m * r * 4);
@@ -299,25 +299,19 @@ int check_moe_dev(const void *X, int64_t m, const int64_t *dcounts, int32_t E, c
 // Launch plan of the grouped layer's rank-r products: the row projections (T = X_e A_e^T,
 // U = dY_e B_e) run over every expert's 64-row blocks in one launch, split over the reduction
 // like the single layer's; the M-reductions (dA_e, dB_e) run over (expert, column tile, split)
-// in one launch, aiming at about 1024 workgroups, each expert's rows cut into that many splits.
-// The split counts depend on the row total only, so the same routing gives the same sums in the
-// same order whether it is given on the host or on the device.
+// in one launch (mreduce_splits over E experts), each expert's rows cut into that many splits. The split counts depend on the row total only, so the same routing
+// gives the same sums in the same order whether it is given on the host or on the device, and
+// one expert gives the single layer's.
 struct MoePlan {
   int sp_k = 1, sp_n = 1, sa = 1, sb = 1;
 };
 
-MoePlan moe_plan(int64_t mtotal, int32_t E, int64_t n, int64_t k) {
+MoePlan moe_plan(int64_t mtotal, int32_t E, int64_t n, int64_t k, int32_t r) {
   MoePlan pl;
   pl.sp_k = nf4q::rowproj_splits(mtotal, k);
   pl.sp_n = nf4q::rowproj_splits(mtotal, n);
-  auto mr = [&](int64_t C) {
-    const int64_t ct = (C + 127) / 128;
-    int64_t sp = (1024 + ct * E - 1) / (ct * E);
-    sp = std::min<int64_t>(sp, std::max<int64_t>(1, (mtotal + 63) / 64));
-    return (int)std::max<int64_t>(sp, 1);
-  };
-  pl.sa = mr(k);
-  pl.sb = mr(n);
+  pl.sa = nf4q::mreduce_splits(mtotal, k, r, E);
+  pl.sb = nf4q::mreduce_splits(mtotal, n, r, E);
   return pl;
 }
 
@@ -337,7 +331,7 @@ MoeWs moe_ws_layout(int64_t mtotal, int32_t E, int64_t n, int64_t k, int32_t r, 
   const int64_t pieces = std::min<int64_t>(nf4q::kDxMaxWidth, nf4q::kDxMaxPieces * blocks * ((k + 255) / 256));
   size_t p = (size_t)pieces * nf4q::kDxPieceFloats * 4;
   if (r > 0) {
-    const MoePlan pl = moe_plan(mtotal, E, n, k);
+    const MoePlan pl = moe_plan(mtotal, E, n, k, r);
     w.u = align256((size_t)mtotal * r * 2);
     w.bt = align256((size_t)r * E * n * 2);
     w.t = w.u;
@@ -882,7 +876,7 @@ int moe_fwd_impl(const void *X, const Moe &mo, int32_t E, const nf4_tensor *W, c
     nf4q::GroupArgs g64;
     st = moe_groups(mo, E, 1, &g64, 64, table, 2);
     if (st) return st;
-    const MoePlan pl = moe_plan(mo.mtotal, E, mo.n, k);
+    const MoePlan pl = moe_plan(mo.mtotal, E, mo.n, k, r);
     he = nf4q::launch_rowproj_grouped((const uint16_t *)X, k, (const uint16_t *)A, (int64_t)r * k, k,
                                       mo.mtotal, k, r, pl.sp_k,
                                       (float *)(base + lay.table + lay.u + lay.bt + lay.t), (uint16_t *)T,
@@ -920,7 +914,7 @@ int moe_bwd_impl(const void *dY, const void *X, const Moe &mo, int32_t E, const 
   // U = dY_e B_e for every expert's rows in one grouped row projection (and T = X_e A_e^T the
   // same way when the caller keeps none), B_e from one transpose of the stacked B: Bt [r, E n],
   // expert e's columns e n .. e n + n - 1
-  const MoePlan pl = moe_plan(mo.mtotal, E, n, k);
+  const MoePlan pl = moe_plan(mo.mtotal, E, n, k, r);
   nf4q::GroupArgs g64;
   st = moe_groups(mo, E, 1, &g64, 64, table, 2);
   if (st) return st;

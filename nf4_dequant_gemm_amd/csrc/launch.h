@@ -180,7 +180,7 @@ int rowproj_splits(int64_t M, int64_t L);
 hipError_t launch_mreduce(const uint16_t *P, const uint16_t *Q, int64_t ldq, int64_t M, int64_t C,
                           int r, float s, int splits, float *part, uint16_t *out,
                           bool transposed_out, hipStream_t st);
-int mreduce_splits(int64_t M, int64_t C);
+int mreduce_splits(int64_t M, int64_t C, int r, int E = 1);
 
 // dst[j][l] = src[l][j] for a bf16 [L][r] matrix.
 hipError_t launch_transpose(const uint16_t *src, int64_t L, int r, uint16_t *dst, hipStream_t st);

@@ -565,9 +565,20 @@ __global__ void mreduce_final_kernel(const float *__restrict__ part, int64_t C, 
   }
 }
 
-int mreduce_splits(int64_t M, int64_t C) {
-  const int64_t ct = (C + kMR_BC - 1) / kMR_BC;
-  int64_t s = (1024 + ct - 1) / ct;
+// Splits of the M-reduction over C / 128 column tiles. One layer: as many as let ONE round of
+// workgroups fill the GPU, so that each workgroup streams the longest run of rows and no partial
+// round trails (measured: the backward's rank-r part of the mlp_up shape 0.153 -> 0.130 ms). A
+// round is the 256 CUs times the workgroups one CU holds, which the LDS staging of a workgroup sets
+// (two 64-row stages of Q and of P: 45-74 KB by the rank): 3 for up to 32 ranks, 2 up to 64, 1
+// above (gfx950, hipcc's resource report). E > 1 experts: about 1024 workgroups, more than a
+// round, since a split covers part of one expert's rows, whose count varies with the routing, and
+// shorter splits keep the largest expert's from setting the time (one round measured 1-3% slower
+// on the grouped backward). One expert gives the single layer's count.
+int mreduce_splits(int64_t M, int64_t C, int r, int E) {
+  const int tj = (r + 15) / 16;
+  const int64_t round = 256 * (tj <= 2 ? 3 : tj <= 4 ? 2 : 1);
+  const int64_t tiles = (C + kMR_BC - 1) / kMR_BC * (E > 0 ? E : 1);
+  int64_t s = E > 1 ? (1024 + tiles - 1) / tiles : round / tiles;
   const int64_t maxs = (M + kMR_BM - 1) / kMR_BM;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
