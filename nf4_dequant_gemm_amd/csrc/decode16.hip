@@ -26,12 +26,14 @@
 //   * wave (g, j) takes block j of every stage for tiles 4g .. 4g + 3 (3 tiles for g = 1), so each
 //     X fragment is read from LDS once per block and serves every tile of the wave; the four
 //     partial sums of a tile meet in LDS at the end;
-//   * the four 3-tile waves (g = 1) issue every copy; the 4-tile waves (g = 0) issue none, which
-//     leaves their vector-memory counter to loads the compiler tracks. With the adapter A given
-//     (NF4) they form T = X A^T themselves: wave (0, j) multiplies the X fragments of block j it
-//     already holds by A's matching 16-byte pieces, loaded straight into registers two stages
-//     ahead (2 MFMAs per rank tile of 16 and stage), and the four block sums of T meet in LDS at the
-//     end, so the decode forward needs no separate launch for T. The E2M1 form's 4-tile waves are
+//   * one group of four waves issues every copy, the other none, which leaves its vector-memory
+//     counter to loads the compiler tracks. With the adapter A given (NF4) the copies go to the
+//     3-tile waves (g = 1) and the 4-tile waves form T = X A^T themselves: wave (0, j) multiplies
+//     the X fragments of block j it already holds by A's matching 16-byte pieces, loaded straight
+//     into registers two stages ahead (2 MFMAs per rank tile of 16 and stage), and the four block
+//     sums of T meet in LDS at the end, so the decode forward needs no separate launch for T.
+//     Without it (T given or as split partials) the NF4 form gives the copies to the 4-tile waves
+//     (measured faster: 28.6-28.9 against 30.3 us on the 28672 x 8192 weight); The E2M1 form's 4-tile waves are
 //     at the register limit (the same work cost it 8 us of a 34 us launch); it has LDS to spare,
 //     so there (r <= 16) the copying waves also copy A's slice of each stage next to X's, in the
 //     same layout, and form T from LDS with the X fragments they hold.
@@ -205,14 +207,15 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   const i32x4 rX = rsrc_words(g.X, g.M * K * 2);
   const i32x4 rAw = rsrc_words(g.A, kTlds ? (int64_t)g.r * K * 2 : 0);   // ranks past r read as zero
 
-  // Copy roles, per stage (6 copies for each of waves 4..7, none for waves 0..3), with w = wave % 4:
+  // Copy roles, per stage (6 copies for each wave of the copying group, none for the other), with
+  // w = wave % 4:
   // the codes are 14 pieces of 1 KB, rows 8 i .. 8 i + 7: lane L -> row 8 i + L / 8, LDS chunk
   // L % 8, which holds the row's 16-byte chunk (L % 8) ^ ((row / 2) % 8); wave w copies pieces w,
   // w + 4, w + 8 and, for w < 2, w + 12. X is 8 pieces, rows 2 i, 2 i + 1: lane L -> row
   // 2 i + L / 32, LDS chunk L % 32 holding chunk (L % 32) ^ (row % 16) of the row's 512 bytes; wave
   // w copies pieces w and w + 4. Waves w = 2, 3 copy the run scale of the stage's group for rows
   // 64 (w - 2) + L. Once every 4 stages, waves w = 0, 1 also copy the int8 codes of the next 4
-  // groups (16 bytes) for rows 64 w + L into a code window. (Used by waves 4..7 only.)
+  // groups (16 bytes) for rows 64 w + L into a code window. (Used by the copying group only.)
   const int cw = wave & 3;
   auto code_voff = [&](int i) {
     const int r = 8 * i + (lane >> 3);
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // Copies of stage st into slot dst (look-ahead past the end re-reads the last stage into a slot
   // nobody reads any more); with the window flag, waves w = 0, 1 also copy the block codes of
   // stages st .. st + 3 into window qw. Stage numbers here are the workgroup's own order; the
-  // group of K they read is rotated by rot. Called by waves 4..7 only.
+  // group of K they read is rotated by rot. Called by the copying group only.
   auto group_of = [&](int st) {
     st = st < nst ? st : nst - 1;
     st += rot;
@@ -313,6 +316,9 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // block jb (lane (nl, gl): T[4 gl + v][16 q + nl]). Ranks past r and rows of X past M read as
   // zero.
   const int grp = wave >> 2, jb = wave & 3;
+  // the copying wave group: the 4-tile waves (0) for NF4 with T given, else the 3-tile waves (1)
+  // (E2M1's 4-tile waves spill with the copies; NF4 forming T costs 3.3 us on the 3-tile waves)
+  constexpr int kCopyGrp = (!kFP4 && kQ == 0) ? 0 : 1;
   const int nl = lane & 15, gl = lane >> 4;
   f32x4 tacc[kQ > 0 ? kQ : 1];
   u32x4 abuf[2][kQ > 0 ? kQ : 1][2];
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     }
   }
 
-  if (grp == 1) {
+  if (grp == kCopyGrp) {
     dma(0, lds_addr(slot0), true, lds_addr(qwin0));
     dma(1, lds_addr(slot1), false, 0);
     dma(2, lds_addr(slot2), false, 0);
@@ -514,12 +520,13 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
     tmma(x0, x1, sb, role);
   };
 
-  // Stage st (slot st % 4, code window st / 4 % 2). Waves 4..7: wait until this wave's copies of
-  // st have landed (those of st + 1 and st + 2 may stay in flight), barrier (everyone's copies of
-  // st have landed and everyone is done with stage st - 1, whose slot the next copies overwrite),
-  // copies of st + 3, then the stage's MFMAs. Waves 0..3: the barrier, the stage's MFMAs, then
-  // (kQ > 0) the A pieces of stage st + 2 into the buffer the stage has just used. The window of stages 4 j .. 4 j + 3 is copied with
-  // stage 4 j (issued in stage 4 j - 3, after window j - 2 was last read in stage 4 j - 5).
+  // Stage st (slot st % 4, code window st / 4 % 2). The copying group: wait until this wave's
+  // copies of st have landed (those of st + 1 and st + 2 may stay in flight), barrier (everyone's
+  // copies of st have landed and everyone is done with stage st - 1, whose slot the next copies
+  // overwrite), copies of st + 3, then the stage's MFMAs. The other group: the barrier, the
+  // stage's MFMAs, then (NF4, kQ > 0) the A pieces of stage st + 2 into the buffer the stage has
+  // just used. The window of stages 4 j .. 4 j + 3 is copied with stage 4 j (issued in stage
+  // 4 j - 3, after window j - 2 was last read in stage 4 j - 5).
   auto stage = [&](int st, int i, int win, auto nt, auto role) {
     const uint32_t sb = opaque(lds_addr(slot(i)));
     const uint32_t qb = opaque(lds_addr(win ? qwin1 : qwin0) + 4 * i);   // 4 codes of each row
@@ -564,14 +571,14 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
         if (st + j < nst) stage(st + j, j & 3, j >> 2, nt, role);
     }
   };
-  if (grp == 1) {
-    walk(CopyRole{}, TileCount<3>{});
+  if (grp == kCopyGrp) {
+    if constexpr (kCopyGrp == 0) walk(CopyRole{}, TileCount<4>{}); else walk(CopyRole{}, TileCount<3>{});
   } else {
     // the first A pieces (stages 0 and 1) here, on this branch only: issued before the branch, the
     // compiler would count them as possibly in flight on the copying waves' path too and wait for
     // them there
     if constexpr (!kFP4 && kQ > 0) { aload(0); aload(1); }
-    walk(TRole{}, TileCount<4>{});
+    if constexpr (kCopyGrp == 0) walk(TRole{}, TileCount<3>{}); else walk(TRole{}, TileCount<4>{});
     // the look-ahead A pieces of the last two stages retired here, as the compiler sees it (an
     // s_waitcnt it emits itself, vmcnt(0)), so that no path into the copying waves' loop carries
     // loads it would wait for there
