@@ -319,6 +319,11 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
   // the copying wave group: the 4-tile waves (0) for NF4 with T given, else the 3-tile waves (1)
   // (E2M1's 4-tile waves spill with the copies; NF4 forming T costs 3.3 us on the 3-tile waves)
   constexpr int kCopyGrp = (!kFP4 && kQ == 0) ? 0 : 1;
+  // Each stage's instructions kept in the stage (the compiler otherwise moves MFMAs of one stage
+  // past the next stage's barrier): measured faster in these two forms (NF4 with T given 28.3-28.6
+  // against 28.7-28.8 us, E2M1 forming T 35.5 against 36.4 us), slower in E2M1 with T given (34.0
+  // against 33.2-33.6 us) and equal in NF4 forming T.
+  constexpr bool kPin = (!kFP4 && kQ == 0) || kTlds;
   const int nl = lane & 15, gl = lane >> 4;
   f32x4 tacc[kQ > 0 ? kQ : 1];
   u32x4 abuf[2][kQ > 0 ? kQ : 1][2];
@@ -541,11 +546,13 @@ __global__ __launch_bounds__(kThreads) void decode16_fwd_kernel(Dec16Args g) {
       const int in = (i + 3) & 3;                      // phase of stage st + 3
       dma(st + 3, lds_addr(slot(in)), in == 0, lds_addr(win ? qwin0 : qwin1));
       consume(sb, qb, nt, role);
+      if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
     } else {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       tpar = st & 1;
       consume(sb, qb, nt, role);
       if constexpr (!kFP4 && kQ > 0) aload(st + 2);
+      if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
     }
   };
   // One stage loop per wave group (each runs nst stages with one barrier each).
